@@ -1,0 +1,291 @@
+// Row set-up, embedding gather, RMSNorm, RoPE with the paged KV write, the
+// softmax passes of the LM head, small device scatters and KV import / export.
+//
+// The decoder reading (pre-norm RMSNorm, rotate-half RoPE, grouped-query heads)
+// is the plain Qwen3-8B-shaped one; the pages fix only that draft and verify
+// share one KV cache (shibing624 reading notes of the Uno paper, method core).
+#include "uno_internal.h"
+
+namespace {
+
+__device__ float block_sum_256(float v, float* sh) {
+  // wave64 reduction, then the 4 wave totals in a fixed order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+
+__global__ void k_rows_setup(RowsSetup a) {
+  const int R = a.n * a.rows_per_seq;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int i = r / a.rows_per_seq, j = r % a.rows_per_seq;
+  const int sid = a.call_seq[i];
+  const int n = a.len ? a.len[sid] : 0;
+  int tok = 0, pos = 0;
+  uint8_t g = 0;
+  switch (a.mode) {
+    case 0:  // draft: [t, MASK x (B-1)] at n..n+B-1, gate [0, 1, ..., 1]
+      tok = (j == 0) ? a.pending[sid] : a.mask_id;
+      pos = n + j;
+      g = (j > 0) ? 1 : 0;
+      break;
+    case 1:  // verify: [y_1..y_B] at n+1..n+B, gate 0
+      tok = a.draft_tok[(size_t)i * a.B + j];
+      pos = n + 1 + j;
+      g = 0;
+      break;
+    case 2:  // caller rows
+      tok = a.in_tok ? a.in_tok[r] : 0;
+      pos = a.in_pos[r];
+      g = a.in_gate[r];
+      break;
+    default:  // prefill rows of one sequence
+      tok = a.in_tok[r];
+      pos = a.pos0 + r;
+      g = 0;
+      break;
+  }
+  a.row_tok[r] = tok;
+  a.row_pos[r] = pos;
+  a.row_gate[r] = g;
+  if (j == 0 && a.call_n) {
+    a.call_n[i] = n;
+    a.call_it[i] = a.iter ? a.iter[sid] : 0;
+  }
+}
+
+template <typename T>
+__global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
+                        const float* __restrict__ hidden_in, int d, int V, float* x,
+                        int32_t* err) {
+  const int r = blockIdx.x;
+  float* xr = x + (size_t)r * d;
+  if (hidden_in) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = hidden_in[(size_t)r * d + c];
+    return;
+  }
+  int t = tok[r];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0 && err) atomicOr(err, UNO_DEVERR_NUMERIC);
+    t = 0;
+  }
+  const T* er = E + (size_t)t * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = to_f(er[c]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, int d, float eps, T* out) {
+  __shared__ float sh[4];
+  const int r = blockIdx.x;
+  const float* xr = x + (size_t)r * d;
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
+  ss = block_sum_256(ss, sh);
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    out[(size_t)r * d + c] = from_f<T>(xr[c] * rs * to_f(g[c]));
+}
+
+template <typename T>
+__device__ T* kv_slot(const KvLayout& kv, int layer, int which, int seq, int pos, int h,
+                      int32_t* err) {
+  const int pi = pos / kv.page_size;
+  if (pos < 0 || pi >= kv.max_pages_per_seq) {
+    if (err) atomicOr(err, UNO_DEVERR_BOUNDS);
+    return nullptr;
+  }
+  const int page = kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi];
+  if (page < 0 || page >= kv.n_pages) {
+    if (err) atomicOr(err, UNO_DEVERR_BOUNDS);
+    return nullptr;
+  }
+  const size_t off =
+      ((((size_t)(layer * 2 + which) * kv.n_pages + page) * kv.n_kv_heads + h) * kv.page_size +
+       (pos % kv.page_size)) * kv.head_dim;
+  return reinterpret_cast<T*>(kv.pool) + off;
+}
+
+// One block per row: rotate q and k (pairs i, i + hd/2), store q, and write k / v
+// into the row's KV page slot.
+template <typename T>
+__global__ void k_rope_kv(const float* __restrict__ qkv, int rows_per_seq,
+                          const int32_t* __restrict__ call_seq,
+                          const int32_t* __restrict__ row_pos, int Hq,
+                          const float* __restrict__ rcos, const float* __restrict__ rsin,
+                          T* qbuf, KvLayout kv, int layer, int32_t* err) {
+  const int r = blockIdx.x;
+  const int hd = kv.head_dim, half = hd / 2, Hkv = kv.n_kv_heads;
+  const int pos = row_pos[r];
+  const int seq = call_seq[r / rows_per_seq];
+  const int ld = (Hq + 2 * Hkv) * hd;
+  if (pos < 0 || pos >= kv.max_pages_per_seq * kv.page_size) {   // beyond the RoPE table
+    if (threadIdx.x == 0 && err) atomicOr(err, UNO_DEVERR_BOUNDS);
+    return;
+  }
+  const float* src = qkv + (size_t)r * ld;
+  const float* cr = rcos + (size_t)pos * half;
+  const float* sr = rsin + (size_t)pos * half;
+  // q heads
+  for (int e = threadIdx.x; e < Hq * half; e += blockDim.x) {
+    const int h = e / half, i = e % half;
+    const float x1 = src[h * hd + i], x2 = src[h * hd + i + half];
+    const float c = cr[i], s = sr[i];
+    T* dst = qbuf + (size_t)r * Hq * hd + h * hd;
+    dst[i] = from_f<T>(x1 * c - x2 * s);
+    dst[i + half] = from_f<T>(x2 * c + x1 * s);
+  }
+  // k heads
+  for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
+    const int h = e / half, i = e % half;
+    const float* ks = src + Hq * hd + h * hd;
+    const float x1 = ks[i], x2 = ks[i + half];
+    const float c = cr[i], s = sr[i];
+    T* dst = kv_slot<T>(kv, layer, 0, seq, pos, h, err);
+    if (dst) {
+      dst[i] = from_f<T>(x1 * c - x2 * s);
+      dst[i + half] = from_f<T>(x2 * c + x1 * s);
+    }
+  }
+  // v heads
+  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
+    const int h = e / hd, i = e % hd;
+    T* dst = kv_slot<T>(kv, layer, 1, seq, pos, h, err);
+    if (dst) dst[i] = from_f<T>(src[(Hq + Hkv) * hd + h * hd + i]);
+  }
+}
+
+// Reduce the per-tile (max, sum exp) partials of one logits row (fixed order).
+__global__ void __launch_bounds__(256)
+k_row_stats(const float* __restrict__ tile_stats, int n_tiles, float* row_ml) {
+  __shared__ float shm[256], shs[256];
+  const int r = blockIdx.x;
+  const float* ts = tile_stats + (size_t)r * n_tiles * 2;
+  float m = -INFINITY, s = 0.0f;
+  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+    const float mt = ts[2 * t], st = ts[2 * t + 1];
+    if (mt == -INFINITY) continue;
+    if (mt > m) { s = s * expf(m - mt) + st; m = mt; }
+    else s += st * expf(mt - m);
+  }
+  shm[threadIdx.x] = m;
+  shs[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int i = 0; i < (int)blockDim.x; ++i) M = fmaxf(M, shm[i]);
+    float S = 0.0f;
+    for (int i = 0; i < (int)blockDim.x; ++i)
+      if (shm[i] != -INFINITY) S += shs[i] * expf(shm[i] - M);
+    row_ml[2 * r] = M;
+    row_ml[2 * r + 1] = S;
+  }
+}
+
+__global__ void k_softmax(const float* __restrict__ logits, const float* __restrict__ row_ml,
+                          int V, float* probs) {
+  const int r = blockIdx.y;
+  const float M = row_ml[2 * r], inv = 1.0f / row_ml[2 * r + 1];
+  const size_t base = (size_t)r * V;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x)
+    probs[base + j] = expf(logits[base + j] - M) * inv;
+}
+
+__global__ void k_set_list(SetList l) {
+  for (int i = threadIdx.x; i < l.count; i += blockDim.x) l.dst[l.idx[i]] = l.val[i];
+}
+
+// Contiguous [layers][len][Hkv][hd] <-> pages of one sequence.
+template <typename T>
+__global__ void k_kv_copy(KvLayout kv, int seq, int len, T* k, T* v, int to_pages) {
+  const int pos = blockIdx.x, layer = blockIdx.y;
+  const int hd = kv.head_dim, Hkv = kv.n_kv_heads;
+  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
+    const int h = e / hd, i = e % hd;
+    const size_t c = (((size_t)layer * len + pos) * Hkv + h) * hd + i;
+    T* pk = kv_slot<T>(kv, layer, 0, seq, pos, h, nullptr);
+    T* pv = kv_slot<T>(kv, layer, 1, seq, pos, h, nullptr);
+    if (!pk || !pv) continue;
+    if (to_pages) { pk[i] = k[c]; pv[i] = v[c]; }
+    else { k[c] = pk[i]; v[c] = pv[i]; }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s) {
+  const int R = a.n * a.rows_per_seq;
+  if (R <= 0) return hipSuccess;
+  k_rows_setup<<<(R + 255) / 256, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
+                        int V, float* x, int32_t* err, hipStream_t s) {
+  k_embed<T><<<R, 256, 0, s>>>(E, tok, hidden_in, d, V, x, err);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rmsnorm(const float* x, const T* g, int R, int d, float eps, T* out,
+                          hipStream_t s) {
+  k_rmsnorm<T><<<R, 256, 0, s>>>(x, g, d, eps, out);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32_t* call_seq,
+                          const int32_t* row_pos, int n_q_heads, const float* rope_cos,
+                          const float* rope_sin, T* qbuf, const KvLayout& kv, int layer,
+                          int32_t* err, hipStream_t s) {
+  k_rope_kv<T><<<R, 256, 0, s>>>(qkv, rows_per_seq, call_seq, row_pos, n_q_heads, rope_cos,
+                                 rope_sin, qbuf, kv, layer, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* row_ml,
+                            hipStream_t s) {
+  k_row_stats<<<R, 256, 0, s>>>(tile_stats, n_tiles, row_ml);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax(const float* logits, const float* row_ml, int R, int V, float* probs,
+                          hipStream_t s) {
+  const int bx = (V + 1023) / 1024 < 64 ? (V + 1023) / 1024 : 64;
+  k_softmax<<<dim3(bx, R), 256, 0, s>>>(logits, row_ml, V, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_list(const SetList& l, hipStream_t s) {
+  if (l.count <= 0) return hipSuccess;
+  k_set_list<<<1, 256, 0, s>>>(l);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,
+                          hipStream_t s) {
+  if (len <= 0) return hipSuccess;
+  k_kv_copy<T><<<dim3(len, kv.n_layers), 256, 0, s>>>(kv, seq, len, k, v, to_pages);
+  return hipGetLastError();
+}
+
+#define UNO_INST(T)                                                                         \
+  template hipError_t launch_embed<T>(const T*, const int32_t*, const float*, int, int, int, \
+                                      float*, int32_t*, hipStream_t);                       \
+  template hipError_t launch_rmsnorm<T>(const float*, const T*, int, int, float, T*,         \
+                                        hipStream_t);                                       \
+  template hipError_t launch_rope_kv<T>(const float*, int, int, const int32_t*,              \
+                                        const int32_t*, int, const float*, const float*, T*, \
+                                        const KvLayout&, int, int32_t*, hipStream_t);       \
+  template hipError_t launch_kv_copy<T>(const KvLayout&, int, int, T*, T*, int, hipStream_t);
+UNO_INST(float)
+UNO_INST(bf16)

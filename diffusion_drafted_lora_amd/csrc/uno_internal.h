@@ -1,0 +1,224 @@
+// Internal declarations shared by the HIP sources of libuno (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define UNO_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------- storage types
+template <typename T> UNO_DEV float to_f(T v);
+template <> UNO_DEV float to_f<float>(float v) { return v; }
+template <> UNO_DEV float to_f<bf16>(bf16 v) { return (float)v; }
+template <typename T> UNO_DEV T from_f(float v);
+template <> UNO_DEV float from_f<float>(float v) { return v; }
+template <> UNO_DEV bf16 from_f<bf16>(float v) { return (bf16)v; }  // round to nearest even
+
+// Device error bits (sticky per context, OR-ed by kernels).
+enum : int32_t {
+  UNO_DEVERR_NUMERIC = 1,   // NaN / negative / >1 probability, or a row without mass
+  UNO_DEVERR_BOUNDS = 2,    // a KV position outside the sequence's reserved pages
+};
+
+// ------------------------------------------------------------- Philox4x64-10
+// Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11):
+// round multipliers and the Weyl key increments of the 4x64 variant.
+#define PHILOX_M0 0xD2E7470EE14C6C93ull
+#define PHILOX_M1 0xCA5A826395121157ull
+#define PHILOX_W0 0x9E3779B97F4A7C15ull
+#define PHILOX_W1 0xBB67AE8584CAA73Bull
+
+enum : int32_t { STREAM_DRAFT = 0, STREAM_ACCEPT = 1, STREAM_RESAMPLE = 2 };
+
+// Word 0 of Philox4x64-10(key = (k0, k1), counter = (c0, c1, c2, 0)).
+UNO_DEV uint64_t philox_word0(uint64_t k0, uint64_t k1, uint64_t c0, uint64_t c1,
+                              uint64_t c2) {
+  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += PHILOX_W0; k1 += PHILOX_W1; }
+    const uint64_t hi0 = __umul64hi(PHILOX_M0, x0), lo0 = PHILOX_M0 * x0;
+    const uint64_t hi1 = __umul64hi(PHILOX_M1, x2), lo1 = PHILOX_M1 * x2;
+    const uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+    x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
+  }
+  return x0;
+}
+
+// The draw deciding absolute position `pos` in `stream` at iteration `it`.
+UNO_DEV uint64_t draw_word(uint64_t seed, int32_t seq_id, int32_t pos, int32_t stream,
+                           int32_t it) {
+  return philox_word0(seed, (uint64_t)(uint32_t)seq_id, (uint64_t)(uint32_t)pos,
+                      (uint64_t)(uint32_t)stream, (uint64_t)(uint32_t)it);
+}
+
+// Uniform in [0, 1 - 2^-24]: the top 24 bits of the word, exact in float32.
+UNO_DEV float unif24(uint64_t w) { return (float)(uint32_t)(w >> 40) * 0x1p-24f; }
+
+// Integer weight trunc(w * 2^40); flags NaN / negative / > 1 and treats them as 0.
+UNO_DEV uint64_t int_weight(float w, int32_t* err) {
+  if (!(w >= 0.0f && w <= 1.0f)) {   // catches NaN too
+    if (err) atomicOr(err, UNO_DEVERR_NUMERIC);
+    return 0;
+  }
+  return (uint64_t)(w * 0x1p40f);    // exact scaling; the cast truncates
+}
+
+// ------------------------------------------------------------------- sampling
+// A categorical row to draw from: mode 0 -> weights a[j]; mode 1 -> the residual
+// max(0, a[j] - b[j]) with a fallback to a[j] when the residual has no mass.
+struct RowDesc {
+  const float* a;
+  const float* b;
+  int32_t mode;
+  int32_t pad;
+  uint64_t word;
+  int32_t* out;
+};
+
+UNO_DEV float row_weight(const RowDesc& d, int mode, int j) {
+  float w = d.a[j];
+  if (mode == 1) w = fmaxf(w - d.b[j], 0.0f);   // float32 subtraction
+  return w;
+}
+
+constexpr int CDF_CHUNK = 2048;  // elements per chunk of the integer CDF
+constexpr int CDF_THREADS = 256;
+
+// ------------------------------------------------------------ GEMM interfaces
+enum GemmEpi : int32_t {
+  EPI_STORE_F32 = 0,   // out_f32[m, n] = acc
+  EPI_LORA_U = 1,      // out_t[m, n] = gate[m] ? T(scale * acc) : 0
+  EPI_RESID = 2,       // resid[m, n] += acc
+  EPI_SWIGLU = 3,      // out_t[m, n] = T(silu(acc_gate) * acc_up)    (paired segments)
+  EPI_LOGITS = 4,      // out_f32[m, n] = acc (MASK column -inf) + per-tile max / sum-exp
+};
+
+struct GemmSeg {
+  const void* W;     // [N, K] of the storage type
+  const void* Bl;    // LoRA up [N, r] (or null)
+  const void* U;     // LoRA intermediate [M, ldu] for this segment (or null)
+  int32_t n0;        // first output column of this segment
+  int32_t N;         // columns of this segment
+  int32_t ldu;
+  int32_t pad;
+};
+
+struct GemmArgs {
+  const void* X;     // activations [M, ldx] of the storage type
+  int32_t ldx, M, K, r;
+  GemmSeg seg[4];
+  int32_t nseg;
+  int32_t paired;    // 1: segment 0 and 1 are computed at the same columns (SwiGLU)
+  int32_t epi;
+  int32_t ldo;
+  void* out;
+  float* resid;
+  const uint8_t* gate;
+  float scale;
+  int32_t mask_col;  // EPI_LOGITS: column forced to -inf
+  float* tile_stats; // EPI_LOGITS: [M, n_tiles, 2] (max, sum exp)
+  int32_t n_tiles;   // EPI_LOGITS: total 16-column tiles
+  int32_t pad2;
+};
+
+// ------------------------------------------------------------------ launchers
+// Every launcher enqueues on `s` and returns the hipGetLastError of its launch.
+template <typename T> hipError_t launch_gemm(const GemmArgs& a, int n_cols_total, hipStream_t s);
+
+struct RowsSetup {
+  int32_t mode;          // 0 draft, 1 verify, 2 forward (caller rows), 3 prefill
+  int32_t n, rows_per_seq, B, mask_id;
+  const int32_t* call_seq;   // [n] sequence ids
+  const int32_t* len;        // [max_seqs]
+  const int32_t* pending;    // [max_seqs]
+  const int32_t* iter;       // [max_seqs]
+  const int32_t* draft_tok;  // [n, B] (verify)
+  const int32_t* in_tok;     // forward / prefill: [n * rows]
+  const int32_t* in_pos;     // forward: [n * rows]; prefill: first position (scalar in pos0)
+  const uint8_t* in_gate;    // forward: [n * rows]
+  int32_t pos0;              // prefill: position of the first row
+  int32_t* row_tok;
+  int32_t* row_pos;
+  uint8_t* row_gate;
+  int32_t* call_n;           // [n] pending position n of each call sequence
+  int32_t* call_it;          // [n] iteration
+};
+hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s);
+
+template <typename T>
+hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
+                        int V, float* x, int32_t* err, hipStream_t s);
+template <typename T>
+hipError_t launch_rmsnorm(const float* x, const T* g, int R, int d, float eps, T* out,
+                          hipStream_t s);
+
+struct KvLayout {
+  void* pool;
+  int32_t n_pages, n_kv_heads, page_size, head_dim, n_layers;
+  const int32_t* block_table;   // [max_seqs, max_pages_per_seq]
+  int32_t max_pages_per_seq;
+  int32_t pad;
+};
+
+template <typename T>
+hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32_t* call_seq,
+                          const int32_t* row_pos, int n_q_heads, const float* rope_cos,
+                          const float* rope_sin, T* qbuf, const KvLayout& kv, int layer,
+                          int32_t* err, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;             // [R, Hq * hd] of T
+  void* out;                 // [R, Hq * hd] of T
+  const int32_t* row_pos;    // [R]
+  const int32_t* call_seq;   // [n]
+  int32_t n, rows_per_seq, n_q_heads, n_chunks, chunk;
+  float scale;
+  float* part_o;             // [R * Hq, n_chunks, hd]
+  float* part_ml;            // [R * Hq, n_chunks, 2]
+  int32_t layer;
+  int32_t pad;
+};
+template <typename T> hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv,
+                                                  hipStream_t s);
+
+hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* row_ml,
+                            hipStream_t s);
+hipError_t launch_softmax(const float* logits, const float* row_ml, int R, int V, float* probs,
+                          hipStream_t s);
+
+hipError_t launch_draft_desc(const float* probs, int n, int B, int V, uint64_t seed,
+                             const int32_t* call_seq, const int32_t* call_n,
+                             const int32_t* call_it, int32_t* out_tok, RowDesc* desc,
+                             hipStream_t s);
+hipError_t launch_sample_desc(const float* w, int rows, int V, uint64_t seed,
+                              const int32_t* seq_ids, const int32_t* pos, const int32_t* it,
+                              int stream_id, int32_t* out, RowDesc* desc, hipStream_t s);
+hipError_t launch_cdf(const RowDesc* desc, int rows, int V, uint64_t* chunk_tot,
+                      int32_t* err, hipStream_t s);
+// q rows of sequence s start at q + s * q_stride * V (q_2 first).
+hipError_t launch_accept_test(uint64_t seed, int n, int B, int V, const float* p,
+                              const float* q, int q_stride, const int32_t* draft,
+                              const int32_t* call_seq, const int32_t* call_n,
+                              const int32_t* call_it, int32_t* k_out, int32_t* z_out,
+                              RowDesc* desc, int32_t* err, hipStream_t s);
+hipError_t launch_accept_commit(int n, int B, const int32_t* draft, const int32_t* k,
+                                const int32_t* z, const int32_t* call_seq, int32_t* out,
+                                int32_t* n_out, int32_t* len, int32_t* pending, int32_t* iter,
+                                hipStream_t s);
+
+struct SetList {            // small device scatter passed by value: dst[idx[i]] = val[i]
+  int32_t* dst;
+  int32_t count;
+  int32_t idx[240];
+  int32_t val[240];
+};
+hipError_t launch_set_list(const SetList& l, hipStream_t s);
+
+template <typename T>
+hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,
+                          hipStream_t s);

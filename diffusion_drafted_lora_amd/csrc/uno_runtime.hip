@@ -1,0 +1,900 @@
+// Host runtime of libuno: context, workspace layout, KV page allocator, argument
+// validation, the forward plan and the C ABI of include/uno.h.
+//
+// The plan follows the method's two forwards per iteration (shibing624 reading
+// notes of the Uno paper, section on the Psi-Spec sampler): a draft forward of
+// [t, MASK x (B-1)] with the LoRA gated on for the mask rows, sampling of the
+// drafted block, then an AR-only verify forward of the block, the accept/resample
+// test and the commit.  No host synchronisation happens inside an iteration: the
+// sequence state lives on the device, the host keeps only an upper bound of each
+// sequence's length (refreshed from an asynchronous snapshot) to reserve pages.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/uno.h"
+#include "uno_internal.h"
+
+template <typename T> size_t attn_smem_bytes(int G, int hd);
+
+namespace {
+
+constexpr int kMaxChunks = 64;        // context chunks per (row, head) in attention
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_last_error = "";
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t len, pending, iter, err, block_table, rope_cos, rope_sin;
+  size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate;
+  size_t x, xn, qkv, qbuf, obuf, hbuf, ubuf;
+  size_t part_o, part_ml;
+  size_t logits, tile_stats, row_ml, probs_d, probs_v;
+  size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32;
+  size_t total;
+};
+
+int pages_per_seq(const uno_config& c) { return (c.max_seq_len + c.page_size - 1) / c.page_size; }
+
+Layout make_layout(const uno_config& c) {
+  Layout L{};
+  const size_t ts = c.dtype == UNO_BF16 ? 2 : 4;
+  const size_t R = (size_t)c.max_rows;
+  const size_t S = (size_t)c.max_seqs;
+  const size_t d = c.d_model, q = (size_t)c.n_q_heads * c.head_dim,
+               kv = (size_t)c.n_kv_heads * c.head_dim, F = c.ffn_dim, V = c.vocab,
+               r = c.lora_rank > 0 ? c.lora_rank : 0, B = c.block_size;
+  const size_t n_chunks_cdf = (V + CDF_CHUNK - 1) / CDF_CHUNK;
+  const size_t rows_any = std::max(R, S * B);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  L.len = take(S * 4);
+  L.pending = take(S * 4);
+  L.iter = take(S * 4);
+  L.err = take(4);
+  L.block_table = take(S * pages_per_seq(c) * 4);
+  const size_t rope_rows = (size_t)pages_per_seq(c) * c.page_size;
+  L.rope_cos = take(rope_rows * (c.head_dim / 2) * 4);
+  L.rope_sin = take(rope_rows * (c.head_dim / 2) * 4);
+  L.call_seq = take(S * 4);
+  L.call_n = take(S * 4);
+  L.call_it = take(S * 4);
+  L.row_tok = take(R * 4);
+  L.row_pos = take(R * 4);
+  L.row_gate = take(R);
+  L.x = take(R * d * 4);
+  L.xn = take(R * d * ts);
+  L.qkv = take(R * (q + 2 * kv) * 4);
+  L.qbuf = take(R * q * ts);
+  L.obuf = take(R * q * ts);
+  L.hbuf = take(R * F * ts);
+  L.ubuf = take(R * 3 * r * ts + 16);
+  L.part_o = take(R * c.n_q_heads * kMaxChunks * c.head_dim * 4);
+  L.part_ml = take(R * c.n_q_heads * kMaxChunks * 2 * 4);
+  L.logits = take(R * V * 4);
+  L.tile_stats = take(R * (V / 16) * 2 * 4);
+  L.row_ml = take(R * 2 * 4);
+  L.probs_d = take(S * B * V * 4);
+  L.probs_v = take(S * B * V * 4);
+  L.desc = take(rows_any * sizeof(RowDesc));
+  L.chunk_tot = take(rows_any * n_chunks_cdf * 8);
+  L.draft_tok = take(S * B * 4);
+  L.acc_k = take(S * 4);
+  L.acc_z = take(S * 4);
+  L.aux_i32 = take(rows_any * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+struct uno_ctx {
+  uno_config cfg{};
+  bool bf16 = false;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  void* kv = nullptr;
+  Layout L{};
+  int maxpp = 0;
+  // weights
+  const void* embed = nullptr;
+  const void* lm_head = nullptr;
+  const void* final_norm = nullptr;
+  std::vector<const void*> attn_norm, mlp_norm, w[7], la[7], lb[7];
+  bool has_lora = false;
+  // host page bookkeeping
+  std::vector<int> free_pages;
+  std::vector<std::vector<int>> seq_pages;
+  std::vector<int> len_hi;          // upper bound of each committed length
+  std::vector<char> live;           // sequence has been prefilled / imported
+  std::vector<int> pt_idx, pt_val;  // pending block-table writes
+  std::vector<int> uploaded_call;   // call_seq contents on the device
+  // draft bookkeeping
+  std::vector<int> drafted_ids;
+  // asynchronous length snapshot
+  int32_t* snap_host = nullptr;
+  hipEvent_t snap_event = nullptr;
+  bool snap_inflight = false;
+  std::vector<int> snap_base;
+  std::string err;
+
+  template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
+};
+
+namespace {
+
+uno_status fail(uno_ctx* c, uno_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  g_last_error = msg;
+  return s;
+}
+
+uno_status hip_fail(uno_ctx* c, hipError_t e, const char* where) {
+  return fail(c, UNO_ERR_DEVICE, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define UNO_HIP(ctx, call)                                   \
+  do {                                                       \
+    hipError_t e_ = (call);                                  \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, #call);   \
+  } while (0)
+
+uno_status check_config(const uno_config* c) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null config");
+  if (c->n_layers < 1 || c->d_model < 16 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 2 || c->ffn_dim < 16 || c->vocab < 16 || c->max_seqs < 1 ||
+      c->max_seq_len < 2 || c->page_size < 1 || c->n_pages < 1 || c->block_size < 1)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "config sizes out of range");
+  if (c->mask_id != c->vocab - 1) return fail(nullptr, UNO_ERR_INVALID_ARG, "mask_id must be vocab-1");
+  if (c->block_size > 64) return fail(nullptr, UNO_ERR_UNSUPPORTED, "block_size > 64");
+  if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, UNO_ERR_INVALID_ARG, "Hq % Hkv != 0");
+  if (c->head_dim % 2 || c->head_dim > 256) return fail(nullptr, UNO_ERR_UNSUPPORTED, "head_dim");
+  if (16 * (c->n_q_heads / c->n_kv_heads) * c->head_dim > 256 * 64)
+    return fail(nullptr, UNO_ERR_UNSUPPORTED, "query group too large for the attention tile");
+  if (c->vocab % 16 || c->d_model % 16 || c->ffn_dim % 16 ||
+      (c->n_q_heads * c->head_dim) % 16 || (c->n_kv_heads * c->head_dim) % 16)
+    return fail(nullptr, UNO_ERR_UNSUPPORTED, "dimensions must be multiples of 16");
+  if (c->vocab > CDF_CHUNK * 1024) return fail(nullptr, UNO_ERR_UNSUPPORTED, "vocab too large");
+  if (c->dtype != UNO_F32 && c->dtype != UNO_BF16) return fail(nullptr, UNO_ERR_INVALID_ARG, "dtype");
+  if (c->dtype == UNO_BF16) {
+    if (c->d_model % 32 || c->ffn_dim % 32 || (c->n_q_heads * c->head_dim) % 32)
+      return fail(nullptr, UNO_ERR_UNSUPPORTED, "bf16 needs K dims multiple of 32");
+    if (c->lora_rank % 32) return fail(nullptr, UNO_ERR_UNSUPPORTED, "bf16 LoRA rank % 32");
+  }
+  if (c->lora_rank < 0) return fail(nullptr, UNO_ERR_INVALID_ARG, "lora_rank < 0");
+  if (c->lora_rank > 0 && c->lora_rank % 8 && c->dtype == UNO_F32)
+    return fail(nullptr, UNO_ERR_UNSUPPORTED, "lora rank");
+  if (c->max_rows < c->max_seqs * c->block_size)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "max_rows < max_seqs * block_size");
+  return UNO_OK;
+}
+
+size_t kv_bytes(const uno_config& c) {
+  const size_t ts = c.dtype == UNO_BF16 ? 2 : 4;
+  return (size_t)c.n_layers * 2 * c.n_pages * c.n_kv_heads * c.page_size * c.head_dim * ts;
+}
+
+KvLayout kv_layout(uno_ctx* c) {
+  KvLayout k{};
+  k.pool = c->kv;
+  k.n_pages = c->cfg.n_pages;
+  k.n_kv_heads = c->cfg.n_kv_heads;
+  k.page_size = c->cfg.page_size;
+  k.head_dim = c->cfg.head_dim;
+  k.n_layers = c->cfg.n_layers;
+  k.block_table = c->at<int32_t>(c->L.block_table);
+  k.max_pages_per_seq = c->maxpp;
+  return k;
+}
+
+// Scatter a list of int32 values into device memory (kernel arguments carry the
+// data, so nothing is staged in host memory).
+uno_status scatter(uno_ctx* c, int32_t* dst, const std::vector<int>& idx,
+                   const std::vector<int>& val) {
+  for (size_t a = 0; a < idx.size(); a += 240) {
+    SetList l{};
+    l.dst = dst;
+    l.count = (int)std::min<size_t>(240, idx.size() - a);
+    for (int i = 0; i < l.count; ++i) { l.idx[i] = idx[a + i]; l.val[i] = val[a + i]; }
+    UNO_HIP(c, launch_set_list(l, c->stream));
+  }
+  return UNO_OK;
+}
+
+uno_status flush_pages(uno_ctx* c) {
+  if (c->pt_idx.empty()) return UNO_OK;
+  uno_status s = scatter(c, c->at<int32_t>(c->L.block_table), c->pt_idx, c->pt_val);
+  c->pt_idx.clear();
+  c->pt_val.clear();
+  return s;
+}
+
+// Reserve pages so that each sequence holds positions [0, upto[i]).  All or nothing.
+uno_status reserve(uno_ctx* c, const std::vector<int>& seqs, const std::vector<int>& upto) {
+  const int ps = c->cfg.page_size;
+  size_t need = 0;
+  for (size_t i = 0; i < seqs.size(); ++i) {
+    const int want = (upto[i] + ps - 1) / ps;
+    if (upto[i] > c->cfg.max_seq_len || want > c->maxpp)
+      return fail(c, UNO_ERR_INVALID_ARG, "sequence would exceed max_seq_len");
+    const int have = (int)c->seq_pages[seqs[i]].size();
+    if (want > have) need += want - have;
+  }
+  if (need > c->free_pages.size()) return fail(c, UNO_ERR_OUT_OF_PAGES, "KV page pool exhausted");
+  for (size_t i = 0; i < seqs.size(); ++i) {
+    const int want = (upto[i] + ps - 1) / ps;
+    auto& pg = c->seq_pages[seqs[i]];
+    while ((int)pg.size() < want) {
+      const int p = c->free_pages.back();
+      c->free_pages.pop_back();
+      c->pt_idx.push_back(seqs[i] * c->maxpp + (int)pg.size());
+      c->pt_val.push_back(p);
+      pg.push_back(p);
+    }
+  }
+  return UNO_OK;
+}
+
+uno_status upload_call(uno_ctx* c, const std::vector<int>& seqs) {
+  std::vector<int> idx, val;
+  if (c->uploaded_call.size() < seqs.size()) c->uploaded_call.resize(seqs.size(), -1);
+  for (size_t i = 0; i < seqs.size(); ++i)
+    if (c->uploaded_call[i] != seqs[i]) {
+      idx.push_back((int)i);
+      val.push_back(seqs[i]);
+      c->uploaded_call[i] = seqs[i];
+    }
+  return scatter(c, c->at<int32_t>(c->L.call_seq), idx, val);
+}
+
+// Fold a finished length snapshot into the host bounds.
+void poll_snapshot(uno_ctx* c) {
+  if (!c->snap_inflight) return;
+  if (hipEventQuery(c->snap_event) != hipSuccess) return;
+  for (int s = 0; s < c->cfg.max_seqs; ++s)
+    if (c->live[s]) c->len_hi[s] = c->snap_host[s] + (c->len_hi[s] - c->snap_base[s]);
+  c->snap_inflight = false;
+}
+
+uno_status start_snapshot(uno_ctx* c) {
+  if (c->snap_inflight) return UNO_OK;
+  UNO_HIP(c, hipMemcpyAsync(c->snap_host, c->at<int32_t>(c->L.len),
+                            sizeof(int32_t) * c->cfg.max_seqs, hipMemcpyDeviceToHost, c->stream));
+  UNO_HIP(c, hipEventRecord(c->snap_event, c->stream));
+  c->snap_base = c->len_hi;
+  c->snap_inflight = true;
+  return UNO_OK;
+}
+
+uno_status exact_lengths(uno_ctx* c) {
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  c->snap_inflight = false;
+  std::vector<int32_t> lens(c->cfg.max_seqs);
+  UNO_HIP(c, hipMemcpy(lens.data(), c->at<int32_t>(c->L.len), sizeof(int32_t) * lens.size(),
+                       hipMemcpyDeviceToHost));
+  for (int s = 0; s < c->cfg.max_seqs; ++s)
+    if (c->live[s]) c->len_hi[s] = lens[s];
+  return UNO_OK;
+}
+
+uno_status check_seqs(uno_ctx* c, int32_t n, const int32_t* ids, std::vector<int>& out,
+                      bool need_live) {
+  if (n < 1 || n > c->cfg.max_seqs || !ids) return fail(c, UNO_ERR_INVALID_ARG, "bad sequence count");
+  out.assign(ids, ids + n);
+  std::vector<char> seen(c->cfg.max_seqs, 0);
+  for (int s : out) {
+    if (s < 0 || s >= c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "sequence id out of range");
+    if (seen[s]) return fail(c, UNO_ERR_INVALID_ARG, "duplicate sequence id");
+    seen[s] = 1;
+    if (need_live && !c->live[s]) return fail(c, UNO_ERR_STATE, "sequence not prefilled");
+  }
+  return UNO_OK;
+}
+
+// ----------------------------------------------------------------- forward plan
+struct FwdIn {
+  int mode;                 // RowsSetup mode
+  int n, rows_per_seq;
+  const int32_t* in_tok;
+  const float* in_hidden;
+  const int32_t* in_pos;
+  const uint8_t* in_gate;
+  int pos0;
+  int ctx_bound;            // every row position is < ctx_bound
+  bool lora;                // run the LoRA phase (some gate may be on)
+  float* hidden_out;
+  float* probs_out;         // softmax of the logits (nullptr: no LM head)
+  float* logits_out;        // copy of the logits (optional)
+};
+
+template <typename T>
+uno_status forward_t(uno_ctx* c, const FwdIn& f) {
+  const uno_config& g = c->cfg;
+  hipStream_t s = c->stream;
+  const int R = f.n * f.rows_per_seq;
+  const int d = g.d_model, hd = g.head_dim, Hq = g.n_q_heads, Hkv = g.n_kv_heads;
+  const int qd = Hq * hd, kvd = Hkv * hd, F = g.ffn_dim, V = g.vocab, r = g.lora_rank;
+  const bool lora = f.lora && c->has_lora && r > 0;
+  const float sc = lora ? g.lora_alpha / (float)r : 0.0f;
+  int32_t* err = c->at<int32_t>(c->L.err);
+
+  RowsSetup rs{};
+  rs.mode = f.mode;
+  rs.n = f.n;
+  rs.rows_per_seq = f.rows_per_seq;
+  rs.B = g.block_size;
+  rs.mask_id = g.mask_id;
+  rs.call_seq = c->at<int32_t>(c->L.call_seq);
+  rs.len = c->at<int32_t>(c->L.len);
+  rs.pending = c->at<int32_t>(c->L.pending);
+  rs.iter = c->at<int32_t>(c->L.iter);
+  rs.draft_tok = c->at<int32_t>(c->L.draft_tok);
+  rs.in_tok = f.in_tok;
+  rs.in_pos = f.in_pos;
+  rs.in_gate = f.in_gate;
+  rs.pos0 = f.pos0;
+  rs.row_tok = c->at<int32_t>(c->L.row_tok);
+  rs.row_pos = c->at<int32_t>(c->L.row_pos);
+  rs.row_gate = c->at<uint8_t>(c->L.row_gate);
+  rs.call_n = c->at<int32_t>(c->L.call_n);
+  rs.call_it = c->at<int32_t>(c->L.call_it);
+  UNO_HIP(c, launch_rows_setup(rs, s));
+
+  float* x = c->at<float>(c->L.x);
+  T* xn = c->at<T>(c->L.xn);
+  float* qkv = c->at<float>(c->L.qkv);
+  T* qbuf = c->at<T>(c->L.qbuf);
+  T* obuf = c->at<T>(c->L.obuf);
+  T* hbuf = c->at<T>(c->L.hbuf);
+  T* ubuf = c->at<T>(c->L.ubuf);
+  const uint8_t* gate = c->at<uint8_t>(c->L.row_gate);
+
+  if (!f.in_hidden && !c->embed) return fail(c, UNO_ERR_INVALID_ARG, "no embedding table");
+  UNO_HIP(c, launch_embed<T>(reinterpret_cast<const T*>(c->embed), rs.row_tok, f.in_hidden, R, d,
+                             V, x, err, s));
+
+  KvLayout kv = kv_layout(c);
+  // attention chunking: enough workgroups, at most kMaxChunks chunks
+  const int row_tiles = (f.rows_per_seq + 15) / 16;
+  const int groups = f.n * Hkv * row_tiles;
+  int target = std::max(1, std::min(kMaxChunks, (2048 + groups - 1) / groups));
+  int chunk = (f.ctx_bound + target - 1) / target;
+  chunk = std::max(32, (chunk + 31) / 32 * 32);
+  const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
+  if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
+
+  auto lora_down = [&](const T* X, int K, int nproj, const int* pidx, int l) -> uno_status {
+    GemmArgs a{};
+    a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = 0;
+    a.nseg = nproj;
+    for (int i = 0; i < nproj; ++i) {
+      a.seg[i].W = c->la[pidx[i]][l];
+      a.seg[i].n0 = i * r;
+      a.seg[i].N = r;
+    }
+    a.epi = EPI_LORA_U; a.ldo = nproj * r; a.out = ubuf; a.gate = gate; a.scale = sc;
+    UNO_HIP(c, launch_gemm<T>(a, nproj * r, s));
+    return UNO_OK;
+  };
+
+  for (int l = 0; l < g.n_layers; ++l) {
+    // --- attention block
+    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->attn_norm[l]), R, d, g.rms_eps, xn, s));
+    static const int pqkv[3] = {0, 1, 2};
+    if (lora) { uno_status st = lora_down(xn, d, 3, pqkv, l); if (st) return st; }
+    {
+      GemmArgs a{};
+      a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
+      a.nseg = 3;
+      const int n0s[3] = {0, qd, qd + kvd}, Ns[3] = {qd, kvd, kvd};
+      for (int i = 0; i < 3; ++i) {
+        a.seg[i].W = c->w[i][l];
+        a.seg[i].n0 = n0s[i];
+        a.seg[i].N = Ns[i];
+        if (lora) { a.seg[i].Bl = c->lb[i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 3 * r; }
+      }
+      a.epi = EPI_STORE_F32; a.ldo = qd + 2 * kvd; a.out = qkv;
+      UNO_HIP(c, launch_gemm<T>(a, qd + 2 * kvd, s));
+    }
+    UNO_HIP(c, launch_rope_kv<T>(qkv, R, f.rows_per_seq, rs.call_seq, rs.row_pos, Hq,
+                                 c->at<float>(c->L.rope_cos), c->at<float>(c->L.rope_sin), qbuf,
+                                 kv, l, err, s));
+    {
+      AttnArgs a{};
+      a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
+      a.n = f.n; a.rows_per_seq = f.rows_per_seq; a.n_q_heads = Hq;
+      a.n_chunks = n_chunks; a.chunk = chunk; a.scale = 1.0f / sqrtf((float)hd);
+      a.part_o = c->at<float>(c->L.part_o); a.part_ml = c->at<float>(c->L.part_ml);
+      a.layer = l;
+      UNO_HIP(c, launch_attention<T>(a, kv, s));
+    }
+    static const int po[1] = {3};
+    if (lora) { uno_status st = lora_down(obuf, qd, 1, po, l); if (st) return st; }
+    {
+      GemmArgs a{};
+      a.X = obuf; a.ldx = qd; a.M = R; a.K = qd; a.r = lora ? r : 0;
+      a.nseg = 1;
+      a.seg[0].W = c->w[3][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
+      if (lora) { a.seg[0].Bl = c->lb[3][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
+      a.epi = EPI_RESID; a.ldo = d; a.resid = x;
+      UNO_HIP(c, launch_gemm<T>(a, d, s));
+    }
+    // --- MLP block
+    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->mlp_norm[l]), R, d, g.rms_eps, xn, s));
+    static const int pgu[2] = {4, 5};
+    if (lora) { uno_status st = lora_down(xn, d, 2, pgu, l); if (st) return st; }
+    {
+      GemmArgs a{};
+      a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
+      a.nseg = 2; a.paired = 1;
+      for (int i = 0; i < 2; ++i) {
+        a.seg[i].W = c->w[4 + i][l]; a.seg[i].n0 = 0; a.seg[i].N = F;
+        if (lora) { a.seg[i].Bl = c->lb[4 + i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 2 * r; }
+      }
+      a.epi = EPI_SWIGLU; a.ldo = F; a.out = hbuf;
+      UNO_HIP(c, launch_gemm<T>(a, F, s));
+    }
+    static const int pd[1] = {6};
+    if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l); if (st) return st; }
+    {
+      GemmArgs a{};
+      a.X = hbuf; a.ldx = F; a.M = R; a.K = F; a.r = lora ? r : 0;
+      a.nseg = 1;
+      a.seg[0].W = c->w[6][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
+      if (lora) { a.seg[0].Bl = c->lb[6][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
+      a.epi = EPI_RESID; a.ldo = d; a.resid = x;
+      UNO_HIP(c, launch_gemm<T>(a, d, s));
+    }
+  }
+  if (f.hidden_out)
+    UNO_HIP(c, hipMemcpyAsync(f.hidden_out, x, sizeof(float) * R * d, hipMemcpyDeviceToDevice, s));
+  if (f.probs_out || f.logits_out) {
+    if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
+    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->final_norm), R, d, g.rms_eps, xn, s));
+    GemmArgs a{};
+    a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = 0;
+    a.nseg = 1;
+    a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
+    a.epi = EPI_LOGITS; a.ldo = V; a.out = c->at<float>(c->L.logits);
+    a.mask_col = g.mask_id; a.tile_stats = c->at<float>(c->L.tile_stats); a.n_tiles = V / 16;
+    UNO_HIP(c, launch_gemm<T>(a, V, s));
+    if (f.probs_out) {
+      UNO_HIP(c, launch_row_stats(a.tile_stats, R, V / 16, c->at<float>(c->L.row_ml), s));
+      UNO_HIP(c, launch_softmax(c->at<float>(c->L.logits), c->at<float>(c->L.row_ml), R, V,
+                                f.probs_out, s));
+    }
+    if (f.logits_out)
+      UNO_HIP(c, hipMemcpyAsync(f.logits_out, c->at<float>(c->L.logits), sizeof(float) * R * V,
+                                hipMemcpyDeviceToDevice, s));
+  }
+  return UNO_OK;
+}
+
+uno_status forward(uno_ctx* c, const FwdIn& f) {
+  return c->bf16 ? forward_t<bf16>(c, f) : forward_t<float>(c, f);
+}
+
+uno_status set_state(uno_ctx* c, int seq, int len, int pending, int iter) {
+  uno_status st;
+  if ((st = scatter(c, c->at<int32_t>(c->L.len), {seq}, {len}))) return st;
+  if ((st = scatter(c, c->at<int32_t>(c->L.pending), {seq}, {pending}))) return st;
+  return scatter(c, c->at<int32_t>(c->L.iter), {seq}, {iter});
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+uno_status uno_query_sizes(const uno_config* cfg, size_t* kv_pool_bytes, size_t* workspace_bytes) {
+  uno_status s = check_config(cfg);
+  if (s) return s;
+  if (kv_pool_bytes) *kv_pool_bytes = kv_bytes(*cfg);
+  if (workspace_bytes) *workspace_bytes = make_layout(*cfg).total;
+  return UNO_OK;
+}
+
+uno_status uno_init(const uno_config* cfg, const uno_weights* wts, void* d_kv_pool,
+                    size_t kv_pool_bytes, void* d_workspace, size_t workspace_bytes, void* stream,
+                    uno_ctx** out) {
+  if (!out) return fail(nullptr, UNO_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  uno_status st = check_config(cfg);
+  if (st) return st;
+  if (!wts || !d_kv_pool || !d_workspace)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "null weights / kv pool / workspace");
+  if (kv_pool_bytes < kv_bytes(*cfg)) return fail(nullptr, UNO_ERR_INVALID_ARG, "kv pool too small");
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.total) return fail(nullptr, UNO_ERR_INVALID_ARG, "workspace too small");
+  if (!wts->final_norm || !wts->attn_norm || !wts->mlp_norm)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "null norm weights");
+  const int nl = cfg->n_layers;
+  bool any_lora = false, all_lora = true;
+  for (int p = 0; p < 7; ++p) {
+    if (!wts->w[p]) return fail(nullptr, UNO_ERR_INVALID_ARG, "null projection array");
+    for (int l = 0; l < nl; ++l)
+      if (!wts->w[p][l]) return fail(nullptr, UNO_ERR_INVALID_ARG, "null projection weight");
+    const bool has = wts->lora_a[p] && wts->lora_b[p];
+    any_lora |= has;
+    all_lora &= has;
+    if (has)
+      for (int l = 0; l < nl; ++l)
+        if (!wts->lora_a[p][l] || !wts->lora_b[p][l])
+          return fail(nullptr, UNO_ERR_INVALID_ARG, "null LoRA weight");
+  }
+  if (any_lora && !all_lora)
+    return fail(nullptr, UNO_ERR_UNSUPPORTED, "LoRA must be on all seven projections or none");
+  if (any_lora && cfg->lora_rank <= 0) return fail(nullptr, UNO_ERR_INVALID_ARG, "LoRA without rank");
+  for (int l = 0; l < nl; ++l)
+    if (!wts->attn_norm[l] || !wts->mlp_norm[l]) return fail(nullptr, UNO_ERR_INVALID_ARG, "null norm");
+
+  uno_ctx* c = new (std::nothrow) uno_ctx();
+  if (!c) return fail(nullptr, UNO_ERR_DEVICE, "host allocation failed");
+  c->cfg = *cfg;
+  c->bf16 = cfg->dtype == UNO_BF16;
+  c->stream = reinterpret_cast<hipStream_t>(stream);
+  c->ws = reinterpret_cast<char*>(d_workspace);
+  c->kv = d_kv_pool;
+  c->L = L;
+  c->maxpp = pages_per_seq(*cfg);
+  c->embed = wts->embed;
+  c->lm_head = wts->lm_head;
+  c->final_norm = wts->final_norm;
+  c->attn_norm.assign(wts->attn_norm, wts->attn_norm + nl);
+  c->mlp_norm.assign(wts->mlp_norm, wts->mlp_norm + nl);
+  for (int p = 0; p < 7; ++p) {
+    c->w[p].assign(wts->w[p], wts->w[p] + nl);
+    if (any_lora) {
+      c->la[p].assign(wts->lora_a[p], wts->lora_a[p] + nl);
+      c->lb[p].assign(wts->lora_b[p], wts->lora_b[p] + nl);
+    }
+  }
+  c->has_lora = any_lora;
+  c->free_pages.resize(cfg->n_pages);
+  for (int i = 0; i < cfg->n_pages; ++i) c->free_pages[i] = cfg->n_pages - 1 - i;
+  c->seq_pages.assign(cfg->max_seqs, {});
+  c->len_hi.assign(cfg->max_seqs, 0);
+  c->live.assign(cfg->max_seqs, 0);
+  c->snap_base.assign(cfg->max_seqs, 0);
+
+  auto bad = [&](hipError_t e, const char* w) {
+    uno_status s2 = hip_fail(nullptr, e, w);
+    if (c->snap_host) hipHostFree(c->snap_host);
+    if (c->snap_event) hipEventDestroy(c->snap_event);
+    delete c;
+    return s2;
+  };
+  hipError_t e;
+  if ((e = hipHostMalloc((void**)&c->snap_host, sizeof(int32_t) * cfg->max_seqs, hipHostMallocDefault)))
+    return bad(e, "hipHostMalloc");
+  if ((e = hipEventCreateWithFlags(&c->snap_event, hipEventDisableTiming))) return bad(e, "hipEventCreate");
+  // state: lengths / pending / iterations zero, block table -1, error flag 0
+  if ((e = hipMemsetAsync(c->ws + L.len, 0, L.block_table - L.len, c->stream))) return bad(e, "memset");
+  if ((e = hipMemsetAsync(c->ws + L.block_table, 0xFF,
+                          (size_t)cfg->max_seqs * c->maxpp * 4, c->stream))) return bad(e, "memset");
+  // RoPE table in double on the host: angle = pos * theta^(-2i/hd)
+  const int half = cfg->head_dim / 2;
+  const int rope_rows = c->maxpp * cfg->page_size;
+  std::vector<float> tc((size_t)rope_rows * half), tsn((size_t)rope_rows * half);
+  for (int p = 0; p < rope_rows; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      const double ang = (double)p * inv;
+      tc[(size_t)p * half + i] = (float)std::cos(ang);
+      tsn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+  if ((e = hipMemcpyAsync(c->ws + L.rope_cos, tc.data(), tc.size() * 4, hipMemcpyHostToDevice, c->stream)))
+    return bad(e, "rope upload");
+  if ((e = hipMemcpyAsync(c->ws + L.rope_sin, tsn.data(), tsn.size() * 4, hipMemcpyHostToDevice, c->stream)))
+    return bad(e, "rope upload");
+  if ((e = hipStreamSynchronize(c->stream))) return bad(e, "sync");
+  *out = c;
+  return UNO_OK;
+}
+
+uno_status uno_prefill(uno_ctx* c, int32_t n, const int32_t* seq_ids, const int32_t* d_prompts,
+                       const int32_t* prompt_lens) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  std::vector<int> seqs;
+  uno_status st = check_seqs(c, n, seq_ids, seqs, false);
+  if (st) return st;
+  if (!d_prompts || !prompt_lens) return fail(c, UNO_ERR_INVALID_ARG, "null prompts");
+  for (int i = 0; i < n; ++i)
+    if (prompt_lens[i] < 1 || prompt_lens[i] > c->cfg.max_seq_len)
+      return fail(c, UNO_ERR_INVALID_ARG, "prompt length out of range");
+  if (!c->embed) return fail(c, UNO_ERR_INVALID_ARG, "no embedding table");
+  poll_snapshot(c);
+  std::vector<int> upto(n);
+  for (int i = 0; i < n; ++i) upto[i] = std::max(1, prompt_lens[i] - 1);
+  if ((st = reserve(c, seqs, upto))) return st;
+  if ((st = flush_pages(c))) return st;
+  // the last prompt token (pending) is read on the device
+  std::vector<int32_t> last(n);
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const int P = prompt_lens[i];
+    if ((st = upload_call(c, {seqs[i]}))) return st;
+    for (int a = 0; a < P - 1; a += c->cfg.max_rows) {
+      const int rows = std::min(c->cfg.max_rows, P - 1 - a);
+      FwdIn f{};
+      f.mode = 3; f.n = 1; f.rows_per_seq = rows;
+      f.in_tok = d_prompts + off + a;
+      f.pos0 = a;
+      f.ctx_bound = a + rows;
+      f.lora = false;
+      if ((st = forward(c, f))) return st;
+    }
+    // state: len = P-1, pending = prompt[P-1] (copied on the device), iter = 0
+    if ((st = set_state(c, seqs[i], P - 1, 0, 0))) return st;
+    UNO_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.pending) + seqs[i], d_prompts + off + P - 1,
+                              sizeof(int32_t), hipMemcpyDeviceToDevice, c->stream));
+    c->len_hi[seqs[i]] = P - 1;
+    c->live[seqs[i]] = 1;
+    off += P;
+  }
+  c->drafted_ids.clear();
+  return UNO_OK;
+}
+
+uno_status uno_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_draft, float* d_probs) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  std::vector<int> seqs;
+  uno_status st = check_seqs(c, n, seq_ids, seqs, true);
+  if (st) return st;
+  if (!c->embed || !c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no embedding / LM head");
+  const int B = c->cfg.block_size, V = c->cfg.vocab;
+  poll_snapshot(c);
+  std::vector<int> upto(n);
+  int bound = 0;
+  for (int i = 0; i < n; ++i) {
+    upto[i] = c->len_hi[seqs[i]] + B + 1;
+    if (upto[i] > c->cfg.max_seq_len) {   // the bound may be loose: get exact lengths
+      if ((st = exact_lengths(c))) return st;
+      for (int j = 0; j < n; ++j) upto[j] = c->len_hi[seqs[j]] + B + 1;
+      break;
+    }
+  }
+  for (int i = 0; i < n; ++i) bound = std::max(bound, upto[i]);
+  if ((st = reserve(c, seqs, upto))) return st;
+  if ((st = flush_pages(c))) return st;
+  if ((st = upload_call(c, seqs))) return st;
+  FwdIn f{};
+  f.mode = 0; f.n = n; f.rows_per_seq = B;
+  f.ctx_bound = bound - 1;
+  f.lora = true;
+  f.probs_out = c->at<float>(c->L.probs_d);
+  if ((st = forward(c, f))) return st;
+  hipStream_t s = c->stream;
+  RowDesc* desc = c->at<RowDesc>(c->L.desc);
+  UNO_HIP(c, launch_draft_desc(f.probs_out, n, B, V, c->cfg.seed, c->at<int32_t>(c->L.call_seq),
+                               c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
+                               c->at<int32_t>(c->L.draft_tok), desc, s));
+  UNO_HIP(c, launch_cdf(desc, n * B, V, c->at<uint64_t>(c->L.chunk_tot), c->at<int32_t>(c->L.err), s));
+  if (d_draft)
+    UNO_HIP(c, hipMemcpyAsync(d_draft, c->at<int32_t>(c->L.draft_tok), sizeof(int32_t) * n * B,
+                              hipMemcpyDeviceToDevice, s));
+  if (d_probs)
+    UNO_HIP(c, hipMemcpyAsync(d_probs, f.probs_out, sizeof(float) * (size_t)n * B * V,
+                              hipMemcpyDeviceToDevice, s));
+  c->drafted_ids = seqs;
+  return UNO_OK;
+}
+
+uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_out,
+                      int32_t* d_n_out, float* d_probs) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  std::vector<int> seqs;
+  uno_status st = check_seqs(c, n, seq_ids, seqs, true);
+  if (st) return st;
+  if (seqs != c->drafted_ids) return fail(c, UNO_ERR_STATE, "verify without a matching draft");
+  const int B = c->cfg.block_size, V = c->cfg.vocab;
+  int bound = 0;
+  for (int sq : seqs) bound = std::max(bound, c->len_hi[sq] + B + 1);
+  FwdIn f{};
+  f.mode = 1; f.n = n; f.rows_per_seq = B;
+  f.ctx_bound = bound;
+  f.lora = false;
+  f.probs_out = c->at<float>(c->L.probs_v);
+  if ((st = forward(c, f))) return st;
+  hipStream_t s = c->stream;
+  RowDesc* desc = c->at<RowDesc>(c->L.desc);
+  int32_t* err = c->at<int32_t>(c->L.err);
+  const float* pd = c->at<float>(c->L.probs_d);
+  UNO_HIP(c, launch_accept_test(c->cfg.seed, n, B, V, f.probs_out, pd + V, B,
+                                c->at<int32_t>(c->L.draft_tok), c->at<int32_t>(c->L.call_seq),
+                                c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
+                                c->at<int32_t>(c->L.acc_k), c->at<int32_t>(c->L.acc_z), desc, err, s));
+  UNO_HIP(c, launch_cdf(desc, n, V, c->at<uint64_t>(c->L.chunk_tot), err, s));
+  UNO_HIP(c, launch_accept_commit(n, B, c->at<int32_t>(c->L.draft_tok), c->at<int32_t>(c->L.acc_k),
+                                  c->at<int32_t>(c->L.acc_z), c->at<int32_t>(c->L.call_seq), d_out,
+                                  d_n_out, c->at<int32_t>(c->L.len), c->at<int32_t>(c->L.pending),
+                                  c->at<int32_t>(c->L.iter), s));
+  if (d_probs)
+    UNO_HIP(c, hipMemcpyAsync(d_probs, f.probs_out, sizeof(float) * (size_t)n * B * V,
+                              hipMemcpyDeviceToDevice, s));
+  for (int sq : seqs) c->len_hi[sq] += B + 1;
+  c->drafted_ids.clear();
+  return start_snapshot(c);
+}
+
+uno_status uno_step(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_out, int32_t* d_n_out) {
+  uno_status st = uno_draft(c, n, seq_ids, nullptr, nullptr);
+  if (st) return st;
+  return uno_verify(c, n, seq_ids, d_out, d_n_out, nullptr);
+}
+
+uno_status uno_accept(uno_ctx* c, int32_t n, const float* d_p, const float* d_q, const int32_t* d_draft,
+                      const int32_t* d_seq_ids, const int32_t* d_pos, const int32_t* d_iter,
+                      int32_t* d_out, int32_t* d_n_out) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (n < 1 || n > c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad count");
+  if (!d_p || !d_draft || !d_seq_ids || !d_pos || !d_iter || (!d_q && c->cfg.block_size > 1))
+    return fail(c, UNO_ERR_INVALID_ARG, "null input");
+  const int B = c->cfg.block_size, V = c->cfg.vocab;
+  hipStream_t s = c->stream;
+  RowDesc* desc = c->at<RowDesc>(c->L.desc);
+  int32_t* err = c->at<int32_t>(c->L.err);
+  UNO_HIP(c, launch_accept_test(c->cfg.seed, n, B, V, d_p, d_q, B - 1, d_draft, d_seq_ids, d_pos,
+                                d_iter, c->at<int32_t>(c->L.acc_k), c->at<int32_t>(c->L.acc_z), desc,
+                                err, s));
+  UNO_HIP(c, launch_cdf(desc, n, V, c->at<uint64_t>(c->L.chunk_tot), err, s));
+  UNO_HIP(c, launch_accept_commit(n, B, d_draft, c->at<int32_t>(c->L.acc_k), c->at<int32_t>(c->L.acc_z),
+                                  d_seq_ids, d_out, d_n_out, nullptr, nullptr, nullptr, s));
+  return UNO_OK;
+}
+
+uno_status uno_sample(uno_ctx* c, int32_t rows, const float* d_w, const int32_t* d_seq_ids,
+                      const int32_t* d_pos, const int32_t* d_iter, int32_t stream_id, int32_t* d_idx) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  const int cap = std::max(c->cfg.max_rows, c->cfg.max_seqs * c->cfg.block_size);
+  if (rows < 1 || rows > cap) return fail(c, UNO_ERR_INVALID_ARG, "bad row count");
+  if (!d_w || !d_seq_ids || !d_pos || !d_iter || !d_idx) return fail(c, UNO_ERR_INVALID_ARG, "null input");
+  RowDesc* desc = c->at<RowDesc>(c->L.desc);
+  UNO_HIP(c, launch_sample_desc(d_w, rows, c->cfg.vocab, c->cfg.seed, d_seq_ids, d_pos, d_iter,
+                                stream_id, d_idx, desc, c->stream));
+  UNO_HIP(c, launch_cdf(desc, rows, c->cfg.vocab, c->at<uint64_t>(c->L.chunk_tot),
+                        c->at<int32_t>(c->L.err), c->stream));
+  return UNO_OK;
+}
+
+uno_status uno_forward(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t rows_per_seq,
+                       const int32_t* d_tokens, const float* d_hidden_in, const int32_t* d_pos,
+                       const uint8_t* d_gate, float* d_hidden_out, float* d_logits) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  std::vector<int> seqs;
+  uno_status st = check_seqs(c, n, seq_ids, seqs, false);
+  if (st) return st;
+  if (rows_per_seq < 1 || n * rows_per_seq > c->cfg.max_rows)
+    return fail(c, UNO_ERR_INVALID_ARG, "rows exceed max_rows");
+  if ((!d_tokens && !d_hidden_in) || !d_pos || !d_gate)
+    return fail(c, UNO_ERR_INVALID_ARG, "null row inputs");
+  if (!d_hidden_in && !c->embed) return fail(c, UNO_ERR_INVALID_ARG, "no embedding table");
+  if (d_logits && !c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
+  const int R = n * rows_per_seq;
+  std::vector<int32_t> pos(R);
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  UNO_HIP(c, hipMemcpy(pos.data(), d_pos, sizeof(int32_t) * R, hipMemcpyDeviceToHost));
+  std::vector<int> upto(n, 0);
+  int bound = 0;
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < rows_per_seq; ++j) {
+      const int p = pos[(size_t)i * rows_per_seq + j];
+      if (p < 0 || p >= c->cfg.max_seq_len) return fail(c, UNO_ERR_INVALID_ARG, "position out of range");
+      upto[i] = std::max(upto[i], p + 1);
+      bound = std::max(bound, p + 1);
+    }
+  poll_snapshot(c);
+  if ((st = reserve(c, seqs, upto))) return st;
+  if ((st = flush_pages(c))) return st;
+  if ((st = upload_call(c, seqs))) return st;
+  FwdIn f{};
+  f.mode = 2; f.n = n; f.rows_per_seq = rows_per_seq;
+  f.in_tok = d_tokens; f.in_hidden = d_hidden_in; f.in_pos = d_pos; f.in_gate = d_gate;
+  f.ctx_bound = bound;
+  f.lora = true;
+  f.hidden_out = d_hidden_out;
+  f.logits_out = d_logits;
+  return forward(c, f);
+}
+
+uno_status uno_kv_import(uno_ctx* c, int32_t seq_id, int32_t len, const void* d_k, const void* d_v,
+                         int32_t pending, int32_t iter) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad seq id");
+  if (len < 0 || len >= c->cfg.max_seq_len || (len > 0 && (!d_k || !d_v)))
+    return fail(c, UNO_ERR_INVALID_ARG, "bad length / buffers");
+  if (pending < 0 || pending >= c->cfg.vocab || iter < 0) return fail(c, UNO_ERR_INVALID_ARG, "bad state");
+  poll_snapshot(c);
+  uno_status st;
+  if ((st = reserve(c, {seq_id}, {std::max(len, 1)}))) return st;
+  if ((st = flush_pages(c))) return st;
+  const KvLayout kv = kv_layout(c);
+  if (c->bf16)
+    UNO_HIP(c, launch_kv_copy<bf16>(kv, seq_id, len, (bf16*)d_k, (bf16*)d_v, 1, c->stream));
+  else
+    UNO_HIP(c, launch_kv_copy<float>(kv, seq_id, len, (float*)d_k, (float*)d_v, 1, c->stream));
+  if ((st = set_state(c, seq_id, len, pending, iter))) return st;
+  c->len_hi[seq_id] = len;
+  c->live[seq_id] = 1;
+  return UNO_OK;
+}
+
+uno_status uno_kv_export(uno_ctx* c, int32_t seq_id, int32_t len, void* d_k, void* d_v) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad seq id");
+  if (len < 1 || !d_k || !d_v) return fail(c, UNO_ERR_INVALID_ARG, "bad length / buffers");
+  if ((int)c->seq_pages[seq_id].size() * c->cfg.page_size < len)
+    return fail(c, UNO_ERR_INVALID_ARG, "positions not reserved");
+  const KvLayout kv = kv_layout(c);
+  if (c->bf16)
+    UNO_HIP(c, launch_kv_copy<bf16>(kv, seq_id, len, (bf16*)d_k, (bf16*)d_v, 0, c->stream));
+  else
+    UNO_HIP(c, launch_kv_copy<float>(kv, seq_id, len, (float*)d_k, (float*)d_v, 0, c->stream));
+  return UNO_OK;
+}
+
+uno_status uno_seq_state(uno_ctx* c, int32_t seq_id, int32_t* len, int32_t* pending, int32_t* iter) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad seq id");
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  int32_t v[3];
+  UNO_HIP(c, hipMemcpy(&v[0], c->at<int32_t>(c->L.len) + seq_id, 4, hipMemcpyDeviceToHost));
+  UNO_HIP(c, hipMemcpy(&v[1], c->at<int32_t>(c->L.pending) + seq_id, 4, hipMemcpyDeviceToHost));
+  UNO_HIP(c, hipMemcpy(&v[2], c->at<int32_t>(c->L.iter) + seq_id, 4, hipMemcpyDeviceToHost));
+  if (len) *len = v[0];
+  if (pending) *pending = v[1];
+  if (iter) *iter = v[2];
+  return UNO_OK;
+}
+
+uno_status uno_release(uno_ctx* c, int32_t seq_id) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad seq id");
+  auto& pg = c->seq_pages[seq_id];
+  for (size_t i = 0; i < pg.size(); ++i) {
+    c->pt_idx.push_back(seq_id * c->maxpp + (int)i);
+    c->pt_val.push_back(-1);
+    c->free_pages.push_back(pg[i]);
+  }
+  pg.clear();
+  c->live[seq_id] = 0;
+  c->len_hi[seq_id] = 0;
+  if (std::find(c->drafted_ids.begin(), c->drafted_ids.end(), seq_id) != c->drafted_ids.end())
+    c->drafted_ids.clear();
+  uno_status st = flush_pages(c);
+  if (st) return st;
+  return set_state(c, seq_id, 0, 0, 0);
+}
+
+uno_status uno_sync(uno_ctx* c) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  int32_t e = 0;
+  UNO_HIP(c, hipMemcpy(&e, c->at<int32_t>(c->L.err), 4, hipMemcpyDeviceToHost));
+  poll_snapshot(c);
+  if (e & UNO_DEVERR_BOUNDS) return fail(c, UNO_ERR_DEVICE, "device bounds check tripped");
+  if (e & UNO_DEVERR_NUMERIC) return fail(c, UNO_ERR_NUMERIC, "NaN / negative probability or empty row");
+  return UNO_OK;
+}
+
+int32_t uno_free_pages(const uno_ctx* c) { return c ? (int32_t)c->free_pages.size() : 0; }
+
+const char* uno_last_error(const uno_ctx* c) {
+  return c ? c->err.c_str() : g_last_error.c_str();
+}
+
+void uno_destroy(uno_ctx* c) {
+  if (!c) return;
+  hipStreamSynchronize(c->stream);
+  if (c->snap_host) hipHostFree(c->snap_host);
+  if (c->snap_event) hipEventDestroy(c->snap_event);
+  delete c;
+}
+
+}  // extern "C"

@@ -1,0 +1,321 @@
+"""ctypes binding of libuno (include/uno.h).
+
+Argument marshalling only: every step of the decode runs in the HIP library.
+torch supplies device memory (tensors) and the HIP stream.  The library is loaded
+on first use; a missing library raises (there is no fallback path).
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libuno.so")
+
+UNO_OK = 0
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_PAGES", 3: "STATE", 4: "NUMERIC",
+          5: "DEVICE", 6: "UNSUPPORTED"}
+PROJ = synth.PROJ
+
+EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_verify",
+            "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
+            "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
+            "uno_last_error", "uno_destroy")
+
+
+class UnoError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class UnoConfigC(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads",
+                                         "head_dim", "ffn_dim", "vocab", "mask_id",
+                                         "lora_rank")] + \
+               [("lora_alpha", C.c_float), ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + \
+               [(n, C.c_int32) for n in ("block_size", "page_size", "max_seqs", "max_seq_len",
+                                         "n_pages", "max_rows", "dtype")] + \
+               [("seed", C.c_uint64)]
+
+
+PP = C.POINTER(C.c_void_p)
+
+
+class UnoWeightsC(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("lm_head", C.c_void_p), ("final_norm", C.c_void_p),
+                ("attn_norm", PP), ("mlp_norm", PP),
+                ("w", PP * 7), ("lora_a", PP * 7), ("lora_b", PP * 7)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libuno.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m diffusion_drafted_lora_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, u64 = C.c_void_p, C.c_int32, C.c_uint64
+        P = C.POINTER
+        L.uno_query_sizes.argtypes = [P(UnoConfigC), P(C.c_size_t), P(C.c_size_t)]
+        L.uno_init.argtypes = [P(UnoConfigC), P(UnoWeightsC), vp, C.c_size_t, vp, C.c_size_t, vp,
+                               P(vp)]
+        L.uno_prefill.argtypes = [vp, i32, P(i32), vp, P(i32)]
+        L.uno_draft.argtypes = [vp, i32, P(i32), vp, vp]
+        L.uno_verify.argtypes = [vp, i32, P(i32), vp, vp, vp]
+        L.uno_step.argtypes = [vp, i32, P(i32), vp, vp]
+        L.uno_accept.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.uno_sample.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
+        L.uno_forward.argtypes = [vp, i32, P(i32), i32, vp, vp, vp, vp, vp, vp]
+        L.uno_kv_import.argtypes = [vp, i32, i32, vp, vp, i32, i32]
+        L.uno_kv_export.argtypes = [vp, i32, i32, vp, vp]
+        L.uno_seq_state.argtypes = [vp, i32, P(i32), P(i32), P(i32)]
+        L.uno_release.argtypes = [vp, i32]
+        L.uno_sync.argtypes = [vp]
+        L.uno_free_pages.argtypes = [vp]
+        L.uno_free_pages.restype = i32
+        L.uno_last_error.argtypes = [vp]
+        L.uno_last_error.restype = C.c_char_p
+        L.uno_destroy.argtypes = [vp]
+        L.uno_destroy.restype = None
+        for name in EXPORTED:
+            f = getattr(L, name)
+            if f.restype is C.c_int:  # default restype: status codes
+                f.restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, seed=0):
+    """uno_config for a configs.UnoConfig plus decoding limits."""
+    max_seq_len = max_seq_len or cfg.max_len
+    pages_per_seq = -(-max_seq_len // cfg.page_size)
+    c = UnoConfigC()
+    c.n_layers, c.d_model = cfg.n_layers, cfg.d_model
+    c.n_q_heads, c.n_kv_heads, c.head_dim = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    c.ffn_dim, c.vocab, c.mask_id = cfg.ffn_dim, cfg.vocab, cfg.mask_id
+    c.lora_rank, c.lora_alpha = cfg.lora_rank, cfg.lora_alpha
+    c.rope_theta, c.rms_eps = cfg.rope_theta, cfg.rms_eps
+    c.block_size, c.page_size = cfg.block_size, cfg.page_size
+    c.max_seqs, c.max_seq_len = max_seqs, max_seq_len
+    c.n_pages = n_pages or max_seqs * pages_per_seq
+    c.max_rows = max_rows or max_seqs * cfg.block_size
+    c.dtype = 1 if cfg.dtype == "bf16" else 0
+    c.seed = seed
+    return c
+
+
+def query_sizes(ccfg):
+    kv, ws = C.c_size_t(), C.c_size_t()
+    st = lib().uno_query_sizes(C.byref(ccfg), C.byref(kv), C.byref(ws))
+    if st != UNO_OK:
+        raise UnoError(st, lib().uno_last_error(None).decode())
+    return kv.value, ws.value
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _ptr(t):
+    return C.c_void_p(0) if t is None else C.c_void_p(t.data_ptr())
+
+
+class Engine:
+    """A libuno context over torch-allocated device memory."""
+
+    def __init__(self, cfg, weights, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None,
+                 seed=0, device="cuda", stream=None):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed)
+        kv_bytes, ws_bytes = query_sizes(self.ccfg)
+        self.kv = torch.empty(max(kv_bytes, 1), dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=self.device)
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        self._keep = []
+        wc = UnoWeightsC()
+        self.weights = weights
+
+        def arr(ts):
+            a = (C.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+            self._keep.append(a)
+            return C.cast(a, PP)
+
+        for t in self._all_tensors(weights):
+            if not t.is_contiguous() or t.device != self.device:
+                raise ValueError("weights must be contiguous tensors on the engine's device")
+        wc.embed = weights["embed"].data_ptr() if "embed" in weights else None
+        wc.lm_head = weights["lm_head"].data_ptr() if "lm_head" in weights else None
+        wc.final_norm = weights["final_norm"].data_ptr()
+        L = weights["layers"]
+        wc.attn_norm = arr([l["attn_norm"] for l in L])
+        wc.mlp_norm = arr([l["mlp_norm"] for l in L])
+        has_lora = "la" in L[0] and len(L[0]["la"]) == 7
+        for i, p in enumerate(PROJ):
+            wc.w[i] = arr([l["w"][p] for l in L])
+            if has_lora:
+                wc.lora_a[i] = arr([l["la"][p] for l in L])
+                wc.lora_b[i] = arr([l["lb"][p] for l in L])
+        self._wc = wc
+        h = C.c_void_p()
+        st = lib().uno_init(C.byref(self.ccfg), C.byref(wc), _ptr(self.kv), kv_bytes,
+                            _ptr(self.ws), ws_bytes, C.c_void_p(self.stream.cuda_stream),
+                            C.byref(h))
+        if st != UNO_OK:
+            raise UnoError(st, lib().uno_last_error(None).decode())
+        self.h = h
+
+    @staticmethod
+    def _all_tensors(w):
+        for k in ("embed", "lm_head", "final_norm"):
+            if k in w:
+                yield w[k]
+        for l in w["layers"]:
+            yield l["attn_norm"]
+            yield l["mlp_norm"]
+            for d in ("w", "la", "lb"):
+                for t in l.get(d, {}).values():
+                    yield t
+
+    # ------------------------------------------------------------------ helpers
+    def _check(self, st):
+        if st != UNO_OK:
+            raise UnoError(st, lib().uno_last_error(self.h).decode())
+
+    def _empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device=self.device)
+
+    # -------------------------------------------------------------------- calls
+    def prefill(self, seq_ids, prompts):
+        """prompts: list of 1-D int arrays (host) or one int32 device tensor per seq."""
+        torch = self.torch
+        ids, pids = _i32(seq_ids)
+        lens, plens = _i32([len(p) for p in prompts])
+        cat = torch.cat([torch.as_tensor(np.asarray(p, dtype=np.int32)) if not torch.is_tensor(p)
+                         else p.to(torch.int32).cpu() for p in prompts]).to(self.device)
+        self._check(lib().uno_prefill(self.h, len(ids), pids, _ptr(cat), plens))
+        self._keep_alive = cat  # the copy stays valid until the stream reaches it
+
+    def draft(self, seq_ids, want_probs=False):
+        ids, pids = _i32(seq_ids)
+        B, V = self.cfg.block_size, self.cfg.vocab
+        dr = self._empty((len(ids), B), self.torch.int32)
+        pr = self._empty((len(ids), B, V), self.torch.float32) if want_probs else None
+        self._check(lib().uno_draft(self.h, len(ids), pids, _ptr(dr), _ptr(pr)))
+        return dr, pr
+
+    def verify(self, seq_ids, want_probs=False):
+        ids, pids = _i32(seq_ids)
+        B, V = self.cfg.block_size, self.cfg.vocab
+        out = self._empty((len(ids), B + 1), self.torch.int32)
+        n_out = self._empty((len(ids),), self.torch.int32)
+        pr = self._empty((len(ids), B, V), self.torch.float32) if want_probs else None
+        self._check(lib().uno_verify(self.h, len(ids), pids, _ptr(out), _ptr(n_out), _ptr(pr)))
+        return out, n_out, pr
+
+    def step(self, seq_ids, out=None, n_out=None):
+        ids, pids = _i32(seq_ids)
+        B = self.cfg.block_size
+        if out is None:
+            out = self._empty((len(ids), B + 1), self.torch.int32)
+        if n_out is None:
+            n_out = self._empty((len(ids),), self.torch.int32)
+        self._check(lib().uno_step(self.h, len(ids), pids, _ptr(out), _ptr(n_out)))
+        return out, n_out
+
+    def accept(self, p, q, draft, seq_ids, pos, iters):
+        """Accept kernel on given tensors: p [n,B,V], q [n,B-1,V], draft [n,B]; seq_ids,
+        pos, iters device int32 [n]."""
+        n, B = draft.shape
+        out = self._empty((n, B + 1), self.torch.int32)
+        n_out = self._empty((n,), self.torch.int32)
+        self._check(lib().uno_accept(self.h, n, _ptr(p), _ptr(q), _ptr(draft), _ptr(seq_ids),
+                                     _ptr(pos), _ptr(iters), _ptr(out), _ptr(n_out)))
+        return out, n_out
+
+    def sample(self, w, seq_ids, pos, iters, stream_id):
+        rows = w.shape[0]
+        idx = self._empty((rows,), self.torch.int32)
+        self._check(lib().uno_sample(self.h, rows, _ptr(w), _ptr(seq_ids), _ptr(pos),
+                                     _ptr(iters), stream_id, _ptr(idx)))
+        return idx
+
+    def forward(self, seq_ids, rows_per_seq, pos, gate, tokens=None, hidden_in=None,
+                want_hidden=False, want_logits=False):
+        ids, pids = _i32(seq_ids)
+        R = len(ids) * rows_per_seq
+        hid = self._empty((R, self.cfg.d_model), self.torch.float32) if want_hidden else None
+        lg = self._empty((R, self.cfg.vocab), self.torch.float32) if want_logits else None
+        self._check(lib().uno_forward(self.h, len(ids), pids, rows_per_seq, _ptr(tokens),
+                                      _ptr(hidden_in), _ptr(pos), _ptr(gate), _ptr(hid), _ptr(lg)))
+        return hid, lg
+
+    def kv_import(self, seq_id, k, v, pending, iteration=0):
+        """k, v: device tensors [layers, len, Hkv, hd] of the storage dtype."""
+        self._check(lib().uno_kv_import(self.h, seq_id, k.shape[1], _ptr(k), _ptr(v), pending,
+                                        iteration))
+
+    def kv_export(self, seq_id, length):
+        cfg = self.cfg
+        dt = self.torch.bfloat16 if cfg.dtype == "bf16" else self.torch.float32
+        shape = (cfg.n_layers, length, cfg.n_kv_heads, cfg.head_dim)
+        k, v = self._empty(shape, dt), self._empty(shape, dt)
+        self._check(lib().uno_kv_export(self.h, seq_id, length, _ptr(k), _ptr(v)))
+        return k, v
+
+    def seq_state(self, seq_id):
+        a, b, c = C.c_int32(), C.c_int32(), C.c_int32()
+        self._check(lib().uno_seq_state(self.h, seq_id, C.byref(a), C.byref(b), C.byref(c)))
+        return a.value, b.value, c.value
+
+    def release(self, seq_id):
+        self._check(lib().uno_release(self.h, seq_id))
+
+    def sync(self):
+        self._check(lib().uno_sync(self.h))
+
+    def free_pages(self):
+        return lib().uno_free_pages(self.h)
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().uno_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def to_device(weights_np, cfg, device="cuda"):
+    """Copy a synth.weights_numpy dict to device tensors of the storage dtype."""
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(device)
+
+    out = {k: t(weights_np[k]) for k in ("embed", "lm_head", "final_norm") if k in weights_np}
+    out["layers"] = []
+    for lw in weights_np["layers"]:
+        d = {"attn_norm": t(lw["attn_norm"]), "mlp_norm": t(lw["mlp_norm"]),
+             "w": {p: t(a) for p, a in lw["w"].items()}}
+        if "la" in lw:
+            d["la"] = {p: t(a) for p, a in lw["la"].items()}
+            d["lb"] = {p: t(a) for p, a in lw["lb"].items()}
+        out["layers"].append(d)
+    return out

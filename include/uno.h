@@ -1,0 +1,211 @@
+/*
+ * uno.h -- C ABI of the MI355X (gfx950) Psi-Spec draft-and-verify decode step for
+ * diffusion-augmented LLMs ("Uno").
+ *
+ * The method (pages cited by title and section):
+ *   [summary]  ai-papers-daily summary of "Unlocking Lossless Speedups in LLMs via
+ *              Discrete Diffusion", section "方法关键点" (method key points);
+ *   [blog]     shibing624 reading notes "...Uno 的无损加速之路", sections
+ *              "方法核心：一个模型，两套权重" (method core), "Diffusion Distillation：
+ *              一步蒸馏 + 块级扩散" (distillation), "Ψ-Spec 采样器：起草、验证、两种模式"
+ *              (the Psi-Spec sampler).
+ *   One causal decoder holds the frozen AR weights plus a rank-r LoRA on every
+ *   layer (r 128, alpha 256 for the 8B models) [summary; blog method core].  A draft
+ *   forward (base + LoRA) proposes a block of B tokens in parallel; its first token
+ *   uses the AR weights only and is always accepted.  A verify forward (base only)
+ *   over the same KV cache scores the block, the longest accepted prefix is kept
+ *   and the first rejected position is resampled from max(0, p - q) renormalised
+ *   [blog Psi-Spec sampler].  Two forwards per iteration give 1 <= tokens per
+ *   forward <= (B+1)/2.  One gated forward over [x, z1] with a block-causal mask
+ *   yields teacher (AR) and student (AR+LoRA) logits [blog distillation].
+ *
+ * Readings the library fixes where the pages are silent:
+ *   - decoder: pre-norm RMSNorm, rotate-half RoPE, grouped-query attention, SwiGLU,
+ *     no biases, untied embedding and LM head; the MASK id's logit is -inf;
+ *   - LoRA on all seven projections: y = h W^T + gate * bf16((alpha/r) h A^T) B^T;
+ *   - draft rows [t, MASK x (B-1)] at positions n..n+B-1 with gate [0,1,..,1];
+ *     verify rows [y_1..y_B] at n+1..n+B with gate 0; row r predicts position
+ *     (its own position + 1);
+ *   - accept y_i iff u_i * q_i(y_i) < p_i(y_i) in float32;
+ *   - keyed randomness: Philox4x64-10, key (seed, seq_id), counter (position the
+ *     draw decides, stream, iteration, 0), stream 0 draft / 1 accept / 2 resample;
+ *     a categorical draw is an inverse CDF over trunc(w * 2^40) integers with
+ *     threshold floor(word0 * T / 2^64); a uniform is (word0 >> 40) * 2^-24.
+ *
+ * Conventions for every call:
+ *   - Device pointers are BORROWED: the caller owns weights, the KV pool, the
+ *     workspace and every output buffer; the library frees none of them and calls
+ *     no device allocator.  Pointers named d_* are device memory, others host.
+ *   - Matrices are row-major.  Projection weights are [out, in] (K contiguous),
+ *     LoRA down A is [r, in], LoRA up B is [out, r], embedding and LM head
+ *     [vocab, d_model], norm gains [d_model].  Storage type is float32 or
+ *     bfloat16 as uno_config.dtype says; logits and probabilities are float32.
+ *   - Calls enqueue work on the context's stream and return without waiting,
+ *     except the ones marked "syncs".
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns an error and changes no state.
+ *   - Device-side faults of the method (NaN / negative probabilities, a row with
+ *     no integer mass, a KV write outside a sequence's pages) set a sticky flag
+ *     that uno_sync reports as UNO_ERR_NUMERIC / UNO_ERR_DEVICE.
+ *   - A context belongs to one host thread; calls on one context are serialised
+ *     on its stream.
+ */
+#ifndef UNO_H
+#define UNO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct uno_ctx uno_ctx;
+
+typedef enum {
+  UNO_OK = 0,
+  UNO_ERR_INVALID_ARG = 1,   /* bad shape, pointer, id or size; nothing enqueued      */
+  UNO_ERR_OUT_OF_PAGES = 2,  /* the KV page pool cannot hold the requested positions  */
+  UNO_ERR_STATE = 3,         /* call out of order (e.g. verify without a draft)       */
+  UNO_ERR_NUMERIC = 4,       /* NaN / negative probability or a row with no mass      */
+  UNO_ERR_DEVICE = 5,        /* a HIP call failed, or a device bounds check tripped   */
+  UNO_ERR_UNSUPPORTED = 6    /* a shape this build does not implement                 */
+} uno_status;
+
+typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
+
+/* Model shape and decoding limits.  mask_id must be vocab-1. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, mask_id;
+  int32_t lora_rank;        /* 0: no LoRA (the draft then uses the base weights)    */
+  float lora_alpha, rope_theta, rms_eps;
+  int32_t block_size;       /* B, 1..64                                             */
+  int32_t page_size;        /* tokens per KV page                                   */
+  int32_t max_seqs;         /* sequence ids are 0..max_seqs-1                        */
+  int32_t max_seq_len;      /* positions per sequence the KV cache must hold         */
+  int32_t n_pages;          /* pages in the KV pool                                  */
+  int32_t max_rows;         /* rows one forward may carry (>= max_seqs*block_size)   */
+  int32_t dtype;            /* uno_dtype                                             */
+  uint64_t seed;            /* Philox key word 0                                     */
+} uno_config;
+
+/* Weights: host arrays of device pointers, copied at uno_init (the device memory
+ * they point to must outlive the context).  embed / lm_head may be NULL when only
+ * hidden-state forwards (uno_forward with d_hidden_in / d_hidden_out) are used.
+ * lora_a / lora_b may be NULL (no adapter on that projection).
+ * Projection order: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down. */
+typedef struct {
+  const void* embed;                 /* [vocab, d]                 */
+  const void* lm_head;               /* [vocab, d]                 */
+  const void* final_norm;            /* [d]                        */
+  const void* const* attn_norm;      /* [n_layers] -> [d]          */
+  const void* const* mlp_norm;       /* [n_layers] -> [d]          */
+  const void* const* w[7];           /* [n_layers] -> [out, in]    */
+  const void* const* lora_a[7];      /* [n_layers] -> [r, in]      */
+  const void* const* lora_b[7];      /* [n_layers] -> [out, r]     */
+} uno_weights;
+
+/* Sizes of the caller-allocated KV pool and workspace for a config.
+ * KV pool layout (exposed for inspection only; use uno_kv_import/export):
+ * [layer][K|V][page][kv_head][page_size][head_dim] of the storage type. */
+uno_status uno_query_sizes(const uno_config* cfg, size_t* kv_pool_bytes,
+                           size_t* workspace_bytes);
+
+/* Create a context on the current HIP device.  kv_pool / workspace are device
+ * buffers of at least the queried sizes; stream is a hipStream_t (NULL = the
+ * default stream).  Syncs (uploads the RoPE table). */
+uno_status uno_init(const uno_config* cfg, const uno_weights* weights, void* d_kv_pool,
+                    size_t kv_pool_bytes, void* d_workspace, size_t workspace_bytes,
+                    void* stream, uno_ctx** out);
+
+/* Prefill (the AR forward that fills the KV cache): for each listed sequence,
+ * run gate-0 rows prompt[0..P-2] at positions 0..P-2 and leave prompt[P-1] as the
+ * pending token; the sequence's iteration counter restarts at 0.
+ * seq_ids, prompt_lens: host [n]; d_prompts: device int32, the prompts
+ * concatenated in order.  Each prompt length is >= 1 and <= max_seq_len. */
+uno_status uno_prefill(uno_ctx* ctx, int32_t n, const int32_t* seq_ids,
+                       const int32_t* d_prompts, const int32_t* prompt_lens);
+
+/* Draft forward [blog Psi-Spec sampler]: rows [t, MASK x (B-1)] at n..n+B-1 with
+ * gate [0,1,...,1]; samples y_1 from row 0 (AR) and y_i from row i-1 (q_i).
+ * d_draft: device int32 [n, B] (y_1..y_B), may be NULL.  d_probs: device float32
+ * [n, B, vocab] (row 0 = p(y_1), rows 1.. = q_2..q_B), may be NULL. */
+uno_status uno_draft(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_draft,
+                     float* d_probs);
+
+/* Verify forward + accept/resample + commit [blog Psi-Spec sampler]: rows
+ * [y_1..y_B] at n+1..n+B with gate 0; accepts the longest prefix, resamples the
+ * first rejected slot from max(0, p_k - q_k) (bonus row p_{B+1} if none fails),
+ * commits positions n..n+k-1 and makes z pending.  d_out: device int32 [n, B+1]
+ * (k tokens, then -1); d_n_out: device int32 [n] (k in [2, B+1]).  d_probs: device
+ * float32 [n, B, vocab] (p_2..p_{B+1}), may be NULL.  Needs a preceding uno_draft
+ * of exactly these sequences. */
+uno_status uno_verify(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
+                      int32_t* d_n_out, float* d_probs);
+
+/* One Psi-Spec iteration: uno_draft followed by uno_verify. */
+uno_status uno_step(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
+                    int32_t* d_n_out);
+
+/* Accept/resample on caller-given probabilities (the parity entry of the accept
+ * kernel), using the context's seed and workspace; the sequence state is not
+ * touched.  d_p: [n, B, V] = p_2..p_{B+1}; d_q: [n, B-1, V] = q_2..q_B; d_draft:
+ * [n, B] = y_1..y_B; d_seq_ids, d_pos, d_iter: device int32 [n] (Philox key word 1,
+ * the pending position n, the iteration).  Outputs as uno_verify.  A NaN /
+ * negative / unnormalisable row sets the sticky numeric flag (see uno_sync).
+ * n <= max_seqs. */
+uno_status uno_accept(uno_ctx* ctx, int32_t n, const float* d_p, const float* d_q,
+                      const int32_t* d_draft, const int32_t* d_seq_ids, const int32_t* d_pos,
+                      const int32_t* d_iter, int32_t* d_out, int32_t* d_n_out);
+
+/* Categorical draws on caller-given rows (the parity entry of the sampler):
+ * row r of d_w [rows, V] (float32 weights in [0, 1]) is drawn with
+ * Philox(key = (seed, d_seq_ids[r]), counter = (d_pos[r], stream_id, d_iter[r], 0)).
+ * d_idx: device int32 [rows] (-1 when the row has no integer mass).
+ * rows <= max_rows. */
+uno_status uno_sample(uno_ctx* ctx, int32_t rows, const float* d_w, const int32_t* d_seq_ids,
+                      const int32_t* d_pos, const int32_t* d_iter, int32_t stream_id,
+                      int32_t* d_idx);
+
+/* Raw forward (parity entry): rows_per_seq rows for each listed sequence, row
+ * inputs either tokens (d_tokens [n*rows]) or hidden states (d_hidden_in float32
+ * [n*rows, d]); positions d_pos [n*rows] and gates d_gate (uint8) [n*rows].  Each
+ * row's K/V is written at its position (pages reserved as needed) and a row at
+ * position m attends to its sequence's positions 0..m.  Committed lengths and
+ * pending tokens are not changed.  Outputs (each may be NULL): the final residual
+ * stream d_hidden_out float32 [n*rows, d] (before the final norm) and d_logits
+ * float32 [n*rows, vocab]. */
+uno_status uno_forward(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t rows_per_seq,
+                       const int32_t* d_tokens, const float* d_hidden_in, const int32_t* d_pos,
+                       const uint8_t* d_gate, float* d_hidden_out, float* d_logits);
+
+/* Copy a sequence's K/V for positions [0, len) in from / out to contiguous device
+ * buffers [n_layers][len][n_kv_heads][head_dim] of the storage type.  Import
+ * reserves pages, sets the committed length to len and the pending token and
+ * iteration to the given values. */
+uno_status uno_kv_import(uno_ctx* ctx, int32_t seq_id, int32_t len, const void* d_k,
+                         const void* d_v, int32_t pending, int32_t iter);
+uno_status uno_kv_export(uno_ctx* ctx, int32_t seq_id, int32_t len, void* d_k, void* d_v);
+
+/* Committed length, pending token and iteration of a sequence.  Syncs. */
+uno_status uno_seq_state(uno_ctx* ctx, int32_t seq_id, int32_t* len, int32_t* pending,
+                         int32_t* iter);
+
+/* Return a sequence's pages to the pool. */
+uno_status uno_release(uno_ctx* ctx, int32_t seq_id);
+
+/* Wait for the stream; report sticky device errors.  Syncs. */
+uno_status uno_sync(uno_ctx* ctx);
+
+/* Pages currently free in the pool (host bookkeeping, no sync). */
+int32_t uno_free_pages(const uno_ctx* ctx);
+
+/* Text of the last error on this context (never NULL). */
+const char* uno_last_error(const uno_ctx* ctx);
+
+void uno_destroy(uno_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UNO_H */

@@ -1,0 +1,137 @@
+"""GPU parity on the tiny fp32 decoder: raw forwards, the paged KV cache, and whole
+Psi-Spec iterations against the oracle (logits <= 1e-4 abs, probability TV <=
+1e-3, tokens / accept lengths identical, cache equal to the oracle's)."""
+import numpy as np
+import pytest
+
+from diffusion_drafted_lora_amd import configs, synth
+from oracle import model, psispec
+from tests.gpu_util import dev, engine, host, log
+
+pytestmark = pytest.mark.gpu
+
+TINY = configs.TINY
+LOGIT_TOL = 1e-4
+TV_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def w_np():
+    return synth.weights_numpy(TINY, 1000)
+
+
+def _tv(a, b):
+    return 0.5 * np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).sum(-1)
+
+
+def test_forward_logits_hidden_and_cache(w_np):
+    log("tiny forward")
+    eng = engine(TINY, w_np, max_seqs=2, max_rows=40)
+    r = np.random.default_rng(0)
+    R = 12
+    toks = r.integers(0, TINY.vocab, size=(2, R)).astype(np.int32)
+    pos = np.tile(np.arange(R, dtype=np.int32), (2, 1))
+    gate = (r.random((2, R)) < 0.5).astype(np.uint8)
+    hid, lg = eng.forward([0, 1], R, dev(pos.ravel()), dev(gate.ravel()), tokens=dev(toks.ravel()),
+                          want_hidden=True, want_logits=True)
+    cache = model.new_cache(TINY, 2, 40)
+    ref, xref = model.forward(TINY, w_np, toks, pos, gate, cache)
+    g = host(lg).reshape(2, R, -1)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.abs(g[fin] - ref[fin]).max() <= LOGIT_TOL
+    assert np.abs(host(hid).reshape(2, R, -1) - xref).max() <= LOGIT_TOL
+    # continue both sequences by 4 rows at positions 12..15 (ragged gates)
+    toks2 = r.integers(0, TINY.vocab, size=(2, 4)).astype(np.int32)
+    pos2 = np.tile(np.arange(R, R + 4, dtype=np.int32), (2, 1))
+    gate2 = np.array([[0, 1, 1, 0], [1, 1, 1, 1]], dtype=np.uint8)
+    _, lg2 = eng.forward([0, 1], 4, dev(pos2.ravel()), dev(gate2.ravel()),
+                         tokens=dev(toks2.ravel()), want_logits=True)
+    ref2, _ = model.forward(TINY, w_np, toks2, pos2, gate2, cache)
+    g2 = host(lg2).reshape(2, 4, -1)
+    fin = np.isfinite(ref2)
+    assert np.abs(g2[fin] - ref2[fin]).max() <= LOGIT_TOL
+    for s in range(2):
+        k, v = eng.kv_export(s, R + 4)
+        assert np.abs(host(k) - cache["k"][:, s, : R + 4]).max() <= 1e-5
+        assert np.abs(host(v) - cache["v"][:, s, : R + 4]).max() <= 1e-5
+    eng.sync()
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_decode_iterations_match_oracle(stress):
+    """prefill + 8 iterations of draft / verify / accept / commit on 5 sequences with
+    ragged prompt lengths; every intermediate checked against the oracle."""
+    log(f"tiny decode stress={stress}")
+    w = synth.weights_numpy(TINY, 1001, lm_head_std=0.35, lora_b_std=0.6) if stress \
+        else synth.weights_numpy(TINY, 1000)
+    S, seed = 5, 3000
+    lens = [16, 9, 1, 16, 4]
+    prompts = [synth.prompts(TINY, 2000 + i, 1, L)[0] for i, L in enumerate(lens)]
+    seq_ids = [4, 0, 2, 1, 3]
+    eng = engine(TINY, w, max_seqs=S, max_seq_len=TINY.max_len + 40, seed=seed)
+    eng.prefill(seq_ids, prompts)
+    dec = psispec.Decoder(TINY, w, seq_ids, seed, TINY.max_len + 40)
+    dec.prefill(prompts)
+    hist = []
+    for step in range(8):
+        y_g, pd_g = eng.draft(seq_ids, want_probs=True)
+        out_g, n_g, pv_g = eng.verify(seq_ids, want_probs=True)
+        r = dec.step()
+        pd, pv = host(pd_g), host(pv_g)
+        assert _tv(pd, r["P_d"]).max() <= TV_TOL
+        assert _tv(pv, r["P_v"]).max() <= TV_TOL
+        assert np.abs(pd - r["P_d"]).max() <= 1e-5
+        assert np.array_equal(host(y_g), r["y"].astype(np.int32)), step
+        assert np.array_equal(host(n_g), r["n_out"]), step
+        assert np.array_equal(host(out_g), r["out"]), step
+        hist += r["n_out"].tolist()
+    for i, s in enumerate(seq_ids):
+        L, t, it = eng.seq_state(s)
+        assert (L, t, it) == (int(dec.n[i]), int(dec.t[i]), int(dec.it[i]))
+        k, v = eng.kv_export(s, L)
+        assert np.abs(host(k) - dec.cache["k"][:, i, :L]).max() <= 1e-5
+        assert np.abs(host(v) - dec.cache["v"][:, i, :L]).max() <= 1e-5
+    assert min(hist) >= 2 and max(hist) <= TINY.block_size + 1
+    log(f"accept lengths {sorted(set(hist))}")
+    eng.sync()
+
+
+def test_step_equals_draft_then_verify_and_release(w_np):
+    S = 3
+    prompts = list(synth.prompts(TINY, 2100, S))
+    outs = []
+    for mode in ("step", "split"):
+        eng = engine(TINY, w_np, max_seqs=S, seed=9)
+        eng.prefill([0, 1, 2], prompts)
+        seq = []
+        for _ in range(4):
+            if mode == "step":
+                o, n = eng.step([0, 1, 2])
+            else:
+                eng.draft([0, 1, 2])
+                o, n, _ = eng.verify([0, 1, 2])
+            seq.append((host(o).copy(), host(n).copy()))
+        outs.append(seq)
+        free0 = eng.free_pages()
+        eng.release(1)
+        assert eng.free_pages() > free0
+        eng.sync()
+    for (a, b), (c, d) in zip(*outs):
+        assert np.array_equal(a, c) and np.array_equal(b, d)
+
+
+def test_state_errors(w_np):
+    from diffusion_drafted_lora_amd import uno
+    eng = engine(TINY, w_np, max_seqs=2, seed=9)
+    with pytest.raises(uno.UnoError) as e:
+        eng.draft([0])                       # not prefilled
+    assert e.value.status == 3
+    eng.prefill([0], [synth.prompts(TINY, 1, 1)[0]])
+    with pytest.raises(uno.UnoError) as e:
+        eng.verify([0])                      # no draft
+    assert e.value.status == 3
+    with pytest.raises(uno.UnoError) as e:
+        eng.draft([0, 0])                    # duplicate id
+    assert e.value.status == 1
+    eng.sync()
