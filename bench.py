@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the Psi-Spec draft-and-verify decode step on one MI355X.
+
+Workload (default): a Qwen3-8B-shaped decoder (36 layers, d 4096, 32 q / 8 kv
+heads of 128, SwiGLU 12288, vocab 151936) in bf16 with a gated rank-128 LoRA
+(alpha 256) on all seven projections of every layer, random N(0, 0.02) weights
+generated on the GPU; batch 1, a 1024-token uniform prompt, block B = 16, the
+linear sampler with Philox keys, 16-token KV pages.  A step is one whole
+iteration: the draft forward, the draft draws, the verify forward, the accept /
+resample test and the commit.  W untimed steps, then exactly K timed steps.
+
+Reported: accepted tokens/s (value), positions/s, tokens per forward, whole-step
+algorithmic HBM GB/s, the roofline of the dominant kernel (the gate/up
+gated-LoRA linear, timed with HIP events on the library's stream), a per-class
+kernel time breakdown, and the CPU oracle timed on a bounded sample on the host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "accepted tokens/s/GPU (Ψ-Spec linear, 8B-shape) at bs=1 & bs=128; HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def model_bytes(cfg):
+    """Algorithmic bytes of one forward that do not depend on the context:
+    layer weights (+ LoRA) and the LM head, bf16."""
+    d, q, kv, f, V, r = (cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim, cfg.vocab,
+                         cfg.lora_rank)
+    layer = (q * d + 2 * kv * d + d * q + 2 * f * d + d * f) * 2
+    lora = ((d + q) * r + 2 * (d + kv) * r + (q + d) * r + 2 * (d + f) * r + (f + d) * r) * 2
+    return cfg.n_layers * layer + V * d * 2, cfg.n_layers * lora
+
+
+def kv_bytes_per_pos(cfg):
+    return cfg.n_layers * 2 * cfg.kv_dim * 2
+
+
+def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import model, psispec, rng
+    from diffusion_drafted_lora_amd import configs, synth
+
+    one = cfg.with_(n_layers=1)
+    lw = eng_w["layers"][0]
+    f32 = lambda t: t.float().cpu().numpy()
+    w1 = {"final_norm": np.ones(cfg.d_model, np.float32),
+          "layers": [{"attn_norm": f32(lw["attn_norm"]), "mlp_norm": f32(lw["mlp_norm"]),
+                      "w": {p: f32(t) for p, t in lw["w"].items()},
+                      "la": {p: f32(t) for p, t in lw["la"].items()},
+                      "lb": {p: f32(t) for p, t in lw["lb"].items()}}]}
+    kc = torch.from_numpy(synth.normal(9001, (1, ctx, cfg.n_kv_heads, cfg.head_dim)))
+    kc = kc.to(torch.bfloat16).float().numpy()
+    B = cfg.block_size
+    cache = model.new_cache(one, 1, ctx + B + 2)
+    cache["k"][0, 0, :ctx] = kc[0]
+    cache["v"][0, 0, :ctx] = kc[0]
+    xd = synth.normal(9002, (1, B, cfg.d_model))
+    gate = np.ones((1, B))
+    gate[0, 0] = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        model.forward(one, w1, None, np.arange(ctx, ctx + B)[None], gate, cache, hidden_in=xd,
+                      want_logits=False)
+        model.forward(one, w1, None, np.arange(ctx + 1, ctx + B + 1)[None], np.zeros((1, B)),
+                      cache, hidden_in=xd, want_logits=False)
+        reps += 1
+        if time.perf_counter() - t0 > 8.0 or reps >= 4:
+            break
+    t_layer = (time.perf_counter() - t0) / reps
+    # LM head on 1/8 of the vocabulary, both forwards' rows, scaled by 8
+    W = eng_w["lm_head"][: cfg.vocab // 8].float().cpu().numpy()
+    h = synth.normal(9003, (2 * B, cfg.d_model))
+    t0 = time.perf_counter()
+    lg = model.bf16_round(h) @ W.T
+    model.probs(lg)
+    t_lm = (time.perf_counter() - t0) * 8
+    # draft draws and one accept / resample over the full vocabulary
+    P = synth.prob_rows(9004, (1, B, cfg.vocab))
+    t0 = time.perf_counter()
+    for j in range(B):
+        rng.sample_icdf(P[0, j], rng.draw_word(1, 0, ctx + j, 0, 0))
+    y = np.zeros((1, B), dtype=np.int64)
+    psispec.accept_block(P, P[:, : B - 1], y, 1, [0], [ctx], [0])
+    t_samp = time.perf_counter() - t0
+    t_iter = cfg.n_layers * t_layer + t_lm + t_samp
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": tokens_per_iter / t_iter, "unit": "tokens/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle with bf16 storage rounding: 1 of {cfg.n_layers} layers "
+                   f"(16 draft rows + 16 verify rows at context {ctx}) timed {reps}x, the LM head "
+                   f"on 1/8 of the vocabulary scaled x8, 16 draft draws and one accept/resample; "
+                   f"iteration time = {cfg.n_layers} x layer pair + LM head + sampling = "
+                   f"{t_iter:.2f} s; tokens per iteration {tokens_per_iter:.3f} from the GPU run"),
+        "seconds_per_iteration": t_iter,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--prompt", type=int, default=1024)
+    ap.add_argument("--layers", type=int, default=None, help="(debug) fewer layers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown-steps", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=1002)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the Psi-Spec step is data parallel over sequences "
+              "with no cross-GPU exchange, and this build runs on a single MI355X; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from diffusion_drafted_lora_amd import configs, synth, uno
+
+    cfg = configs.MODEL8B
+    if args.layers:
+        cfg = cfg.with_(n_layers=args.layers)
+    B = cfg.block_size
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    log(f"generating weights ({cfg.n_layers} layers) on the GPU")
+    w = synth.weights_torch(cfg, args.seed, dev)
+    max_new = (args.warmup + args.steps + args.breakdown_steps + 1) * (B + 1)
+    if args.prompt + max_new > cfg.prompt_len + cfg.new_tokens + B + 1:
+        log("note: steps exceed the 1K/8K protocol length; the context grows beyond 9216")
+    max_len = args.prompt + max_new + B + 2
+    eng = uno.Engine(cfg, w, max_seqs=1, max_seq_len=max_len, max_rows=16, seed=3002, device=dev)
+    prompt = synth.prompts(cfg, 2002, 1, args.prompt)[0]
+    log(f"prefill {args.prompt} tokens")
+    t0 = time.perf_counter()
+    eng.prefill([0], [prompt])
+    eng.sync()
+    t_prefill = time.perf_counter() - t0
+    stream = eng.stream
+    K, W = args.steps, args.warmup
+    outs = torch.empty((W + K, B + 1), dtype=torch.int32, device=dev)
+    nouts = torch.empty((W + K,), dtype=torch.int32, device=dev)
+    log(f"warmup {W} steps")
+    for i in range(W):
+        eng.step([0], out=outs[i], n_out=nouts[i:i + 1])
+    eng.sync()
+    ctx0 = eng.seq_state(0)[0]
+    log(f"timed {K} steps from context {ctx0}")
+    eng.timing(["linear_swiglu"])
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(W, W + K):
+        eng.step([0], out=outs[i], n_out=nouts[i:i + 1])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    eng.sync()
+    n_sw, ms_sw, b_sw, f_sw = eng.timing_read("linear_swiglu")
+    eng.timing([])
+    nout = nouts[W:].cpu().numpy().astype(np.int64)
+    ctx1 = eng.seq_state(0)[0]
+    tokens = int(nout.sum())
+    sec = wall
+    # algorithmic bytes of the timed steps
+    fixed, lora = model_bytes(cfg)
+    kvp = kv_bytes_per_pos(cfg)
+    ctxs = ctx0 + np.concatenate([[0], np.cumsum(nout)[:-1]])
+    step_bytes = 2 * fixed + lora + kvp * (2 * ctxs + 2 * B).astype(np.float64)
+    total_bytes = float(step_bytes.sum())
+
+    # per-class breakdown on a few extra steps
+    classes = list(uno.KC)
+    eng.timing(classes)
+    for i in range(args.breakdown_steps):
+        eng.step([0])
+    eng.sync()
+    breakdown = {}
+    for c in classes:
+        n, ms, b, f = eng.timing_read(c)
+        if n:
+            breakdown[c] = {"launches_per_step": n / args.breakdown_steps,
+                            "ms_per_step": ms / args.breakdown_steps,
+                            "GB/s": (b / 1e9) / (ms / 1e3) if ms > 0 else None}
+    eng.timing([])
+
+    tpf = tokens / (2.0 * K)
+    sw_bytes_per_launch = b_sw / max(n_sw, 1)
+    sw_ms = ms_sw / max(n_sw, 1)
+    achieved = (sw_bytes_per_launch / 1e9) / (sw_ms / 1e3)
+    result = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": 1e3 * sec / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random N(0,0.02) weights generated on the GPU, uniform prompt)",
+        "config": {"workload": "qwen3-8b-shape 36L bf16 + gated LoRA r128, batch 1, "
+                               f"prompt {args.prompt}, B {B}, linear Psi-Spec, paged KV (16)",
+                   "batch": 1, "block": B, "layers": cfg.n_layers,
+                   "context_start": int(ctx0), "context_end": int(ctx1)},
+        "positions_per_s": 2 * B * K / sec,
+        "iterations_per_s": K / sec,
+        "tokens_per_forward": tpf,
+        "step_gpu_ms": gpu_ms / K,
+        "hbm_gbs_step_algorithmic": total_bytes / 1e9 / sec,
+        "hbm_frac_step": total_bytes / 1e9 / sec / HBM_PEAK_GBS,
+        "prefill_s": t_prefill,
+        "roofline": {
+            "kernel": "gated-LoRA gate/up linear + SwiGLU (k_gemm_bf16<2,8,2>)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "bytes_per_launch": sw_bytes_per_launch, "us_per_launch": 1e3 * sw_ms,
+            "launches": n_sw,
+        },
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, tokens / K)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,6 +122,11 @@ struct uno_ctx {
   hipEvent_t snap_event = nullptr;
   bool snap_inflight = false;
   std::vector<int> snap_base;
+  // kernel timing
+  uint32_t tmask = 0;
+  std::vector<hipEvent_t> tev;          // event pool, two per recorded launch
+  struct TRec { int cls; int ev; double bytes, flops; };
+  std::vector<TRec> trec;
   std::string err;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
@@ -144,6 +149,52 @@ uno_status hip_fail(uno_ctx* c, hipError_t e, const char* where) {
     hipError_t e_ = (call);                                  \
     if (e_ != hipSuccess) return hip_fail(ctx, e_, #call);   \
   } while (0)
+
+constexpr int kTimedLaunches = 8192;
+
+// Brackets one launch with events when its class is being timed.
+struct Timed {
+  uno_ctx* c;
+  int cls, ev = -1;
+  double bytes, flops;
+  Timed(uno_ctx* c_, int cls_, double b, double f) : c(c_), cls(cls_), bytes(b), flops(f) {
+    if ((c->tmask >> cls) & 1u) {
+      const size_t i = c->trec.size() * 2;
+      if (i + 2 <= c->tev.size() && hipEventRecord(c->tev[i], c->stream) == hipSuccess)
+        ev = (int)i;
+    }
+  }
+  ~Timed() {
+    if (ev >= 0 && hipEventRecord(c->tev[ev + 1], c->stream) == hipSuccess)
+      c->trec.push_back({cls, ev, bytes, flops});
+  }
+};
+
+// Algorithmic bytes and flops of one gated-LoRA linear launch: every weight,
+// LoRA, activation and output element read or written once.
+void gemm_cost(const GemmArgs& a, int ncols, size_t ts, double* bytes, double* flops) {
+  const double M = a.M, K = a.K, r = a.r;
+  const double wcols = a.paired ? 2.0 * ncols : (double)ncols;
+  double b = wcols * K * ts + M * K * ts;
+  double f = 2.0 * M * wcols * K;
+  if (r > 0) {
+    int nl = 0;
+    for (int i = 0; i < a.nseg; ++i) if (a.seg[i].Bl) ++nl;
+    const double lcols = a.paired ? 2.0 * ncols : (double)ncols;
+    b += lcols * r * ts + M * r * nl * ts;
+    f += 2.0 * M * lcols * r;
+  }
+  switch (a.epi) {
+    case EPI_STORE_F32: b += M * ncols * 4; break;
+    case EPI_LORA_U: b += M * ncols * ts; break;
+    case EPI_RESID: b += M * ncols * 8; break;
+    case EPI_SWIGLU: b += M * ncols * ts; break;
+    case EPI_LOGITS: b += M * ncols * 4 + M * (ncols / 16) * 8; break;
+    default: break;
+  }
+  *bytes = b;
+  *flops = f;
+}
 
 uno_status check_config(const uno_config* c) {
   if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null config");
@@ -369,6 +420,13 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
   if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
 
+  auto run_gemm = [&](const GemmArgs& a, int ncols, int cls) -> uno_status {
+    double b, fl;
+    gemm_cost(a, ncols, sizeof(T), &b, &fl);
+    Timed t(c, cls, b, fl);
+    UNO_HIP(c, launch_gemm<T>(a, ncols, s));
+    return UNO_OK;
+  };
   auto lora_down = [&](const T* X, int K, int nproj, const int* pidx, int l) -> uno_status {
     GemmArgs a{};
     a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = 0;
@@ -379,8 +437,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.seg[i].N = r;
     }
     a.epi = EPI_LORA_U; a.ldo = nproj * r; a.out = ubuf; a.gate = gate; a.scale = sc;
-    UNO_HIP(c, launch_gemm<T>(a, nproj * r, s));
-    return UNO_OK;
+    return run_gemm(a, nproj * r, UNO_KC_LORA_DOWN);
   };
 
   for (int l = 0; l < g.n_layers; ++l) {
@@ -400,11 +457,14 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
         if (lora) { a.seg[i].Bl = c->lb[i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 3 * r; }
       }
       a.epi = EPI_STORE_F32; a.ldo = qd + 2 * kvd; a.out = qkv;
-      UNO_HIP(c, launch_gemm<T>(a, qd + 2 * kvd, s));
+      if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
     }
-    UNO_HIP(c, launch_rope_kv<T>(qkv, R, f.rows_per_seq, rs.call_seq, rs.row_pos, Hq,
-                                 c->at<float>(c->L.rope_cos), c->at<float>(c->L.rope_sin), qbuf,
-                                 kv, l, err, s));
+    {
+      Timed t(c, UNO_KC_MISC, 0, 0);
+      UNO_HIP(c, launch_rope_kv<T>(qkv, R, f.rows_per_seq, rs.call_seq, rs.row_pos, Hq,
+                                   c->at<float>(c->L.rope_cos), c->at<float>(c->L.rope_sin), qbuf,
+                                   kv, l, err, s));
+    }
     {
       AttnArgs a{};
       a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
@@ -412,6 +472,13 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.n_chunks = n_chunks; a.chunk = chunk; a.scale = 1.0f / sqrtf((float)hd);
       a.part_o = c->at<float>(c->L.part_o); a.part_ml = c->at<float>(c->L.part_ml);
       a.layer = l;
+      // algorithmic bytes: queries, every visible K/V row of each sequence once
+      // (bounded by ctx_bound), partials written and read, outputs
+      const double kvb = (double)f.n * f.ctx_bound * Hkv * hd * 2 * sizeof(T);
+      const double pb = (double)R * Hq * n_chunks * (hd + 2) * 4 * 2;
+      const double io = (double)R * qd * sizeof(T) * 2;
+      const double fl = 4.0 * R * Hq * hd * (double)f.ctx_bound;
+      Timed t(c, UNO_KC_ATTENTION, kvb + pb + io, fl);
       UNO_HIP(c, launch_attention<T>(a, kv, s));
     }
     static const int po[1] = {3};
@@ -423,7 +490,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.seg[0].W = c->w[3][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
       if (lora) { a.seg[0].Bl = c->lb[3][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
       a.epi = EPI_RESID; a.ldo = d; a.resid = x;
-      UNO_HIP(c, launch_gemm<T>(a, d, s));
+      if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
     // --- MLP block
     UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->mlp_norm[l]), R, d, g.rms_eps, xn, s));
@@ -438,7 +505,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
         if (lora) { a.seg[i].Bl = c->lb[4 + i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 2 * r; }
       }
       a.epi = EPI_SWIGLU; a.ldo = F; a.out = hbuf;
-      UNO_HIP(c, launch_gemm<T>(a, F, s));
+      if (uno_status st = run_gemm(a, F, UNO_KC_LINEAR_SWIGLU)) return st;
     }
     static const int pd[1] = {6};
     if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l); if (st) return st; }
@@ -449,7 +516,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.seg[0].W = c->w[6][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
       if (lora) { a.seg[0].Bl = c->lb[6][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
       a.epi = EPI_RESID; a.ldo = d; a.resid = x;
-      UNO_HIP(c, launch_gemm<T>(a, d, s));
+      if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
   }
   if (f.hidden_out)
@@ -463,8 +530,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
     a.epi = EPI_LOGITS; a.ldo = V; a.out = c->at<float>(c->L.logits);
     a.mask_col = g.mask_id; a.tile_stats = c->at<float>(c->L.tile_stats); a.n_tiles = V / 16;
-    UNO_HIP(c, launch_gemm<T>(a, V, s));
+    if (uno_status st = run_gemm(a, V, UNO_KC_LM_HEAD)) return st;
     if (f.probs_out) {
+      Timed t(c, UNO_KC_SAMPLING, (double)R * V * 8 + (double)R * (V / 16) * 8, 0);
       UNO_HIP(c, launch_row_stats(a.tile_stats, R, V / 16, c->at<float>(c->L.row_ml), s));
       UNO_HIP(c, launch_softmax(c->at<float>(c->L.logits), c->at<float>(c->L.row_ml), R, V,
                                 f.probs_out, s));
@@ -672,6 +740,7 @@ uno_status uno_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_d
   if ((st = forward(c, f))) return st;
   hipStream_t s = c->stream;
   RowDesc* desc = c->at<RowDesc>(c->L.desc);
+  Timed tsm(c, UNO_KC_SAMPLING, (double)n * B * V * 8, 0);
   UNO_HIP(c, launch_draft_desc(f.probs_out, n, B, V, c->cfg.seed, c->at<int32_t>(c->L.call_seq),
                                c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
                                c->at<int32_t>(c->L.draft_tok), desc, s));
@@ -706,6 +775,7 @@ uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_
   RowDesc* desc = c->at<RowDesc>(c->L.desc);
   int32_t* err = c->at<int32_t>(c->L.err);
   const float* pd = c->at<float>(c->L.probs_d);
+  Timed tsm(c, UNO_KC_SAMPLING, (double)n * V * 8 * 2, 0);
   UNO_HIP(c, launch_accept_test(c->cfg.seed, n, B, V, f.probs_out, pd + V, B,
                                 c->at<int32_t>(c->L.draft_tok), c->at<int32_t>(c->L.call_seq),
                                 c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
@@ -883,6 +953,41 @@ uno_status uno_sync(uno_ctx* c) {
   return UNO_OK;
 }
 
+uno_status uno_timing(uno_ctx* c, uint32_t class_mask) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (class_mask && c->tev.empty()) {
+    c->tev.resize(2 * kTimedLaunches, nullptr);
+    for (auto& e : c->tev) UNO_HIP(c, hipEventCreate(&e));
+  }
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  c->trec.clear();
+  c->tmask = class_mask;
+  return UNO_OK;
+}
+
+uno_status uno_timing_read(uno_ctx* c, int32_t cls, int64_t* launches, double* total_ms,
+                           double* bytes, double* flops) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (cls < 0 || cls >= UNO_KC_COUNT) return fail(c, UNO_ERR_INVALID_ARG, "bad kernel class");
+  UNO_HIP(c, hipStreamSynchronize(c->stream));
+  int64_t n = 0;
+  double ms = 0, b = 0, f = 0;
+  for (const auto& r : c->trec) {
+    if (r.cls != cls) continue;
+    float e = 0;
+    UNO_HIP(c, hipEventElapsedTime(&e, c->tev[r.ev], c->tev[r.ev + 1]));
+    ++n;
+    ms += e;
+    b += r.bytes;
+    f += r.flops;
+  }
+  if (launches) *launches = n;
+  if (total_ms) *total_ms = ms;
+  if (bytes) *bytes = b;
+  if (flops) *flops = f;
+  return UNO_OK;
+}
+
 int32_t uno_free_pages(const uno_ctx* c) { return c ? (int32_t)c->free_pages.size() : 0; }
 
 const char* uno_last_error(const uno_ctx* c) {
@@ -894,6 +999,8 @@ void uno_destroy(uno_ctx* c) {
   hipStreamSynchronize(c->stream);
   if (c->snap_host) hipHostFree(c->snap_host);
   if (c->snap_event) hipEventDestroy(c->snap_event);
+  for (auto e : c->tev)
+    if (e) hipEventDestroy(e);
   delete c;
 }
 

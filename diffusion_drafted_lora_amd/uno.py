@@ -22,7 +22,11 @@ PROJ = synth.PROJ
 EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_verify",
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
-            "uno_last_error", "uno_destroy")
+            "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_read")
+
+# kernel classes of uno_timing (uno_kernel_class)
+KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
+      "sampling": 5, "misc": 6}
 
 
 class UnoError(RuntimeError):
@@ -84,6 +88,9 @@ def lib():
         L.uno_last_error.restype = C.c_char_p
         L.uno_destroy.argtypes = [vp]
         L.uno_destroy.restype = None
+        L.uno_timing.argtypes = [vp, C.c_uint32]
+        L.uno_timing_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double), P(C.c_double),
+                                      P(C.c_double)]
         for name in EXPORTED:
             f = getattr(L, name)
             if f.restype is C.c_int:  # default restype: status codes
@@ -285,6 +292,20 @@ class Engine:
 
     def sync(self):
         self._check(lib().uno_sync(self.h))
+
+    def timing(self, classes=()):
+        """Start recording launches of the named kernel classes (empty: stop)."""
+        mask = 0
+        for c in classes:
+            mask |= 1 << KC[c]
+        self._check(lib().uno_timing(self.h, mask))
+
+    def timing_read(self, cls):
+        """(launches, total ms, algorithmic bytes, flops) recorded for a class."""
+        n, ms, b, f = C.c_int64(), C.c_double(), C.c_double(), C.c_double()
+        self._check(lib().uno_timing_read(self.h, KC[cls], C.byref(n), C.byref(ms), C.byref(b),
+                                          C.byref(f)))
+        return n.value, ms.value, b.value, f.value
 
     def free_pages(self):
         return lib().uno_free_pages(self.h)
