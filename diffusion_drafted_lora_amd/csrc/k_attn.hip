@@ -15,6 +15,7 @@
 namespace {
 
 constexpr int SUB = 32;   // keys per LDS sub-chunk
+constexpr int kMaxCombine = 64;   // chunk partials merged per (row, head)
 
 template <typename T, int MAXO>
 __global__ void __launch_bounds__(256)
@@ -153,25 +154,253 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
   }
 }
 
-// Merge the chunk partials of one (row, head) in chunk order.
+// Merge the chunk partials of one (row, head) in chunk order: one thread per
+// chunk loads its (max, sum) at once, thread 0 forms the weights in chunk order,
+// then every thread accumulates its output dimensions with unrolled loads.
 template <typename T>
-__global__ void k_attn_combine(AttnArgs a, int hd) {
+__global__ void __launch_bounds__(128)
+k_attn_combine(AttnArgs a, int hd) {
+  __shared__ float sm[kMaxCombine], ssum[kMaxCombine], sf[kMaxCombine];
+  __shared__ float sL;
   const int r = blockIdx.x / a.n_q_heads, h = blockIdx.x % a.n_q_heads;
   const int nc = min(a.row_pos[r] / a.chunk + 1, a.n_chunks);
   const size_t ph0 = ((size_t)r * a.n_q_heads + h) * a.n_chunks;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[(ph0 + c) * 2]);
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    float L = 0.0f, acc = 0.0f;
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    sm[c] = a.part_ml[(ph0 + c) * 2];
+    ssum[c] = a.part_ml[(ph0 + c) * 2 + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, sm[c]);
+    float L = 0.0f;
     for (int c = 0; c < nc; ++c) {
-      const float mc = a.part_ml[(ph0 + c) * 2];
-      if (mc == -INFINITY) continue;
-      const float f = expf(mc - M);
-      L += a.part_ml[(ph0 + c) * 2 + 1] * f;
-      acc += a.part_o[(ph0 + c) * hd + d] * f;
+      const float f = (sm[c] == -INFINITY) ? 0.0f : expf(sm[c] - M);
+      sf[c] = f;
+      L += ssum[c] * f;
     }
-    reinterpret_cast<T*>(a.out)[(size_t)r * a.n_q_heads * hd + h * hd + d] =
-        from_f<T>(L > 0.0f ? acc / L : 0.0f);
+    sL = L;
+  }
+  __syncthreads();
+  const float inv = sL > 0.0f ? 1.0f / sL : 0.0f;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    const float* po = a.part_o + ph0 * hd + d;
+    float acc = 0.0f;
+    int c = 0;
+    for (; c + 8 <= nc; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(c + u) * hd];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u] * sf[c + u];
+    }
+    for (; c < nc; ++c) acc += po[(size_t)c * hd] * sf[c];
+    reinterpret_cast<T*>(a.out)[(size_t)r * a.n_q_heads * hd + h * hd + d] = from_f<T>(acc * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA variant (head_dim 128).  Wave g of the workgroup owns query head
+// kvh * G + g for the tile's 16 rows.  Per 64-key sub-chunk: K (row-major) and
+// V (transposed) are staged in LDS; S = Q K^T on v_mfma_f32_16x16x32_bf16 with Q
+// held in registers; the online softmax runs in the accumulator layout (lane l
+// holds rows 4*(l/16)+i of column l%16); P goes through LDS to become the A
+// operand of P V.  Output accumulators share the row layout of S, so the
+// rescale by exp(m_old - m_new) needs no data movement.
+constexpr int MK = 64;            // keys per sub-chunk
+constexpr int HD = 128;           // head dim of the MFMA path
+constexpr int KPAD = HD + 8;      // LDS row of K (bf16), 16-byte pad
+constexpr int VPAD = MK + 8;      // LDS row of V^T (bf16)
+constexpr int PPAD = MK + 8;      // LDS row of P (bf16)
+
+__global__ void __launch_bounds__(512)
+k_attn_mfma(AttnArgs a, KvLayout kv) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  bf16* sK = reinterpret_cast<bf16*>(smem_raw);                 // [MK][KPAD]
+  bf16* sVt = sK + MK * KPAD;                                   // [HD][VPAD]
+  bf16* sP = sVt + HD * VPAD;                                   // [G][16][PPAD]
+  __shared__ int sPos[16];
+
+  const int c = blockIdx.x, kvh = blockIdx.y;
+  const int row_tiles = (a.rows_per_seq + 15) / 16;
+  const int si = blockIdx.z / row_tiles, rt = blockIdx.z % row_tiles;
+  const int Hkv = kv.n_kv_heads, G = a.n_q_heads / Hkv;
+  const int seq = a.call_seq[si];
+  const int r0 = si * a.rows_per_seq + rt * 16;
+  const int nrows = min(16, a.rows_per_seq - rt * 16);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
+  const int r16 = lane & 15, grp = lane >> 4;
+
+  // Loads that do not depend on each other go out together: row positions, the Q
+  // fragments of this wave's head, and (below) the first sub-chunk's K/V.
+  if (tid < 16) sPos[tid] = (tid < nrows) ? a.row_pos[r0 + tid] : -1;
+  const int kbeg = c * a.chunk;
+  int kend = kbeg + MK;      // provisional bound of the first sub-chunk
+  const int head = kvh * G + w;
+  const bf16* Q = reinterpret_cast<const bf16*>(a.q);
+  bf16x8 qf[HD / 32];
+  {
+    const bool ok = r16 < nrows;
+    const bf16* qr = Q + (size_t)(r0 + (ok ? r16 : 0)) * a.n_q_heads * HD + head * HD;
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + ks * 32 + grp * 8);
+      qf[ks] = ok ? v : bf16x8{};
+    }
+  }
+  // scores are scaled into the exp2 domain
+  const float sc = a.scale * 1.4426950408889634f;
+
+  float m[4], l[4];
+  f32x4 o[HD / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+#pragma unroll
+  for (int d = 0; d < HD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16* pool = reinterpret_cast<const bf16*>(kv.pool);
+  bf16* myP = sP + w * 16 * PPAD;
+  // K / V of a 64-key sub-chunk in 16-byte pieces (16 per key); each thread holds
+  // its pieces of K and of V in registers, prefetched one sub-chunk ahead.
+  constexpr int PF_MAX = MK * (HD / 8) / 256;          // 4 for >= 256 threads
+  const int npf = (MK * (HD / 8) + nthr - 1) / nthr;
+  bf16x8 pk[PF_MAX], pv[PF_MAX];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < PF_MAX; ++q) {
+      const int e = tid + q * nthr;
+      bf16x8 kk = {}, vv = {};
+      if (q < npf && e < MK * (HD / 8)) {
+        const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8, p = k0 + key;
+        const int pi = p / kv.page_size;
+        const int page = (p < kend && pi < kv.max_pages_per_seq)
+                             ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi] : -1;
+        if (page >= 0 && page < kv.n_pages) {
+          const size_t kb = ((((size_t)(a.layer * 2) * kv.n_pages + page) * Hkv + kvh) *
+                                 kv.page_size + (p % kv.page_size)) * HD + d8;
+          const size_t vb = ((((size_t)(a.layer * 2 + 1) * kv.n_pages + page) * Hkv + kvh) *
+                                 kv.page_size + (p % kv.page_size)) * HD + d8;
+          kk = *reinterpret_cast<const bf16x8*>(pool + kb);
+          vv = *reinterpret_cast<const bf16x8*>(pool + vb);
+        }
+      }
+      pk[q] = kk;
+      pv[q] = vv;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < PF_MAX; ++q) {
+      const int e = tid + q * nthr;
+      if (q < npf && e < MK * (HD / 8)) {
+        const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = pk[q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sVt[(d8 + j) * VPAD + key] = pv[q][j];
+      }
+    }
+  };
+  // first sub-chunk: positions beyond the rows are read (from reserved pages only)
+  // and masked below; this keeps the position reads off the critical path
+  fetch(kbeg);
+  __syncthreads();
+  int maxpos = -1;
+  for (int i = 0; i < nrows; ++i) maxpos = max(maxpos, sPos[i]);
+  if (kbeg > maxpos) return;
+  kend = min(kbeg + a.chunk, maxpos + 1);
+  int rpos[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rpos[i] = sPos[grp * 4 + i];
+  for (int k0 = kbeg; k0 < kend; k0 += MK) {
+    __syncthreads();               // previous sub-chunk fully consumed
+    stage();
+    if (k0 + MK < kend) fetch(k0 + MK);
+    __syncthreads();
+    // S = Q K^T for 4 key tiles of 16
+    f32x4 s[MK / 16];
+#pragma unroll
+    for (int j = 0; j < MK / 16; ++j) {
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sK + (j * 16 + r16) * KPAD + ks * 32 + grp * 8);
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[j], 0, 0, 0);
+      }
+    }
+    // mask, online softmax (rows 4*grp+i, column = key j*16 + r16)
+    float mt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < MK / 16; ++j) {
+        const int p = k0 + j * 16 + r16;
+        float v = s[j][i] * sc;
+        if (p >= kend || p > rpos[i]) v = -INFINITY;
+        s[j][i] = v;
+        mx = fmaxf(mx, v);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+      mt[i] = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(m[i], mt[i]);
+      const float f = (m[i] == -INFINITY) ? 0.0f : exp2f(m[i] - mn);
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < MK / 16; ++j) {
+        const float pv = (s[j][i] == -INFINITY) ? 0.0f : exp2f(s[j][i] - mn);
+        s[j][i] = pv;
+        ps += pv;
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 16);
+      l[i] = l[i] * f + ps;
+      m[i] = mn;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) o[d][i] *= f;
+    }
+    // P to LDS (bf16), row-major [16][MK]
+#pragma unroll
+    for (int j = 0; j < MK / 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) myP[(grp * 4 + i) * PPAD + j * 16 + r16] = (bf16)s[j][i];
+    __syncthreads();
+    // O += P V
+#pragma unroll
+    for (int ks = 0; ks < MK / 32; ++ks) {
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(myP + r16 * PPAD + ks * 32 + grp * 8);
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) {
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + (d * 16 + r16) * VPAD + ks * 32 + grp * 8);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[d], 0, 0, 0);
+      }
+    }
+  }
+  // partials (or the final output when the context has one chunk)
+  const bool single = a.n_chunks == 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = grp * 4 + i;
+    if (row >= nrows) continue;
+    const size_t rr = (size_t)(r0 + row);
+    if (single) {
+      const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
+      bf16* out = reinterpret_cast<bf16*>(a.out) + rr * a.n_q_heads * HD + head * HD;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) out[d * 16 + r16] = (bf16)(o[d][i] * inv);
+    } else {
+      const size_t ph = (rr * a.n_q_heads + head) * a.n_chunks + c;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) a.part_o[ph * HD + d * 16 + r16] = o[d][i];
+      if (r16 == 0) {
+        // stats in the natural-log domain, as the combine expects
+        a.part_ml[ph * 2] = m[i] * 0.6931471805599453f;
+        a.part_ml[ph * 2 + 1] = l[i];
+      }
+    }
   }
 }
 
@@ -189,25 +418,36 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   if (16 * G * kv.head_dim > 256 * 64 || a.chunk % SUB != 0) return hipErrorInvalidValue;
   const int R = a.n * a.rows_per_seq;
   if (R <= 0) return hipSuccess;
-  const size_t smem = attn_smem_bytes<T>(G, kv.head_dim);
-  const int nown = (16 * G * kv.head_dim + 255) / 256;
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   dim3 grid(a.n_chunks, kv.n_kv_heads, a.n * row_tiles);
+  const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G >= 4 && G <= 8 && a.chunk % MK == 0;
+  if (mfma) {
+    const size_t smem = (size_t)(MK * KPAD + HD * VPAD + G * 16 * PPAD) * 2;
+    if (smem > 64 * 1024) {
+      hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (ea != hipSuccess) return ea;
+    }
+    k_attn_mfma<<<grid, 64 * G, smem, s>>>(a, kv);
+  } else {
+    const size_t smem = attn_smem_bytes<T>(G, kv.head_dim);
+    const int nown = (16 * G * kv.head_dim + 255) / 256;
 #define UNO_ATTN_CASE(MO)                                                                   \
   if (nown <= MO) {                                                                         \
-    static bool set = false;                                                                \
-    if (!set) {                                                                             \
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial<T, MO>),      \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);          \
-      set = true;                                                                           \
+    if (smem > 64 * 1024) {                                                                 \
+      hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial<T, MO>), \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+      if (ea != hipSuccess) return ea;                                                      \
     }                                                                                       \
     k_attn_partial<T, MO><<<grid, 256, smem, s>>>(a, kv);                                   \
   } else
-  UNO_ATTN_CASE(1) UNO_ATTN_CASE(4) UNO_ATTN_CASE(16) UNO_ATTN_CASE(32) UNO_ATTN_CASE(64)
-  return hipErrorInvalidValue;
+    UNO_ATTN_CASE(1) UNO_ATTN_CASE(4) UNO_ATTN_CASE(16) UNO_ATTN_CASE(32) UNO_ATTN_CASE(64)
+    return hipErrorInvalidValue;
 #undef UNO_ATTN_CASE
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.n_chunks == 1 && mfma) return hipSuccess;   // the MFMA kernel wrote the outputs directly
   k_attn_combine<T><<<R * a.n_q_heads, kv.head_dim < 256 ? kv.head_dim : 256, 0, s>>>(
       a, kv.head_dim);
   return hipGetLastError();

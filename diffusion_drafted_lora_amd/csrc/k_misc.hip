@@ -61,23 +61,41 @@ __global__ void k_rows_setup(RowsSetup a) {
   }
 }
 
+// x[r] = E[tok[r]] (or the given hidden row); also the first RMSNorm's input
+// xg = T(x * g) and the fixed-point sum of x^2 (2^-32 units).
 template <typename T>
-__global__ void k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
-                        const float* __restrict__ hidden_in, int d, int V, float* x,
-                        int32_t* err) {
+__global__ void __launch_bounds__(256)
+k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
+        const float* __restrict__ hidden_in, int d, int V, float* x, const T* g, T* xg,
+        long long* ss, int32_t* err) {
+  __shared__ float sh[4];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * d;
-  if (hidden_in) {
-    for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = hidden_in[(size_t)r * d + c];
-    return;
+  const T* er = nullptr;
+  if (!hidden_in) {
+    int t = tok[r];
+    if (t < 0 || t >= V) {
+      if (threadIdx.x == 0 && err) atomicOr(err, UNO_DEVERR_NUMERIC);
+      t = 0;
+    }
+    er = E + (size_t)t * d;
   }
-  int t = tok[r];
-  if (t < 0 || t >= V) {
-    if (threadIdx.x == 0 && err) atomicOr(err, UNO_DEVERR_NUMERIC);
-    t = 0;
+  float sq = 0.0f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    const float v = hidden_in ? hidden_in[(size_t)r * d + c] : to_f(er[c]);
+    xr[c] = v;
+    if (xg) xg[(size_t)r * d + c] = from_f<T>(v * to_f(g[c]));
+    sq += v * v;
   }
-  const T* er = E + (size_t)t * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = to_f(er[c]);
+  if (ss) {
+    // per-wave partials in fixed point, so the total does not depend on order
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if ((threadIdx.x & 63) == 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(ss + r),
+                (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
+  }
+  (void)sh;
 }
 
 template <typename T>
@@ -162,30 +180,50 @@ __global__ void k_rope_kv(const float* __restrict__ qkv, int rows_per_seq,
   }
 }
 
-// Reduce the per-tile (max, sum exp) partials of one logits row (fixed order).
-__global__ void __launch_bounds__(256)
+// Reduce the per-tile (max, sum exp) partials of one logits row (fixed order):
+// each of the 1024 threads merges a strided subset with its loads issued first,
+// then thread 0 merges the thread results in thread order.
+__global__ void __launch_bounds__(1024)
 k_row_stats(const float* __restrict__ tile_stats, int n_tiles, float* row_ml) {
-  __shared__ float shm[256], shs[256];
+  __shared__ float shm[1024], shs[1024];
   const int r = blockIdx.x;
-  const float* ts = tile_stats + (size_t)r * n_tiles * 2;
+  const float2* ts = reinterpret_cast<const float2*>(tile_stats + (size_t)r * n_tiles * 2);
   float m = -INFINITY, s = 0.0f;
-  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
-    const float mt = ts[2 * t], st = ts[2 * t + 1];
-    if (mt == -INFINITY) continue;
-    if (mt > m) { s = s * expf(m - mt) + st; m = mt; }
-    else s += st * expf(mt - m);
+  for (int t0 = threadIdx.x; t0 < n_tiles; t0 += 4 * blockDim.x) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * blockDim.x;
+      v[u] = t < n_tiles ? ts[t] : make_float2(-INFINITY, 0.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mt = v[u].x, st = v[u].y;
+      if (mt == -INFINITY) continue;
+      if (mt > m) { s = s * expf(m - mt) + st; m = mt; }
+      else s += st * expf(mt - m);
+    }
   }
   shm[threadIdx.x] = m;
   shs[threadIdx.x] = s;
   __syncthreads();
+  // tree merge in a fixed pairing (deterministic)
+  for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      const float m1 = shm[threadIdx.x], s1 = shs[threadIdx.x];
+      const float m2 = shm[threadIdx.x + off], s2 = shs[threadIdx.x + off];
+      const float M = fmaxf(m1, m2);
+      float S = 0.0f;
+      if (m1 != -INFINITY) S += s1 * expf(m1 - M);
+      if (m2 != -INFINITY) S += s2 * expf(m2 - M);
+      shm[threadIdx.x] = M;
+      shs[threadIdx.x] = S;
+    }
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int i = 0; i < (int)blockDim.x; ++i) M = fmaxf(M, shm[i]);
-    float S = 0.0f;
-    for (int i = 0; i < (int)blockDim.x; ++i)
-      if (shm[i] != -INFINITY) S += shs[i] * expf(shm[i] - M);
-    row_ml[2 * r] = M;
-    row_ml[2 * r + 1] = S;
+    row_ml[2 * r] = shm[0];
+    row_ml[2 * r + 1] = shs[0];
   }
 }
 
@@ -229,8 +267,9 @@ hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
-                        int V, float* x, int32_t* err, hipStream_t s) {
-  k_embed<T><<<R, 256, 0, s>>>(E, tok, hidden_in, d, V, x, err);
+                        int V, float* x, const T* g, T* xg, long long* ss, int32_t* err,
+                        hipStream_t s) {
+  k_embed<T><<<R, 256, 0, s>>>(E, tok, hidden_in, d, V, x, g, xg, ss, err);
   return hipGetLastError();
 }
 
@@ -253,7 +292,7 @@ hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32
 
 hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* row_ml,
                             hipStream_t s) {
-  k_row_stats<<<R, 256, 0, s>>>(tile_stats, n_tiles, row_ml);
+  k_row_stats<<<R, 1024, 0, s>>>(tile_stats, n_tiles, row_ml);
   return hipGetLastError();
 }
 
@@ -280,7 +319,8 @@ hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int 
 
 #define UNO_INST(T)                                                                         \
   template hipError_t launch_embed<T>(const T*, const int32_t*, const float*, int, int, int, \
-                                      float*, int32_t*, hipStream_t);                       \
+                                      float*, const T*, T*, long long*, int32_t*,           \
+                                      hipStream_t);                                         \
   template hipError_t launch_rmsnorm<T>(const float*, const T*, int, int, float, T*,         \
                                         hipStream_t);                                       \
   template hipError_t launch_rope_kv<T>(const float*, int, int, const int32_t*,              \

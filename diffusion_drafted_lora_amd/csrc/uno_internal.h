@@ -89,8 +89,17 @@ UNO_DEV float row_weight(const RowDesc& d, int mode, int j) {
 constexpr int CDF_CHUNK = 2048;  // elements per chunk of the integer CDF
 constexpr int CDF_THREADS = 256;
 
+struct KvLayout {
+  void* pool;
+  int32_t n_pages, n_kv_heads, page_size, head_dim, n_layers;
+  const int32_t* block_table;   // [max_seqs, max_pages_per_seq]
+  int32_t max_pages_per_seq;
+  int32_t pad;
+};
+
 // ------------------------------------------------------------ GEMM interfaces
 enum GemmEpi : int32_t {
+  EPI_QKV = 5,         // pair-permuted q|k|v columns: RoPE, q -> qbuf, k / v -> KV pages
   EPI_STORE_F32 = 0,   // out_f32[m, n] = acc
   EPI_LORA_U = 1,      // out_t[m, n] = gate[m] ? T(scale * acc) : 0
   EPI_RESID = 2,       // resid[m, n] += acc
@@ -98,10 +107,16 @@ enum GemmEpi : int32_t {
   EPI_LOGITS = 4,      // out_f32[m, n] = acc (MASK column -inf) + per-tile max / sum-exp
 };
 
+// LoRA intermediates accumulated in fixed point: t = sum x*A in units of 2^-32
+// (int64, order-independent integer sums).
+constexpr float LORA_FX_SCALE = 4294967296.0f;     // 2^32
+constexpr double LORA_FX_INV = 1.0 / 4294967296.0;
+
 struct GemmSeg {
   const void* W;     // [N, K] of the storage type
   const void* Bl;    // LoRA up [N, r] (or null)
-  const void* U;     // LoRA intermediate [M, ldu] for this segment (or null)
+  const void* U;     // LoRA intermediate [M, ldu] of the storage type (or null)
+  const long long* Ufx;  // bf16 path: fixed-point t [M, ldu] (u = gate * bf16(scale * t))
   int32_t n0;        // first output column of this segment
   int32_t N;         // columns of this segment
   int32_t ldu;
@@ -123,8 +138,43 @@ struct GemmArgs {
   int32_t mask_col;  // EPI_LOGITS: column forced to -inf
   float* tile_stats; // EPI_LOGITS: [M, n_tiles, 2] (max, sum exp)
   int32_t n_tiles;   // EPI_LOGITS: total 16-column tiles
-  int32_t pad2;
+  int32_t zero_n;    // int64 words of zero_ptr cleared by workgroup 0
+  long long* zero_ptr;
+  // RMSNorm input: X holds the stored x*g; the base accumulator of row m is
+  // scaled by rs = 1 / sqrt(ss_in[m] * 2^-32 / d + eps) (ss_in: fixed-point sum x^2)
+  const long long* ss_in;
+  float inv_d, eps;
+  // EPI_RESID producer: also store xg_out[m, n] = T(x_new * g_next[n]) and add the
+  // row's x_new^2 (fixed point) to ss_out[m]
+  void* xg_out;
+  const void* g_next;
+  long long* ss_out;
+  // EPI_QKV
+  const int32_t* row_pos;
+  const int32_t* call_seq;
+  int32_t rows_per_seq, n_q_heads;
+  const float* rcos;
+  const float* rsin;
+  void* qbuf;
+  KvLayout kv;
+  int32_t layer;
+  int32_t* err;
 };
+
+// LoRA down-projection of a group of projections sharing one input:
+// t[m, p*r + j] += sum_k X[m, k] * A_p[j, k] (fixed point, int64 atomics).
+struct LoraDownArgs {
+  const void* X;
+  int32_t ldx, M, K, r;
+  const void* A[4];
+  int32_t nproj;
+  int32_t kchunk;
+  long long* t;      // [M, nproj * r]
+  const long long* ss_in;   // RMSNorm input (see GemmArgs), or null
+  float inv_d, eps;
+};
+hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
+hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s);
 
 // ------------------------------------------------------------------ launchers
 // Every launcher enqueues on `s` and returns the hipGetLastError of its launch.
@@ -150,20 +200,15 @@ struct RowsSetup {
 };
 hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s);
 
+// x[r] = E[tok[r]] (or hidden_in[r]); also xg[r] = T(x * g) and ss[r] += sum x^2.
 template <typename T>
 hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
-                        int V, float* x, int32_t* err, hipStream_t s);
+                        int V, float* x, const T* g, T* xg, long long* ss, int32_t* err,
+                        hipStream_t s);
 template <typename T>
 hipError_t launch_rmsnorm(const float* x, const T* g, int R, int d, float eps, T* out,
                           hipStream_t s);
 
-struct KvLayout {
-  void* pool;
-  int32_t n_pages, n_kv_heads, page_size, head_dim, n_layers;
-  const int32_t* block_table;   // [max_seqs, max_pages_per_seq]
-  int32_t max_pages_per_seq;
-  int32_t pad;
-};
 
 template <typename T>
 hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32_t* call_seq,

@@ -33,7 +33,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t len, pending, iter, err, block_table, rope_cos, rope_sin;
   size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate;
-  size_t x, xn, qkv, qbuf, obuf, hbuf, ubuf;
+  size_t x, xn, qbuf, obuf, hbuf, ubuf, tfx, ss;
   size_t part_o, part_ml;
   size_t logits, tile_stats, row_ml, probs_d, probs_v;
   size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32;
@@ -70,11 +70,12 @@ Layout make_layout(const uno_config& c) {
   L.row_gate = take(R);
   L.x = take(R * d * 4);
   L.xn = take(R * d * ts);
-  L.qkv = take(R * (q + 2 * kv) * 4);
   L.qbuf = take(R * q * ts);
   L.obuf = take(R * q * ts);
   L.hbuf = take(R * F * ts);
   L.ubuf = take(R * 3 * r * ts + 16);
+  L.tfx = take(4 * R * 3 * r * 8 + 16);     // four fixed-point LoRA intermediates
+  L.ss = take((size_t)(2 * c.n_layers + 1) * R * 8);   // fixed-point sums of x^2
   L.part_o = take(R * c.n_q_heads * kMaxChunks * c.head_dim * 4);
   L.part_ml = take(R * c.n_q_heads * kMaxChunks * 2 * 4);
   L.logits = take(R * V * 4);
@@ -371,6 +372,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   const int R = f.n * f.rows_per_seq;
   const int d = g.d_model, hd = g.head_dim, Hq = g.n_q_heads, Hkv = g.n_kv_heads;
   const int qd = Hq * hd, kvd = Hkv * hd, F = g.ffn_dim, V = g.vocab, r = g.lora_rank;
+  const int L = g.n_layers;
   const bool lora = f.lora && c->has_lora && r > 0;
   const float sc = lora ? g.lora_alpha / (float)r : 0.0f;
   int32_t* err = c->at<int32_t>(c->L.err);
@@ -395,28 +397,47 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   rs.row_gate = c->at<uint8_t>(c->L.row_gate);
   rs.call_n = c->at<int32_t>(c->L.call_n);
   rs.call_it = c->at<int32_t>(c->L.call_it);
-  UNO_HIP(c, launch_rows_setup(rs, s));
+  {
+    Timed t(c, UNO_KC_MISC, 0, 0);
+    UNO_HIP(c, launch_rows_setup(rs, s));
+  }
 
   float* x = c->at<float>(c->L.x);
-  T* xn = c->at<T>(c->L.xn);
-  float* qkv = c->at<float>(c->L.qkv);
+  T* xg = c->at<T>(c->L.xn);      // gain-scaled RMSNorm input of the next consumer
   T* qbuf = c->at<T>(c->L.qbuf);
   T* obuf = c->at<T>(c->L.obuf);
   T* hbuf = c->at<T>(c->L.hbuf);
   T* ubuf = c->at<T>(c->L.ubuf);
   const uint8_t* gate = c->at<uint8_t>(c->L.row_gate);
-
+  // fixed-point sums of x^2 per row: [2l] before attention of layer l, [2l+1]
+  // before its MLP, [2L] before the LM head
+  long long* ssb = c->at<long long>(c->L.ss);
+  auto SS = [&](int i) { return ssb + (size_t)i * R; };
+  long long* tfx = c->at<long long>(c->L.tfx);
+  const size_t tstride = (size_t)R * 3 * r;
+  long long* Bfx[4] = {tfx, tfx + tstride, tfx + 2 * tstride, tfx + 3 * tstride};
+  {
+    Timed t(c, UNO_KC_MISC, 0, 0);
+    UNO_HIP(c, launch_zero_i64(ssb, (size_t)(2 * L + 1) * R, s));
+    if (lora && c->bf16) UNO_HIP(c, launch_zero_i64(tfx, 4 * tstride, s));
+  }
   if (!f.in_hidden && !c->embed) return fail(c, UNO_ERR_INVALID_ARG, "no embedding table");
-  UNO_HIP(c, launch_embed<T>(reinterpret_cast<const T*>(c->embed), rs.row_tok, f.in_hidden, R, d,
-                             V, x, err, s));
+  {
+    Timed t(c, UNO_KC_MISC, 0, 0);
+    UNO_HIP(c, launch_embed<T>(reinterpret_cast<const T*>(c->embed), rs.row_tok, f.in_hidden,
+                               R, d, V, x, reinterpret_cast<const T*>(c->attn_norm[0]), xg,
+                               SS(0), err, s));
+  }
 
   KvLayout kv = kv_layout(c);
-  // attention chunking: enough workgroups, at most kMaxChunks chunks
+  // attention chunking: split the context until ~2048 workgroups exist (each
+  // workgroup's latency chain is short; the batch alone may already provide
+  // them), 64-key multiples, at most kMaxChunks chunks
   const int row_tiles = (f.rows_per_seq + 15) / 16;
   const int groups = f.n * Hkv * row_tiles;
   int target = std::max(1, std::min(kMaxChunks, (2048 + groups - 1) / groups));
   int chunk = (f.ctx_bound + target - 1) / target;
-  chunk = std::max(32, (chunk + 31) / 32 * 32);
+  chunk = std::max(64, (chunk + 63) / 64 * 64);
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
   if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
 
@@ -427,7 +448,32 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     UNO_HIP(c, launch_gemm<T>(a, ncols, s));
     return UNO_OK;
   };
-  auto lora_down = [&](const T* X, int K, int nproj, const int* pidx, int l) -> uno_status {
+  auto norm_in = [&](GemmArgs& a, int ss_idx) {
+    a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
+  };
+  // LoRA down-projections.  bf16: split-K MFMA into fixed-point buffers B0..B3
+  // (qkv, o, gate/up, down), each cleared by a later kernel of the chain (the
+  // zero_ptr of the consumer GEMMs) and all cleared once per forward above.
+  // float32: a GEMM storing the gated, scaled intermediate.
+  auto lora_down = [&](const T* X, int K, int nproj, const int* pidx, int l, int buf,
+                       int ss_idx) -> uno_status {
+    if (c->bf16) {
+      LoraDownArgs a{};
+      a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = r; a.nproj = nproj; a.t = Bfx[buf];
+      if (ss_idx >= 0) { a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps; }
+      for (int i = 0; i < nproj; ++i) a.A[i] = c->la[pidx[i]][l];
+      const int tiles = nproj * r / 16 * ((R + 15) / 16);
+      const int tgt = std::max(1, (512 + tiles - 1) / tiles);
+      int ks = 1;
+      for (int cand = 1; cand <= K / 64; ++cand)
+        if ((K / 64) % cand == 0 && cand <= tgt) ks = cand;
+      a.kchunk = K / ks;
+      const double b = (double)nproj * r * K * sizeof(T) + (double)R * K * sizeof(T) +
+                       (double)R * nproj * r * 8 * 2;
+      Timed t(c, UNO_KC_LORA_DOWN, b, 2.0 * R * nproj * r * K);
+      UNO_HIP(c, launch_lora_down(a, s));
+      return UNO_OK;
+    }
     GemmArgs a{};
     a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = 0;
     a.nseg = nproj;
@@ -436,34 +482,45 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.seg[i].n0 = i * r;
       a.seg[i].N = r;
     }
+    if (ss_idx >= 0) norm_in(a, ss_idx);
     a.epi = EPI_LORA_U; a.ldo = nproj * r; a.out = ubuf; a.gate = gate; a.scale = sc;
     return run_gemm(a, nproj * r, UNO_KC_LORA_DOWN);
   };
+  // attach the LoRA up-projection of segment `i` reading group buffer `buf`
+  auto lora_up = [&](GemmArgs& a, int i, int proj, int l, int buf, int col, int ld) {
+    a.seg[i].Bl = c->lb[proj][l];
+    if (c->bf16) a.seg[i].Ufx = Bfx[buf] + col;
+    else a.seg[i].U = ubuf + col;
+    a.seg[i].ldu = ld;
+    a.gate = gate;
+    a.scale = sc;
+  };
+  auto clear = [&](GemmArgs& a, int buf, int cols) {
+    if (lora && c->bf16) { a.zero_ptr = Bfx[buf]; a.zero_n = R * cols; }
+  };
 
-  for (int l = 0; l < g.n_layers; ++l) {
-    // --- attention block
-    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->attn_norm[l]), R, d, g.rms_eps, xn, s));
+  for (int l = 0; l < L; ++l) {
+    // --- attention block: q|k|v (+LoRA) with RoPE and the paged K/V write
     static const int pqkv[3] = {0, 1, 2};
-    if (lora) { uno_status st = lora_down(xn, d, 3, pqkv, l); if (st) return st; }
+    if (lora) { uno_status st = lora_down(xg, d, 3, pqkv, l, 0, 2 * l); if (st) return st; }
     {
       GemmArgs a{};
-      a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
+      a.X = xg; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
       a.nseg = 3;
       const int n0s[3] = {0, qd, qd + kvd}, Ns[3] = {qd, kvd, kvd};
       for (int i = 0; i < 3; ++i) {
         a.seg[i].W = c->w[i][l];
         a.seg[i].n0 = n0s[i];
         a.seg[i].N = Ns[i];
-        if (lora) { a.seg[i].Bl = c->lb[i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 3 * r; }
+        if (lora) lora_up(a, i, i, l, 0, i * r, 3 * r);
       }
-      a.epi = EPI_STORE_F32; a.ldo = qd + 2 * kvd; a.out = qkv;
+      clear(a, 3, r);
+      norm_in(a, 2 * l);
+      a.epi = EPI_QKV;
+      a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
+      a.n_q_heads = Hq; a.rcos = c->at<float>(c->L.rope_cos); a.rsin = c->at<float>(c->L.rope_sin);
+      a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
       if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
-    }
-    {
-      Timed t(c, UNO_KC_MISC, 0, 0);
-      UNO_HIP(c, launch_rope_kv<T>(qkv, R, f.rows_per_seq, rs.call_seq, rs.row_pos, Hq,
-                                   c->at<float>(c->L.rope_cos), c->at<float>(c->L.rope_sin), qbuf,
-                                   kv, l, err, s));
     }
     {
       AttnArgs a{};
@@ -475,47 +532,54 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       // algorithmic bytes: queries, every visible K/V row of each sequence once
       // (bounded by ctx_bound), partials written and read, outputs
       const double kvb = (double)f.n * f.ctx_bound * Hkv * hd * 2 * sizeof(T);
-      const double pb = (double)R * Hq * n_chunks * (hd + 2) * 4 * 2;
+      const double pb = n_chunks > 1 ? (double)R * Hq * n_chunks * (hd + 2) * 4 * 2 : 0.0;
       const double io = (double)R * qd * sizeof(T) * 2;
       const double fl = 4.0 * R * Hq * hd * (double)f.ctx_bound;
       Timed t(c, UNO_KC_ATTENTION, kvb + pb + io, fl);
       UNO_HIP(c, launch_attention<T>(a, kv, s));
     }
     static const int po[1] = {3};
-    if (lora) { uno_status st = lora_down(obuf, qd, 1, po, l); if (st) return st; }
+    if (lora) { uno_status st = lora_down(obuf, qd, 1, po, l, 1, -1); if (st) return st; }
     {
       GemmArgs a{};
       a.X = obuf; a.ldx = qd; a.M = R; a.K = qd; a.r = lora ? r : 0;
       a.nseg = 1;
       a.seg[0].W = c->w[3][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
-      if (lora) { a.seg[0].Bl = c->lb[3][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
+      if (lora) lora_up(a, 0, 3, l, 1, 0, r);
+      clear(a, 0, 3 * r);
       a.epi = EPI_RESID; a.ldo = d; a.resid = x;
+      a.xg_out = xg; a.g_next = c->mlp_norm[l]; a.ss_out = SS(2 * l + 1);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
     // --- MLP block
-    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->mlp_norm[l]), R, d, g.rms_eps, xn, s));
     static const int pgu[2] = {4, 5};
-    if (lora) { uno_status st = lora_down(xn, d, 2, pgu, l); if (st) return st; }
+    if (lora) { uno_status st = lora_down(xg, d, 2, pgu, l, 2, 2 * l + 1); if (st) return st; }
     {
       GemmArgs a{};
-      a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
+      a.X = xg; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
       a.nseg = 2; a.paired = 1;
       for (int i = 0; i < 2; ++i) {
         a.seg[i].W = c->w[4 + i][l]; a.seg[i].n0 = 0; a.seg[i].N = F;
-        if (lora) { a.seg[i].Bl = c->lb[4 + i][l]; a.seg[i].U = ubuf + i * r; a.seg[i].ldu = 2 * r; }
+        if (lora) lora_up(a, i, 4 + i, l, 2, i * r, 2 * r);
       }
+      clear(a, 1, r);
+      norm_in(a, 2 * l + 1);
       a.epi = EPI_SWIGLU; a.ldo = F; a.out = hbuf;
       if (uno_status st = run_gemm(a, F, UNO_KC_LINEAR_SWIGLU)) return st;
     }
     static const int pd[1] = {6};
-    if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l); if (st) return st; }
+    if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l, 3, -1); if (st) return st; }
     {
       GemmArgs a{};
       a.X = hbuf; a.ldx = F; a.M = R; a.K = F; a.r = lora ? r : 0;
       a.nseg = 1;
       a.seg[0].W = c->w[6][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
-      if (lora) { a.seg[0].Bl = c->lb[6][l]; a.seg[0].U = ubuf; a.seg[0].ldu = r; }
+      if (lora) lora_up(a, 0, 6, l, 3, 0, r);
+      clear(a, 2, 2 * r);
       a.epi = EPI_RESID; a.ldo = d; a.resid = x;
+      a.xg_out = xg;
+      a.g_next = (l + 1 < L) ? c->attn_norm[l + 1] : c->final_norm;
+      a.ss_out = SS(2 * l + 2);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
   }
@@ -523,11 +587,11 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     UNO_HIP(c, hipMemcpyAsync(f.hidden_out, x, sizeof(float) * R * d, hipMemcpyDeviceToDevice, s));
   if (f.probs_out || f.logits_out) {
     if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
-    UNO_HIP(c, launch_rmsnorm<T>(x, reinterpret_cast<const T*>(c->final_norm), R, d, g.rms_eps, xn, s));
     GemmArgs a{};
-    a.X = xn; a.ldx = d; a.M = R; a.K = d; a.r = 0;
+    a.X = xg; a.ldx = d; a.M = R; a.K = d; a.r = 0;
     a.nseg = 1;
     a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
+    norm_in(a, 2 * L);
     a.epi = EPI_LOGITS; a.ldo = V; a.out = c->at<float>(c->L.logits);
     a.mask_col = g.mask_id; a.tile_stats = c->at<float>(c->L.tile_stats); a.n_tiles = V / 16;
     if (uno_status st = run_gemm(a, V, UNO_KC_LM_HEAD)) return st;

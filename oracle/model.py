@@ -20,9 +20,10 @@ id is vocab-1 and its logit is -inf.
 
 Numerics: float64 throughout.  When ``cfg.dtype == "bf16"`` values are rounded to
 bfloat16 (round-to-nearest-even) at the points where the library stores bf16:
-the normalised GEMM inputs, the scaled LoRA intermediate, q/k/v after RoPE (the
-KV cache), the attention output and the SwiGLU product.  The residual stream,
-logits and probabilities are never rounded.
+the gain-scaled GEMM input x*g of every RMSNorm (the per-row 1/rms factor is
+applied after the product, exactly), the scaled LoRA intermediate, q/k/v after
+RoPE (the KV cache), the attention output and the SwiGLU product.  The residual
+stream, logits and probabilities are never rounded.
 
 Weights are a dict (see ``tests``' generators): W for projection P is [out, in]
 (so y = h @ W.T), LoRA down A_P is [r, in] and up B_P is [out, r].
@@ -57,6 +58,16 @@ def bf16_round(x):
 def _store(cfg, x):
     """The library's storage rounding: bf16 for bf16 configs, none otherwise."""
     return bf16_round(x) if cfg.dtype == "bf16" else np.asarray(x, dtype=np.float64)
+
+
+def norm_input(cfg, x, g, eps):
+    """RMSNorm as a GEMM input: the stored gain-scaled x*g times the exact 1/rms.
+
+    Mathematically rms_norm(x, g); in bf16 configs the rounding sits on x*g.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rs = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return _store(cfg, x * g) * rs
 
 
 def rms_norm(x, g, eps):
@@ -140,7 +151,7 @@ def layer_forward(cfg, lw, x, pos, gate, kcache, vcache, visible, slots=None):
     def proj(name, h):
         return gated_lora_linear(cfg, h, w[name], la.get(name), lb.get(name), gate)
 
-    h = _store(cfg, rms_norm(x, lw["attn_norm"], cfg.rms_eps))
+    h = norm_input(cfg, x, lw["attn_norm"], cfg.rms_eps)
     q = proj("q", h).reshape(S, R, Hq, hd)
     k = proj("k", h).reshape(S, R, Hkv, hd)
     v = proj("v", h).reshape(S, R, Hkv, hd)
@@ -153,7 +164,7 @@ def layer_forward(cfg, lw, x, pos, gate, kcache, vcache, visible, slots=None):
     o = attention(q, kcache, vcache, visible)
     o = _store(cfg, o.reshape(S, R, Hq * hd))
     x = x + proj("o", o)
-    h2 = _store(cfg, rms_norm(x, lw["mlp_norm"], cfg.rms_eps))
+    h2 = norm_input(cfg, x, lw["mlp_norm"], cfg.rms_eps)
     g = proj("gate", h2)
     u = proj("up", h2)
     a = _store(cfg, g / (1.0 + np.exp(-g)) * u)
@@ -163,7 +174,7 @@ def layer_forward(cfg, lw, x, pos, gate, kcache, vcache, visible, slots=None):
 
 def lm_logits(cfg, weights, x):
     """Final RMSNorm, LM head, and the MASK column forced to -inf."""
-    hf = _store(cfg, rms_norm(x, weights["final_norm"], cfg.rms_eps))
+    hf = norm_input(cfg, x, weights["final_norm"], cfg.rms_eps)
     logits = hf @ weights["lm_head"].T
     logits[..., cfg.mask_id] = -np.inf
     return logits

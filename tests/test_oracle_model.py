@@ -220,3 +220,17 @@ def test_bf16_storage_points_are_bf16(tiny_w):
     k = cache["k"][:, 0, :5]
     assert np.array_equal(model.bf16_round(k), k)
     assert np.abs(k).max() > 0
+
+
+def test_norm_input_is_rms_norm():
+    """The GEMM-input form of RMSNorm equals the library RMSNorm exactly in fp32
+    configs and within bf16 rounding in bf16 configs."""
+    r = np.random.default_rng(9)
+    x = r.standard_normal((5, 64)) * 2
+    g = r.standard_normal(64)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), 1e-6).numpy()
+    assert np.allclose(model.norm_input(TINY, x, g, 1e-6), ref, rtol=1e-12, atol=1e-12)
+    cfg = TINY.with_(dtype="bf16")
+    y = model.norm_input(cfg, x, g, 1e-6)
+    assert np.allclose(y, ref, rtol=2.0 ** -8, atol=1e-12)
+    assert not np.allclose(y, ref, rtol=1e-9, atol=0)
