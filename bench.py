@@ -46,6 +46,74 @@ def kv_bytes_per_pos(cfg):
     return cfg.n_layers * 2 * cfg.kv_dim * 2
 
 
+def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs128"):
+    """Large-batch leg: `batch` sequences at context `ctx` (prefilled from uniform
+    prompts when ctx <= prompt_len, else filled with seeded synthetic K/V), then
+    `warmup` + `steps` timed iterations.  Returns a dict of measurements."""
+    import numpy as np
+    import torch
+    from diffusion_drafted_lora_amd import synth, uno
+
+    B = cfg.block_size
+    max_len = ctx + (warmup + steps + 2) * (B + 1) + B + 2
+    eng = uno.Engine(cfg, w, max_seqs=batch, max_seq_len=max_len, max_rows=batch * B,
+                     seed=3003, device=dev)
+    ids = list(range(batch))
+    t0 = time.perf_counter()
+    if ctx <= prompt_len:
+        prompts = synth.prompts(cfg, 2003, batch, ctx + 1)
+        log(f"{log_prefix}: prefill {batch} x {ctx + 1} tokens")
+        eng.prefill(ids, list(prompts))
+    else:
+        log(f"{log_prefix}: importing synthetic K/V of {ctx} positions for {batch} sequences")
+        g = torch.Generator(device=dev)
+        g.manual_seed(4003)
+        shape = (cfg.n_layers, ctx, cfg.n_kv_heads, cfg.head_dim)
+        k = torch.empty(shape, dtype=torch.float32, device=dev).normal_(0, 1, generator=g).to(torch.bfloat16)
+        v = torch.empty(shape, dtype=torch.float32, device=dev).normal_(0, 1, generator=g).to(torch.bfloat16)
+        for sq in ids:
+            eng.kv_import(sq, k, v, pending=sq % (cfg.vocab - 1))
+        del k, v
+    eng.sync()
+    t_fill = time.perf_counter() - t0
+    outs = torch.empty((batch, B + 1), dtype=torch.int32, device=dev)
+    nouts = torch.empty((warmup + steps, batch), dtype=torch.int32, device=dev)
+    for i in range(warmup):
+        eng.step(ids, out=outs, n_out=nouts[i])
+    eng.sync()
+    cls = ["linear", "linear_swiglu", "lora_down", "lm_head", "attention"]
+    eng.timing(cls)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        eng.step(ids, out=outs, n_out=nouts[i])
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    eng.sync()
+    tok = int(nouts[warmup:].sum().item())
+    gemm_ms = gemm_fl = 0.0
+    breakdown = {}
+    for c in cls:
+        n, ms, b, f = eng.timing_read(c)
+        breakdown[c] = {"ms_per_step": ms / steps, "TFLOP/s": f / 1e12 / (ms / 1e3) if ms else None,
+                        "GB/s": b / 1e9 / (ms / 1e3) if ms else None}
+        if c != "attention":
+            gemm_ms += ms
+            gemm_fl += f
+    eng.timing([])
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    mfma_tflops = gemm_fl / 1e12 / (gemm_ms / 1e3)
+    return {
+        "batch": batch, "context_start": ctx, "steps": steps, "warmup": warmup,
+        "accepted_tokens_per_s": tok / sec, "positions_per_s": 2 * B * batch * steps / sec,
+        "ms_per_step": 1e3 * sec / steps, "tokens_per_forward": tok / (2.0 * batch * steps),
+        "gemm_mfma_tflops": mfma_tflops, "gemm_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
+        "fill_s": t_fill, "breakdown": breakdown,
+    }
+
+
 def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -121,6 +189,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=8)
     ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--bs128-steps", type=int, default=6,
+                    help="timed iterations of the batch-128 leg (0 skips it)")
+    ap.add_argument("--bs128-ctx", type=str, default="1024",
+                    help="comma-separated starting contexts of the batch-128 leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -240,6 +312,12 @@ def main():
         },
         "breakdown": breakdown,
     }
+    if args.bs128_steps > 0:
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+        result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
+                           for c in args.bs128_ctx.split(",")]
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(cfg, w, tokens / K)

@@ -67,13 +67,13 @@ UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int pos, in
               kv.page_size + (pos % kv.page_size)) * kv.head_dim;
 }
 
-// Epilogue of one element (row m, lane column c) of each of the NT tiles.  `fin`
-// holds the finished 16x16 tile 0 (needed for the RoPE partner), indexed r*16+c.
-// Every thread of a 16-lane row group calls this (row sums use shuffles); `ok`
-// says whether row m exists.
+// Epilogue of one element (row m, lane column c) of each of the NT tiles.  `finr`
+// holds the 16 finished values of this row in tile 0 (the RoPE partner is
+// finr[c ^ 8]).  Every thread of a 16-lane row group calls this (row sums use
+// shuffles); `ok` says whether row m exists.
 template <typename T, int NT>
-UNO_DEV void epilogue(const GemmArgs& a, int m, int row, int c, int tile0, int col_paired,
-                      const float* v, const float* fin, bool ok) {
+UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired,
+                      const float* v, const float* finr, bool ok) {
   switch (a.epi) {
     case EPI_STORE_F32:
       if (ok)
@@ -131,7 +131,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int row, int c, int tile0, int c
           if (a.err) atomicOr(a.err, UNO_DEVERR_BOUNDS);
           break;
         }
-        const float x1 = fin[row * 16 + (c & 7)], x2 = fin[row * 16 + (c & 7) + 8];
+        const float x1 = finr[c & 7], x2 = finr[(c & 7) + 8];
         const float cs = a.rcos[(size_t)pos * half + i], sn = a.rsin[(size_t)pos * half + i];
         val = (c < 8) ? x1 * cs - x2 * sn : x2 * cs + x1 * sn;
       }
@@ -301,7 +301,191 @@ k_gemm_bf16(GemmArgs a) {
     const int row = e >> 4, c = e & 15;
     const int m = mt * 16 + row;
     if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v, m < a.M);
-    else epilogue<bf16, NT>(a, m, row, c, tile0, col_paired, v, fin, m < a.M);
+    else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v, fin + row * 16, m < a.M);
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Large-M variant (prefill, large batch, the distillation forward): a 128-row x
+// 128-column tile per workgroup (2 x 2 waves of 64 x 64, i.e. 4 x 4 MFMA tiles
+// each), K in steps of 64 through padded (bank-conflict-free) LDS tiles of X and
+// W, the next K step prefetched into registers while the current one is
+// multiplied.  The LoRA up-projection runs as extra K steps (A = the gated
+// fixed-point intermediate, B = LoRA up rows).  In the paired (SwiGLU) case the W
+// tile holds 64 gate rows and the matching 64 up rows, so the output is 128 x 64.
+// When the N-tiles divide evenly over the 8 XCDs, all M-blocks of one N-tile run on
+// one XCD and share its W tile in that XCD's L2.
+constexpr int BM = 128, BN = 128, BK = 64, BKP = BK + 8;
+
+__global__ void __launch_bounds__(256)
+k_gemm_big(GemmArgs a, int mblocks) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  bf16* sA = reinterpret_cast<bf16*>(smem_raw);        // [BM][BKP]
+  bf16* sB = sA + BM * BKP;                             // [BN][BKP]
+  float* sC = reinterpret_cast<float*>(smem_raw);      // [BM][BN] after the K loop
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int lin = blockIdx.x, nb_n = gridDim.x / mblocks;
+  int nb, mb;
+  if (nb_n % 8 == 0) {                 // XCD-aware order (workgroups go round-robin to XCDs)
+    const int xcd = lin % 8, slot = lin / 8;
+    nb = xcd + 8 * (slot / mblocks);
+    mb = slot % mblocks;
+  } else {
+    nb = lin / mblocks;
+    mb = lin % mblocks;
+  }
+  const int m0 = mb * BM;
+  const int outc = a.paired ? BN / 2 : BN;
+  const int c0 = nb * outc;
+
+  // segment and in-segment weight row of tile row j
+  auto wrow = [&](int j, int* seg) -> int {
+    if (a.paired) { *seg = j / 64; return c0 + (j % 64); }
+    const int col = tile_col(a, (c0 + j) / 16, (c0 + j) % 16);
+    const int sgi = find_seg(a, col);
+    *seg = sgi;
+    return col - a.seg[sgi].n0;
+  };
+  // each thread copies 4 16-byte pieces of A and 4 of B per K step:
+  // piece p = tid + 256 * q -> tile row p / 8, k offset (p % 8) * 8
+  const bf16* srcB[4];
+  const bf16* srcBl[4];
+  int rowA[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = tid + 256 * q, row = p / 8;
+    int sg;
+    const int wr = wrow(row, &sg);
+    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + (size_t)wr * a.K;
+    srcBl[q] = a.seg[sg].Bl ? reinterpret_cast<const bf16*>(a.seg[sg].Bl) + (size_t)wr * a.r
+                            : nullptr;
+    rowA[q] = m0 + row;
+  }
+  if (a.zero_ptr && blockIdx.x == 0)
+    for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
+
+  const bf16* X = reinterpret_cast<const bf16*>(a.X);
+  const bf16x8 zero8 = {};
+  bf16x8 ra[4], rb[4];
+  auto fetch = [&](int k) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q, kk = k + (p % 8) * 8;
+      ra[q] = rowA[q] < a.M ? load8(X + (size_t)rowA[q] * a.ldx + kk) : zero8;
+      rb[q] = load8(srcB[q] + kk);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = a.K / BK;
+  fetch(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q, row = p / 8, ko = (p % 8) * 8;
+      *reinterpret_cast<bf16x8*>(sA + row * BKP + ko) = ra[q];
+      *reinterpret_cast<bf16x8*>(sB + row * BKP + ko) = rb[q];
+    }
+    if (kt + 1 < nk) fetch((kt + 1) * BK);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + r16) * BKP + ks * 32 + kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + j * 16 + r16) * BKP + ks * 32 + kq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // RMSNorm: scale rows of the base product by 1 / rms(x)
+  if (a.ss_in) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rs = rs_of(a, m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j][e] *= rs;
+      }
+  }
+  // LoRA phase: B = LoRA up rows via LDS; A = gate * bf16(scale * t) formed from
+  // the fixed-point intermediate of the segment each 16-column tile belongs to
+  if (a.r > 0) {
+    for (int kr = 0; kr < a.r; kr += BK) {
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = tid + 256 * q, row = p / 8, ko = (p % 8) * 8;
+        *reinterpret_cast<bf16x8*>(sB + row * BKP + ko) = srcBl[q] ? load8(srcBl[q] + kr + ko) : zero8;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int sg;
+        (void)wrow(wn * 64 + j * 16, &sg);
+        const GemmSeg& S = a.seg[sg];
+        if (!S.Ufx || !S.Bl) continue;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+          const bf16x8 bfr =
+              *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + j * 16 + r16) * BKP + ks * 32 + kq);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 64 + i * 16 + r16;
+            bf16x8 af = zero8;
+            if (m < a.M && (a.gate == nullptr || a.gate[m] != 0)) {
+              const long long* tp = S.Ufx + (size_t)m * S.ldu + kr + ks * 32 + kq;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                af[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
+            }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // stage the finished tile in LDS and run the epilogue per 16 x 16 sub-tile:
+  // 16 groups of 16 threads, group g takes sub-tiles g, g + 16, ...
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sC[(wm * 64 + i * 16 + (lane >> 4) * 4 + e) * BN + wn * 64 + j * 16 + r16] = acc[i][j][e];
+  __syncthreads();
+  const int g = tid >> 4, c = tid & 15;
+  const int sub_n = outc / 16;
+  for (int st = g; st < (BM / 16) * sub_n; st += 16) {
+    const int sr = st / sub_n, sc = st % sub_n;
+    const int tile0 = c0 / 16 + sc;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int row = sr * 16 + rr, m = m0 + row;
+      const float* finr = sC + row * BN + sc * 16;
+      float v[2];
+      v[0] = finr[c];
+      v[1] = a.paired ? finr[64 + c] : 0.0f;
+      if (a.epi == EPI_LOGITS) logits_epilogue<1>(a, m, c, tile0, v, m < a.M);
+      else if (a.paired) epilogue<bf16, 2>(a, m, c, tile0, c0 + sc * 16, v, finr, m < a.M);
+      else epilogue<bf16, 1>(a, m, c, tile0, 0, v, finr, m < a.M);
+    }
   }
 }
 
@@ -368,7 +552,7 @@ k_gemm_f32(GemmArgs a) {
   fin[e] = v[0];
   __syncthreads();
   if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v, ok);
-  else epilogue<float, NT>(a, m, row, c, tile0, col_paired, v, fin, ok);
+  else epilogue<float, NT>(a, m, c, tile0, col_paired, v, fin + row * 16, ok);
 }
 
 // LoRA down-projection: one wave per (16 columns, K chunk, 16 rows); the fp32
@@ -440,6 +624,15 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   if (a.M <= 0) return hipSuccess;
   if (a.K % 32 != 0 || (a.r % 32) != 0 || n_cols_total % 16 != 0) return hipErrorInvalidValue;
   if (a.epi == EPI_QKV && (a.kv.head_dim % 16 != 0)) return hipErrorInvalidValue;
+  const int outc = a.paired ? BN / 2 : BN;
+  if (a.M >= 64 && a.K % BK == 0 && a.r % BK == 0 && n_cols_total % outc == 0 &&
+      (a.epi != EPI_QKV || a.kv.head_dim % BN == 0 || BN % a.kv.head_dim == 0)) {
+    const int mblocks = (a.M + BM - 1) / BM;
+    const int nblocks = n_cols_total / outc;
+    const size_t smem = (size_t)BM * BN * 4;
+    k_gemm_big<<<nblocks * mblocks, 256, smem, s>>>(a, mblocks);
+    return hipGetLastError();
+  }
   const int mtiles = (a.M + 15) / 16;
   dim3 grid(n_cols_total / 16, mtiles);
   if (a.paired) {

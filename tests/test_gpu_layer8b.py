@@ -110,3 +110,39 @@ def test_repeat_is_bit_identical(setup):
     a, _ = eng.forward([0], 16, dev(pos), dev(gate), hidden_in=dev(x), want_hidden=True)
     b, _ = eng.forward([0], 16, dev(pos), dev(gate), hidden_in=dev(x), want_hidden=True)
     assert np.array_equal(host(a), host(b))
+
+
+def test_large_m_rows_two_sequences():
+    """96 rows (the large-M kernel, with a ragged 128-row tile): two sequences of
+    48 rows each against their own contexts, gates mixed, LoRA on."""
+    import torch
+    log("layer8b: large-M rows")
+    w = synth.weights_numpy(CFG, 1001, with_embed=False)
+    eng = engine(CFG, w, max_seqs=2, max_seq_len=CTX + 128, max_rows=96)
+    cache = model.new_cache(CFG, 2, CTX + 128)
+    ctxs = [CTX, CTX - 300]
+    for s in range(2):
+        kc = torch.from_numpy(synth.normal(7001 + s, (1, ctxs[s], CFG.n_kv_heads, CFG.head_dim)))
+        vc = torch.from_numpy(synth.normal(7101 + s, (1, ctxs[s], CFG.n_kv_heads, CFG.head_dim)))
+        kc, vc = kc.to(torch.bfloat16), vc.to(torch.bfloat16)
+        eng.kv_import(s, dev(kc.float().numpy(), torch.bfloat16), dev(vc.float().numpy(), torch.bfloat16),
+                      pending=0)
+        cache["k"][0, s, :ctxs[s]] = kc.float().numpy()[0]
+        cache["v"][0, s, :ctxs[s]] = vc.float().numpy()[0]
+    rows = 48
+    pos = np.stack([np.arange(c, c + rows) for c in ctxs]).astype(np.int32)
+    gate = (np.arange(2 * rows).reshape(2, rows) % 3 != 0).astype(np.uint8)
+    x = synth.normal(7201, (2, rows, CFG.d_model))
+    hid, _ = eng.forward([0, 1], rows, dev(pos.ravel()), dev(gate.ravel()),
+                         hidden_in=dev(x.reshape(-1, CFG.d_model)), want_hidden=True)
+    ex_cache = {"k": cache["k"].copy(), "v": cache["v"].copy()}
+    _, ref = model.forward(CFG, w, None, pos, gate, cache, hidden_in=x, want_logits=False)
+    _, ex = model.forward(CFG.with_(dtype="f32"), w, None, pos, gate, ex_cache, hidden_in=x,
+                          want_logits=False)
+    _check(host(hid).reshape(2, rows, -1), ref, ex, "large-M")
+    for s in range(2):
+        k, v = eng.kv_export(s, ctxs[s] + rows)
+        k = host(k.float())[:, ctxs[s]:]
+        o = cache["k"][:, s, ctxs[s]:ctxs[s] + rows]
+        assert np.all(np.abs(k - o) <= 2.0 ** -7 * np.abs(o) + 2e-3)
+    eng.sync()
