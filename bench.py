@@ -17,6 +17,7 @@ kernel time breakdown, and the CPU oracle timed on a bounded sample on the host.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +27,50 @@ sys.path.insert(0, ROOT)
 METRIC = "accepted tokens/s/GPU (Ψ-Spec linear, 8B-shape) at bs=1 & bs=128; HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_bf16_gateup_bs1_8b.txt")
+KERNEL_SOURCES = ("diffusion_drafted_lora_amd/csrc/k_linear.hip",
+                  "diffusion_drafted_lora_amd/csrc/uno_internal.h")
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the gate/up linear kernel and its launcher."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary is missing or
+    was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def copy_probe(mib):
+    """A plain elementwise kernel of known size (reads and writes mib MiB each,
+    three launches) whose FETCH_SIZE / WRITE_SIZE counters scale the kernel's."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def log(msg):
@@ -193,6 +238,8 @@ def main():
                     help="timed iterations of the batch-128 leg (0 skips it)")
     ap.add_argument("--bs128-ctx", type=str, default="1024",
                     help="comma-separated starting contexts of the batch-128 leg")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise copy of MIB MiB (HBM counter scale)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -211,13 +258,17 @@ def main():
     B = cfg.block_size
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     log(f"generating weights ({cfg.n_layers} layers) on the GPU")
     w = synth.weights_torch(cfg, args.seed, dev)
     max_new = (args.warmup + args.steps + args.breakdown_steps + 1) * (B + 1)
     if args.prompt + max_new > cfg.prompt_len + cfg.new_tokens + B + 1:
         log("note: steps exceed the 1K/8K protocol length; the context grows beyond 9216")
     max_len = args.prompt + max_new + B + 2
-    eng = uno.Engine(cfg, w, max_seqs=1, max_seq_len=max_len, max_rows=16, seed=3002, device=dev)
+    # 256-row prefill chunks run on the large-M kernel, so the skinny decode kernels
+    # only ever see the decode steps' 16-row blocks.
+    eng = uno.Engine(cfg, w, max_seqs=1, max_seq_len=max_len, max_rows=256, seed=3002, device=dev)
     prompt = synth.prompts(cfg, 2002, 1, args.prompt)[0]
     log(f"prefill {args.prompt} tokens")
     t0 = time.perf_counter()
@@ -306,7 +357,7 @@ def main():
         "roofline": {
             "kernel": "gated-LoRA gate/up linear + SwiGLU (k_gemm_bf16<2,16,2>)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
             "bytes_per_launch": sw_bytes_per_launch, "us_per_launch": 1e3 * sw_ms,
             "launches": n_sw,
         },

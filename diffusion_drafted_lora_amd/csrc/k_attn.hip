@@ -3,7 +3,10 @@
 // Method: draft and verify read one KV cache (shibing624 reading notes of the Uno
 // paper, method core); a row at position m attends to its sequence's committed
 // context plus the in-flight block up to itself, i.e. positions 0..m, because
-// every block row's K/V is written at its position before attention runs.
+// every block row's K/V is written at its position before attention runs.  The
+// distillation forward over [x, z1] (same notes, "Diffusion Distillation") uses
+// per-row windows instead: an x row sees x up to itself, a z1 row of block b sees
+// the clean blocks before b and z1 of block b up to itself.
 //
 // Split-context decomposition: a workgroup owns (sequence, KV head, 16-row tile,
 // context chunk); the G = Hq / Hkv query heads of its KV head and the 16 rows
@@ -16,6 +19,45 @@ namespace {
 
 constexpr int SUB = 32;   // keys per LDS sub-chunk
 constexpr int kMaxCombine = 64;   // chunk partials merged per (row, head)
+
+// Visible-slot window (a, c, d) of row r: slots [0, a) and [c, d].
+UNO_DEV void row_window(const AttnArgs& a, int r, bool ok, int* av, int* cv, int* dv) {
+  *av = 0; *cv = INT_MAX; *dv = -1;
+  if (!ok) return;
+  if (a.row_vis) {
+    *av = a.row_vis[3 * (size_t)r];
+    *cv = a.row_vis[3 * (size_t)r + 1];
+    *dv = a.row_vis[3 * (size_t)r + 2];
+  } else {
+    *av = a.row_pos[r] + 1;
+  }
+}
+
+// Keys of a 16-row tile: virtual index p < A is slot p, p >= A is slot C + p - A.
+// sw holds a[16], c[16], d[16].  The second range starts at or after A.
+UNO_DEV void tile_window(const int* sw, int* A, int* C, int* nv) {
+  int am = 0, cm = INT_MAX, dm = -1;
+  for (int i = 0; i < 16; ++i) {
+    am = max(am, sw[i]);
+    if (sw[16 + i] <= sw[32 + i]) { cm = min(cm, sw[16 + i]); dm = max(dm, sw[32 + i]); }
+  }
+  cm = max(cm, am);
+  *A = am;
+  *C = cm;
+  *nv = am + (dm >= cm ? dm - cm + 1 : 0);
+}
+
+UNO_DEV int vslot(int p, int A, int C) { return p < A ? p : C + (p - A); }
+UNO_DEV bool seen(int sl, int av, int cv, int dv) { return sl < av || (sl >= cv && sl <= dv); }
+
+// Every row's chunk count, written once per tile (chunk 0, KV head 0) for the
+// combine; a window longer than n_chunks chunks trips the bounds flag.
+UNO_DEV void publish_nc(const AttnArgs& a, int c, int kvh, int tid, int r0, int nrows, int nv) {
+  if (c != 0 || kvh != 0 || tid >= nrows) return;
+  const int nc = (nv + a.chunk - 1) / a.chunk;
+  a.row_nc[r0 + tid] = min(nc, a.n_chunks);
+  if (nc > a.n_chunks && a.err) atomicOr(a.err, UNO_DEVERR_BOUNDS);
+}
 
 template <typename T, int MAXO>
 __global__ void __launch_bounds__(256)
@@ -36,18 +78,19 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
   float* sM = sS + NQ * SUB;                         // [NQ] running max
   float* sL = sM + NQ;                               // [NQ] running sum
   float* sF = sL + NQ;                               // [NQ] rescale factor
-  int* sPos = reinterpret_cast<int*>(sF + NQ);       // [16]
-  T* sK = reinterpret_cast<T*>(sPos + 16);           // [SUB][kstride]
+  int* sW = reinterpret_cast<int*>(sF + NQ);         // [3][16] row windows
+  T* sK = reinterpret_cast<T*>(sW + 48);             // [SUB][kstride]
   T* sV = sK + SUB * kstride;                        // [SUB][kstride]
 
   const int tid = threadIdx.x;
-  if (tid < 16) sPos[tid] = (tid < nrows) ? a.row_pos[r0 + tid] : -1;
+  if (tid < 16) row_window(a, r0 + tid, tid < nrows, sW + tid, sW + 16 + tid, sW + 32 + tid);
   __syncthreads();
-  int maxpos = -1;
-  for (int i = 0; i < nrows; ++i) maxpos = max(maxpos, sPos[i]);
+  int At, Ct, nv;
+  tile_window(sW, &At, &Ct, &nv);
+  publish_nc(a, c, kvh, tid, r0, nrows, nv);
   const int kbeg = c * a.chunk;
-  if (kbeg > maxpos) return;           // no row sees this chunk (never combined)
-  const int kend = min(kbeg + a.chunk, maxpos + 1);
+  if (kbeg >= nv) return;              // no row sees this chunk (never combined)
+  const int kend = min(kbeg + a.chunk, nv);
 
   // queries: qi = g * 16 + row, head = kvh * G + g
   const T* Q = reinterpret_cast<const T*>(a.q);
@@ -67,20 +110,20 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
   const T* Kp = reinterpret_cast<const T*>(kv.pool);
   for (int k0 = kbeg; k0 < kend; k0 += SUB) {
     __syncthreads();
-    // load K / V of positions k0 .. k0+SUB-1 (only positions < kend are read)
+    // load K / V of virtual keys k0 .. k0+SUB-1 (only keys < kend are read)
     for (int e = tid; e < SUB * hd; e += 256) {
-      const int j = e / hd, d = e % hd, p = k0 + j;
+      const int j = e / hd, d = e % hd, p = k0 + j, sl = vslot(p, At, Ct);
       T kvk = from_f<T>(0.0f), kvv = from_f<T>(0.0f);
-      const int page = (p < kend && p / kv.page_size < kv.max_pages_per_seq)
-                           ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + p / kv.page_size]
+      const int page = (p < kend && sl / kv.page_size < kv.max_pages_per_seq)
+                           ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + sl / kv.page_size]
                            : -1;
       if (page >= 0 && page < kv.n_pages) {
         const size_t base =
             (((size_t)(a.layer * 2) * kv.n_pages + page) * Hkv + kvh) * kv.page_size +
-            (p % kv.page_size);
+            (sl % kv.page_size);
         const size_t vbase =
             (((size_t)(a.layer * 2 + 1) * kv.n_pages + page) * Hkv + kvh) * kv.page_size +
-            (p % kv.page_size);
+            (sl % kv.page_size);
         kvk = Kp[base * hd + d];
         kvv = Kp[vbase * hd + d];
       }
@@ -90,10 +133,9 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
     __syncthreads();
     // scores
     for (int e = tid; e < NQ * SUB; e += 256) {
-      const int qi = e / SUB, j = e % SUB, p = k0 + j;
-      const int rpos = sPos[qi % 16];
+      const int qi = e / SUB, j = e % SUB, p = k0 + j, rw = qi % 16;
       float s = -INFINITY;
-      if (p < kend && p <= rpos) {
+      if (p < kend && seen(vslot(p, At, Ct), sW[rw], sW[16 + rw], sW[32 + rw])) {
         const float* q = sQ + qi * hd;
         const T* kr = sK + j * kstride;
         float acc = 0.0f;
@@ -163,7 +205,7 @@ k_attn_combine(AttnArgs a, int hd) {
   __shared__ float sm[kMaxCombine], ssum[kMaxCombine], sf[kMaxCombine];
   __shared__ float sL;
   const int r = blockIdx.x / a.n_q_heads, h = blockIdx.x % a.n_q_heads;
-  const int nc = min(a.row_pos[r] / a.chunk + 1, a.n_chunks);
+  const int nc = a.row_nc[r];
   const size_t ph0 = ((size_t)r * a.n_q_heads + h) * a.n_chunks;
   for (int c = threadIdx.x; c < nc; c += blockDim.x) {
     sm[c] = a.part_ml[(ph0 + c) * 2];
@@ -219,7 +261,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   bf16* sK = reinterpret_cast<bf16*>(smem_raw);                 // [MK][KPAD]
   bf16* sVt = sK + MK * KPAD;                                   // [HD][VPAD]
   bf16* sP = sVt + HD * VPAD;                                   // [G][16][PPAD]
-  __shared__ int sPos[16];
+  __shared__ int sW[48];                                        // row windows a, c, d
 
   const int c = blockIdx.x, kvh = blockIdx.y;
   const int row_tiles = (a.rows_per_seq + 15) / 16;
@@ -231,11 +273,13 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
   const int r16 = lane & 15, grp = lane >> 4;
 
-  // Loads that do not depend on each other go out together: row positions, the Q
-  // fragments of this wave's head, and (below) the first sub-chunk's K/V.
-  if (tid < 16) sPos[tid] = (tid < nrows) ? a.row_pos[r0 + tid] : -1;
+  // Loads that do not depend on each other go out together: row windows, the Q
+  // fragments of this wave's head, and (below, for plain causal rows whose keys
+  // are slots 0..pos) the first sub-chunk's K/V.
+  if (tid < 16) row_window(a, r0 + tid, tid < nrows, sW + tid, sW + 16 + tid, sW + 32 + tid);
   const int kbeg = c * a.chunk;
   int kend = kbeg + MK;      // provisional bound of the first sub-chunk
+  int At = INT_MAX, Ct = 0;  // identity key numbering until the windows are known
   const int head = kvh * G + w;
   const bf16* Q = reinterpret_cast<const bf16*>(a.q);
   bf16x8 qf[HD / 32];
@@ -272,14 +316,14 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       bf16x8 kk = {}, vv = {};
       if (q < npf && e < MK * (HD / 8)) {
         const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8, p = k0 + key;
-        const int pi = p / kv.page_size;
+        const int sl = vslot(p, At, Ct), pi = sl / kv.page_size;
         const int page = (p < kend && pi < kv.max_pages_per_seq)
                              ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi] : -1;
         if (page >= 0 && page < kv.n_pages) {
           const size_t kb = ((((size_t)(a.layer * 2) * kv.n_pages + page) * Hkv + kvh) *
-                                 kv.page_size + (p % kv.page_size)) * HD + d8;
+                                 kv.page_size + (sl % kv.page_size)) * HD + d8;
           const size_t vb = ((((size_t)(a.layer * 2 + 1) * kv.n_pages + page) * Hkv + kvh) *
-                                 kv.page_size + (p % kv.page_size)) * HD + d8;
+                                 kv.page_size + (sl % kv.page_size)) * HD + d8;
           kk = *reinterpret_cast<const bf16x8*>(pool + kb);
           vv = *reinterpret_cast<const bf16x8*>(pool + vb);
         }
@@ -288,32 +332,44 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       pv[q] = vv;
     }
   };
-  auto stage = [&]() {
+  // Keys at or beyond kend are staged as zeros: masked keys get probability 0, and
+  // 0 * V must stay 0 (a slot that was never written may hold a NaN pattern).
+  auto stage = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < PF_MAX; ++q) {
       const int e = tid + q * nthr;
       if (q < npf && e < MK * (HD / 8)) {
         const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = pk[q];
+        const bool live = k0 + key < kend;
+        const bf16x8 kk = live ? pk[q] : bf16x8{}, vv = live ? pv[q] : bf16x8{};
+        *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = kk;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sVt[(d8 + j) * VPAD + key] = pv[q][j];
+        for (int j = 0; j < 8; ++j) sVt[(d8 + j) * VPAD + key] = vv[j];
       }
     }
   };
-  // first sub-chunk: positions beyond the rows are read (from reserved pages only)
-  // and masked below; this keeps the position reads off the critical path
-  fetch(kbeg);
+  // first sub-chunk of plain causal rows: slots beyond the rows are read (from
+  // reserved pages only) and zeroed at staging; this keeps the window reads off
+  // the critical path
+  const bool causal = a.row_vis == nullptr;
+  if (causal) fetch(kbeg);
   __syncthreads();
-  int maxpos = -1;
-  for (int i = 0; i < nrows; ++i) maxpos = max(maxpos, sPos[i]);
-  if (kbeg > maxpos) return;
-  kend = min(kbeg + a.chunk, maxpos + 1);
-  int rpos[4];
+  int nv;
+  tile_window(sW, &At, &Ct, &nv);
+  publish_nc(a, c, kvh, tid, r0, nrows, nv);
+  if (kbeg >= nv) return;
+  kend = min(kbeg + a.chunk, nv);
+  if (!causal) fetch(kbeg);
+  int ra[4], rc[4], rd[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rpos[i] = sPos[grp * 4 + i];
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = sW[grp * 4 + i];
+    rc[i] = sW[16 + grp * 4 + i];
+    rd[i] = sW[32 + grp * 4 + i];
+  }
   for (int k0 = kbeg; k0 < kend; k0 += MK) {
     __syncthreads();               // previous sub-chunk fully consumed
-    stage();
+    stage(k0);
     if (k0 + MK < kend) fetch(k0 + MK);
     __syncthreads();
     // S = Q K^T for 4 key tiles of 16
@@ -328,15 +384,20 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       }
     }
     // mask, online softmax (rows 4*grp+i, column = key j*16 + r16)
+    int ksl[MK / 16];
+#pragma unroll
+    for (int j = 0; j < MK / 16; ++j) {
+      const int p = k0 + j * 16 + r16;
+      ksl[j] = p < kend ? vslot(p, At, Ct) : INT_MAX;
+    }
     float mt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < MK / 16; ++j) {
-        const int p = k0 + j * 16 + r16;
         float v = s[j][i] * sc;
-        if (p >= kend || p > rpos[i]) v = -INFINITY;
+        if (ksl[j] == INT_MAX || !seen(ksl[j], ra[i], rc[i], rd[i])) v = -INFINITY;
         s[j][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -409,7 +470,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
 template <typename T>
 size_t attn_smem_bytes(int G, int hd) {
   const int NQ = 16 * G;
-  return (size_t)(NQ * hd + NQ * SUB + 3 * NQ + 16) * 4 + (size_t)2 * SUB * (hd + 2) * sizeof(T);
+  return (size_t)(NQ * hd + NQ * SUB + 3 * NQ + 48) * 4 + (size_t)2 * SUB * (hd + 2) * sizeof(T);
 }
 
 template <typename T>

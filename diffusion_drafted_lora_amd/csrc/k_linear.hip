@@ -141,7 +141,8 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
         const int which = head < Hq + Hkv ? 0 : 1;
         const int h = head - Hq - which * Hkv;
         const int seq = a.call_seq[m / a.rows_per_seq];
-        T* dst = kv_dst<T>(a.kv, a.layer, which, seq, pos, h, a.err);
+        const int slot = a.row_slot ? a.row_slot[m] : pos;
+        T* dst = kv_dst<T>(a.kv, a.layer, which, seq, slot, h, a.err);
         if (dst) dst[dim] = from_f<T>(val);
       }
       break;

@@ -1,5 +1,6 @@
-// Row set-up, embedding gather, RMSNorm, RoPE with the paged KV write, the
-// softmax passes of the LM head, small device scatters and KV import / export.
+// Row set-up, embedding gather, the softmax passes of the LM head, the total
+// variation of the distillation forward, small device scatters and KV import /
+// export.
 //
 // The decoder reading (pre-norm RMSNorm, rotate-half RoPE, grouped-query heads)
 // is the plain Qwen3-8B-shaped one; the pages fix only that draft and verify
@@ -46,6 +47,23 @@ __global__ void k_rows_setup(RowsSetup a) {
       pos = a.in_pos[r];
       g = a.in_gate[r];
       break;
+    case 4: {  // distillation: [x | MASK^L], both halves at RoPE positions 0..L-1
+      // (Uno reading notes, "Diffusion Distillation": one forward over [x, z1]
+      // with a block-causal mask; the gated LoRA is off on x and on on z1)
+      const int Lx = a.rows_per_seq / 2;
+      const bool noisy = j >= Lx;
+      const int jj = noisy ? j - Lx : j;
+      tok = noisy ? a.mask_id : a.in_tok[(size_t)i * Lx + jj];
+      pos = jj;
+      g = noisy ? 1 : 0;
+      const int b0 = jj / a.B * a.B;
+      a.row_slot[r] = j;
+      // x row: slots [0, jj]; z1 row of block b: x slots [0, bB) and z1 slots bB..jj
+      a.row_vis[3 * r] = noisy ? b0 : jj + 1;
+      a.row_vis[3 * r + 1] = noisy ? Lx + b0 : INT_MAX;
+      a.row_vis[3 * r + 2] = noisy ? Lx + jj : -1;
+      break;
+    }
     default:  // prefill rows of one sequence
       tok = a.in_tok[r];
       pos = a.pos0 + r;
@@ -99,20 +117,6 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256)
-k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, int d, float eps, T* out) {
-  __shared__ float sh[4];
-  const int r = blockIdx.x;
-  const float* xr = x + (size_t)r * d;
-  float ss = 0.0f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
-  ss = block_sum_256(ss, sh);
-  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += blockDim.x)
-    out[(size_t)r * d + c] = from_f<T>(xr[c] * rs * to_f(g[c]));
-}
-
-template <typename T>
 __device__ T* kv_slot(const KvLayout& kv, int layer, int which, int seq, int pos, int h,
                       int32_t* err) {
   const int pi = pos / kv.page_size;
@@ -129,55 +133,6 @@ __device__ T* kv_slot(const KvLayout& kv, int layer, int which, int seq, int pos
       ((((size_t)(layer * 2 + which) * kv.n_pages + page) * kv.n_kv_heads + h) * kv.page_size +
        (pos % kv.page_size)) * kv.head_dim;
   return reinterpret_cast<T*>(kv.pool) + off;
-}
-
-// One block per row: rotate q and k (pairs i, i + hd/2), store q, and write k / v
-// into the row's KV page slot.
-template <typename T>
-__global__ void k_rope_kv(const float* __restrict__ qkv, int rows_per_seq,
-                          const int32_t* __restrict__ call_seq,
-                          const int32_t* __restrict__ row_pos, int Hq,
-                          const float* __restrict__ rcos, const float* __restrict__ rsin,
-                          T* qbuf, KvLayout kv, int layer, int32_t* err) {
-  const int r = blockIdx.x;
-  const int hd = kv.head_dim, half = hd / 2, Hkv = kv.n_kv_heads;
-  const int pos = row_pos[r];
-  const int seq = call_seq[r / rows_per_seq];
-  const int ld = (Hq + 2 * Hkv) * hd;
-  if (pos < 0 || pos >= kv.max_pages_per_seq * kv.page_size) {   // beyond the RoPE table
-    if (threadIdx.x == 0 && err) atomicOr(err, UNO_DEVERR_BOUNDS);
-    return;
-  }
-  const float* src = qkv + (size_t)r * ld;
-  const float* cr = rcos + (size_t)pos * half;
-  const float* sr = rsin + (size_t)pos * half;
-  // q heads
-  for (int e = threadIdx.x; e < Hq * half; e += blockDim.x) {
-    const int h = e / half, i = e % half;
-    const float x1 = src[h * hd + i], x2 = src[h * hd + i + half];
-    const float c = cr[i], s = sr[i];
-    T* dst = qbuf + (size_t)r * Hq * hd + h * hd;
-    dst[i] = from_f<T>(x1 * c - x2 * s);
-    dst[i + half] = from_f<T>(x2 * c + x1 * s);
-  }
-  // k heads
-  for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
-    const int h = e / half, i = e % half;
-    const float* ks = src + Hq * hd + h * hd;
-    const float x1 = ks[i], x2 = ks[i + half];
-    const float c = cr[i], s = sr[i];
-    T* dst = kv_slot<T>(kv, layer, 0, seq, pos, h, err);
-    if (dst) {
-      dst[i] = from_f<T>(x1 * c - x2 * s);
-      dst[i + half] = from_f<T>(x2 * c + x1 * s);
-    }
-  }
-  // v heads
-  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
-    const int h = e / hd, i = e % hd;
-    T* dst = kv_slot<T>(kv, layer, 1, seq, pos, h, err);
-    if (dst) dst[i] = from_f<T>(src[(Hq + Hkv) * hd + h * hd + i]);
-  }
 }
 
 // Reduce the per-tile (max, sum exp) partials of one logits row (fixed order):
@@ -236,6 +191,32 @@ __global__ void k_softmax(const float* __restrict__ logits, const float* __restr
     probs[base + j] = expf(logits[base + j] - M) * inv;
 }
 
+// Total variation of one row pair: 0.5 * sum_v |p_T(v) - p_S(v)| with p = exp(l - max)
+// / sum; strided per-thread sums, then a fixed-order block reduction.
+__global__ void __launch_bounds__(256)
+k_tv(const float* __restrict__ tl, const float* __restrict__ sl, const float* __restrict__ tml,
+     const float* __restrict__ sml, int V, float* tv) {
+  __shared__ float sh[4];
+  const int r = blockIdx.x;
+  const float mt = tml[2 * r], it = 1.0f / tml[2 * r + 1];
+  const float ms = sml[2 * r], is = 1.0f / sml[2 * r + 1];
+  const float* t = tl + (size_t)r * V;
+  const float* s = sl + (size_t)r * V;
+  float acc = 0.0f;
+  for (int j = threadIdx.x; j < V; j += blockDim.x)
+    acc += fabsf(expf(t[j] - mt) * it - expf(s[j] - ms) * is);
+  acc = block_sum_256(acc, sh);
+  if (threadIdx.x == 0) tv[r] = 0.5f * acc;
+}
+
+__global__ void k_tv_blocks(const float* __restrict__ tv_row, int nb, int B, float* tv_block) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nb) return;
+  float acc = 0.0f;
+  for (int i = 0; i < B; ++i) acc += tv_row[(size_t)b * B + i];
+  tv_block[b] = acc / (float)B;
+}
+
 __global__ void k_set_list(SetList l) {
   for (int i = threadIdx.x; i < l.count; i += blockDim.x) l.dst[l.idx[i]] = l.val[i];
 }
@@ -273,23 +254,6 @@ hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, 
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_rmsnorm(const float* x, const T* g, int R, int d, float eps, T* out,
-                          hipStream_t s) {
-  k_rmsnorm<T><<<R, 256, 0, s>>>(x, g, d, eps, out);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32_t* call_seq,
-                          const int32_t* row_pos, int n_q_heads, const float* rope_cos,
-                          const float* rope_sin, T* qbuf, const KvLayout& kv, int layer,
-                          int32_t* err, hipStream_t s) {
-  k_rope_kv<T><<<R, 256, 0, s>>>(qkv, rows_per_seq, call_seq, row_pos, n_q_heads, rope_cos,
-                                 rope_sin, qbuf, kv, layer, err);
-  return hipGetLastError();
-}
-
 hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* row_ml,
                             hipStream_t s) {
   k_row_stats<<<R, 1024, 0, s>>>(tile_stats, n_tiles, row_ml);
@@ -300,6 +264,20 @@ hipError_t launch_softmax(const float* logits, const float* row_ml, int R, int V
                           hipStream_t s) {
   const int bx = (V + 1023) / 1024 < 64 ? (V + 1023) / 1024 : 64;
   k_softmax<<<dim3(bx, R), 256, 0, s>>>(logits, row_ml, V, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_tv(const float* t_logits, const float* s_logits, const float* t_ml,
+                     const float* s_ml, int L, int V, float* tv_row, hipStream_t s) {
+  if (L <= 0) return hipSuccess;
+  k_tv<<<L, 256, 0, s>>>(t_logits, s_logits, t_ml, s_ml, V, tv_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_tv_blocks(const float* tv_row, int L, int B, float* tv_block, hipStream_t s) {
+  if (L <= 0 || B <= 0 || L % B) return hipErrorInvalidValue;
+  const int nb = L / B;
+  k_tv_blocks<<<(nb + 255) / 256, 256, 0, s>>>(tv_row, nb, B, tv_block);
   return hipGetLastError();
 }
 
@@ -321,11 +299,6 @@ hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int 
   template hipError_t launch_embed<T>(const T*, const int32_t*, const float*, int, int, int, \
                                       float*, const T*, T*, long long*, int32_t*,           \
                                       hipStream_t);                                         \
-  template hipError_t launch_rmsnorm<T>(const float*, const T*, int, int, float, T*,         \
-                                        hipStream_t);                                       \
-  template hipError_t launch_rope_kv<T>(const float*, int, int, const int32_t*,              \
-                                        const int32_t*, int, const float*, const float*, T*, \
-                                        const KvLayout&, int, int32_t*, hipStream_t);       \
   template hipError_t launch_kv_copy<T>(const KvLayout&, int, int, T*, T*, int, hipStream_t);
 UNO_INST(float)
 UNO_INST(bf16)

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -149,8 +150,10 @@ struct GemmArgs {
   void* xg_out;
   const void* g_next;
   long long* ss_out;
-  // EPI_QKV
+  // EPI_QKV: q/k rotated at row_pos[m]; K/V written at slot row_slot[m] of the
+  // row's sequence (row_pos[m] when row_slot is null)
   const int32_t* row_pos;
+  const int32_t* row_slot;
   const int32_t* call_seq;
   int32_t rows_per_seq, n_q_heads;
   const float* rcos;
@@ -181,7 +184,8 @@ hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int n_cols_total, hipStream_t s);
 
 struct RowsSetup {
-  int32_t mode;          // 0 draft, 1 verify, 2 forward (caller rows), 3 prefill
+  int32_t mode;          // 0 draft, 1 verify, 2 forward (caller rows), 3 prefill,
+                         // 4 distillation rows [x | MASK^L] (B = its block size)
   int32_t n, rows_per_seq, B, mask_id;
   const int32_t* call_seq;   // [n] sequence ids
   const int32_t* len;        // [max_seqs]
@@ -195,6 +199,8 @@ struct RowsSetup {
   int32_t* row_tok;
   int32_t* row_pos;
   uint8_t* row_gate;
+  int32_t* row_slot;         // mode 4: KV slot of each row
+  int32_t* row_vis;          // mode 4: [R][3] visible slots [0, a) and [c, d]
   int32_t* call_n;           // [n] pending position n of each call sequence
   int32_t* call_it;          // [n] iteration
 };
@@ -205,21 +211,18 @@ template <typename T>
 hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
                         int V, float* x, const T* g, T* xg, long long* ss, int32_t* err,
                         hipStream_t s);
-template <typename T>
-hipError_t launch_rmsnorm(const float* x, const T* g, int R, int d, float eps, T* out,
-                          hipStream_t s);
 
-
-template <typename T>
-hipError_t launch_rope_kv(const float* qkv, int R, int rows_per_seq, const int32_t* call_seq,
-                          const int32_t* row_pos, int n_q_heads, const float* rope_cos,
-                          const float* rope_sin, T* qbuf, const KvLayout& kv, int layer,
-                          int32_t* err, hipStream_t s);
-
+// Attention rows see, in their sequence's KV slots, [0, row_pos] -- or, when
+// row_vis is given, the slots [0, a) and [c, d] with (a, c, d) = row_vis[r]
+// (the distillation forward's block-causal mask over [x, z1]).  The keys a
+// 16-row tile walks are the union of its rows' windows, numbered virtually:
+// [0, A) then [C, D] (A = max a, C = min c, D = max d).
 struct AttnArgs {
   const void* q;             // [R, Hq * hd] of T
   void* out;                 // [R, Hq * hd] of T
   const int32_t* row_pos;    // [R]
+  const int32_t* row_vis;    // [R][3] or null
+  int32_t* row_nc;           // [R] context chunks that hold each row's partials
   const int32_t* call_seq;   // [n]
   int32_t n, rows_per_seq, n_q_heads, n_chunks, chunk;
   float scale;
@@ -227,6 +230,7 @@ struct AttnArgs {
   float* part_ml;            // [R * Hq, n_chunks, 2]
   int32_t layer;
   int32_t pad;
+  int32_t* err;              // device error flags
 };
 template <typename T> hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv,
                                                   hipStream_t s);
@@ -235,6 +239,11 @@ hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* 
                             hipStream_t s);
 hipError_t launch_softmax(const float* logits, const float* row_ml, int R, int V, float* probs,
                           hipStream_t s);
+// Per-row total variation 0.5 * sum_v |softmax(T_i) - softmax(S_i)| of L row pairs
+// (logits with row stats (max, sum exp)), then the mean over each block of B rows.
+hipError_t launch_tv(const float* t_logits, const float* s_logits, const float* t_ml,
+                     const float* s_ml, int L, int V, float* tv_row, hipStream_t s);
+hipError_t launch_tv_blocks(const float* tv_row, int L, int B, float* tv_block, hipStream_t s);
 
 hipError_t launch_draft_desc(const float* probs, int n, int B, int V, uint64_t seed,
                              const int32_t* call_seq, const int32_t* call_n,

@@ -32,11 +32,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t len, pending, iter, err, block_table, rope_cos, rope_sin;
-  size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate;
+  size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate, row_slot, row_vis, row_nc;
   size_t x, xn, qbuf, obuf, hbuf, ubuf, tfx, ss;
   size_t part_o, part_ml;
   size_t logits, tile_stats, row_ml, probs_d, probs_v;
-  size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32;
+  size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32, tv;
   size_t total;
 };
 
@@ -68,6 +68,9 @@ Layout make_layout(const uno_config& c) {
   L.row_tok = take(R * 4);
   L.row_pos = take(R * 4);
   L.row_gate = take(R);
+  L.row_slot = take(R * 4);
+  L.row_vis = take(R * 3 * 4);
+  L.row_nc = take(R * 4);
   L.x = take(R * d * 4);
   L.xn = take(R * d * ts);
   L.qbuf = take(R * q * ts);
@@ -89,6 +92,7 @@ Layout make_layout(const uno_config& c) {
   L.acc_k = take(S * 4);
   L.acc_z = take(S * 4);
   L.aux_i32 = take(rows_any * 4);
+  L.tv = take(R * 4);
   L.total = o;
   return L;
 }
@@ -151,7 +155,7 @@ uno_status hip_fail(uno_ctx* c, hipError_t e, const char* where) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, #call);   \
   } while (0)
 
-constexpr int kTimedLaunches = 8192;
+constexpr int kTimedLaunches = 32768;
 
 // Brackets one launch with events when its class is being timed.
 struct Timed {
@@ -363,6 +367,14 @@ struct FwdIn {
   float* hidden_out;
   float* probs_out;         // softmax of the logits (nullptr: no LM head)
   float* logits_out;        // copy of the logits (optional)
+  // distillation forward (mode 4): rows [x | MASK^L] per sequence, block size dB;
+  // teacher / student logits [n, L, V] (nullptr: workspace), per-row TV [n, L]
+  // (nullptr: workspace) and per-block TV [n, L / dB] (nullptr: not formed)
+  int dB;
+  float* teacher;
+  float* student;
+  float* tv_row;
+  float* tv_block;
 };
 
 template <typename T>
@@ -395,6 +407,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   rs.row_tok = c->at<int32_t>(c->L.row_tok);
   rs.row_pos = c->at<int32_t>(c->L.row_pos);
   rs.row_gate = c->at<uint8_t>(c->L.row_gate);
+  rs.row_slot = c->at<int32_t>(c->L.row_slot);
+  rs.row_vis = c->at<int32_t>(c->L.row_vis);
+  if (f.mode == 4) rs.B = f.dB;
   rs.call_n = c->at<int32_t>(c->L.call_n);
   rs.call_it = c->at<int32_t>(c->L.call_it);
   {
@@ -518,6 +533,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       norm_in(a, 2 * l);
       a.epi = EPI_QKV;
       a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
+      if (f.mode == 4) a.row_slot = rs.row_slot;
       a.n_q_heads = Hq; a.rcos = c->at<float>(c->L.rope_cos); a.rsin = c->at<float>(c->L.rope_sin);
       a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
       if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
@@ -525,16 +541,23 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     {
       AttnArgs a{};
       a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
+      a.row_vis = f.mode == 4 ? rs.row_vis : nullptr;
+      a.row_nc = c->at<int32_t>(c->L.row_nc);
+      a.err = err;
       a.n = f.n; a.rows_per_seq = f.rows_per_seq; a.n_q_heads = Hq;
       a.n_chunks = n_chunks; a.chunk = chunk; a.scale = 1.0f / sqrtf((float)hd);
       a.part_o = c->at<float>(c->L.part_o); a.part_ml = c->at<float>(c->L.part_ml);
       a.layer = l;
       // algorithmic bytes: queries, every visible K/V row of each sequence once
-      // (bounded by ctx_bound), partials written and read, outputs
-      const double kvb = (double)f.n * f.ctx_bound * Hkv * hd * 2 * sizeof(T);
+      // (bounded by ctx_bound; [x, z1]: 2L rows), partials written and read, outputs
+      const double kv_rows = f.mode == 4 ? (double)f.rows_per_seq : (double)f.ctx_bound;
+      const double kvb = (double)f.n * kv_rows * Hkv * hd * 2 * sizeof(T);
       const double pb = n_chunks > 1 ? (double)R * Hq * n_chunks * (hd + 2) * 4 * 2 : 0.0;
       const double io = (double)R * qd * sizeof(T) * 2;
-      const double fl = 4.0 * R * Hq * hd * (double)f.ctx_bound;
+      // flops: 4 * hd per (query head, visible key); [x, z1] row i sees i + 1 keys
+      const double Lx = f.rows_per_seq / 2.0;
+      const double fl = f.mode == 4 ? 4.0 * f.n * Hq * hd * Lx * (Lx + 1.0)
+                                    : 4.0 * R * Hq * hd * (double)f.ctx_bound;
       Timed t(c, UNO_KC_ATTENTION, kvb + pb + io, fl);
       UNO_HIP(c, launch_attention<T>(a, kv, s));
     }
@@ -585,6 +608,41 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   }
   if (f.hidden_out)
     UNO_HIP(c, hipMemcpyAsync(f.hidden_out, x, sizeof(float) * R * d, hipMemcpyDeviceToDevice, s));
+  if (f.mode == 4) {
+    // teacher = x-row logits (AR weights), student = z1-row logits (AR + LoRA)
+    if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
+    const int Lx = f.rows_per_seq / 2, nt = V / 16;
+    float* lg = c->at<float>(c->L.logits);
+    float* ts = c->at<float>(c->L.tile_stats);
+    float* ml = c->at<float>(c->L.row_ml);
+    std::vector<float*> dst(2 * f.n);
+    for (int i = 0; i < f.n; ++i)
+      for (int h = 0; h < 2; ++h) {
+        const size_t r0 = (size_t)i * f.rows_per_seq + (size_t)h * Lx;
+        float* user = h == 0 ? f.teacher : f.student;
+        float* o = user ? user + (size_t)i * Lx * V : lg + r0 * V;
+        dst[2 * i + h] = o;
+        GemmArgs a{};
+        a.X = xg + r0 * d; a.ldx = d; a.M = Lx; a.K = d; a.r = 0;
+        a.nseg = 1;
+        a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
+        a.ss_in = SS(2 * L) + r0; a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
+        a.epi = EPI_LOGITS; a.ldo = V; a.out = o;
+        a.mask_col = g.mask_id; a.tile_stats = ts + r0 * nt * 2; a.n_tiles = nt;
+        if (uno_status st = run_gemm(a, V, UNO_KC_LM_HEAD)) return st;
+      }
+    Timed t(c, UNO_KC_SAMPLING, (double)R * V * 4 + (double)R * nt * 8, 0);
+    UNO_HIP(c, launch_row_stats(ts, R, nt, ml, s));
+    for (int i = 0; i < f.n; ++i) {
+      const size_t r0 = (size_t)i * f.rows_per_seq;
+      float* tvr = (f.tv_row ? f.tv_row : c->at<float>(c->L.tv)) + (size_t)i * Lx;
+      UNO_HIP(c, launch_tv(dst[2 * i], dst[2 * i + 1], ml + r0 * 2, ml + (r0 + Lx) * 2, Lx, V,
+                           tvr, s));
+      if (f.tv_block)
+        UNO_HIP(c, launch_tv_blocks(tvr, Lx, f.dB, f.tv_block + (size_t)i * (Lx / f.dB), s));
+    }
+    return UNO_OK;
+  }
   if (f.probs_out || f.logits_out) {
     if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
     GemmArgs a{};
@@ -935,6 +993,62 @@ uno_status uno_forward(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t ro
   f.hidden_out = d_hidden_out;
   f.logits_out = d_logits;
   return forward(c, f);
+}
+
+uno_status uno_distill_forward(uno_ctx* c, int32_t batch, int32_t L, int32_t B, const int32_t* d_x,
+                               float* d_teacher, float* d_student, float* d_tv_row,
+                               float* d_tv_block) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (batch < 1 || L < 1 || B < 1 || L % B) return fail(c, UNO_ERR_INVALID_ARG, "bad batch / L / B");
+  if (!d_x) return fail(c, UNO_ERR_INVALID_ARG, "null tokens");
+  if (2 * L > c->cfg.max_rows || 2 * L > c->cfg.max_seq_len)
+    return fail(c, UNO_ERR_INVALID_ARG, "2L exceeds max_rows or max_seq_len");
+  if (!c->embed || !c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no embedding / LM head");
+  if (!c->drafted_ids.empty()) return fail(c, UNO_ERR_STATE, "a drafted block awaits verification");
+  // scratch sequences: slots holding no sequence and no pages
+  std::vector<int> slots;
+  for (int s = 0; s < c->cfg.max_seqs; ++s)
+    if (!c->live[s] && c->seq_pages[s].empty()) slots.push_back(s);
+  const int ps = c->cfg.page_size, pps = (2 * L + ps - 1) / ps;
+  int nb = std::min<int>((int)slots.size(), c->cfg.max_rows / (2 * L));
+  nb = std::min<int>(nb, (int)c->free_pages.size() / pps);
+  nb = std::min(nb, batch);
+  if (nb < 1) return fail(c, UNO_ERR_OUT_OF_PAGES, "no free sequence slot / pages for [x, z1]");
+  const size_t V = c->cfg.vocab;
+  poll_snapshot(c);
+  for (int g0 = 0; g0 < batch; g0 += nb) {
+    const int n = std::min(nb, batch - g0);
+    std::vector<int> seqs(slots.begin(), slots.begin() + n);
+    uno_status st;
+    if ((st = reserve(c, seqs, std::vector<int>(n, 2 * L)))) return st;
+    if ((st = flush_pages(c))) return st;
+    if ((st = upload_call(c, seqs))) return st;
+    FwdIn f{};
+    f.mode = 4; f.n = n; f.rows_per_seq = 2 * L;
+    f.in_tok = d_x + (size_t)g0 * L;
+    f.ctx_bound = L + 32;     // the virtual key count of any 16-row tile is at most L + 16
+    f.lora = true;
+    f.dB = B;
+    f.teacher = d_teacher ? d_teacher + (size_t)g0 * L * V : nullptr;
+    f.student = d_student ? d_student + (size_t)g0 * L * V : nullptr;
+    f.tv_row = d_tv_row ? d_tv_row + (size_t)g0 * L : nullptr;
+    f.tv_block = d_tv_block ? d_tv_block + (size_t)g0 * (L / B) : nullptr;
+    st = forward(c, f);
+    // the pages go back to the pool (stream-ordered after the forward)
+    for (int s : seqs) {
+      auto& pg = c->seq_pages[s];
+      for (size_t i = 0; i < pg.size(); ++i) {
+        c->pt_idx.push_back(s * c->maxpp + (int)i);
+        c->pt_val.push_back(-1);
+        c->free_pages.push_back(pg[i]);
+      }
+      pg.clear();
+    }
+    uno_status st2 = flush_pages(c);
+    if (st) return st;
+    if (st2) return st2;
+  }
+  return UNO_OK;
 }
 
 uno_status uno_kv_import(uno_ctx* c, int32_t seq_id, int32_t len, const void* d_k, const void* d_v,

@@ -22,7 +22,8 @@ PROJ = synth.PROJ
 EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_verify",
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
-            "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_read")
+            "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_read",
+            "uno_distill_forward")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -147,6 +148,7 @@ class Engine:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed)
+        self.n_pages = self.ccfg.n_pages
         kv_bytes, ws_bytes = query_sizes(self.ccfg)
         self.kv = torch.empty(max(kv_bytes, 1), dtype=torch.uint8, device=self.device)
         self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=self.device)
@@ -268,6 +270,27 @@ class Engine:
         self._check(lib().uno_forward(self.h, len(ids), pids, rows_per_seq, _ptr(tokens),
                                       _ptr(hidden_in), _ptr(pos), _ptr(gate), _ptr(hid), _ptr(lg)))
         return hid, lg
+
+    def distill_forward(self, x, B, teacher=None, student=None, tv_row=None, tv_block=None,
+                        want_logits=True):
+        """[x, MASK^L] forward of each row of x (device int32 [batch, L]) with block
+        size B.  Returns (teacher, student, tv_row, tv_block); logits are allocated
+        unless passed in (or want_logits is False: then None, only TV formed)."""
+        torch = self.torch
+        batch, L = x.shape
+        V = self.cfg.vocab
+        if want_logits:
+            if teacher is None:
+                teacher = self._empty((batch, L, V), torch.float32)
+            if student is None:
+                student = self._empty((batch, L, V), torch.float32)
+        if tv_row is None:
+            tv_row = self._empty((batch, L), torch.float32)
+        if tv_block is None:
+            tv_block = self._empty((batch, L // B), torch.float32)
+        self._check(lib().uno_distill_forward(self.h, batch, L, B, _ptr(x), _ptr(teacher),
+                                              _ptr(student), _ptr(tv_row), _ptr(tv_block)))
+        return teacher, student, tv_row, tv_block
 
     def kv_import(self, seq_id, k, v, pending, iteration=0):
         """k, v: device tensors [layers, len, Hkv, hd] of the storage dtype."""

@@ -179,6 +179,28 @@ uno_status uno_forward(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t 
                        const int32_t* d_tokens, const float* d_hidden_in, const int32_t* d_pos,
                        const uint8_t* d_gate, float* d_hidden_out, float* d_logits);
 
+/* Distillation-style forward (Uno reading notes, "Diffusion Distillation": the
+ * clean sequence x and the fully corrupted z1 = MASK^L run as [x, z1] in ONE
+ * forward under a block-causal mask, the gated LoRA off on x rows and on on z1
+ * rows, giving teacher (AR) and student (AR + LoRA) logits together, compared by
+ * a block-wise total variation; ai-papers-daily summary, method key points).
+ *   d_x        device int32 [batch, L] clean tokens in [0, vocab)
+ *   d_teacher  device float32 [batch, L, vocab] x-row logits (MASK column -inf),
+ *              or NULL
+ *   d_student  device float32 [batch, L, vocab] z1-row logits, or NULL
+ *   d_tv_row   device float32 [batch, L]: TV_i = 0.5 * sum_v |p_T,i - p_S,i|, or NULL
+ *   d_tv_block device float32 [batch, L/B]: mean of TV_i over each block, or NULL
+ * Row i of x and row i of z1 both sit at RoPE position i and both predict token
+ * i+1.  Visibility: x row i sees x[0..i]; z1 row i of block b = i / B sees x[0, bB)
+ * and z1[bB..i].  Requires L % B == 0, 2L <= max_rows and 2L <= max_seq_len.
+ * The [x, z1] K/V live in sequence slots that hold no sequence and no pages
+ * (UNO_ERR_OUT_OF_PAGES when there is none, or too few free pages for 2L
+ * positions); the call borrows them and returns them, so committed sequences are
+ * untouched.  UNO_ERR_STATE between uno_draft and uno_verify.  Asynchronous. */
+uno_status uno_distill_forward(uno_ctx* ctx, int32_t batch, int32_t L, int32_t B,
+                               const int32_t* d_x, float* d_teacher, float* d_student,
+                               float* d_tv_row, float* d_tv_block);
+
 /* Copy a sequence's K/V for positions [0, len) in from / out to contiguous device
  * buffers [n_layers][len][n_kv_heads][head_dim] of the storage type.  Import
  * reserves pages, sets the committed length to len and the pending token and
@@ -196,14 +218,14 @@ uno_status uno_seq_state(uno_ctx* ctx, int32_t seq_id, int32_t* len, int32_t* pe
  * stream, and the algorithmic bytes and flops each launch must move / execute
  * (weights, activations, LoRA, KV and outputs it reads or writes once) are
  * accumulated.  uno_timing clears the record; uno_timing_read syncs and reports
- * one class.  At most 65536 launches are recorded per enable. */
+ * one class.  At most 32768 launches are recorded per enable. */
 typedef enum {
   UNO_KC_LINEAR = 0,        /* gated-LoRA linear: q/k/v, o, down              */
   UNO_KC_LINEAR_SWIGLU = 1, /* gated-LoRA gate/up with the SwiGLU epilogue    */
   UNO_KC_LORA_DOWN = 2,     /* LoRA down-projection (the gated intermediate)  */
   UNO_KC_ATTENTION = 3,     /* paged block-causal attention (both kernels)    */
   UNO_KC_LM_HEAD = 4,       /* LM head with the softmax statistics            */
-  UNO_KC_SAMPLING = 5,      /* softmax, draws, accept / resample, commit      */
+  UNO_KC_SAMPLING = 5,      /* softmax, TV, draws, accept / resample, commit  */
   UNO_KC_MISC = 6,          /* row set-up, embedding, norms, RoPE / KV write  */
   UNO_KC_COUNT = 7
 } uno_kernel_class;
