@@ -159,6 +159,58 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     }
 
 
+def run_distill(cfg, w, dev, batch, L, B, reps):
+    """The [x, z1] distillation forward: `batch` sequences of L uniform clean tokens
+    with L MASK tokens, block size B; teacher and student logits written to
+    [batch, L, vocab] float32 buffers, per-row and per-block TV.  Returns ms per
+    forward, MFMA TFLOP/s over the dense work and the per-class breakdown."""
+    import torch
+    from diffusion_drafted_lora_amd import synth, uno
+
+    rows = max(2 * L, min(batch, 2) * 2 * L)
+    eng = uno.Engine(cfg, w, max_seqs=batch, max_seq_len=2 * L + 16, max_rows=rows,
+                     seed=3004, device=dev)
+    x = torch.from_numpy(synth.prompts(cfg, 2004, batch, L)).to(torch.int32).to(dev)
+    V = cfg.vocab
+    teacher = torch.empty((batch, L, V), dtype=torch.float32, device=dev)
+    student = torch.empty((batch, L, V), dtype=torch.float32, device=dev)
+    tv_row = torch.empty((batch, L), dtype=torch.float32, device=dev)
+    tv_block = torch.empty((batch, L // B), dtype=torch.float32, device=dev)
+    log(f"distill: warmup, batch {batch} x [{L} | {L}], B {B}")
+    eng.distill_forward(x, B, teacher, student, tv_row, tv_block)
+    eng.sync()
+    cls = ["linear", "linear_swiglu", "lora_down", "lm_head", "attention", "sampling"]
+    eng.timing(cls)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        eng.distill_forward(x, B, teacher, student, tv_row, tv_block)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    eng.sync()
+    breakdown = {}
+    for c in cls:
+        n, ms, b, f = eng.timing_read(c)
+        breakdown[c] = {"ms_per_forward": ms / reps,
+                        "TFLOP/s": f / 1e12 / (ms / 1e3) if ms and f else None,
+                        "GB/s": b / 1e9 / (ms / 1e3) if ms else None}
+    eng.timing([])
+    tvb = tv_block.float().mean().item()
+    eng.close()
+    del eng, teacher, student
+    torch.cuda.empty_cache()
+    d, q, kv, F, r = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim, cfg.lora_rank
+    R = batch * 2 * L
+    dense = 2.0 * R * (cfg.n_layers * (q * d + 2 * kv * d + d * q + 3 * F * d) + V * d)
+    lora = 2.0 * (R / 2) * cfg.n_layers * r * ((d + q) + 2 * (d + kv) + (q + d) + 2 * (d + F) + (F + d))
+    attn = 4.0 * batch * cfg.n_q_heads * cfg.head_dim * L * (L + 1) * cfg.n_layers
+    total = dense + lora + attn
+    return {"batch": batch, "L": L, "B": B, "reps": reps, "ms_per_forward": 1e3 * sec,
+            "tflop_per_forward": total / 1e12, "tflops": total / 1e12 / sec,
+            "mfma_frac": total / 1e12 / sec / BF16_PEAK_TFLOPS,
+            "rows_per_s": R / sec, "mean_tv_block": tvb, "breakdown": breakdown}
+
+
 def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -238,6 +290,9 @@ def main():
                     help="timed iterations of the batch-128 leg (0 skips it)")
     ap.add_argument("--bs128-ctx", type=str, default="1024",
                     help="comma-separated starting contexts of the batch-128 leg")
+    ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
+                    help="distillation-forward leg (batch, L, block size); 'none' skips it")
+    ap.add_argument("--distill-reps", type=int, default=2)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy of MIB MiB (HBM counter scale)")
     args = ap.parse_args()
@@ -363,12 +418,15 @@ def main():
         },
         "breakdown": breakdown,
     }
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
     if args.bs128_steps > 0:
-        eng.close()
-        del eng
-        torch.cuda.empty_cache()
         result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
                            for c in args.bs128_ctx.split(",")]
+    if args.distill != "none":
+        db, dl, dbs = (int(v) for v in args.distill.split(","))
+        result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(cfg, w, tokens / K)
