@@ -489,7 +489,7 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
       if (ea != hipSuccess) return ea;
     }
-    k_attn_mfma<<<grid, 64 * G, smem, s>>>(a, kv);
+    uno_launch(k_attn_mfma, grid, 64 * G, smem, s, a, kv);
   } else {
     const size_t smem = attn_smem_bytes<T>(G, kv.head_dim);
     const int nown = (16 * G * kv.head_dim + 255) / 256;
@@ -500,7 +500,7 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
       if (ea != hipSuccess) return ea;                                                      \
     }                                                                                       \
-    k_attn_partial<T, MO><<<grid, 256, smem, s>>>(a, kv);                                   \
+    uno_launch(k_attn_partial<T, MO>, grid, 256, smem, s, a, kv);                                   \
   } else
     UNO_ATTN_CASE(1) UNO_ATTN_CASE(4) UNO_ATTN_CASE(16) UNO_ATTN_CASE(32) UNO_ATTN_CASE(64)
     return hipErrorInvalidValue;
@@ -509,7 +509,7 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_chunks == 1 && mfma) return hipSuccess;   // the MFMA kernel wrote the outputs directly
-  k_attn_combine<T><<<R * a.n_q_heads, kv.head_dim < 256 ? kv.head_dim : 256, 0, s>>>(
+  uno_launch(k_attn_combine<T>, R * a.n_q_heads, kv.head_dim < 256 ? kv.head_dim : 256, 0, s, 
       a, kv.head_dim);
   return hipGetLastError();
 }

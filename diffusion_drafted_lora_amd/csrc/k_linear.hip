@@ -609,14 +609,14 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.K % a.kchunk || a.kchunk % 64 || a.r % 16) return hipErrorInvalidValue;
   dim3 grid(a.nproj * a.r / 16, a.K / a.kchunk, (a.M + 15) / 16);
-  k_lora_down<<<grid, 64, 0, s>>>(a);
+  uno_launch(k_lora_down, grid, 64, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
-  k_zero_i64<<<blocks, 256, 0, s>>>(p, n);
+  uno_launch(k_zero_i64, blocks, 256, 0, s, p, n);
   return hipGetLastError();
 }
 
@@ -631,26 +631,26 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
     const int mblocks = (a.M + BM - 1) / BM;
     const int nblocks = n_cols_total / outc;
     const size_t smem = (size_t)BM * BN * 4;
-    k_gemm_big<<<nblocks * mblocks, 256, smem, s>>>(a, mblocks);
+    uno_launch(k_gemm_big, nblocks * mblocks, 256, smem, s, a, mblocks);
     return hipGetLastError();
   }
   const int mtiles = (a.M + 15) / 16;
   dim3 grid(n_cols_total / 16, mtiles);
   if (a.paired) {
-    if (a.K % 512 == 0) k_gemm_bf16<2, 16, 2><<<grid, 1024, 0, s>>>(a);
-    else if (a.K % 128 == 0) k_gemm_bf16<2, 4, 1><<<grid, 256, 0, s>>>(a);
-    else k_gemm_bf16<2, 1, 1><<<grid, 64, 0, s>>>(a);
+    if (a.K % 512 == 0) uno_launch(k_gemm_bf16<2, 16, 2>, grid, 1024, 0, s, a);
+    else if (a.K % 128 == 0) uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
+    else uno_launch(k_gemm_bf16<2, 1, 1>, grid, 64, 0, s, a);
   } else {
     if (a.epi == EPI_LOGITS && n_cols_total % 64 == 0 && a.K % 512 == 0) {
       // wide N: four column tiles per workgroup share each activation fragment
       dim3 g4(n_cols_total / 64, mtiles);
-      k_gemm_bf16<4, 16, 2><<<g4, 1024, 0, s>>>(a);
+      uno_launch(k_gemm_bf16<4, 16, 2>, g4, 1024, 0, s, a);
     } else if (a.K % 1024 == 0) {
-      k_gemm_bf16<1, 16, 4><<<grid, 1024, 0, s>>>(a);
+      uno_launch(k_gemm_bf16<1, 16, 4>, grid, 1024, 0, s, a);
     } else if (a.K % 128 == 0) {
-      k_gemm_bf16<1, 4, 1><<<grid, 256, 0, s>>>(a);
+      uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
     } else {
-      k_gemm_bf16<1, 1, 1><<<grid, 64, 0, s>>>(a);
+      uno_launch(k_gemm_bf16<1, 1, 1>, grid, 64, 0, s, a);
     }
   }
   return hipGetLastError();
@@ -662,7 +662,7 @@ hipError_t launch_gemm<float>(const GemmArgs& a, int n_cols_total, hipStream_t s
   if (a.epi == EPI_LOGITS && n_cols_total % 16 != 0) return hipErrorInvalidValue;
   const int mtiles = (a.M + 15) / 16;
   dim3 grid((n_cols_total + 15) / 16, mtiles);
-  if (a.paired) k_gemm_f32<2><<<grid, 256, 0, s>>>(a);
-  else k_gemm_f32<1><<<grid, 256, 0, s>>>(a);
+  if (a.paired) uno_launch(k_gemm_f32<2>, grid, 256, 0, s, a);
+  else uno_launch(k_gemm_f32<1>, grid, 256, 0, s, a);
   return hipGetLastError();
 }

@@ -242,7 +242,7 @@ __global__ void k_kv_copy(KvLayout kv, int seq, int len, T* k, T* v, int to_page
 hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s) {
   const int R = a.n * a.rows_per_seq;
   if (R <= 0) return hipSuccess;
-  k_rows_setup<<<(R + 255) / 256, 256, 0, s>>>(a);
+  uno_launch(k_rows_setup, (R + 255) / 256, 256, 0, s, a);
   return hipGetLastError();
 }
 
@@ -250,40 +250,40 @@ template <typename T>
 hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
                         int V, float* x, const T* g, T* xg, long long* ss, int32_t* err,
                         hipStream_t s) {
-  k_embed<T><<<R, 256, 0, s>>>(E, tok, hidden_in, d, V, x, g, xg, ss, err);
+  uno_launch(k_embed<T>, R, 256, 0, s, E, tok, hidden_in, d, V, x, g, xg, ss, err);
   return hipGetLastError();
 }
 
 hipError_t launch_row_stats(const float* tile_stats, int R, int n_tiles, float* row_ml,
                             hipStream_t s) {
-  k_row_stats<<<R, 1024, 0, s>>>(tile_stats, n_tiles, row_ml);
+  uno_launch(k_row_stats, R, 1024, 0, s, tile_stats, n_tiles, row_ml);
   return hipGetLastError();
 }
 
 hipError_t launch_softmax(const float* logits, const float* row_ml, int R, int V, float* probs,
                           hipStream_t s) {
   const int bx = (V + 1023) / 1024 < 64 ? (V + 1023) / 1024 : 64;
-  k_softmax<<<dim3(bx, R), 256, 0, s>>>(logits, row_ml, V, probs);
+  uno_launch(k_softmax, dim3(bx, R), 256, 0, s, logits, row_ml, V, probs);
   return hipGetLastError();
 }
 
 hipError_t launch_tv(const float* t_logits, const float* s_logits, const float* t_ml,
                      const float* s_ml, int L, int V, float* tv_row, hipStream_t s) {
   if (L <= 0) return hipSuccess;
-  k_tv<<<L, 256, 0, s>>>(t_logits, s_logits, t_ml, s_ml, V, tv_row);
+  uno_launch(k_tv, L, 256, 0, s, t_logits, s_logits, t_ml, s_ml, V, tv_row);
   return hipGetLastError();
 }
 
 hipError_t launch_tv_blocks(const float* tv_row, int L, int B, float* tv_block, hipStream_t s) {
   if (L <= 0 || B <= 0 || L % B) return hipErrorInvalidValue;
   const int nb = L / B;
-  k_tv_blocks<<<(nb + 255) / 256, 256, 0, s>>>(tv_row, nb, B, tv_block);
+  uno_launch(k_tv_blocks, (nb + 255) / 256, 256, 0, s, tv_row, nb, B, tv_block);
   return hipGetLastError();
 }
 
 hipError_t launch_set_list(const SetList& l, hipStream_t s) {
   if (l.count <= 0) return hipSuccess;
-  k_set_list<<<1, 256, 0, s>>>(l);
+  uno_launch(k_set_list, 1, 256, 0, s, l);
   return hipGetLastError();
 }
 
@@ -291,7 +291,7 @@ template <typename T>
 hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,
                           hipStream_t s) {
   if (len <= 0) return hipSuccess;
-  k_kv_copy<T><<<dim3(len, kv.n_layers), 256, 0, s>>>(kv, seq, len, k, v, to_pages);
+  uno_launch(k_kv_copy<T>, dim3(len, kv.n_layers), 256, 0, s, kv, seq, len, k, v, to_pages);
   return hipGetLastError();
 }
 

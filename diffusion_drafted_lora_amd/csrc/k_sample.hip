@@ -245,8 +245,8 @@ hipError_t launch_cdf(const RowDesc* desc, int rows, int V, uint64_t* chunk_tot,
   const int n_chunks = (V + CDF_CHUNK - 1) / CDF_CHUNK;
   if (rows <= 0) return hipSuccess;
   if (n_chunks > 1024) return hipErrorInvalidValue;
-  k_cdf_chunks<<<dim3(n_chunks, rows), CDF_THREADS, 0, s>>>(desc, V, n_chunks, chunk_tot, err);
-  k_cdf_select<<<rows, CDF_THREADS, 0, s>>>(desc, V, n_chunks, chunk_tot, err);
+  uno_launch(k_cdf_chunks, dim3(n_chunks, rows), CDF_THREADS, 0, s, desc, V, n_chunks, chunk_tot, err);
+  uno_launch(k_cdf_select, rows, CDF_THREADS, 0, s, desc, V, n_chunks, chunk_tot, err);
   return hipGetLastError();
 }
 
@@ -255,7 +255,7 @@ hipError_t launch_draft_desc(const float* probs, int n, int B, int V, uint64_t s
                              const int32_t* call_it, int32_t* out_tok, RowDesc* desc,
                              hipStream_t s) {
   const int rows = n * B;
-  k_draft_desc<<<(rows + 127) / 128, 128, 0, s>>>(probs, n, B, V, seed, call_seq, call_n,
+  uno_launch(k_draft_desc, (rows + 127) / 128, 128, 0, s, probs, n, B, V, seed, call_seq, call_n,
                                                   call_it, out_tok, desc);
   return hipGetLastError();
 }
@@ -263,7 +263,7 @@ hipError_t launch_draft_desc(const float* probs, int n, int B, int V, uint64_t s
 hipError_t launch_sample_desc(const float* w, int rows, int V, uint64_t seed,
                               const int32_t* seq_ids, const int32_t* pos, const int32_t* it,
                               int stream_id, int32_t* out, RowDesc* desc, hipStream_t s) {
-  k_sample_desc<<<(rows + 127) / 128, 128, 0, s>>>(w, rows, V, seed, seq_ids, pos, it,
+  uno_launch(k_sample_desc, (rows + 127) / 128, 128, 0, s, w, rows, V, seed, seq_ids, pos, it,
                                                    stream_id, out, desc);
   return hipGetLastError();
 }
@@ -274,7 +274,7 @@ hipError_t launch_accept_test(uint64_t seed, int n, int B, int V, const float* p
                               const int32_t* call_it, int32_t* k_out, int32_t* z_out,
                               RowDesc* desc, int32_t* err, hipStream_t s) {
   if (B > 65) return hipErrorInvalidValue;
-  k_accept_test<<<n, 64, 0, s>>>(seed, B, V, p, q, q_stride, draft, call_seq, call_n, call_it,
+  uno_launch(k_accept_test, n, 64, 0, s, seed, B, V, p, q, q_stride, draft, call_seq, call_n, call_it,
                                  k_out, z_out, desc, err);
   return hipGetLastError();
 }
@@ -284,7 +284,7 @@ hipError_t launch_accept_commit(int n, int B, const int32_t* draft, const int32_
                                 int32_t* n_out, int32_t* len, int32_t* pending, int32_t* iter,
                                 hipStream_t s) {
   const int threads = ((B + 1 + 63) / 64) * 64;
-  k_accept_commit<<<n, threads, 0, s>>>(B, draft, k, z, call_seq, out, n_out, len, pending,
+  uno_launch(k_accept_commit, n, threads, 0, s, B, draft, k, z, call_seq, out, n_out, len, pending,
                                         iter);
   return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <climits>
 
@@ -18,6 +19,24 @@ template <> UNO_DEV float to_f<bf16>(bf16 v) { return (float)v; }
 template <typename T> UNO_DEV T from_f(float v);
 template <> UNO_DEV float from_f<float>(float v) { return v; }
 template <> UNO_DEV bf16 from_f<bf16>(float v) { return (bf16)v; }  // round to nearest even
+
+// ------------------------------------------------------------- kernel launches
+// Every launch goes through uno_launch.  When the runtime has armed a timer on
+// the calling thread, the launch takes the timer's next event pair, which HIP
+// stamps with that kernel's own start and end (hipExtLaunchKernel), so the time
+// between kernels is not counted.
+struct KernelTimer {
+  virtual bool next(hipEvent_t* start, hipEvent_t* stop) = 0;
+};
+extern thread_local KernelTimer* g_kernel_timer;
+
+template <typename... KArgs, typename... Args>
+inline void uno_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t smem,
+                       hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_kernel_timer && !g_kernel_timer->next(&e0, &e1)) e0 = e1 = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e0, e1, 0, static_cast<KArgs>(args)...);
+}
 
 // Device error bits (sticky per context, OR-ed by kernels).
 enum : int32_t {

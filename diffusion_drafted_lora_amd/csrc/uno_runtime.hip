@@ -130,7 +130,7 @@ struct uno_ctx {
   // kernel timing
   uint32_t tmask = 0;
   std::vector<hipEvent_t> tev;          // event pool, two per recorded launch
-  struct TRec { int cls; int ev; double bytes, flops; };
+  struct TRec { int cls; int ev; double bytes, flops; bool call; };
   std::vector<TRec> trec;
   std::string err;
 
@@ -156,22 +156,34 @@ uno_status hip_fail(uno_ctx* c, hipError_t e, const char* where) {
   } while (0)
 
 constexpr int kTimedLaunches = 32768;
+}  // namespace
 
-// Brackets one launch with events when its class is being timed.
-struct Timed {
+thread_local KernelTimer* g_kernel_timer = nullptr;
+
+namespace {
+
+// Arms the kernel timer for the launches of one call of a timed class: each of
+// its kernels gets an event pair stamped with that kernel's start and end; the
+// call's algorithmic bytes and flops go with its first kernel.
+struct Timed : KernelTimer {
   uno_ctx* c;
-  int cls, ev = -1;
+  int cls;
   double bytes, flops;
-  Timed(uno_ctx* c_, int cls_, double b, double f) : c(c_), cls(cls_), bytes(b), flops(f) {
-    if ((c->tmask >> cls) & 1u) {
-      const size_t i = c->trec.size() * 2;
-      if (i + 2 <= c->tev.size() && hipEventRecord(c->tev[i], c->stream) == hipSuccess)
-        ev = (int)i;
-    }
+  bool first = true;
+  KernelTimer* saved;
+  Timed(uno_ctx* c_, int cls_, double b, double f)
+      : c(c_), cls(cls_), bytes(b), flops(f), saved(g_kernel_timer) {
+    g_kernel_timer = ((c->tmask >> cls) & 1u) ? this : nullptr;
   }
-  ~Timed() {
-    if (ev >= 0 && hipEventRecord(c->tev[ev + 1], c->stream) == hipSuccess)
-      c->trec.push_back({cls, ev, bytes, flops});
+  ~Timed() { g_kernel_timer = saved; }
+  bool next(hipEvent_t* e0, hipEvent_t* e1) override {
+    const size_t i = c->trec.size() * 2;
+    if (i + 2 > c->tev.size()) return false;
+    *e0 = c->tev[i];
+    *e1 = c->tev[i + 1];
+    c->trec.push_back({cls, (int)i, first ? bytes : 0.0, first ? flops : 0.0, first});
+    first = false;
+    return true;
   }
 };
 
@@ -1154,7 +1166,7 @@ uno_status uno_timing_read(uno_ctx* c, int32_t cls, int64_t* launches, double* t
     if (r.cls != cls) continue;
     float e = 0;
     UNO_HIP(c, hipEventElapsedTime(&e, c->tev[r.ev], c->tev[r.ev + 1]));
-    ++n;
+    if (r.call) ++n;
     ms += e;
     b += r.bytes;
     f += r.flops;

@@ -213,12 +213,15 @@ uno_status uno_kv_export(uno_ctx* ctx, int32_t seq_id, int32_t len, void* d_k, v
 uno_status uno_seq_state(uno_ctx* ctx, int32_t seq_id, int32_t* len, int32_t* pending,
                          int32_t* iter);
 
-/* Kernel timing (instrumentation).  While enabled, launches of the kernel classes
- * in class_mask (bit i = class i) are bracketed by HIP events on the context's
- * stream, and the algorithmic bytes and flops each launch must move / execute
- * (weights, activations, LoRA, KV and outputs it reads or writes once) are
- * accumulated.  uno_timing clears the record; uno_timing_read syncs and reports
- * one class.  At most 32768 launches are recorded per enable. */
+/* Kernel timing (instrumentation).  While enabled, every kernel of the classes in
+ * class_mask (bit i = class i) is launched with a pair of HIP events that the
+ * runtime stamps with that kernel's own start and end on the context's stream
+ * (gaps between kernels are not counted), and the algorithmic bytes and flops
+ * each call must move / execute (weights, activations, LoRA, KV and outputs it
+ * reads or writes once) are accumulated.  uno_timing clears the record;
+ * uno_timing_read syncs and reports one class: calls (a call of a class may run
+ * more than one kernel), summed kernel milliseconds, bytes and flops.  At most
+ * 32768 kernels are recorded per enable. */
 typedef enum {
   UNO_KC_LINEAR = 0,        /* gated-LoRA linear: q/k/v, o, down              */
   UNO_KC_LINEAR_SWIGLU = 1, /* gated-LoRA gate/up with the SwiGLU epilogue    */
@@ -226,7 +229,7 @@ typedef enum {
   UNO_KC_ATTENTION = 3,     /* paged block-causal attention (both kernels)    */
   UNO_KC_LM_HEAD = 4,       /* LM head with the softmax statistics            */
   UNO_KC_SAMPLING = 5,      /* softmax, TV, draws, accept / resample, commit  */
-  UNO_KC_MISC = 6,          /* row set-up, embedding, norms, RoPE / KV write  */
+  UNO_KC_MISC = 6,          /* row set-up, embedding, buffer clears           */
   UNO_KC_COUNT = 7
 } uno_kernel_class;
 uno_status uno_timing(uno_ctx* ctx, uint32_t class_mask);
