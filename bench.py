@@ -211,7 +211,21 @@ def run_distill(cfg, w, dev, batch, L, B, reps):
             "rows_per_s": R / sec, "mean_tv_block": tvb, "breakdown": breakdown}
 
 
-def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
+def cpu_sample_weights(cfg, w):
+    """Host float32 copies of what the CPU baseline runs on: layer 0 and the first
+    eighth of the LM head (row-major, before packing)."""
+    import numpy as np
+    lw = w["layers"][0]
+    f32 = lambda t: t.float().cpu().numpy()
+    w1 = {"final_norm": np.ones(cfg.d_model, np.float32),
+          "layers": [{"attn_norm": f32(lw["attn_norm"]), "mlp_norm": f32(lw["mlp_norm"]),
+                      "w": {p: f32(t) for p, t in lw["w"].items()},
+                      "la": {p: f32(t) for p, t in lw["la"].items()},
+                      "lb": {p: f32(t) for p, t in lw["lb"].items()}}]}
+    return w1, f32(w["lm_head"][: cfg.vocab // 8])
+
+
+def cpu_baseline(cfg, sample_w, tokens_per_iter, ctx=1024):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import torch
@@ -220,13 +234,7 @@ def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
     from diffusion_drafted_lora_amd import configs, synth
 
     one = cfg.with_(n_layers=1)
-    lw = eng_w["layers"][0]
-    f32 = lambda t: t.float().cpu().numpy()
-    w1 = {"final_norm": np.ones(cfg.d_model, np.float32),
-          "layers": [{"attn_norm": f32(lw["attn_norm"]), "mlp_norm": f32(lw["mlp_norm"]),
-                      "w": {p: f32(t) for p, t in lw["w"].items()},
-                      "la": {p: f32(t) for p, t in lw["la"].items()},
-                      "lb": {p: f32(t) for p, t in lw["lb"].items()}}]}
+    w1, W = sample_w
     kc = torch.from_numpy(synth.normal(9001, (1, ctx, cfg.n_kv_heads, cfg.head_dim)))
     kc = kc.to(torch.bfloat16).float().numpy()
     B = cfg.block_size
@@ -248,7 +256,6 @@ def cpu_baseline(cfg, eng_w, tokens_per_iter, ctx=1024):
             break
     t_layer = (time.perf_counter() - t0) / reps
     # LM head on 1/8 of the vocabulary, both forwards' rows, scaled by 8
-    W = eng_w["lm_head"][: cfg.vocab // 8].float().cpu().numpy()
     h = synth.normal(9003, (2 * B, cfg.d_model))
     t0 = time.perf_counter()
     lg = model.bf16_round(h) @ W.T
@@ -317,6 +324,9 @@ def main():
         copy_probe(args.copy_probe)
     log(f"generating weights ({cfg.n_layers} layers) on the GPU")
     w = synth.weights_torch(cfg, args.seed, dev)
+    sample_w = None if args.no_cpu_baseline else cpu_sample_weights(cfg, w)
+    w = uno.pack_weights(cfg, w)      # the kernels' fragment-tiled layout, once
+    torch.cuda.empty_cache()
     max_new = (args.warmup + args.steps + args.breakdown_steps + 1) * (B + 1)
     if args.prompt + max_new > cfg.prompt_len + cfg.new_tokens + B + 1:
         log("note: steps exceed the 1K/8K protocol length; the context grows beyond 9216")
@@ -429,7 +439,7 @@ def main():
         result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(cfg, w, tokens / K)
+        result["cpu_baseline"] = cpu_baseline(cfg, sample_w, tokens / K)
     print(json.dumps(result), flush=True)
 
 

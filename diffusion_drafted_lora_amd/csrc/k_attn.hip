@@ -237,7 +237,7 @@ k_attn_combine(AttnArgs a, int hd) {
       for (int u = 0; u < 8; ++u) acc += v[u] * sf[c + u];
     }
     for (; c < nc; ++c) acc += po[(size_t)c * hd] * sf[c];
-    reinterpret_cast<T*>(a.out)[(size_t)r * a.n_q_heads * hd + h * hd + d] = from_f<T>(acc * inv);
+    reinterpret_cast<T*>(a.out)[act_off<T>(r, h * hd + d, a.n_q_heads * hd)] = from_f<T>(acc * inv);
   }
 }
 
@@ -449,9 +449,10 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
     const size_t rr = (size_t)(r0 + row);
     if (single) {
       const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
-      bf16* out = reinterpret_cast<bf16*>(a.out) + rr * a.n_q_heads * HD + head * HD;
+      bf16* out = reinterpret_cast<bf16*>(a.out);
 #pragma unroll
-      for (int d = 0; d < HD / 16; ++d) out[d * 16 + r16] = (bf16)(o[d][i] * inv);
+      for (int d = 0; d < HD / 16; ++d)
+        out[frag_off((int)rr, head * HD + d * 16 + r16, a.n_q_heads * HD)] = (bf16)(o[d][i] * inv);
     } else {
       const size_t ph = (rr * a.n_q_heads + head) * a.n_chunks + c;
 #pragma unroll

@@ -67,14 +67,14 @@ UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int pos, in
               kv.page_size + (pos % kv.page_size)) * kv.head_dim;
 }
 
-// Epilogue of one element (row m, lane column c) of each of the NT tiles.  `finr`
-// holds the 16 finished values of this row in tile 0 (the RoPE partner is
-// finr[c ^ 8]).  Every thread of a 16-lane row group calls this (row sums use
+// Epilogue of one element (row m, lane column c) of each of the NT tiles.  `vp`
+// is the finished tile-0 value of column c ^ 8 of the same row (the RoPE
+// partner).  Every thread of a 16-lane row group calls this (row sums use
 // shuffles); `ok` says whether row m exists.
-template <typename T, int NT>
+template <typename T, int NT, int EPI = -1>
 UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired,
-                      const float* v, const float* finr, bool ok) {
-  switch (a.epi) {
+                      const float* v, float vp, bool ok) {
+  switch (EPI >= 0 ? EPI : a.epi) {
     case EPI_STORE_F32:
       if (ok)
         for (int t = 0; t < NT; ++t)
@@ -96,7 +96,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
           const float xn = a.resid[(size_t)m * a.ldo + col] + v[t];
           a.resid[(size_t)m * a.ldo + col] = xn;
           if (a.xg_out)
-            reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.ldo + col] =
+            reinterpret_cast<T*>(a.xg_out)[act_off<T>(m, col, a.ldo)] =
                 from_f<T>(xn * to_f(reinterpret_cast<const T*>(a.g_next)[col]));
           sq += xn * xn;
         }
@@ -113,7 +113,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
     case EPI_SWIGLU: {
       if (!ok) break;
       const float g = v[0], u = v[1];
-      reinterpret_cast<T*>(a.out)[(size_t)m * a.ldo + col_paired + c] =
+      reinterpret_cast<T*>(a.out)[act_off<T>(m, col_paired + c, a.ldo)] =
           from_f<T>(g / (1.0f + expf(-g)) * u);
       break;
     }
@@ -131,7 +131,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
           if (a.err) atomicOr(a.err, UNO_DEVERR_BOUNDS);
           break;
         }
-        const float x1 = finr[c & 7], x2 = finr[(c & 7) + 8];
+        const float x1 = c < 8 ? v[0] : vp, x2 = c < 8 ? vp : v[0];
         const float cs = a.rcos[(size_t)pos * half + i], sn = a.rsin[(size_t)pos * half + i];
         val = (c < 8) ? x1 * cs - x2 * sn : x2 * cs + x1 * sn;
       }
@@ -183,33 +183,35 @@ k_gemm_bf16(GemmArgs a) {
   const int mt = blockIdx.y;
   const int grp = blockIdx.x;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int nkb = a.K / 32, nrb = a.r / 32;
 
-  // weight-row pointers of this lane's column in each tile, and LoRA operands
+  // this lane's fragment in block 0 of each tile's packed weight rows (and LoRA up)
   const bf16* Wp[NT];
   const bf16* Bp[NT];
   const long long* Up[NT];
   int ldu[NT];
   int tile0, col_paired = 0;
   if (a.paired) {
-    const int c0 = grp * 16;
-    col_paired = c0;
+    col_paired = grp * 16;
     tile0 = grp;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const GemmSeg& sg = a.seg[t];
-      Wp[t] = reinterpret_cast<const bf16*>(sg.W) + (size_t)(c0 + r16) * a.K;
-      Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)(c0 + r16) * a.r : nullptr;
+      Wp[t] = reinterpret_cast<const bf16*>(sg.W) + (size_t)grp * nkb * 512 + lane * 8;
+      Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)grp * nrb * 512 + lane * 8
+                    : nullptr;
       Up[t] = sg.Ufx;
       ldu[t] = sg.ldu;
     }
   } else {
     tile0 = grp * NT;
-    const GemmSeg& sg = a.seg[find_seg(a, tile_col(a, tile0, 0))];
+    const GemmSeg& sg = a.seg[find_seg(a, tile0 * 16)];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int lc = tile_col(a, tile0 + t, r16) - sg.n0;
-      Wp[t] = reinterpret_cast<const bf16*>(sg.W) + (size_t)lc * a.K;
-      Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)lc * a.r : nullptr;
+      const int rb = tile0 + t - sg.n0 / 16;
+      Wp[t] = reinterpret_cast<const bf16*>(sg.W) + (size_t)rb * nkb * 512 + lane * 8;
+      Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)rb * nrb * 512 + lane * 8
+                    : nullptr;
       Up[t] = sg.Ufx;
       ldu[t] = sg.ldu;
     }
@@ -220,37 +222,36 @@ k_gemm_bf16(GemmArgs a) {
 
   const int m_lane = mt * 16 + r16;
   const bool row_ok = m_lane < a.M;
-  const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)(row_ok ? m_lane : 0) * a.ldx;
+  const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)mt * nkb * 512 + lane * 8;
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- base phase: this wave's K slice
-  const int kslice = a.K / WAVES;
-  const int kb = w * kslice, ke = kb + kslice;
-  int k = kb;
+  // ---- base phase: this wave's share of the 32-wide K blocks
+  const int jb = w * nkb / WAVES, je = (w + 1) * nkb / WAVES;
+  int j = jb;
   const bf16x8 zero8 = {};
-  for (; k + 32 * KU <= ke; k += 32 * KU) {
+  for (; j + KU <= je; j += KU) {
     bf16x8 af[KU], bfr[NT][KU];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) af[u] = row_ok ? load8(Xp + k + u * 32 + kq) : zero8;
+    for (int u = 0; u < KU; ++u) af[u] = row_ok ? load8(Xp + (size_t)(j + u) * 512) : zero8;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int u = 0; u < KU; ++u) bfr[t][u] = load8(Wp[t] + k + u * 32 + kq);
+      for (int u = 0; u < KU; ++u) bfr[t][u] = load8(Wp[t] + (size_t)(j + u) * 512);
 #pragma unroll
     for (int u = 0; u < KU; ++u)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], bfr[t][u], acc[t], 0, 0, 0);
   }
-  for (; k < ke; k += 32) {
-    const bf16x8 af = row_ok ? load8(Xp + k + kq) : zero8;
+  for (; j < je; ++j) {
+    const bf16x8 af = row_ok ? load8(Xp + (size_t)j * 512) : zero8;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Wp[t] + k + kq), acc[t], 0,
-                                                       0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Wp[t] + (size_t)j * 512), acc[t],
+                                                       0, 0, 0);
   }
   // ---- RMSNorm: scale rows of the base product by 1 / rms(x)
   if (a.ss_in) {
@@ -265,19 +266,19 @@ k_gemm_bf16(GemmArgs a) {
   // ---- LoRA phase: k over the rank, A = gate * bf16(scale * t), B = LoRA up
   if (a.r > 0) {
     const bool on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
-    for (int kr = w * 32; kr < a.r; kr += 32 * WAVES) {
+    for (int jr = w; jr < nrb; jr += WAVES) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (Up[t] == nullptr || Bp[t] == nullptr) continue;
         bf16x8 af = zero8;
         if (on) {
-          const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + kr + kq;
+          const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             af[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Bp[t] + kr + kq), acc[t],
-                                                         0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Bp[t] + (size_t)jr * 512),
+                                                         acc[t], 0, 0, 0);
       }
     }
   }
@@ -302,191 +303,225 @@ k_gemm_bf16(GemmArgs a) {
     const int row = e >> 4, c = e & 15;
     const int m = mt * 16 + row;
     if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v, m < a.M);
-    else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v, fin + row * 16, m < a.M);
+    else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v, fin[row * 16 + (c ^ 8)], m < a.M);
   }
 }
 
 
 // ---------------------------------------------------------------------------
-// Large-M variant (prefill, large batch, the distillation forward): a 128-row x
-// 128-column tile per workgroup (2 x 2 waves of 64 x 64, i.e. 4 x 4 MFMA tiles
-// each), K in steps of 64 through padded (bank-conflict-free) LDS tiles of X and
-// W, the next K step prefetched into registers while the current one is
-// multiplied.  The LoRA up-projection runs as extra K steps (A = the gated
-// fixed-point intermediate, B = LoRA up rows).  In the paired (SwiGLU) case the W
-// tile holds 64 gate rows and the matching 64 up rows, so the output is 128 x 64.
-// When the N-tiles divide evenly over the 8 XCDs, all M-blocks of one N-tile run on
-// one XCD and share its W tile in that XCD's L2.
-constexpr int BM = 128, BN = 128, BK = 64, BKP = BK + 8;
+// Large-M variant (prefill, large batch, the distillation forward): a BM x BN
+// output tile per workgroup of WM x WN wavefronts (each a (BM/WM) x (BN/WN) block
+// of 16 x 16 MFMA tiles), K in steps of 32 through double-buffered, padded
+// (bank-conflict-free) LDS tiles: step k+1 is fetched from HBM / L2 into
+// registers while step k is multiplied, then written to the other buffer, one
+// barrier per step.  A wavefront's 64 lanes fetch one 16 x 32 fragment block as
+// 1 KB contiguous.  The LoRA up-projection runs as extra K steps over the rank
+// (A = gate * bf16(scale * t) formed from the fixed-point intermediate, B = the
+// LoRA up rows of the tile's segment).  Paired (SwiGLU) tiles interleave 16 gate
+// rows and the matching 16 up rows, so a wavefront holds both halves of its
+// outputs.  Workgroups of one column block are numbered onto one XCD (its L2 then
+// serves that W tile to every row block).  The epilogue runs from the
+// accumulators: in the MFMA layout the 16 lanes of a row group hold 16
+// consecutive columns of one row, which is the epilogue's row group.
+constexpr int TBK = 32, TBKP = TBK + 8;
 
-__global__ void __launch_bounds__(256)
-k_gemm_big(GemmArgs a, int mblocks) {
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ void __launch_bounds__(64 * WM * WN)
+k_gemm_tile(GemmArgs a, int nbm, int nbn) {
+  constexpr int NTH = 64 * WM * WN, TM = BM / WM, TN = BN / WN;
+  constexpr int PA = BM * TBK / 8 / NTH, PB = BN * TBK / 8 / NTH;
+  static_assert(PA * NTH * 8 == BM * TBK && PB * NTH * 8 == BN * TBK, "piece split");
+  static_assert(TN % 32 == 0, "paired wave tiles hold whole gate/up pairs");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16* sA = reinterpret_cast<bf16*>(smem_raw);        // [BM][BKP]
-  bf16* sB = sA + BM * BKP;                             // [BN][BKP]
-  float* sC = reinterpret_cast<float*>(smem_raw);      // [BM][BN] after the K loop
+  bf16* sA = reinterpret_cast<bf16*>(smem_raw);       // [2][BM][TBKP]
+  bf16* sB = sA + 2 * BM * TBKP;                      // [2][BN][TBKP]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int lin = blockIdx.x, nb_n = gridDim.x / mblocks;
-  int nb, mb;
-  if (nb_n % 8 == 0) {                 // XCD-aware order (workgroups go round-robin to XCDs)
-    const int xcd = lin % 8, slot = lin / 8;
-    nb = xcd + 8 * (slot / mblocks);
-    mb = slot % mblocks;
-  } else {
-    nb = lin / mblocks;
-    mb = lin % mblocks;
-  }
+  const int total = nbm * nbn, per = (total + 7) / 8;
+  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= total) return;
+  const int nb = t / nbm, mb = t % nbm;
   const int m0 = mb * BM;
   const int outc = a.paired ? BN / 2 : BN;
   const int c0 = nb * outc;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int nkb = a.K / 32, nrb = a.r / 32;
 
-  // segment and in-segment weight row of tile row j
-  auto wrow = [&](int j, int* seg) -> int {
-    if (a.paired) { *seg = j / 64; return c0 + (j % 64); }
-    const int col = tile_col(a, (c0 + j) / 16, (c0 + j) % 16);
-    const int sgi = find_seg(a, col);
-    *seg = sgi;
-    return col - a.seg[sgi].n0;
+  if (a.zero_ptr && t == 0)
+    for (int i = tid; i < a.zero_n; i += NTH) a.zero_ptr[i] = 0;
+
+  // B tile row -> (segment, packed row in it); the non-paired tile lies in one segment
+  const int sg0 = a.paired ? 0 : find_seg(a, c0);
+  auto brow = [&](int r, int* sg) -> int {
+    if (a.paired) { *sg = (r >> 4) & 1; return c0 + (r >> 5) * 16 + (r & 15); }
+    *sg = sg0;
+    return c0 + r - a.seg[sg0].n0;
   };
-  // each thread copies 4 16-byte pieces of A and 4 of B per K step:
-  // piece p = tid + 256 * q -> tile row p / 8, k offset (p % 8) * 8
-  const bf16* srcB[4];
-  const bf16* srcBl[4];
-  int rowA[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = tid + 256 * q, row = p / 8;
-    int sg;
-    const int wr = wrow(row, &sg);
-    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + (size_t)wr * a.K;
-    srcBl[q] = a.seg[sg].Bl ? reinterpret_cast<const bf16*>(a.seg[sg].Bl) + (size_t)wr * a.r
-                            : nullptr;
-    rowA[q] = m0 + row;
-  }
-  if (a.zero_ptr && blockIdx.x == 0)
-    for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
-
+  // piece p of a [R][32] step: fragment block p / 64, slot p % 64 -> row
+  // (p / 64) * 16 + p % 16, k offset ((p % 64) / 16) * 8
   const bf16* X = reinterpret_cast<const bf16*>(a.X);
-  const bf16x8 zero8 = {};
-  bf16x8 ra[4], rb[4];
-  auto fetch = [&](int k) {
+  const bf16* srcA[PA];
+  const bf16* srcB[PB];
+  bool okA[PA];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int p = tid + 256 * q, kk = k + (p % 8) * 8;
-      ra[q] = rowA[q] < a.M ? load8(X + (size_t)rowA[q] * a.ldx + kk) : zero8;
-      rb[q] = load8(srcB[q] + kk);
+  for (int q = 0; q < PA; ++q) {
+    const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+    okA[q] = m0 + row < a.M;
+    srcA[q] = X + frag_off(okA[q] ? m0 + row : 0, ko, a.K);
+  }
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+    int sg;
+    const int wr = brow(row, &sg);
+    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + frag_off(wr, ko, a.K);
+  }
+  // LoRA steps: one pass over the rank per segment of the tile that has an adapter
+  int lseg[2], nls = 0;
+  if (a.r > 0) {
+    const int s_lo = a.paired ? 0 : sg0, s_hi = a.paired ? 1 : sg0;
+    for (int sgi = s_lo; sgi <= s_hi; ++sgi)
+      if (a.seg[sgi].Ufx && a.seg[sgi].Bl) lseg[nls++] = sgi;
+  }
+
+  const bf16x8 zero8 = {};
+  bf16x8 ra[PA], rb[PB];
+  auto fetch = [&](int st) {
+    const size_t off = (size_t)st * 512;
+#pragma unroll
+    for (int q = 0; q < PA; ++q) ra[q] = okA[q] ? load8(srcA[q] + off) : zero8;
+#pragma unroll
+    for (int q = 0; q < PB; ++q) rb[q] = load8(srcB[q] + off);
+  };
+  // LoRA step jr of segment sgi: A = gate * bf16(scale * t), B = that segment's rows
+  auto fetch_lora = [&](int sgi, int jr) {
+    const GemmSeg& S = a.seg[sgi];
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+      const int m = m0 + row;
+      bf16x8 v = zero8;
+      if (okA[q] && (a.gate == nullptr || a.gate[m] != 0)) {
+        const long long* tp = S.Ufx + (size_t)m * S.ldu + jr * 32 + ko;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
+      }
+      ra[q] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+      int sg;
+      const int wr = brow(row, &sg);
+      rb[q] = sg == sgi ? load8(reinterpret_cast<const bf16*>(S.Bl) + frag_off(wr, jr * 32 + ko, a.r))
+                        : zero8;
     }
   };
-  f32x4 acc[4][4];
+  auto stage = [&](int buf) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < PA; ++q) {
+      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+      *reinterpret_cast<bf16x8*>(sA + (buf * BM + row) * TBKP + ko) = ra[q];
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = a.K / BK;
+    for (int q = 0; q < PB; ++q) {
+      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
+      *reinterpret_cast<bf16x8*>(sB + (buf * BN + row) * TBKP + ko) = rb[q];
+    }
+  };
+
+  f32x4 acc[TM / 16][TN / 16];
+#pragma unroll
+  for (int i = 0; i < TM / 16; ++i)
+#pragma unroll
+    for (int j = 0; j < TN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int buf) {
+    bf16x8 af[TM / 16], bfr[TN / 16];
+#pragma unroll
+    for (int i = 0; i < TM / 16; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(sA + (buf * BM + wm * TM + i * 16 + r16) * TBKP + kq);
+#pragma unroll
+    for (int j = 0; j < TN / 16; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (buf * BN + wn * TN + j * 16 + r16) * TBKP + kq);
+#pragma unroll
+    for (int i = 0; i < TM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 16; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  // base K loop
   fetch(0);
-  for (int kt = 0; kt < nk; ++kt) {
+  stage(0);
+  __syncthreads();
+  for (int st = 0; st < nkb; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nkb) fetch(st + 1);
+    mma(buf);
+    if (st + 1 < nkb) stage(buf ^ 1);
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int p = tid + 256 * q, row = p / 8, ko = (p % 8) * 8;
-      *reinterpret_cast<bf16x8*>(sA + row * BKP + ko) = ra[q];
-      *reinterpret_cast<bf16x8*>(sB + row * BKP + ko) = rb[q];
-    }
-    if (kt + 1 < nk) fetch((kt + 1) * BK);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + r16) * BKP + ks * 32 + kq);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + j * 16 + r16) * BKP + ks * 32 + kq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
   }
-  // RMSNorm: scale rows of the base product by 1 / rms(x)
+  // RMSNorm: the base product's rows scale by 1 / rms(x) before the LoRA steps
   if (a.ss_in) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float rs = rs_of(a, m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e);
+        const float rs = rs_of(a, m0 + wm * TM + i * 16 + (lane >> 4) * 4 + e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j][e] *= rs;
+        for (int j = 0; j < TN / 16; ++j) acc[i][j][e] *= rs;
       }
   }
-  // LoRA phase: B = LoRA up rows via LDS; A = gate * bf16(scale * t) formed from
-  // the fixed-point intermediate of the segment each 16-column tile belongs to
-  if (a.r > 0) {
-    for (int kr = 0; kr < a.r; kr += BK) {
+  // LoRA steps over the rank, one pass per segment of the tile with an adapter
+  const int nl = nls * nrb;
+  if (nl > 0) {
+    fetch_lora(lseg[0], 0);
+    stage(0);
+    __syncthreads();
+    for (int st = 0; st < nl; ++st) {
+      const int buf = st & 1;
+      if (st + 1 < nl) fetch_lora(lseg[(st + 1) / nrb], (st + 1) % nrb);
+      mma(buf);
+      if (st + 1 < nl) stage(buf ^ 1);
       __syncthreads();
+    }
+  }
+
+  // epilogue: one column slice of BN / WN at a time is staged in LDS (fp32) by the
+  // wavefronts that own it; then every 16-thread group takes 16 x 16 sub-tiles of
+  // the slice (a group is one row's 16 consecutive columns, the epilogue's row group)
+  float* sC = reinterpret_cast<float*>(smem_raw);     // [BM][TN]
+  const int g = tid >> 4, c = tid & 15;
+  const int sub_n = a.paired ? TN / 32 : TN / 16;
+  for (int pass = 0; pass < WN; ++pass) {
+    if (wn == pass) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int p = tid + 256 * q, row = p / 8, ko = (p % 8) * 8;
-        *reinterpret_cast<bf16x8*>(sB + row * BKP + ko) = srcBl[q] ? load8(srcBl[q] + kr + ko) : zero8;
-      }
-      __syncthreads();
+      for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int sg;
-        (void)wrow(wn * 64 + j * 16, &sg);
-        const GemmSeg& S = a.seg[sg];
-        if (!S.Ufx || !S.Bl) continue;
+        for (int j = 0; j < TN / 16; ++j)
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-          const bf16x8 bfr =
-              *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + j * 16 + r16) * BKP + ks * 32 + kq);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 64 + i * 16 + r16;
-            bf16x8 af = zero8;
-            if (m < a.M && (a.gate == nullptr || a.gate[m] != 0)) {
-              const long long* tp = S.Ufx + (size_t)m * S.ldu + kr + ks * 32 + kq;
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                af[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
-            }
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[i][j], 0, 0, 0);
-          }
+          for (int e = 0; e < 4; ++e)
+            sC[(wm * TM + i * 16 + (lane >> 4) * 4 + e) * TN + j * 16 + r16] = acc[i][j][e];
+    }
+    __syncthreads();
+    for (int stl = g; stl < (BM / 16) * sub_n; stl += NTH / 16) {
+      const int sr = stl / sub_n, sc = stl % sub_n;
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = sr * 16 + rr, m = m0 + row;
+        const float* fr = sC + row * TN;
+        if (EPI == EPI_SWIGLU) {
+          const int tile = c0 / 16 + (pass * TN) / 32 + sc;
+          float v[2] = {fr[sc * 32 + c], fr[sc * 32 + 16 + c]};
+          epilogue<bf16, 2, EPI_SWIGLU>(a, m, c, tile, tile * 16, v, 0.0f, m < a.M);
+        } else {
+          const int tile = c0 / 16 + (pass * TN) / 16 + sc;
+          float v[2] = {fr[sc * 16 + c], 0.0f};
+          if (EPI == EPI_LOGITS) logits_epilogue<1>(a, m, c, tile, v, m < a.M);
+          else epilogue<bf16, 1, EPI>(a, m, c, tile, 0, v, fr[sc * 16 + (c ^ 8)], m < a.M);
         }
       }
     }
-  }
-  // stage the finished tile in LDS and run the epilogue per 16 x 16 sub-tile:
-  // 16 groups of 16 threads, group g takes sub-tiles g, g + 16, ...
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sC[(wm * 64 + i * 16 + (lane >> 4) * 4 + e) * BN + wn * 64 + j * 16 + r16] = acc[i][j][e];
-  __syncthreads();
-  const int g = tid >> 4, c = tid & 15;
-  const int sub_n = outc / 16;
-  for (int st = g; st < (BM / 16) * sub_n; st += 16) {
-    const int sr = st / sub_n, sc = st % sub_n;
-    const int tile0 = c0 / 16 + sc;
-    for (int rr = 0; rr < 16; ++rr) {
-      const int row = sr * 16 + rr, m = m0 + row;
-      const float* finr = sC + row * BN + sc * 16;
-      float v[2];
-      v[0] = finr[c];
-      v[1] = a.paired ? finr[64 + c] : 0.0f;
-      if (a.epi == EPI_LOGITS) logits_epilogue<1>(a, m, c, tile0, v, m < a.M);
-      else if (a.paired) epilogue<bf16, 2>(a, m, c, tile0, c0 + sc * 16, v, finr, m < a.M);
-      else epilogue<bf16, 1>(a, m, c, tile0, 0, v, finr, m < a.M);
-    }
+    __syncthreads();
   }
 }
 
@@ -553,7 +588,7 @@ k_gemm_f32(GemmArgs a) {
   fin[e] = v[0];
   __syncthreads();
   if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v, ok);
-  else epilogue<float, NT>(a, m, c, tile0, col_paired, v, fin + row * 16, ok);
+  else epilogue<float, NT>(a, m, c, tile0, col_paired, v, fin[row * 16 + (c ^ 8)], ok);
 }
 
 // LoRA down-projection: one wave per (16 columns, K chunk, 16 rows); the fp32
@@ -564,19 +599,21 @@ __global__ void __launch_bounds__(64)
 k_lora_down(LoraDownArgs a) {
   const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4, kq = grp * 8;
   const int col0 = blockIdx.x * 16, kc = blockIdx.y, mt = blockIdx.z;
-  const int p = col0 / a.r, lc = col0 % a.r;
-  const bf16* Ap = reinterpret_cast<const bf16*>(a.A[p]) + (size_t)(lc + r16) * a.K;
+  const int p = col0 / a.r, lc = col0 % a.r, nkb = a.K / 32;
+  // fragment-tiled operands: block (row block, k / 32), this lane's 16 bytes
+  const bf16* Ap = reinterpret_cast<const bf16*>(a.A[p]) + (size_t)(lc / 16) * nkb * 512 + lane * 8;
   const int m_lane = mt * 16 + r16;
   const bool row_ok = m_lane < a.M;
-  const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)(row_ok ? m_lane : 0) * a.ldx;
+  const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)mt * nkb * 512 + lane * 8;
   const int kb = kc * a.kchunk, ke = kb + a.kchunk;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero8 = {};
   for (int k = kb; k < ke; k += 64) {
-    const bf16x8 x0 = row_ok ? load8(Xp + k + kq) : zero8;
-    const bf16x8 x1 = row_ok ? load8(Xp + k + 32 + kq) : zero8;
-    const bf16x8 w0 = load8(Ap + k + kq);
-    const bf16x8 w1 = load8(Ap + k + 32 + kq);
+    const size_t j0 = (size_t)(k / 32) * 512, j1 = j0 + 512;
+    const bf16x8 x0 = row_ok ? load8(Xp + j0) : zero8;
+    const bf16x8 x1 = row_ok ? load8(Xp + j1) : zero8;
+    const bf16x8 w0 = load8(Ap + j0);
+    const bf16x8 w1 = load8(Ap + j1);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, w0, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, w1, acc, 0, 0, 0);
   }
@@ -620,34 +657,92 @@ hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Large-M tile choice: the biggest tile that still gives every CU a workgroup and
+// whose column blocks do not straddle a segment boundary.  Returns false when no
+// tile fits (the skinny kernel then runs).
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
+  const int outc = a.paired ? BN / 2 : BN;
+  const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
+  const int grid = (nbm * nbn + 7) / 8 * 8;
+  const size_t smem = std::max((size_t)2 * (BM + BN) * TBKP * sizeof(bf16),
+                               (size_t)BM * (BN / WN) * sizeof(float));
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tile<BM, BN, WM, WN, EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  uno_launch(k_gemm_tile<BM, BN, WM, WN, EPI>, grid, 64 * WM * WN, (uint32_t)smem, s, a, nbm, nbn);
+  return hipGetLastError();
+}
+
+bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
+  const int outc = a.paired ? BN / 2 : BN;
+  if (n_cols_total % outc) return false;
+  if (!a.paired)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n0 % BN || a.seg[i].N % BN) return false;
+  return true;
+}
+
+bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
+  if (a.K % 32 || a.r % 32) return false;
+  const long cu = 256;
+  auto blocks = [&](int BM, int BN) {
+    const int outc = a.paired ? BN / 2 : BN;
+    return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc);
+  };
+  int cfg;
+  if (tile_fits(a, n_cols_total, 256) && blocks(256, 256) >= cu) cfg = 0;
+  else if (tile_fits(a, n_cols_total, 256) && blocks(128, 256) >= cu) cfg = 1;
+  else if (tile_fits(a, n_cols_total, 128) && blocks(256, 128) >= cu) cfg = 2;
+  else if (tile_fits(a, n_cols_total, 128)) cfg = 3;
+  else return false;
+  if (a.paired != (a.epi == EPI_SWIGLU)) return false;
+#define UNO_TILE_EPI(E)                                                        \
+  case E:                                                                      \
+    switch (cfg) {                                                             \
+      case 0: *err = run_tile<256, 256, 4, 4, E>(a, n_cols_total, s); break;   \
+      case 1: *err = run_tile<128, 256, 2, 4, E>(a, n_cols_total, s); break;   \
+      case 2: *err = run_tile<256, 128, 4, 2, E>(a, n_cols_total, s); break;   \
+      default: *err = run_tile<128, 128, 2, 2, E>(a, n_cols_total, s); break;  \
+    }                                                                          \
+    return true;
+  switch (a.epi) {
+    UNO_TILE_EPI(EPI_STORE_F32)
+    UNO_TILE_EPI(EPI_RESID)
+    UNO_TILE_EPI(EPI_SWIGLU)
+    UNO_TILE_EPI(EPI_LOGITS)
+    UNO_TILE_EPI(EPI_QKV)
+    default: return false;
+  }
+#undef UNO_TILE_EPI
+}
+
 template <>
 hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.K % 32 != 0 || (a.r % 32) != 0 || n_cols_total % 16 != 0) return hipErrorInvalidValue;
   if (a.epi == EPI_QKV && (a.kv.head_dim % 16 != 0)) return hipErrorInvalidValue;
-  const int outc = a.paired ? BN / 2 : BN;
-  if (a.M >= 64 && a.K % BK == 0 && a.r % BK == 0 && n_cols_total % outc == 0 &&
-      (a.epi != EPI_QKV || a.kv.head_dim % BN == 0 || BN % a.kv.head_dim == 0)) {
-    const int mblocks = (a.M + BM - 1) / BM;
-    const int nblocks = n_cols_total / outc;
-    const size_t smem = (size_t)BM * BN * 4;
-    uno_launch(k_gemm_big, nblocks * mblocks, 256, smem, s, a, mblocks);
-    return hipGetLastError();
+  if (a.M >= 64) {
+    hipError_t e;
+    if (launch_tile(a, n_cols_total, s, &e)) return e;
   }
   const int mtiles = (a.M + 15) / 16;
+  const int nkb = a.K / 32;
   dim3 grid(n_cols_total / 16, mtiles);
   if (a.paired) {
-    if (a.K % 512 == 0) uno_launch(k_gemm_bf16<2, 16, 2>, grid, 1024, 0, s, a);
-    else if (a.K % 128 == 0) uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
+    if (nkb >= 64) uno_launch(k_gemm_bf16<2, 16, 4>, grid, 1024, 0, s, a);
+    else if (nkb >= 4) uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
     else uno_launch(k_gemm_bf16<2, 1, 1>, grid, 64, 0, s, a);
   } else {
-    if (a.epi == EPI_LOGITS && n_cols_total % 64 == 0 && a.K % 512 == 0) {
+    if (a.epi == EPI_LOGITS && n_cols_total % 64 == 0 && a.nseg == 1 && nkb >= 32) {
       // wide N: four column tiles per workgroup share each activation fragment
       dim3 g4(n_cols_total / 64, mtiles);
       uno_launch(k_gemm_bf16<4, 16, 2>, g4, 1024, 0, s, a);
-    } else if (a.K % 1024 == 0) {
-      uno_launch(k_gemm_bf16<1, 16, 4>, grid, 1024, 0, s, a);
-    } else if (a.K % 128 == 0) {
+    } else if (nkb >= 64) {
+      uno_launch(k_gemm_bf16<1, 8, 8>, grid, 512, 0, s, a);
+    } else if (nkb >= 4) {
       uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
     } else {
       uno_launch(k_gemm_bf16<1, 1, 1>, grid, 64, 0, s, a);

@@ -102,7 +102,7 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     const float v = hidden_in ? hidden_in[(size_t)r * d + c] : to_f(er[c]);
     xr[c] = v;
-    if (xg) xg[(size_t)r * d + c] = from_f<T>(v * to_f(g[c]));
+    if (xg) xg[act_off<T>(r, c, d)] = from_f<T>(v * to_f(g[c]));
     sq += v * v;
   }
   if (ss) {
@@ -217,6 +217,25 @@ __global__ void k_tv_blocks(const float* __restrict__ tv_row, int nb, int B, flo
   tv_block[b] = acc / (float)B;
 }
 
+// One thread per 16-byte piece of the fragment-tiled output.
+__global__ void k_pack(const bf16* __restrict__ src, bf16* __restrict__ dst, int rows, int cols,
+                       int pair_hd) {
+  const size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (q >= (size_t)rows * cols / 8) return;
+  const int cb_n = cols / 32;
+  const size_t block = q / 64;
+  const int lane = (int)(q % 64);
+  const int r = (int)(block / cb_n) * 16 + (lane & 15);
+  const int c = (int)(block % cb_n) * 32 + (lane >> 4) * 8;
+  int sr = r;
+  if (pair_hd > 0) {
+    const int i = r % pair_hd, j = i / 16, cc = i % 16;
+    sr = r - i + (cc < 8 ? 8 * j + cc : pair_hd / 2 + 8 * j + (cc - 8));
+  }
+  *reinterpret_cast<uint4*>(dst + q * 8) =
+      *reinterpret_cast<const uint4*>(src + (size_t)sr * cols + c);
+}
+
 __global__ void k_set_list(SetList l) {
   for (int i = threadIdx.x; i < l.count; i += blockDim.x) l.dst[l.idx[i]] = l.val[i];
 }
@@ -278,6 +297,14 @@ hipError_t launch_tv_blocks(const float* tv_row, int L, int B, float* tv_block, 
   if (L <= 0 || B <= 0 || L % B) return hipErrorInvalidValue;
   const int nb = L / B;
   uno_launch(k_tv_blocks, (nb + 255) / 256, 256, 0, s, tv_row, nb, B, tv_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const bf16* src, bf16* dst, int rows, int cols, int pair_hd, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return hipErrorInvalidValue;
+  if (pair_hd > 0 && (pair_hd % 16 || rows % pair_hd)) return hipErrorInvalidValue;
+  const size_t n = (size_t)rows * cols / 8;
+  uno_launch(k_pack, (unsigned)((n + 255) / 256), 256, 0, s, src, dst, rows, cols, pair_hd);
   return hipGetLastError();
 }
 

@@ -38,6 +38,29 @@ inline void uno_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t
   hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e0, e1, 0, static_cast<KArgs>(args)...);
 }
 
+// ------------------------------------------------------ fragment-tiled layout
+// bf16 matrices that feed the MFMA kernels -- projection / LoRA / LM-head weights
+// and the activations the linear kernels read -- are stored as 16 x 32 blocks of
+// an [R, C] matrix (R a multiple of 16, C of 32), block (r / 16, c / 32) at
+// ((r / 16) * (C / 32) + c / 32) * 512, and inside a block the element (r, c) at
+// lane (c % 32) / 8 * 16 + r % 16, item c % 8: the operand order of
+// v_mfma_f32_16x16x32_bf16 (lane l: row l % 16, k (l / 16) * 8 .. + 8), so a
+// wavefront reads one block as one contiguous 1 KB access.
+UNO_DEV size_t frag_off(int r, int c, int C) {
+  return ((size_t)(r >> 4) * (size_t)(C >> 5) + (size_t)(c >> 5)) * 512 +
+         (size_t)((((c & 31) >> 3) << 4) + (r & 15)) * 8 + (c & 7);
+}
+// Row-major for float32 contexts, fragment-tiled for bf16.
+template <typename T> UNO_DEV size_t act_off(int r, int c, int C) {
+  return sizeof(T) == 2 ? frag_off(r, c, C) : (size_t)r * C + c;
+}
+inline size_t round16(size_t r) { return (r + 15) / 16 * 16; }
+
+// Row-major [rows, cols] bf16 -> fragment-tiled; pair_hd > 0 also reorders the
+// rows of each pair_hd-row head so that every 16-row block holds rows
+// 8j .. 8j+7 and pair_hd/2 + 8j .. +7 (the RoPE pairs of one tile).
+hipError_t launch_pack(const bf16* src, bf16* dst, int rows, int cols, int pair_hd, hipStream_t s);
+
 // Device error bits (sticky per context, OR-ed by kernels).
 enum : int32_t {
   UNO_DEVERR_NUMERIC = 1,   // NaN / negative / >1 probability, or a row without mass
@@ -238,7 +261,7 @@ hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, 
 // [0, A) then [C, D] (A = max a, C = min c, D = max d).
 struct AttnArgs {
   const void* q;             // [R, Hq * hd] of T
-  void* out;                 // [R, Hq * hd] of T
+  void* out;                 // [R, Hq * hd] of T (activation layout: act_off)
   const int32_t* row_pos;    // [R]
   const int32_t* row_vis;    // [R][3] or null
   int32_t* row_nc;           // [R] context chunks that hold each row's partials

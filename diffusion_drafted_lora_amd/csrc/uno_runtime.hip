@@ -72,10 +72,11 @@ Layout make_layout(const uno_config& c) {
   L.row_vis = take(R * 3 * 4);
   L.row_nc = take(R * 4);
   L.x = take(R * d * 4);
-  L.xn = take(R * d * ts);
+  // activations read by the linear kernels: fragment-tiled in bf16, whole 16-row blocks
+  L.xn = take(round16(R) * d * ts);
   L.qbuf = take(R * q * ts);
-  L.obuf = take(R * q * ts);
-  L.hbuf = take(R * F * ts);
+  L.obuf = take(round16(R) * q * ts);
+  L.hbuf = take(round16(R) * F * ts);
   L.ubuf = take(R * 3 * r * ts + 16);
   L.tfx = take(4 * R * 3 * r * 8 + 16);     // four fixed-point LoRA intermediates
   L.ss = take((size_t)(2 * c.n_layers + 1) * R * 8);   // fixed-point sums of x^2
@@ -635,7 +636,8 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
         float* o = user ? user + (size_t)i * Lx * V : lg + r0 * V;
         dst[2 * i + h] = o;
         GemmArgs a{};
-        a.X = xg + r0 * d; a.ldx = d; a.M = Lx; a.K = d; a.r = 0;
+        a.X = xg + r0 * d;   // r0 is a multiple of 16 in bf16 (a whole fragment block)
+        a.ldx = d; a.M = Lx; a.K = d; a.r = 0;
         a.nseg = 1;
         a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
         a.ss_in = SS(2 * L) + r0; a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
@@ -693,6 +695,19 @@ uno_status set_state(uno_ctx* c, int seq, int len, int pending, int iter) {
 
 // ====================================================================== C ABI
 extern "C" {
+
+uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t cols,
+                           int32_t pair_hd, void* stream) {
+  if (!d_src || !d_dst || d_src == d_dst)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "pack: null or aliased buffers");
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 32 ||
+      (pair_hd && (pair_hd < 0 || pair_hd % 16 || rows % pair_hd)))
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "pack: rows % 16, cols % 32 and rows % pair_hd must be 0");
+  hipError_t e = launch_pack(static_cast<const bf16*>(d_src), static_cast<bf16*>(d_dst), rows, cols,
+                             pair_hd, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, UNO_ERR_DEVICE, std::string("pack: ") + hipGetErrorString(e));
+  return UNO_OK;
+}
 
 uno_status uno_query_sizes(const uno_config* cfg, size_t* kv_pool_bytes, size_t* workspace_bytes) {
   uno_status s = check_config(cfg);
@@ -1015,6 +1030,8 @@ uno_status uno_distill_forward(uno_ctx* c, int32_t batch, int32_t L, int32_t B, 
   if (!d_x) return fail(c, UNO_ERR_INVALID_ARG, "null tokens");
   if (2 * L > c->cfg.max_rows || 2 * L > c->cfg.max_seq_len)
     return fail(c, UNO_ERR_INVALID_ARG, "2L exceeds max_rows or max_seq_len");
+  if (c->bf16 && L % 16)
+    return fail(c, UNO_ERR_INVALID_ARG, "bf16 contexts need L to be a multiple of 16");
   if (!c->embed || !c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no embedding / LM head");
   if (!c->drafted_ids.empty()) return fail(c, UNO_ERR_STATE, "a drafted block awaits verification");
   // scratch sequences: slots holding no sequence and no pages

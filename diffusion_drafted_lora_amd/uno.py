@@ -23,7 +23,7 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
             "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_read",
-            "uno_distill_forward")
+            "uno_distill_forward", "uno_pack_weight")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -165,6 +165,8 @@ class Engine:
         for t in self._all_tensors(weights):
             if not t.is_contiguous() or t.device != self.device:
                 raise ValueError("weights must be contiguous tensors on the engine's device")
+        weights = pack_weights(cfg, weights)
+        self.weights = weights      # the context reads these tensors: keep them alive
         wc.embed = weights["embed"].data_ptr() if "embed" in weights else None
         wc.lm_head = weights["lm_head"].data_ptr() if "lm_head" in weights else None
         wc.final_norm = weights["final_norm"].data_ptr()
@@ -343,6 +345,42 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+def pack_weights(cfg, w):
+    """For bf16 models, a copy of the device weight dict `w` with the LM head, the
+    projections and the LoRA matrices in the fragment-tiled layout of
+    uno_pack_weight (q / k / v and their LoRA up with the rotary pair order);
+    float32 models, or an already packed dict, are returned as they are."""
+    if cfg.dtype != "bf16" or w.get("_packed"):
+        return w
+    import torch
+
+    def pk(t, pair_hd):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16 and t.dim() == 2):
+            raise ValueError("pack_weights needs contiguous 2-D bf16 device tensors")
+        out = torch.empty_like(t)
+        st = lib().uno_pack_weight(_ptr(t), _ptr(out), t.shape[0], t.shape[1], pair_hd,
+                                   C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream))
+        if st != UNO_OK:
+            raise UnoError(st, lib().uno_last_error(None).decode())
+        return out
+
+    out = {k: w[k] for k in ("embed", "final_norm") if k in w}
+    if "lm_head" in w:
+        out["lm_head"] = pk(w["lm_head"], 0)
+    out["layers"] = []
+    for lw in w["layers"]:
+        d = {"attn_norm": lw["attn_norm"], "mlp_norm": lw["mlp_norm"], "w": {}}
+        for p, t in lw["w"].items():
+            d["w"][p] = pk(t, cfg.head_dim if p in ("q", "k", "v") else 0)
+        if "la" in lw:
+            d["la"] = {p: pk(t, 0) for p, t in lw["la"].items()}
+            d["lb"] = {p: pk(t, cfg.head_dim if p in ("q", "k", "v") else 0)
+                       for p, t in lw["lb"].items()}
+        out["layers"].append(d)
+    out["_packed"] = True
+    return out
 
 
 def to_device(weights_np, cfg, device="cuda"):

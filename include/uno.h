@@ -93,7 +93,11 @@ typedef struct {
  * they point to must outlive the context).  embed / lm_head may be NULL when only
  * hidden-state forwards (uno_forward with d_hidden_in / d_hidden_out) are used.
  * lora_a / lora_b may be NULL (no adapter on that projection).
- * Projection order: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down. */
+ * Projection order: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down.
+ * float32 contexts take every matrix row-major.  bf16 contexts take lm_head, w,
+ * lora_a and lora_b in the fragment-tiled layout that uno_pack_weight produces
+ * from the row-major matrix (q, k, v and their lora_b packed with pair_hd =
+ * head_dim, all others with pair_hd = 0); embed and the norms stay row-major. */
 typedef struct {
   const void* embed;                 /* [vocab, d]                 */
   const void* lm_head;               /* [vocab, d]                 */
@@ -104,6 +108,19 @@ typedef struct {
   const void* const* lora_a[7];      /* [n_layers] -> [r, in]      */
   const void* const* lora_b[7];      /* [n_layers] -> [out, r]     */
 } uno_weights;
+
+/* Repack a row-major bf16 matrix [rows, cols] (device) into the fragment-tiled
+ * layout the bf16 kernels stream (device, rows * cols elements, not aliasing
+ * d_src): 16 x 32 blocks in row-block-major order, and inside a block element
+ * (r, c) at position ((c % 32) / 8 * 16 + r % 16) * 8 + c % 8, which is the
+ * operand order of the 16x16x32 bf16 matrix instruction, so one wavefront reads
+ * a block as one contiguous 1 KB access.  pair_hd > 0 (q / k / v weights and
+ * LoRA up-projections) also orders the rows of each head of pair_hd rows so
+ * that each 16-row block holds rows 8j..8j+7 and pair_hd/2+8j..+7, the rotary
+ * pairs of one output tile.  Requires rows % 16 == 0, cols % 32 == 0 and
+ * rows % pair_hd == 0.  Enqueued on stream (a hipStream_t); no context needed. */
+uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t cols,
+                           int32_t pair_hd, void* stream);
 
 /* Sizes of the caller-allocated KV pool and workspace for a config.
  * KV pool layout (exposed for inspection only; use uno_kv_import/export):
@@ -192,7 +209,8 @@ uno_status uno_forward(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t 
  *   d_tv_block device float32 [batch, L/B]: mean of TV_i over each block, or NULL
  * Row i of x and row i of z1 both sit at RoPE position i and both predict token
  * i+1.  Visibility: x row i sees x[0..i]; z1 row i of block b = i / B sees x[0, bB)
- * and z1[bB..i].  Requires L % B == 0, 2L <= max_rows and 2L <= max_seq_len.
+ * and z1[bB..i].  Requires L % B == 0, 2L <= max_rows and 2L <= max_seq_len (and
+ * L % 16 == 0 in bf16 contexts: the halves start on whole 16-row blocks).
  * The [x, z1] K/V live in sequence slots that hold no sequence and no pages
  * (UNO_ERR_OUT_OF_PAGES when there is none, or too few free pages for 2L
  * positions); the call borrows them and returns them, so committed sequences are

@@ -122,10 +122,10 @@ def w8():
     return synth.weights_numpy(CFG8, 1001, with_embed=True)
 
 
-@pytest.mark.parametrize("L,B", [(40, 8), (64, 16), (64, 4)])
+@pytest.mark.parametrize("L,B", [(48, 8), (64, 16), (64, 4)])
 def test_layer8b_distill_forward(w8, L, B):
-    """L = 40: 16-row tiles straddle x and z1 rows and the LM head runs on the
-    skinny kernel (40 rows); L = 64: the large-M kernels."""
+    """L = 48: the LM head runs on the skinny kernel (48 rows); L = 64: the large-M
+    kernels; B = 4 and 8: one 16-row attention tile spans several blocks."""
     log(f"layer8b distill L={L} B={B}")
     eng = engine(CFG8, w8, max_seqs=1, max_seq_len=2 * L + 16, max_rows=2 * L)
     x = synth.prompts(CFG8, 7300 + L + B, 1, L).astype(np.int32)
@@ -148,3 +148,10 @@ def test_layer8b_distill_forward(w8, L, B):
         assert gex <= 1.25 * noise.mean()
     _check_tv(host(tv), host(tvb), T_g, S_g, T_o, S_o, tv_o, B, 1e-5)
     del eng
+
+
+def test_layer8b_distill_needs_whole_row_blocks(w8):
+    eng = engine(CFG8, w8, max_seqs=1, max_seq_len=96, max_rows=80)
+    x = dev(synth.prompts(CFG8, 7399, 1, 40).astype(np.int32))
+    with pytest.raises(uno.UnoError, match="INVALID_ARG"):
+        eng.distill_forward(x, 8)
