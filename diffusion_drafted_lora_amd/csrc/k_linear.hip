@@ -30,7 +30,7 @@ UNO_DEV bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p)
 
 UNO_DEV float rs_of(const GemmArgs& a, int m) {
   if (!a.ss_in || m >= a.M) return 1.0f;
-  const float ms = (float)((double)a.ss_in[m] * LORA_FX_INV) * a.inv_d;
+  const float ms = fx_to_float(a.ss_in[m]) * a.inv_d;
   return 1.0f / sqrtf(ms + a.eps);
 }
 
@@ -216,9 +216,13 @@ k_gemm_bf16(GemmArgs a) {
       ldu[t] = sg.ldu;
     }
   }
-  // workgroup 0 clears a fixed-point buffer that a later kernel accumulates into
-  if (a.zero_ptr && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < a.zero_n; i += WAVES * 64) a.zero_ptr[i] = 0;
+  // every workgroup clears its share of a fixed-point buffer a later kernel fills
+  if (a.zero_ptr) {
+    const long nwg = (long)gridDim.x * gridDim.y, wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    const long share = ((long)a.zero_n + nwg - 1) / nwg;
+    const long z0 = wg * share, z1 = min((long)a.zero_n, z0 + share);
+    for (long i = z0 + threadIdx.x; i < z1; i += WAVES * 64) a.zero_ptr[i] = 0;
+  }
 
   const int m_lane = mt * 16 + r16;
   const bool row_ok = m_lane < a.M;
@@ -275,7 +279,7 @@ k_gemm_bf16(GemmArgs a) {
           const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            af[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
+            af[e] = (bf16)(a.scale * fx_to_float(tp[e]));
         }
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Bp[t] + (size_t)jr * 512),
                                                          acc[t], 0, 0, 0);
@@ -307,6 +311,108 @@ k_gemm_bf16(GemmArgs a) {
   }
 }
 
+
+// Eight consecutive finished columns col .. col+7 (col % 8 == 0) of row m of the
+// large-M kernel: v holds them, vp the eight of columns col ^ 8 (the RoPE
+// partners inside the 16-column tile).  Stores are 16 / 32 bytes wide.  EPI_RESID
+// returns the eight x_new^2 summed (the caller reduces the row); LOGITS pairs with
+// the neighbouring lane (lane ^ 1 holds the other half of the 16-column tile).
+template <int EPI>
+UNO_DEV float epilogue8(const GemmArgs& a, int m, int col, const float* v, const float* vp,
+                        bool ok) {
+  if (EPI == EPI_STORE_F32) {
+    if (ok) {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)m * a.ldo + col);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    return 0.0f;
+  }
+  if (EPI == EPI_RESID) {
+    if (!ok) return 0.0f;
+    float4* r = reinterpret_cast<float4*>(a.resid + (size_t)m * a.ldo + col);
+    const float4 r0 = r[0], r1 = r[1];
+    float xn[8] = {r0.x + v[0], r0.y + v[1], r0.z + v[2], r0.w + v[3],
+                   r1.x + v[4], r1.y + v[5], r1.z + v[6], r1.w + v[7]};
+    r[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
+    r[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
+    float sq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += xn[e] * xn[e];
+    if (a.xg_out) {
+      const bf16x8 gg = load8(reinterpret_cast<const bf16*>(a.g_next) + col);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)(xn[e] * (float)gg[e]);
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.xg_out) + frag_off(m, col, a.ldo)) = o;
+    }
+    return sq;
+  }
+  if (EPI == EPI_QKV) {
+    if (!ok) return 0.0f;
+    const int hd = a.kv.head_dim, half = hd / 2, tph = hd / 16;
+    const int tile = col / 16, hi = (col / 8) & 1;
+    const int head = tile / tph, j = tile % tph;
+    const int dim0 = hi ? half + 8 * j : 8 * j;     // first of 8 consecutive dims
+    const int pos = a.row_pos[m];
+    const int Hq = a.n_q_heads, Hkv = a.kv.n_kv_heads;
+    bf16x8 o;
+    if (head < Hq + Hkv) {                          // q or k: rotate the pairs
+      if (pos < 0 || pos >= a.kv.max_pages_per_seq * a.kv.page_size) {
+        if (a.err) atomicOr(a.err, UNO_DEVERR_BOUNDS);
+        return 0.0f;
+      }
+      const float* cr = a.rcos + (size_t)pos * half + 8 * j;
+      const float* sr = a.rsin + (size_t)pos * half + 8 * j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = hi ? vp[e] : v[e], x2 = hi ? v[e] : vp[e];
+        o[e] = (bf16)(hi ? x2 * cr[e] + x1 * sr[e] : x1 * cr[e] - x2 * sr[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    }
+    bf16* dst;
+    if (head < Hq) {
+      dst = reinterpret_cast<bf16*>(a.qbuf) + (size_t)m * Hq * hd + head * hd + dim0;
+    } else {
+      const int which = head < Hq + Hkv ? 0 : 1;
+      const int h = head - Hq - which * Hkv;
+      const int seq = a.call_seq[m / a.rows_per_seq];
+      const int slot = a.row_slot ? a.row_slot[m] : pos;
+      dst = kv_dst<bf16>(a.kv, a.layer, which, seq, slot, h, a.err);
+      if (!dst) return 0.0f;
+      dst += dim0;
+    }
+    *reinterpret_cast<bf16x8*>(dst) = o;
+    return 0.0f;
+  }
+  if (EPI == EPI_LOGITS) {
+    float l[8], mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      l[e] = (col + e == a.mask_col) ? -INFINITY : v[e];
+      mx = fmaxf(mx, l[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    float se = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) se += (l[e] == -INFINITY) ? 0.0f : expf(l[e] - mx);
+    se += __shfl_xor(se, 1);
+    if (ok) {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)m * a.ldo + col);
+      o[0] = make_float4(l[0], l[1], l[2], l[3]);
+      o[1] = make_float4(l[4], l[5], l[6], l[7]);
+      if (((col / 8) & 1) == 0) {
+        a.tile_stats[((size_t)m * a.n_tiles + col / 16) * 2] = mx;
+        a.tile_stats[((size_t)m * a.n_tiles + col / 16) * 2 + 1] = se;
+      }
+    }
+    return 0.0f;
+  }
+  return 0.0f;
+}
 
 // ---------------------------------------------------------------------------
 // Large-M variant (prefill, large batch, the distillation forward): a BM x BN
@@ -347,8 +453,12 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int nkb = a.K / 32, nrb = a.r / 32;
 
-  if (a.zero_ptr && t == 0)
-    for (int i = tid; i < a.zero_n; i += NTH) a.zero_ptr[i] = 0;
+  // every workgroup clears its share of a fixed-point buffer a later kernel fills
+  if (a.zero_ptr) {
+    const long share = ((long)a.zero_n + total - 1) / total;
+    const long z0 = (long)t * share, z1 = min((long)a.zero_n, z0 + share);
+    for (long i = z0 + tid; i < z1; i += NTH) a.zero_ptr[i] = 0;
+  }
 
   // B tile row -> (segment, packed row in it); the non-paired tile lies in one segment
   const int sg0 = a.paired ? 0 : find_seg(a, c0);
@@ -405,7 +515,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
         const long long* tp = S.Ufx + (size_t)m * S.ldu + jr * 32 + ko;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          v[e] = (bf16)(float)((double)a.scale * ((double)tp[e] * LORA_FX_INV));
+          v[e] = (bf16)(a.scale * fx_to_float(tp[e]));
       }
       ra[q] = v;
     }
@@ -488,11 +598,17 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   }
 
   // epilogue: one column slice of BN / WN at a time is staged in LDS (fp32) by the
-  // wavefronts that own it; then every 16-thread group takes 16 x 16 sub-tiles of
-  // the slice (a group is one row's 16 consecutive columns, the epilogue's row group)
-  float* sC = reinterpret_cast<float*>(smem_raw);     // [BM][TN]
-  const int g = tid >> 4, c = tid & 15;
-  const int sub_n = a.paired ? TN / 32 : TN / 16;
+  // wavefronts that own it; then each thread finishes items of 8 consecutive
+  // columns of one row (16 / 32-byte stores).  A thread keeps the same rows in
+  // every slice, so RESID sums each row's squares in registers and adds them once.
+  constexpr int TNP = TN + 4;                          // padded row: rows 4 banks apart
+  float* sC = reinterpret_cast<float*>(smem_raw);     // [BM][TNP]
+  constexpr int IPR = (EPI == EPI_SWIGLU ? TN / 2 : TN) / 8;     // items per row
+  constexpr int ITEMS = BM * IPR / NTH;
+  static_assert(ITEMS * NTH == BM * IPR && NTH % IPR == 0, "epilogue items");
+  float rsq[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) rsq[k] = 0.0f;
   for (int pass = 0; pass < WN; ++pass) {
     if (wn == pass) {
 #pragma unroll
@@ -501,27 +617,46 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
         for (int j = 0; j < TN / 16; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sC[(wm * TM + i * 16 + (lane >> 4) * 4 + e) * TN + j * 16 + r16] = acc[i][j][e];
+            sC[(wm * TM + i * 16 + (lane >> 4) * 4 + e) * TNP + j * 16 + r16] = acc[i][j][e];
     }
     __syncthreads();
-    for (int stl = g; stl < (BM / 16) * sub_n; stl += NTH / 16) {
-      const int sr = stl / sub_n, sc = stl % sub_n;
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = sr * 16 + rr, m = m0 + row;
-        const float* fr = sC + row * TN;
-        if (EPI == EPI_SWIGLU) {
-          const int tile = c0 / 16 + (pass * TN) / 32 + sc;
-          float v[2] = {fr[sc * 32 + c], fr[sc * 32 + 16 + c]};
-          epilogue<bf16, 2, EPI_SWIGLU>(a, m, c, tile, tile * 16, v, 0.0f, m < a.M);
-        } else {
-          const int tile = c0 / 16 + (pass * TN) / 16 + sc;
-          float v[2] = {fr[sc * 16 + c], 0.0f};
-          if (EPI == EPI_LOGITS) logits_epilogue<1>(a, m, c, tile, v, m < a.M);
-          else epilogue<bf16, 1, EPI>(a, m, c, tile, 0, v, fr[sc * 16 + (c ^ 8)], m < a.M);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int it = tid + NTH * k, row = it / IPR, cl = (it % IPR) * 8, m = m0 + row;
+      const float* fr = sC + row * TNP;
+      float v[8], vp[8];
+      if (EPI == EPI_SWIGLU) {
+        // slice column pairs: 16 gate | 16 up per 16 outputs
+        const int q = cl / 16, h8 = cl % 16;
+        float g[8], u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { g[e] = fr[q * 32 + h8 + e]; u[e] = fr[q * 32 + 16 + h8 + e]; }
+        if (m < a.M) {
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)(g[e] / (1.0f + expf(-g[e])) * u[e]);
+          const int col = c0 + (pass * TN) / 2 + cl;
+          *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.out) + frag_off(m, col, a.ldo)) = o;
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { v[e] = fr[cl + e]; vp[e] = fr[(cl ^ 8) + e]; }
+        rsq[k] += epilogue8<EPI>(a, m, c0 + pass * TN + cl, v, vp, m < a.M);
       }
     }
     __syncthreads();
+  }
+  if (EPI == EPI_RESID && a.ss_out) {
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      float sq = rsq[k];
+#pragma unroll
+      for (int off = IPR / 2; off > 0; off >>= 1) sq += __shfl_xor(sq, off, IPR);
+      const int it = tid + NTH * k, m = m0 + it / IPR;
+      if (it % IPR == 0 && m < a.M)
+        atomicAdd(reinterpret_cast<unsigned long long*>(a.ss_out + m),
+                  (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
+    }
   }
 }
 
@@ -624,7 +759,7 @@ k_lora_down(LoraDownArgs a) {
     if (m < a.M) {
       float v = acc[i];
       if (a.ss_in) {
-        const float ms = (float)((double)a.ss_in[m] * LORA_FX_INV) * a.inv_d;
+        const float ms = fx_to_float(a.ss_in[m]) * a.inv_d;
         v *= 1.0f / sqrtf(ms + a.eps);
       }
       const long long q = (long long)llrintf(v * LORA_FX_SCALE);
@@ -666,7 +801,7 @@ hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
   const int grid = (nbm * nbn + 7) / 8 * 8;
   const size_t smem = std::max((size_t)2 * (BM + BN) * TBKP * sizeof(bf16),
-                               (size_t)BM * (BN / WN) * sizeof(float));
+                               (size_t)BM * (BN / WN + 4) * sizeof(float));
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tile<BM, BN, WM, WN, EPI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -692,12 +827,19 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
     const int outc = a.paired ? BN / 2 : BN;
     return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc);
   };
-  int cfg;
-  if (tile_fits(a, n_cols_total, 256) && blocks(256, 256) >= cu) cfg = 0;
-  else if (tile_fits(a, n_cols_total, 256) && blocks(128, 256) >= cu) cfg = 1;
-  else if (tile_fits(a, n_cols_total, 128) && blocks(256, 128) >= cu) cfg = 2;
-  else if (tile_fits(a, n_cols_total, 128)) cfg = 3;
-  else return false;
+  // prefer two workgroups per CU (one's epilogue overlaps the other's K loop),
+  // then one, then the smallest tile
+  const bool f256 = tile_fits(a, n_cols_total, 256), f128 = tile_fits(a, n_cols_total, 128);
+  int cfg = -1;
+  for (const long want : {2 * cu, cu}) {
+    if (f256 && blocks(256, 256) >= want) cfg = 0;
+    else if (f256 && blocks(128, 256) >= want) cfg = 1;
+    else if (f128 && blocks(256, 128) >= want) cfg = 2;
+    else if (f128 && blocks(128, 128) >= want) cfg = 3;
+    if (cfg >= 0) break;
+  }
+  if (cfg < 0 && f128) cfg = 3;
+  if (cfg < 0) return false;
   if (a.paired != (a.epi == EPI_SWIGLU)) return false;
 #define UNO_TILE_EPI(E)                                                        \
   case E:                                                                      \

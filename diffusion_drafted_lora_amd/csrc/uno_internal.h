@@ -154,6 +154,11 @@ enum GemmEpi : int32_t {
 // (int64, order-independent integer sums).
 constexpr float LORA_FX_SCALE = 4294967296.0f;     // 2^32
 constexpr double LORA_FX_INV = 1.0 / 4294967296.0;
+// t * 2^-32 in float from the two 32-bit halves (t = hi * 2^32 + lo, lo >= 0):
+// two native conversions and one fma, within one float ulp of the exact value.
+UNO_DEV float fx_to_float(long long t) {
+  return fmaf((float)(unsigned)(t & 0xffffffffll), 0x1p-32f, (float)(int)(t >> 32));
+}
 
 struct GemmSeg {
   const void* W;     // [N, K] of the storage type
