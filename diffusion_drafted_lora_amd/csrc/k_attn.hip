@@ -107,25 +107,17 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
 #pragma unroll
   for (int i = 0; i < MAXO; ++i) o[i] = 0.0f;
 
-  const T* Kp = reinterpret_cast<const T*>(kv.pool);
   for (int k0 = kbeg; k0 < kend; k0 += SUB) {
     __syncthreads();
     // load K / V of virtual keys k0 .. k0+SUB-1 (only keys < kend are read)
     for (int e = tid; e < SUB * hd; e += 256) {
       const int j = e / hd, d = e % hd, p = k0 + j, sl = vslot(p, At, Ct);
       T kvk = from_f<T>(0.0f), kvv = from_f<T>(0.0f);
-      const int page = (p < kend && sl / kv.page_size < kv.max_pages_per_seq)
-                           ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + sl / kv.page_size]
-                           : -1;
-      if (page >= 0 && page < kv.n_pages) {
-        const size_t base =
-            (((size_t)(a.layer * 2) * kv.n_pages + page) * Hkv + kvh) * kv.page_size +
-            (sl % kv.page_size);
-        const size_t vbase =
-            (((size_t)(a.layer * 2 + 1) * kv.n_pages + page) * Hkv + kvh) * kv.page_size +
-            (sl % kv.page_size);
-        kvk = Kp[base * hd + d];
-        kvv = Kp[vbase * hd + d];
+      const int page = p < kend ? kv_page(kv, seq, sl) : -1;
+      if (page >= 0) {
+        const int tk = sl % kv.page_size;
+        kvk = kv_block<const T>(kv, a.layer, 0, page, kvh)[kv_elem(kv, 0, tk, d)];
+        kvv = kv_block<const T>(kv, a.layer, 1, page, kvh)[kv_elem(kv, 1, tk, d)];
       }
       sK[j * kstride + d] = kvk;
       sV[j * kstride + d] = kvv;
@@ -302,12 +294,15 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
 #pragma unroll
   for (int d = 0; d < HD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16* pool = reinterpret_cast<const bf16*>(kv.pool);
   bf16* myP = sP + w * 16 * PPAD;
-  // K / V of a 64-key sub-chunk in 16-byte pieces (16 per key); each thread holds
-  // its pieces of K and of V in registers, prefetched one sub-chunk ahead.
+  // K / V of a 64-key sub-chunk in 16-byte pieces, prefetched into registers one
+  // sub-chunk ahead.  K piece e: key e / 16, dims (e % 16) * 8 .. +7 (a token row).
+  // V piece e: dim (e % 256) / 2, keys ((e / 256) * 2 + e % 2) * 8 .. +7 (the V block
+  // is dim-major, so eight consecutive tokens of one dim are 16 contiguous bytes;
+  // pieces whose eight keys are not eight aligned slots of one page go by element).
   constexpr int PF_MAX = MK * (HD / 8) / 256;          // 4 for >= 256 threads
   const int npf = (MK * (HD / 8) + nthr - 1) / nthr;
+  const int ps = kv.page_size;
   bf16x8 pk[PF_MAX], pv[PF_MAX];
   auto fetch = [&](int k0) {
 #pragma unroll
@@ -316,16 +311,25 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       bf16x8 kk = {}, vv = {};
       if (q < npf && e < MK * (HD / 8)) {
         const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8, p = k0 + key;
-        const int sl = vslot(p, At, Ct), pi = sl / kv.page_size;
-        const int page = (p < kend && pi < kv.max_pages_per_seq)
-                             ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi] : -1;
-        if (page >= 0 && page < kv.n_pages) {
-          const size_t kb = ((((size_t)(a.layer * 2) * kv.n_pages + page) * Hkv + kvh) *
-                                 kv.page_size + (sl % kv.page_size)) * HD + d8;
-          const size_t vb = ((((size_t)(a.layer * 2 + 1) * kv.n_pages + page) * Hkv + kvh) *
-                                 kv.page_size + (sl % kv.page_size)) * HD + d8;
-          kk = *reinterpret_cast<const bf16x8*>(pool + kb);
-          vv = *reinterpret_cast<const bf16x8*>(pool + vb);
+        const int sl = vslot(p, At, Ct);
+        const int page = p < kend ? kv_page(kv, seq, sl) : -1;
+        if (page >= 0)
+          kk = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 0, page, kvh) +
+                                                kv_elem(kv, 0, sl % ps, d8));
+        const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1, p0 = k0 + jj * 8;
+        const int s0 = vslot(p0, At, Ct);
+        if (p0 + 7 < kend && s0 % 8 == 0 && vslot(p0 + 7, At, Ct) == s0 + 7) {
+          const int pg = kv_page(kv, seq, s0);
+          if (pg >= 0)
+            vv = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 1, pg, kvh) +
+                                                  kv_elem(kv, 1, s0 % ps, d));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int pj = p0 + j, sj = vslot(pj, At, Ct);
+            const int pg = pj < kend ? kv_page(kv, seq, sj) : -1;
+            if (pg >= 0) vv[j] = kv_block<const bf16>(kv, a.layer, 1, pg, kvh)[kv_elem(kv, 1, sj % ps, d)];
+          }
         }
       }
       pk[q] = kk;
@@ -340,11 +344,13 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       const int e = tid + q * nthr;
       if (q < npf && e < MK * (HD / 8)) {
         const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-        const bool live = k0 + key < kend;
-        const bf16x8 kk = live ? pk[q] : bf16x8{}, vv = live ? pv[q] : bf16x8{};
-        *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = kk;
+        *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = k0 + key < kend ? pk[q] : bf16x8{};
+        const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1;
+        bf16x8 vv = pv[q];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sVt[(d8 + j) * VPAD + key] = vv[j];
+        for (int j = 0; j < 8; ++j)
+          if (k0 + jj * 8 + j >= kend) vv[j] = (bf16)0.0f;
+        *reinterpret_cast<bf16x8*>(sVt + d * VPAD + jj * 8) = vv;
       }
     }
   };
@@ -482,7 +488,8 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   if (R <= 0) return hipSuccess;
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   dim3 grid(a.n_chunks, kv.n_kv_heads, a.n * row_tiles);
-  const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G >= 4 && G <= 8 && a.chunk % MK == 0;
+  const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G >= 4 && G <= 8 && a.chunk % MK == 0 &&
+                    kv.page_size % 8 == 0;
   if (mfma) {
     const size_t smem = (size_t)(MK * KPAD + HD * VPAD + G * 16 * PPAD) * 2;
     if (smem > 64 * 1024) {

@@ -52,19 +52,16 @@ UNO_DEV int find_seg(const GemmArgs& a, int col) {
   return s;
 }
 
+// (page, KV head) block holding a slot of a sequence, or null (bounds flag set)
 template <typename T>
-UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int pos, int h,
+UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int slot, int h,
                   int32_t* err) {
-  const int pi = pos / kv.page_size;
-  const int page = (pos >= 0 && pi < kv.max_pages_per_seq)
-                       ? kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi] : -1;
-  if (page < 0 || page >= kv.n_pages) {
+  const int page = kv_page(kv, seq, slot);
+  if (page < 0) {
     if (err) atomicOr(err, UNO_DEVERR_BOUNDS);
     return nullptr;
   }
-  return reinterpret_cast<T*>(kv.pool) +
-         ((((size_t)(layer * 2 + which) * kv.n_pages + page) * kv.n_kv_heads + h) *
-              kv.page_size + (pos % kv.page_size)) * kv.head_dim;
+  return kv_block<T>(kv, layer, which, page, h);
 }
 
 // Epilogue of one element (row m, lane column c) of each of the NT tiles.  `vp`
@@ -143,7 +140,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
         const int seq = a.call_seq[m / a.rows_per_seq];
         const int slot = a.row_slot ? a.row_slot[m] : pos;
         T* dst = kv_dst<T>(a.kv, a.layer, which, seq, slot, h, a.err);
-        if (dst) dst[dim] = from_f<T>(val);
+        if (dst) dst[kv_elem(a.kv, which, slot % a.kv.page_size, dim)] = from_f<T>(val);
       }
       break;
     }
@@ -373,19 +370,24 @@ UNO_DEV float epilogue8(const GemmArgs& a, int m, int col, const float* v, const
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
     }
-    bf16* dst;
     if (head < Hq) {
-      dst = reinterpret_cast<bf16*>(a.qbuf) + (size_t)m * Hq * hd + head * hd + dim0;
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qbuf) + (size_t)m * Hq * hd +
+                                 head * hd + dim0) = o;
     } else {
       const int which = head < Hq + Hkv ? 0 : 1;
       const int h = head - Hq - which * Hkv;
       const int seq = a.call_seq[m / a.rows_per_seq];
       const int slot = a.row_slot ? a.row_slot[m] : pos;
-      dst = kv_dst<bf16>(a.kv, a.layer, which, seq, slot, h, a.err);
-      if (!dst) return 0.0f;
-      dst += dim0;
+      bf16* blk = kv_dst<bf16>(a.kv, a.layer, which, seq, slot, h, a.err);
+      if (!blk) return 0.0f;
+      const int tk = slot % a.kv.page_size;
+      if (which == 0) {
+        *reinterpret_cast<bf16x8*>(blk + kv_elem(a.kv, 0, tk, dim0)) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) blk[kv_elem(a.kv, 1, tk, dim0 + e)] = o[e];
+      }
     }
-    *reinterpret_cast<bf16x8*>(dst) = o;
     return 0.0f;
   }
   if (EPI == EPI_LOGITS) {

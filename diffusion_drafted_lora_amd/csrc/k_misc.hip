@@ -116,24 +116,6 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
   (void)sh;
 }
 
-template <typename T>
-__device__ T* kv_slot(const KvLayout& kv, int layer, int which, int seq, int pos, int h,
-                      int32_t* err) {
-  const int pi = pos / kv.page_size;
-  if (pos < 0 || pi >= kv.max_pages_per_seq) {
-    if (err) atomicOr(err, UNO_DEVERR_BOUNDS);
-    return nullptr;
-  }
-  const int page = kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi];
-  if (page < 0 || page >= kv.n_pages) {
-    if (err) atomicOr(err, UNO_DEVERR_BOUNDS);
-    return nullptr;
-  }
-  const size_t off =
-      ((((size_t)(layer * 2 + which) * kv.n_pages + page) * kv.n_kv_heads + h) * kv.page_size +
-       (pos % kv.page_size)) * kv.head_dim;
-  return reinterpret_cast<T*>(kv.pool) + off;
-}
 
 // Reduce the per-tile (max, sum exp) partials of one logits row (fixed order):
 // each of the 1024 threads merges a strided subset with its loads issued first,
@@ -245,14 +227,15 @@ template <typename T>
 __global__ void k_kv_copy(KvLayout kv, int seq, int len, T* k, T* v, int to_pages) {
   const int pos = blockIdx.x, layer = blockIdx.y;
   const int hd = kv.head_dim, Hkv = kv.n_kv_heads;
+  const int page = kv_page(kv, seq, pos), tk = pos % kv.page_size;
+  if (page < 0) return;
   for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
     const int h = e / hd, i = e % hd;
     const size_t c = (((size_t)layer * len + pos) * Hkv + h) * hd + i;
-    T* pk = kv_slot<T>(kv, layer, 0, seq, pos, h, nullptr);
-    T* pv = kv_slot<T>(kv, layer, 1, seq, pos, h, nullptr);
-    if (!pk || !pv) continue;
-    if (to_pages) { pk[i] = k[c]; pv[i] = v[c]; }
-    else { k[c] = pk[i]; v[c] = pv[i]; }
+    T* pk = kv_block<T>(kv, layer, 0, page, h) + kv_elem(kv, 0, tk, i);
+    T* pv = kv_block<T>(kv, layer, 1, page, h) + kv_elem(kv, 1, tk, i);
+    if (to_pages) { *pk = k[c]; *pv = v[c]; }
+    else { k[c] = *pk; v[c] = *pv; }
   }
 }
 

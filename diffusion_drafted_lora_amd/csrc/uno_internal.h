@@ -140,6 +140,27 @@ struct KvLayout {
   int32_t pad;
 };
 
+// One (page, KV head) block of the pool holds page_size tokens x head_dim: K
+// token-major ([token][dim], a token's K row contiguous) and V dim-major
+// ([dim][token], eight consecutive tokens of one dim contiguous: the B-operand
+// order of the P.V product).
+template <typename T>
+UNO_DEV T* kv_block(const KvLayout& kv, int layer, int which, int page, int h) {
+  return reinterpret_cast<T*>(kv.pool) +
+         (((size_t)(layer * 2 + which) * kv.n_pages + page) * kv.n_kv_heads + h) *
+             (size_t)kv.page_size * kv.head_dim;
+}
+UNO_DEV size_t kv_elem(const KvLayout& kv, int which, int t, int d) {
+  return which == 0 ? (size_t)t * kv.head_dim + d : (size_t)d * kv.page_size + t;
+}
+// page of a slot of a sequence, or -1 outside its reserved pages
+UNO_DEV int kv_page(const KvLayout& kv, int seq, int slot) {
+  const int pi = slot / kv.page_size;
+  if (slot < 0 || pi >= kv.max_pages_per_seq) return -1;
+  const int page = kv.block_table[(size_t)seq * kv.max_pages_per_seq + pi];
+  return (page >= 0 && page < kv.n_pages) ? page : -1;
+}
+
 // ------------------------------------------------------------ GEMM interfaces
 enum GemmEpi : int32_t {
   EPI_QKV = 5,         // pair-permuted q|k|v columns: RoPE, q -> qbuf, k / v -> KV pages
@@ -186,7 +207,7 @@ struct GemmArgs {
   int32_t mask_col;  // EPI_LOGITS: column forced to -inf
   float* tile_stats; // EPI_LOGITS: [M, n_tiles, 2] (max, sum exp)
   int32_t n_tiles;   // EPI_LOGITS: total 16-column tiles
-  int32_t zero_n;    // int64 words of zero_ptr cleared by workgroup 0
+  int32_t zero_n;    // int64 words of zero_ptr cleared (spread over the workgroups)
   long long* zero_ptr;
   // RMSNorm input: X holds the stored x*g; the base accumulator of row m is
   // scaled by rs = 1 / sqrt(ss_in[m] * 2^-32 / d + eps) (ss_in: fixed-point sum x^2)

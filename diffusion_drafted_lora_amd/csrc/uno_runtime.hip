@@ -458,12 +458,12 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   }
 
   KvLayout kv = kv_layout(c);
-  // attention chunking: split the context until ~2048 workgroups exist (each
-  // workgroup's latency chain is short; the batch alone may already provide
-  // them), 64-key multiples, at most kMaxChunks chunks
+  // attention chunking: split the context until ~1024 workgroups exist (a large
+  // batch provides them unsplit, which also saves the partial-merge pass), 64-key
+  // multiples, at most kMaxChunks chunks
   const int row_tiles = (f.rows_per_seq + 15) / 16;
   const int groups = f.n * Hkv * row_tiles;
-  int target = std::max(1, std::min(kMaxChunks, (2048 + groups - 1) / groups));
+  int target = std::max(1, std::min(kMaxChunks, (1024 + groups - 1) / groups));
   int chunk = (f.ctx_bound + target - 1) / target;
   chunk = std::max(64, (chunk + 63) / 64 * 64);
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;

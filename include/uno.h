@@ -124,7 +124,8 @@ uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t
 
 /* Sizes of the caller-allocated KV pool and workspace for a config.
  * KV pool layout (exposed for inspection only; use uno_kv_import/export):
- * [layer][K|V][page][kv_head][page_size][head_dim] of the storage type. */
+ * [layer][K|V][page][kv_head] blocks of page_size x head_dim of the storage type,
+ * K token-major ([token][dim]) and V dim-major ([dim][token]). */
 uno_status uno_query_sizes(const uno_config* cfg, size_t* kv_pool_bytes,
                            size_t* workspace_bytes);
 
