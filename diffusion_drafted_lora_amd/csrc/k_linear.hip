@@ -30,7 +30,7 @@ UNO_DEV bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p)
 
 UNO_DEV float rs_of(const GemmArgs& a, int m) {
   if (!a.ss_in || m >= a.M) return 1.0f;
-  const float ms = fx_to_float(a.ss_in[m]) * a.inv_d;
+  const float ms = fx_to_float(ss_row(a.ss_in, m)) * a.inv_d;
   return 1.0f / sqrtf(ms + a.eps);
 }
 
@@ -68,9 +68,18 @@ UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int slot, i
 // is the finished tile-0 value of column c ^ 8 of the same row (the RoPE
 // partner).  Every thread of a 16-lane row group calls this (row sums use
 // shuffles); `ok` says whether row m exists.
+// Epilogue operands that do not depend on the product, which the skinny kernel
+// loads before its K loop: the residual values and next-norm gains of the
+// thread's columns (EPI_RESID) and the row's position (EPI_QKV).
+template <int NT> struct EpiPre {
+  float res[NT];
+  float g[NT];
+  int pos;
+};
+
 template <typename T, int NT, int EPI = -1>
 UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired,
-                      const float* v, float vp, bool ok) {
+                      const float* v, float vp, bool ok, const EpiPre<NT>* pre = nullptr) {
   switch (EPI >= 0 ? EPI : a.epi) {
     case EPI_STORE_F32:
       if (ok)
@@ -90,20 +99,19 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       for (int t = 0; t < NT; ++t) {
         const int col = (tile0 + t) * 16 + c;
         if (ok) {
-          const float xn = a.resid[(size_t)m * a.ldo + col] + v[t];
+          const float xn = (pre ? pre->res[t] : a.resid[(size_t)m * a.ldo + col]) + v[t];
           a.resid[(size_t)m * a.ldo + col] = xn;
-          if (a.xg_out)
-            reinterpret_cast<T*>(a.xg_out)[act_off<T>(m, col, a.ldo)] =
-                from_f<T>(xn * to_f(reinterpret_cast<const T*>(a.g_next)[col]));
+          if (a.xg_out) {
+            const float gn = pre ? pre->g[t] : to_f(reinterpret_cast<const T*>(a.g_next)[col]);
+            reinterpret_cast<T*>(a.xg_out)[act_off<T>(m, col, a.ldo)] = from_f<T>(xn * gn);
+          }
           sq += xn * xn;
         }
       }
       if (a.ss_out) {
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 16);
-        if (ok && c == 0)
-          atomicAdd(reinterpret_cast<unsigned long long*>(a.ss_out + m),
-                    (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
+        if (ok && c == 0) ss_add(a.ss_out, m, blockIdx.x, sq);
       }
       break;
     }
@@ -120,7 +128,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       const int head = tile0 / tph, j = tile0 % tph;
       const int i = 8 * j + (c & 7);                 // pair index within the head
       const int dim = (c < 8) ? i : half + i;
-      const int pos = a.row_pos[m];
+      const int pos = pre ? pre->pos : a.row_pos[m];
       const int Hq = a.n_q_heads, Hkv = a.kv.n_kv_heads;
       float val = v[0];
       if (head < Hq + Hkv) {                         // q or k: rotate the pair
@@ -174,6 +182,7 @@ UNO_DEV void logits_epilogue(const GemmArgs& a, int m, int c, int tile0, const f
 template <int NT, int WAVES, int KU>
 __global__ void __launch_bounds__(WAVES * 64)
 k_gemm_bf16(GemmArgs a) {
+  static_assert(WAVES >= 4, "threads 0..255 own the 256 outputs of a tile");
   __shared__ float red[WAVES][NT][256];
   __shared__ float fin[256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,6 +195,7 @@ k_gemm_bf16(GemmArgs a) {
   const bf16* Wp[NT];
   const bf16* Bp[NT];
   const long long* Up[NT];
+  const bf16* Uu[NT];     // gated, scaled bf16 intermediate (large-M down-projection)
   int ldu[NT];
   int tile0, col_paired = 0;
   if (a.paired) {
@@ -198,6 +208,7 @@ k_gemm_bf16(GemmArgs a) {
       Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)grp * nrb * 512 + lane * 8
                     : nullptr;
       Up[t] = sg.Ufx;
+      Uu[t] = reinterpret_cast<const bf16*>(sg.U);
       ldu[t] = sg.ldu;
     }
   } else {
@@ -210,6 +221,7 @@ k_gemm_bf16(GemmArgs a) {
       Bp[t] = sg.Bl ? reinterpret_cast<const bf16*>(sg.Bl) + (size_t)rb * nrb * 512 + lane * 8
                     : nullptr;
       Up[t] = sg.Ufx;
+      Uu[t] = reinterpret_cast<const bf16*>(sg.U);
       ldu[t] = sg.ldu;
     }
   }
@@ -224,6 +236,58 @@ k_gemm_bf16(GemmArgs a) {
   const int m_lane = mt * 16 + r16;
   const bool row_ok = m_lane < a.M;
   const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)mt * nkb * 512 + lane * 8;
+
+  // ---- operands that do not depend on the product, loaded before the K loop so
+  // their latency hides behind the weight stream
+  // (a) row sums of x^2: lane l holds banks 4 (l % 4) .. +3 of row l / 4 of the tile
+  i64x2 ssq0 = {0, 0}, ssq1 = {0, 0};
+  if (a.ss_in && mt * 16 + (lane >> 2) < a.M) {
+    const i64x2* sp = reinterpret_cast<const i64x2*>(
+        a.ss_in + (size_t)(mt * 16 + (lane >> 2)) * SS_BANKS + (lane & 3) * 4);
+    ssq0 = sp[0];
+    ssq1 = sp[1];
+  }
+  // (b) LoRA: wave w's first rank block -- the raw fixed-point t of its row and
+  // the up-projection fragment
+  // (four-tile LM-head instances have no adapter and keep their registers)
+  constexpr bool kPreLora = NT <= 2;
+  const bool lora_pre = kPreLora && a.r > 0 && w < nrb && Uu[0] == nullptr;
+  i64x2 tq[NT][4];
+  bf16x8 bq[NT];
+  bool gate_on = false;
+  if (lora_pre) {
+    gate_on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bq[t] = bf16x8{};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tq[t][q] = i64x2{0, 0};
+      if (Up[t] == nullptr || Bp[t] == nullptr) continue;
+      if (row_ok) {
+        const i64x2* tp = reinterpret_cast<const i64x2*>(Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tq[t][q] = tp[q];
+      }
+      bq[t] = load8(Bp[t] + (size_t)w * 512);
+    }
+  }
+  // (c) epilogue operands of this thread's output element (threads 0..255)
+  EpiPre<NT> pre{};
+  {
+    const int e = threadIdx.x & 255, m = mt * 16 + (e >> 4), c = e & 15;
+    if (threadIdx.x < 256 && m < a.M) {
+      if (a.epi == EPI_RESID) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int col = (tile0 + t) * 16 + c;
+          pre.res[t] = a.resid[(size_t)m * a.ldo + col];
+          pre.g[t] = a.xg_out ? to_f(reinterpret_cast<const bf16*>(a.g_next)[col]) : 0.0f;
+        }
+      } else if (a.epi == EPI_QKV) {
+        pre.pos = a.row_pos[m];
+      }
+    }
+  }
 
   f32x4 acc[NT];
 #pragma unroll
@@ -256,27 +320,47 @@ k_gemm_bf16(GemmArgs a) {
   }
   // ---- RMSNorm: scale rows of the base product by 1 / rms(x)
   if (a.ss_in) {
+    long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float rs = rs_of(a, mt * 16 + (lane >> 4) * 4 + i);
+      const long long tot = __shfl(sq, ((lane >> 4) * 4 + i) * 4);
+      const float rs = 1.0f / sqrtf(fx_to_float(tot) * a.inv_d + a.eps);
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t][i] *= rs;
     }
   }
 
   // ---- LoRA phase: k over the rank, A = gate * bf16(scale * t), B = LoRA up
+  if (a.r > 0 && !lora_pre) gate_on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
+  if (lora_pre) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (Up[t] == nullptr || Bp[t] == nullptr) continue;
+      bf16x8 af = zero8;
+      if (gate_on) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          af[2 * q] = (bf16)(a.scale * fx_to_float(tq[t][q].x));
+          af[2 * q + 1] = (bf16)(a.scale * fx_to_float(tq[t][q].y));
+        }
+      }
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[t], acc[t], 0, 0, 0);
+    }
+  }
   if (a.r > 0) {
-    const bool on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
-    for (int jr = w; jr < nrb; jr += WAVES) {
+    for (int jr = lora_pre ? w + WAVES : w; jr < nrb; jr += WAVES) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (Up[t] == nullptr || Bp[t] == nullptr) continue;
+        if ((Up[t] == nullptr && Uu[t] == nullptr) || Bp[t] == nullptr) continue;
         bf16x8 af = zero8;
-        if (on) {
+        if (Uu[t]) {
+          if (row_ok) af = load8(Uu[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq);
+        } else if (gate_on) {
           const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            af[e] = (bf16)(a.scale * fx_to_float(tp[e]));
+          for (int e = 0; e < 8; ++e) af[e] = (bf16)(a.scale * fx_to_float(tp[e]));
         }
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Bp[t] + (size_t)jr * 512),
                                                          acc[t], 0, 0, 0);
@@ -304,7 +388,7 @@ k_gemm_bf16(GemmArgs a) {
     const int row = e >> 4, c = e & 15;
     const int m = mt * 16 + row;
     if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v, m < a.M);
-    else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v, fin[row * 16 + (c ^ 8)], m < a.M);
+    else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v, fin[row * 16 + (c ^ 8)], m < a.M, &pre);
   }
 }
 
@@ -440,20 +524,23 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   constexpr int PA = BM * TBK / 8 / NTH, PB = BN * TBK / 8 / NTH;
   static_assert(PA * NTH * 8 == BM * TBK && PB * NTH * 8 == BN * TBK, "piece split");
   static_assert(TN % 32 == 0, "paired wave tiles hold whole gate/up pairs");
+  static_assert(NTH >= BM, "one thread per tile row computes its norm");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   bf16* sA = reinterpret_cast<bf16*>(smem_raw);       // [2][BM][TBKP]
   bf16* sB = sA + 2 * BM * TBKP;                      // [2][BN][TBKP]
 
-  const int total = nbm * nbn, per = (total + 7) / 8;
+  const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  const int total = nbm * nbn * nsl, per = (total + 7) / 8;
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= total) return;
-  const int nb = t / nbm, mb = t % nbm;
+  const int slice = t / (nbm * nbn), tt = t % (nbm * nbn);
+  const int nb = tt / nbm, mb = tt % nbm;
   const int m0 = mb * BM;
   const int outc = a.paired ? BN / 2 : BN;
   const int c0 = nb * outc;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int nkb = a.K / 32, nrb = a.r / 32;
+  const int nkb = a.K / 32 / nsl, kb0 = slice * nkb, nrb = a.r / 32;
 
   // every workgroup clears its share of a fixed-point buffer a later kernel fills
   if (a.zero_ptr) {
@@ -479,21 +566,21 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   for (int q = 0; q < PA; ++q) {
     const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
     okA[q] = m0 + row < a.M;
-    srcA[q] = X + frag_off(okA[q] ? m0 + row : 0, ko, a.K);
+    srcA[q] = X + frag_off(okA[q] ? m0 + row : 0, kb0 * 32 + ko, a.K);
   }
 #pragma unroll
   for (int q = 0; q < PB; ++q) {
     const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
     int sg;
     const int wr = brow(row, &sg);
-    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + frag_off(wr, ko, a.K);
+    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + frag_off(wr, kb0 * 32 + ko, a.K);
   }
   // LoRA steps: one pass over the rank per segment of the tile that has an adapter
   int lseg[2], nls = 0;
   if (a.r > 0) {
     const int s_lo = a.paired ? 0 : sg0, s_hi = a.paired ? 1 : sg0;
     for (int sgi = s_lo; sgi <= s_hi; ++sgi)
-      if (a.seg[sgi].Ufx && a.seg[sgi].Bl) lseg[nls++] = sgi;
+      if ((a.seg[sgi].Ufx || a.seg[sgi].U) && a.seg[sgi].Bl) lseg[nls++] = sgi;
   }
 
   const bf16x8 zero8 = {};
@@ -513,11 +600,17 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
       const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
       const int m = m0 + row;
       bf16x8 v = zero8;
-      if (okA[q] && (a.gate == nullptr || a.gate[m] != 0)) {
-        const long long* tp = S.Ufx + (size_t)m * S.ldu + jr * 32 + ko;
+      if (S.U) {
+        // already gated and scaled (the large-M LoRA down-projection's output)
+        if (okA[q]) v = load8(reinterpret_cast<const bf16*>(S.U) + (size_t)m * S.ldu + jr * 32 + ko);
+      } else if (okA[q] && (a.gate == nullptr || a.gate[m] != 0)) {
+        const i64x2* tp = reinterpret_cast<const i64x2*>(S.Ufx + (size_t)m * S.ldu + jr * 32 + ko);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = (bf16)(a.scale * fx_to_float(tp[e]));
+        for (int e = 0; e < 4; ++e) {
+          const i64x2 tv = tp[e];
+          v[2 * e] = (bf16)(a.scale * fx_to_float(tv.x));
+          v[2 * e + 1] = (bf16)(a.scale * fx_to_float(tv.y));
+        }
       }
       ra[q] = v;
     }
@@ -562,8 +655,11 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
       for (int j = 0; j < TN / 16; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
-  // base K loop
+  // base K loop (the first step's loads are in flight while the row norms of the
+  // tile go to LDS; the loop's barriers publish them before their use)
+  __shared__ float s_rs[BM];
   fetch(0);
+  if (a.ss_in && tid < BM) s_rs[tid] = rs_of(a, m0 + tid);
   stage(0);
   __syncthreads();
   for (int st = 0; st < nkb; ++st) {
@@ -579,7 +675,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
     for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float rs = rs_of(a, m0 + wm * TM + i * 16 + (lane >> 4) * 4 + e);
+        const float rs = s_rs[wm * TM + i * 16 + (lane >> 4) * 4 + e];
 #pragma unroll
         for (int j = 0; j < TN / 16; ++j) acc[i][j][e] *= rs;
       }
@@ -627,7 +723,17 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
       const int it = tid + NTH * k, row = it / IPR, cl = (it % IPR) * 8, m = m0 + row;
       const float* fr = sC + row * TNP;
       float v[8], vp[8];
-      if (EPI == EPI_SWIGLU) {
+      if (EPI == EPI_TFX) {
+        if (m < a.M) {
+          i64x2* o = reinterpret_cast<i64x2*>(reinterpret_cast<long long*>(a.out) +
+                                              (size_t)slice * a.slice_stride + (size_t)m * a.ldo +
+                                              c0 + pass * TN + cl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = i64x2{(long long)llrintf(fr[cl + 2 * e] * LORA_FX_SCALE),
+                         (long long)llrintf(fr[cl + 2 * e + 1] * LORA_FX_SCALE)};
+        }
+      } else if (EPI == EPI_SWIGLU) {
         // slice column pairs: 16 gate | 16 up per 16 outputs
         const int q = cl / 16, h8 = cl % 16;
         float g[8], u[8];
@@ -655,9 +761,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
 #pragma unroll
       for (int off = IPR / 2; off > 0; off >>= 1) sq += __shfl_xor(sq, off, IPR);
       const int it = tid + NTH * k, m = m0 + it / IPR;
-      if (it % IPR == 0 && m < a.M)
-        atomicAdd(reinterpret_cast<unsigned long long*>(a.ss_out + m),
-                  (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
+      if (it % IPR == 0 && m < a.M) ss_add(a.ss_out, m, blockIdx.x, sq);
     }
   }
 }
@@ -728,13 +832,18 @@ k_gemm_f32(GemmArgs a) {
   else epilogue<float, NT>(a, m, c, tile0, col_paired, v, fin[row * 16 + (c ^ 8)], ok);
 }
 
-// LoRA down-projection: one wave per (16 columns, K chunk, 16 rows); the fp32
-// partial of its K chunk (times rs for a normalised input) is added in fixed point
-// with 64-bit integer atomics, so the total is exact and independent of the order
-// the chunks land in.
-__global__ void __launch_bounds__(64)
+// LoRA down-projection for a few rows: a workgroup of LD_WAVES wavefronts per
+// (16 columns, K chunk, 16 rows).  The wavefronts split the chunk, their partials
+// are summed in LDS in wave order, and the chunk's sum (times rs for a normalised
+// input) is added to t in fixed point with one 64-bit integer atomic per element,
+// so the total is exact and independent of the order the chunks land in.
+constexpr int LD_WAVES = 8;
+
+__global__ void __launch_bounds__(64 * LD_WAVES)
 k_lora_down(LoraDownArgs a) {
-  const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4, kq = grp * 8;
+  __shared__ float red[LD_WAVES][256];
+  __shared__ float s_rs[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r16 = lane & 15;
   const int col0 = blockIdx.x * 16, kc = blockIdx.y, mt = blockIdx.z;
   const int p = col0 / a.r, lc = col0 % a.r, nkb = a.K / 32;
   // fragment-tiled operands: block (row block, k / 32), this lane's 16 bytes
@@ -742,33 +851,81 @@ k_lora_down(LoraDownArgs a) {
   const int m_lane = mt * 16 + r16;
   const bool row_ok = m_lane < a.M;
   const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)mt * nkb * 512 + lane * 8;
-  const int kb = kc * a.kchunk, ke = kb + a.kchunk;
+  // row sums of x^2 (wave 0): lane l holds banks 4 (l % 4) .. +3 of row l / 4
+  i64x2 ssq0 = {0, 0}, ssq1 = {0, 0};
+  if (a.ss_in && w == 0 && mt * 16 + (lane >> 2) < a.M) {
+    const i64x2* sp = reinterpret_cast<const i64x2*>(
+        a.ss_in + (size_t)(mt * 16 + (lane >> 2)) * SS_BANKS + (lane & 3) * 4);
+    ssq0 = sp[0];
+    ssq1 = sp[1];
+  }
+  // this wave's share of the chunk's 32-wide K blocks, loaded four at a time
+  const int cb = a.kchunk / 32, jb = kc * cb + w * cb / LD_WAVES, je = kc * cb + (w + 1) * cb / LD_WAVES;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero8 = {};
-  for (int k = kb; k < ke; k += 64) {
-    const size_t j0 = (size_t)(k / 32) * 512, j1 = j0 + 512;
-    const bf16x8 x0 = row_ok ? load8(Xp + j0) : zero8;
-    const bf16x8 x1 = row_ok ? load8(Xp + j1) : zero8;
-    const bf16x8 w0 = load8(Ap + j0);
-    const bf16x8 w1 = load8(Ap + j1);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, w0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, w1, acc, 0, 0, 0);
-  }
-  const int ncols = a.nproj * a.r;
+  for (int j = jb; j < je; j += 4) {
+    bf16x8 x[4], wv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = mt * 16 + grp * 4 + i;
+    for (int u = 0; u < 4; ++u) {
+      const bool in = j + u < je;
+      x[u] = (in && row_ok) ? load8(Xp + (size_t)(j + u) * 512) : zero8;
+      wv[u] = in ? load8(Ap + (size_t)(j + u) * 512) : zero8;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[u], wv[u], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w][((lane >> 4) * 4 + i) * 16 + r16] = acc[i];
+  if (w == 0) {
+    long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((lane & 3) == 0)
+      s_rs[lane >> 2] = a.ss_in ? 1.0f / sqrtf(fx_to_float(sq) * a.inv_d + a.eps) : 1.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x, row = e >> 4, m = mt * 16 + row;
     if (m < a.M) {
-      float v = acc[i];
-      if (a.ss_in) {
-        const float ms = fx_to_float(a.ss_in[m]) * a.inv_d;
-        v *= 1.0f / sqrtf(ms + a.eps);
-      }
+      float v = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < LD_WAVES; ++ww) v += red[ww][e];
+      v *= s_rs[row];
       const long long q = (long long)llrintf(v * LORA_FX_SCALE);
-      atomicAdd(reinterpret_cast<unsigned long long*>(a.t + (size_t)m * ncols + col0 + r16),
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.t + (size_t)m * (a.nproj * a.r) + col0 + (e & 15)),
                 (unsigned long long)q);
     }
   }
+}
+
+// Sum of the K-slice partials of the large-M down-projection, gated and scaled to
+// the bf16 operand of the LoRA up-projection: eight columns per thread.
+__global__ void __launch_bounds__(256)
+k_lora_u(const long long* __restrict__ t, int n_slices, long long stride, int M, int ncols,
+         const uint8_t* __restrict__ gate, float scale, bf16* __restrict__ u) {
+  const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  const int per_row = ncols / 8;
+  if (i >= (long)M * per_row) return;
+  const int m = (int)(i / per_row), c = (int)(i % per_row) * 8;
+  const size_t off = (size_t)m * ncols + c;
+  bf16x8 o = {};
+  if (gate == nullptr || gate[m] != 0) {
+    i64x2 acc[4];
+    const i64x2* p = reinterpret_cast<const i64x2*>(t + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = p[e];
+    for (int sl = 1; sl < n_slices; ++sl) {
+      const i64x2* q = reinterpret_cast<const i64x2*>(t + (size_t)sl * stride + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += q[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (bf16)(scale * fx_to_float(acc[e].x));
+      o[2 * e + 1] = (bf16)(scale * fx_to_float(acc[e].y));
+    }
+  }
+  *reinterpret_cast<bf16x8*>(u + off) = o;
 }
 
 __global__ void k_zero_i64(long long* p, size_t n) {
@@ -781,10 +938,44 @@ __global__ void k_zero_i64(long long* p, size_t n) {
 
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.K % a.kchunk || a.kchunk % 64 || a.r % 16) return hipErrorInvalidValue;
+  if (a.kchunk <= 0 || a.K % a.kchunk || a.kchunk % 32 || a.r % 16) return hipErrorInvalidValue;
   dim3 grid(a.nproj * a.r / 16, a.K / a.kchunk, (a.M + 15) / 16);
-  uno_launch(k_lora_down, grid, 64, 0, s, a);
+  uno_launch(k_lora_down, grid, 64 * LD_WAVES, 0, s, a);
   return hipGetLastError();
+}
+
+bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err);
+
+// Large-M LoRA down-projection: the tile kernel with K split into k_slices
+// slices (a power of two up to 16, aiming at four workgroups per CU), each slice
+// storing its fixed-point partial; k_lora_u adds them.
+int lora_down_tile_slices(int M, int K, int ncols) {
+  const long tiles = (long)((M + 127) / 128) * (ncols / 128);
+  int S = 1;
+  while (S < 16 && tiles * S < 1024 && (K / 32) % (2 * S) == 0 && K / 32 / (2 * S) >= 4) S *= 2;
+  return S;
+}
+
+hipError_t launch_lora_u(const long long* t, int n_slices, long long stride, int M, int ncols,
+                         const uint8_t* gate, float scale, bf16* u, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (ncols % 8 || n_slices < 1) return hipErrorInvalidValue;
+  const long n = (long)M * (ncols / 8);
+  uno_launch(k_lora_u, (unsigned)((n + 255) / 256), 256, 0, s, t, n_slices, stride, M, ncols, gate,
+             scale, u);
+  return hipGetLastError();
+}
+
+bool lora_down_tile_fits(int M, int K, int ncols, int k_slices) {
+  return M >= 64 && k_slices >= 1 && K % (32 * k_slices) == 0 && ncols % 128 == 0;
+}
+
+hipError_t launch_lora_down_tile(const GemmArgs& a, int ncols, hipStream_t s) {
+  if (a.epi != EPI_TFX || a.r != 0 || !lora_down_tile_fits(a.M, a.K, ncols, a.k_slices))
+    return hipErrorInvalidValue;
+  hipError_t e;
+  if (!launch_tile(a, ncols, s, &e)) return hipErrorInvalidValue;
+  return e;
 }
 
 hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s) {
@@ -801,7 +992,8 @@ template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int outc = a.paired ? BN / 2 : BN;
   const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
-  const int grid = (nbm * nbn + 7) / 8 * 8;
+  const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  const int grid = (nbm * nbn * nsl + 7) / 8 * 8;
   const size_t smem = std::max((size_t)2 * (BM + BN) * TBKP * sizeof(bf16),
                                (size_t)BM * (BN / WN + 4) * sizeof(float));
   if (smem > 64 * 1024) {
@@ -825,9 +1017,11 @@ bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
   if (a.K % 32 || a.r % 32) return false;
   const long cu = 256;
+  const int nsl = (a.epi == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  if (a.K % (32 * nsl)) return false;
   auto blocks = [&](int BM, int BN) {
     const int outc = a.paired ? BN / 2 : BN;
-    return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc);
+    return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc) * nsl;
   };
   // prefer two workgroups per CU (one's epilogue overlaps the other's K loop),
   // then one, then the smallest tile
@@ -858,6 +1052,7 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
     UNO_TILE_EPI(EPI_SWIGLU)
     UNO_TILE_EPI(EPI_LOGITS)
     UNO_TILE_EPI(EPI_QKV)
+    UNO_TILE_EPI(EPI_TFX)
     default: return false;
   }
 #undef UNO_TILE_EPI
@@ -877,8 +1072,7 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   dim3 grid(n_cols_total / 16, mtiles);
   if (a.paired) {
     if (nkb >= 64) uno_launch(k_gemm_bf16<2, 16, 4>, grid, 1024, 0, s, a);
-    else if (nkb >= 4) uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
-    else uno_launch(k_gemm_bf16<2, 1, 1>, grid, 64, 0, s, a);
+    else uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
   } else {
     if (a.epi == EPI_LOGITS && n_cols_total % 64 == 0 && a.nseg == 1 && nkb >= 32) {
       // wide N: four column tiles per workgroup share each activation fragment
@@ -886,10 +1080,8 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
       uno_launch(k_gemm_bf16<4, 16, 2>, g4, 1024, 0, s, a);
     } else if (nkb >= 64) {
       uno_launch(k_gemm_bf16<1, 8, 8>, grid, 512, 0, s, a);
-    } else if (nkb >= 4) {
-      uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
     } else {
-      uno_launch(k_gemm_bf16<1, 1, 1>, grid, 64, 0, s, a);
+      uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
     }
   }
   return hipGetLastError();

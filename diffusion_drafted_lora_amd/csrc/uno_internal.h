@@ -169,6 +169,7 @@ enum GemmEpi : int32_t {
   EPI_RESID = 2,       // resid[m, n] += acc
   EPI_SWIGLU = 3,      // out_t[m, n] = T(silu(acc_gate) * acc_up)    (paired segments)
   EPI_LOGITS = 4,      // out_f32[m, n] = acc (MASK column -inf) + per-tile max / sum-exp
+  EPI_TFX = 6,         // out_i64[slice][m, n] = acc in 2^-32 fixed point (LoRA down, large M)
 };
 
 // LoRA intermediates accumulated in fixed point: t = sum x*A in units of 2^-32
@@ -181,10 +182,31 @@ UNO_DEV float fx_to_float(long long t) {
   return fmaf((float)(unsigned)(t & 0xffffffffll), 0x1p-32f, (float)(int)(t >> 32));
 }
 
+// Fixed-point row sums of x^2 are spread over SS_BANKS int64 words per row
+// ([row][bank]): a producer adds into the bank of its workgroup, so the hundreds
+// of workgroups of a skinny residual epilogue do not queue on one address, and a
+// consumer adds the banks (integer sums: exact in any order).
+constexpr int SS_BANKS = 16;
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+UNO_DEV long long ss_row(const long long* ss, int m) {
+  const i64x2* p = reinterpret_cast<const i64x2*>(ss + (size_t)m * SS_BANKS);
+  long long t = 0;
+#pragma unroll
+  for (int i = 0; i < SS_BANKS / 2; ++i) {
+    const i64x2 v = p[i];
+    t += v.x + v.y;
+  }
+  return t;
+}
+UNO_DEV void ss_add(long long* ss, int m, int bank, float sq) {
+  atomicAdd(reinterpret_cast<unsigned long long*>(ss + (size_t)m * SS_BANKS + (bank & (SS_BANKS - 1))),
+            (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
+}
+
 struct GemmSeg {
   const void* W;     // [N, K] of the storage type
   const void* Bl;    // LoRA up [N, r] (or null)
-  const void* U;     // LoRA intermediate [M, ldu] of the storage type (or null)
+  const void* U;     // gated, scaled LoRA intermediate [M, ldu] of the storage type (or null)
   const long long* Ufx;  // bf16 path: fixed-point t [M, ldu] (u = gate * bf16(scale * t))
   int32_t n0;        // first output column of this segment
   int32_t N;         // columns of this segment
@@ -230,6 +252,10 @@ struct GemmArgs {
   KvLayout kv;
   int32_t layer;
   int32_t* err;
+  // EPI_TFX (large-M kernel): K is split into k_slices equal slices, slice s
+  // storing its partial sum at out + s * slice_stride (int64 elements)
+  int32_t k_slices;
+  long long slice_stride;
 };
 
 // LoRA down-projection of a group of projections sharing one input:
@@ -245,6 +271,15 @@ struct LoraDownArgs {
   float inv_d, eps;
 };
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
+// Large-M LoRA down-projection on the tile kernel (EPI_TFX, no atomics): false
+// when no tile shape fits the problem (the atomic kernel then serves it).
+bool lora_down_tile_fits(int M, int K, int ncols, int k_slices);
+int lora_down_tile_slices(int M, int K, int ncols);
+hipError_t launch_lora_down_tile(const GemmArgs& a, int ncols, hipStream_t s);
+// u[m, c] = gate[m] ? bf16(scale * sum_s t[s][m, c] * 2^-32) : 0 over the K-slice
+// partials of the large-M down-projection ([M, ncols] each, `stride` apart)
+hipError_t launch_lora_u(const long long* t, int n_slices, long long stride, int M, int ncols,
+                         const uint8_t* gate, float scale, bf16* u, hipStream_t s);
 hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s);
 
 // ------------------------------------------------------------------ launchers

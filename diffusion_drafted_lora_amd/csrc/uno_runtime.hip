@@ -40,6 +40,9 @@ struct Layout {
   size_t total;
 };
 
+// K-slice capacity of the fixed-point LoRA buffers (large-M down-projection)
+size_t tfx_slices(size_t max_rows) { return max_rows <= 4096 ? 4 : 1; }
+
 int pages_per_seq(const uno_config& c) { return (c.max_seq_len + c.page_size - 1) / c.page_size; }
 
 Layout make_layout(const uno_config& c) {
@@ -78,8 +81,11 @@ Layout make_layout(const uno_config& c) {
   L.obuf = take(round16(R) * q * ts);
   L.hbuf = take(round16(R) * F * ts);
   L.ubuf = take(R * 3 * r * ts + 16);
-  L.tfx = take(4 * R * 3 * r * 8 + 16);     // four fixed-point LoRA intermediates
-  L.ss = take((size_t)(2 * c.n_layers + 1) * R * 8);   // fixed-point sums of x^2
+  // four fixed-point LoRA intermediates, each with room for up to TFX_SLICES
+  // K-slice partials of the large-M down-projection
+  L.tfx = take(4 * R * 3 * r * tfx_slices(R) * 8 + 16);
+  static_assert(sizeof(long long) == 8, "fixed-point words");
+  L.ss = take((size_t)(2 * c.n_layers + 1) * R * SS_BANKS * 8);   // fixed-point sums of x^2
   L.part_o = take(R * c.n_q_heads * kMaxChunks * c.head_dim * 4);
   L.part_ml = take(R * c.n_q_heads * kMaxChunks * 2 * 4);
   L.logits = take(R * V * 4);
@@ -438,16 +444,29 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   T* ubuf = c->at<T>(c->L.ubuf);
   const uint8_t* gate = c->at<uint8_t>(c->L.row_gate);
   // fixed-point sums of x^2 per row: [2l] before attention of layer l, [2l+1]
-  // before its MLP, [2L] before the LM head
+  // before its MLP, [2L] before the LM head; SS_BANKS words per row
   long long* ssb = c->at<long long>(c->L.ss);
-  auto SS = [&](int i) { return ssb + (size_t)i * R; };
+  auto SS = [&](int i) { return ssb + (size_t)i * R * SS_BANKS; };
+  // LoRA down-projection of each group (buffer b): qkv, o, gate/up, down.  Large M
+  // (every group fits the tile kernel): tsl[b] K-slice partials stored into the
+  // tfx region, summed, gated and scaled into ubuf -- no atomics, nothing to
+  // clear.  Few rows: integer atomics into buffer b, cleared by a later kernel.
+  const int gK[4] = {d, qd, d, F}, gN[4] = {3 * r, r, 2 * r, r};
   long long* tfx = c->at<long long>(c->L.tfx);
+  const size_t tcap = (size_t)c->cfg.max_rows * 3 * r * tfx_slices(c->cfg.max_rows) * 4;
+  int tsl[4] = {0, 0, 0, 0};
+  bool tile_lora = lora && c->bf16;
+  for (int b = 0; b < 4 && tile_lora; ++b) {
+    tsl[b] = lora_down_tile_slices(R, gK[b], gN[b]);
+    while (tsl[b] > 1 && (size_t)tsl[b] * R * gN[b] > tcap) tsl[b] /= 2;
+    tile_lora = lora_down_tile_fits(R, gK[b], gN[b], tsl[b]);
+  }
   const size_t tstride = (size_t)R * 3 * r;
   long long* Bfx[4] = {tfx, tfx + tstride, tfx + 2 * tstride, tfx + 3 * tstride};
   {
     Timed t(c, UNO_KC_MISC, 0, 0);
-    UNO_HIP(c, launch_zero_i64(ssb, (size_t)(2 * L + 1) * R, s));
-    if (lora && c->bf16) UNO_HIP(c, launch_zero_i64(tfx, 4 * tstride, s));
+    UNO_HIP(c, launch_zero_i64(ssb, (size_t)(2 * L + 1) * R * SS_BANKS, s));
+    if (lora && c->bf16 && !tile_lora) UNO_HIP(c, launch_zero_i64(tfx, 4 * tstride, s));
   }
   if (!f.in_hidden && !c->embed) return fail(c, UNO_ERR_INVALID_ARG, "no embedding table");
   {
@@ -479,22 +498,47 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   auto norm_in = [&](GemmArgs& a, int ss_idx) {
     a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
   };
-  // LoRA down-projections.  bf16: split-K MFMA into fixed-point buffers B0..B3
-  // (qkv, o, gate/up, down), each cleared by a later kernel of the chain (the
-  // zero_ptr of the consumer GEMMs) and all cleared once per forward above.
-  // float32: a GEMM storing the gated, scaled intermediate.
+  // LoRA down-projections.  bf16: fixed-point buffers B0..B3 (qkv, o, gate/up,
+  // down).  Large M: the tile kernel stores tsl[buf] K-slice partials.  Few rows:
+  // split-K MFMA with integer atomics into a buffer that a later kernel of the
+  // chain cleared (the zero_ptr of the consumer GEMMs; all cleared once per
+  // forward above).  float32: a GEMM storing the gated, scaled intermediate.
   auto lora_down = [&](const T* X, int K, int nproj, const int* pidx, int l, int buf,
                        int ss_idx) -> uno_status {
+    if (tile_lora) {
+      GemmArgs a{};
+      a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = 0;
+      a.nseg = nproj;
+      for (int i = 0; i < nproj; ++i) {
+        a.seg[i].W = c->la[pidx[i]][l];
+        a.seg[i].n0 = i * r;
+        a.seg[i].N = r;
+      }
+      if (ss_idx >= 0) norm_in(a, ss_idx);
+      const int nc = nproj * r;
+      a.epi = EPI_TFX; a.ldo = nc; a.out = tfx;
+      a.k_slices = tsl[buf]; a.slice_stride = (long long)R * nc;
+      double b, fl;
+      gemm_cost(a, nc, sizeof(T), &b, &fl);
+      // slices written, then read back with the gates; u written
+      b += (double)R * nc * 8 * tsl[buf] * 2 + (double)R + (double)R * nc * sizeof(T);
+      Timed t(c, UNO_KC_LORA_DOWN, b, fl);
+      UNO_HIP(c, launch_lora_down_tile(a, nc, s));
+      UNO_HIP(c, launch_lora_u(tfx, tsl[buf], a.slice_stride, R, nc, gate, sc,
+                               reinterpret_cast<bf16*>(ubuf), s));
+      return UNO_OK;
+    }
     if (c->bf16) {
       LoraDownArgs a{};
       a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = r; a.nproj = nproj; a.t = Bfx[buf];
       if (ss_idx >= 0) { a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps; }
       for (int i = 0; i < nproj; ++i) a.A[i] = c->la[pidx[i]][l];
+      // about 128 workgroups: K chunks of whole 32-wide blocks
       const int tiles = nproj * r / 16 * ((R + 15) / 16);
-      const int tgt = std::max(1, (512 + tiles - 1) / tiles);
+      const int tgt = std::max(1, (128 + tiles - 1) / tiles);
       int ks = 1;
-      for (int cand = 1; cand <= K / 64; ++cand)
-        if ((K / 64) % cand == 0 && cand <= tgt) ks = cand;
+      for (int cand = 1; cand <= K / 32; ++cand)
+        if ((K / 32) % cand == 0 && cand <= tgt) ks = cand;
       a.kchunk = K / ks;
       const double b = (double)nproj * r * K * sizeof(T) + (double)R * K * sizeof(T) +
                        (double)R * nproj * r * 8 * 2;
@@ -517,14 +561,14 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // attach the LoRA up-projection of segment `i` reading group buffer `buf`
   auto lora_up = [&](GemmArgs& a, int i, int proj, int l, int buf, int col, int ld) {
     a.seg[i].Bl = c->lb[proj][l];
-    if (c->bf16) a.seg[i].Ufx = Bfx[buf] + col;
+    if (c->bf16 && !tile_lora) a.seg[i].Ufx = Bfx[buf] + col;
     else a.seg[i].U = ubuf + col;
     a.seg[i].ldu = ld;
     a.gate = gate;
     a.scale = sc;
   };
   auto clear = [&](GemmArgs& a, int buf, int cols) {
-    if (lora && c->bf16) { a.zero_ptr = Bfx[buf]; a.zero_n = R * cols; }
+    if (lora && c->bf16 && !tile_lora) { a.zero_ptr = Bfx[buf]; a.zero_n = R * cols; }
   };
 
   for (int l = 0; l < L; ++l) {
@@ -640,7 +684,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
         a.ldx = d; a.M = Lx; a.K = d; a.r = 0;
         a.nseg = 1;
         a.seg[0].W = c->lm_head; a.seg[0].n0 = 0; a.seg[0].N = V;
-        a.ss_in = SS(2 * L) + r0; a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
+        a.ss_in = SS(2 * L) + r0 * SS_BANKS; a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
         a.epi = EPI_LOGITS; a.ldo = V; a.out = o;
         a.mask_col = g.mask_id; a.tile_stats = ts + r0 * nt * 2; a.n_tiles = nt;
         if (uno_status st = run_gemm(a, V, UNO_KC_LM_HEAD)) return st;
