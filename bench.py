@@ -29,6 +29,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
+ROOFLINE_EVERY = 7
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_bf16_gateup_bs1_8b.txt")
 KERNEL_SOURCES = ("diffusion_drafted_lora_amd/csrc/k_linear.hip",
                   "diffusion_drafted_lora_amd/csrc/uno_internal.h")
@@ -350,7 +351,9 @@ def main():
     eng.sync()
     ctx0 = eng.seq_state(0)[0]
     log(f"timed {K} steps from context {ctx0}")
-    eng.timing(["linear_swiglu"])
+    # events on one gate/up launch in 7 (7 is prime to the 72 launches of a step,
+    # so every layer and both forwards are sampled evenly)
+    eng.timing(["linear_swiglu"], every=ROOFLINE_EVERY)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -424,7 +427,7 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
             "bytes_per_launch": sw_bytes_per_launch, "us_per_launch": 1e3 * sw_ms,
-            "launches": n_sw,
+            "launches": n_sw, "sampled_every": ROOFLINE_EVERY,
         },
         "breakdown": breakdown,
     }

@@ -246,6 +246,7 @@ constexpr int HD = 128;           // head dim of the MFMA path
 constexpr int KPAD = HD + 8;      // LDS row of K (bf16), 16-byte pad
 constexpr int VPAD = MK + 8;      // LDS row of V^T (bf16)
 constexpr int PPAD = MK + 8;      // LDS row of P (bf16)
+constexpr int PGC = 1024;         // block-table entries cached per workgroup
 
 __global__ void __launch_bounds__(512)
 k_attn_mfma(AttnArgs a, KvLayout kv) {
@@ -254,6 +255,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   bf16* sVt = sK + MK * KPAD;                                   // [HD][VPAD]
   bf16* sP = sVt + HD * VPAD;                                   // [G][16][PPAD]
   __shared__ int sW[48];                                        // row windows a, c, d
+  __shared__ int sPg[PGC];                                      // pages of the chunk's slots
 
   const int c = blockIdx.x, kvh = blockIdx.y;
   const int row_tiles = (a.rows_per_seq + 15) / 16;
@@ -304,6 +306,13 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   const int npf = (MK * (HD / 8) + nthr - 1) / nthr;
   const int ps = kv.page_size;
   bf16x8 pk[PF_MAX], pv[PF_MAX];
+  // page of a slot: from the LDS copy of the chunk's block-table entries once it
+  // is published (pages pl .. pl + npg - 1), else from the block table
+  int pl = 0, npg = 0;
+  auto page_of = [&](int sl) {
+    const int pi = sl / ps - pl;
+    return (pi >= 0 && pi < npg) ? sPg[pi] : kv_page(kv, seq, sl);
+  };
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < PF_MAX; ++q) {
@@ -312,14 +321,14 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       if (q < npf && e < MK * (HD / 8)) {
         const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8, p = k0 + key;
         const int sl = vslot(p, At, Ct);
-        const int page = p < kend ? kv_page(kv, seq, sl) : -1;
+        const int page = p < kend ? page_of(sl) : -1;
         if (page >= 0)
           kk = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 0, page, kvh) +
                                                 kv_elem(kv, 0, sl % ps, d8));
         const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1, p0 = k0 + jj * 8;
         const int s0 = vslot(p0, At, Ct);
         if (p0 + 7 < kend && s0 % 8 == 0 && vslot(p0 + 7, At, Ct) == s0 + 7) {
-          const int pg = kv_page(kv, seq, s0);
+          const int pg = page_of(s0);
           if (pg >= 0)
             vv = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 1, pg, kvh) +
                                                   kv_elem(kv, 1, s0 % ps, d));
@@ -327,7 +336,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int pj = p0 + j, sj = vslot(pj, At, Ct);
-            const int pg = pj < kend ? kv_page(kv, seq, sj) : -1;
+            const int pg = pj < kend ? page_of(sj) : -1;
             if (pg >= 0) vv[j] = kv_block<const bf16>(kv, a.layer, 1, pg, kvh)[kv_elem(kv, 1, sj % ps, d)];
           }
         }
@@ -365,7 +374,26 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   publish_nc(a, c, kvh, tid, r0, nrows, nv);
   if (kbeg >= nv) return;
   kend = min(kbeg + a.chunk, nv);
+  // block-table entries of every slot the chunk reads (two slot ranges: keys
+  // below At are slots themselves, the rest start at slot Ct); published by the
+  // loop's first barrier
+  int npg_all = 0;
+  {
+    int lo = INT_MAX, hi = -1;
+    if (kbeg < At) { lo = kbeg; hi = min(kend, At) - 1; }
+    if (kend > At) {
+      const int b = max(kbeg, At);
+      lo = min(lo, Ct + b - At);
+      hi = max(hi, Ct + kend - 1 - At);
+    }
+    if (hi >= lo && lo >= 0) {
+      const int p0 = lo / ps, p1 = hi / ps;
+      if (p1 - p0 + 1 <= PGC) { pl = p0; npg_all = p1 - p0 + 1; }
+    }
+    for (int i = tid; i < npg_all; i += nthr) sPg[i] = kv_page(kv, seq, (pl + i) * ps);
+  }
   if (!causal) fetch(kbeg);
+  npg = npg_all;
   int ra[4], rc[4], rd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

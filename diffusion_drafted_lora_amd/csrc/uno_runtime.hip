@@ -136,6 +136,8 @@ struct uno_ctx {
   std::vector<int> snap_base;
   // kernel timing
   uint32_t tmask = 0;
+  int32_t tperiod = 1;                  // record every tperiod-th call of a class
+  uint64_t tcalls[UNO_KC_COUNT] = {};
   std::vector<hipEvent_t> tev;          // event pool, two per recorded launch
   struct TRec { int cls; int ev; double bytes, flops; bool call; };
   std::vector<TRec> trec;
@@ -180,7 +182,8 @@ struct Timed : KernelTimer {
   KernelTimer* saved;
   Timed(uno_ctx* c_, int cls_, double b, double f)
       : c(c_), cls(cls_), bytes(b), flops(f), saved(g_kernel_timer) {
-    g_kernel_timer = ((c->tmask >> cls) & 1u) ? this : nullptr;
+    g_kernel_timer = ((c->tmask >> cls) & 1u) && c->tcalls[cls]++ % (uint64_t)c->tperiod == 0
+                         ? this : nullptr;
   }
   ~Timed() { g_kernel_timer = saved; }
   bool next(hipEvent_t* e0, hipEvent_t* e1) override {
@@ -1213,6 +1216,15 @@ uno_status uno_timing(uno_ctx* c, uint32_t class_mask) {
   UNO_HIP(c, hipStreamSynchronize(c->stream));
   c->trec.clear();
   c->tmask = class_mask;
+  for (auto& n : c->tcalls) n = 0;
+  return UNO_OK;
+}
+
+uno_status uno_timing_every(uno_ctx* c, int32_t period) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (period < 1) return fail(c, UNO_ERR_INVALID_ARG, "timing period must be >= 1");
+  c->tperiod = period;
+  for (auto& n : c->tcalls) n = 0;
   return UNO_OK;
 }
 

@@ -22,7 +22,7 @@ PROJ = synth.PROJ
 EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_verify",
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
-            "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_read",
+            "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_every", "uno_timing_read",
             "uno_distill_forward", "uno_pack_weight")
 
 # kernel classes of uno_timing (uno_kernel_class)
@@ -318,11 +318,13 @@ class Engine:
     def sync(self):
         self._check(lib().uno_sync(self.h))
 
-    def timing(self, classes=()):
-        """Start recording launches of the named kernel classes (empty: stop)."""
+    def timing(self, classes=(), every=1):
+        """Start recording launches of the named kernel classes (empty: stop),
+        the first of every `every` calls of each class."""
         mask = 0
         for c in classes:
             mask |= 1 << KC[c]
+        self._check(lib().uno_timing_every(self.h, int(every)))
         self._check(lib().uno_timing(self.h, mask))
 
     def timing_read(self, cls):

@@ -252,6 +252,12 @@ typedef enum {
   UNO_KC_COUNT = 7
 } uno_kernel_class;
 uno_status uno_timing(uno_ctx* ctx, uint32_t class_mask);
+/* Record only the first of every `period` calls of each enabled class (period
+ * >= 1; 1, the default, records every call).  The other calls launch without
+ * events, so the events' own cost stays out of a timed stretch of work while
+ * the recorded calls still sample it evenly.  Stays in force for the context;
+ * uno_timing and this call restart the counting. */
+uno_status uno_timing_every(uno_ctx* ctx, int32_t period);
 uno_status uno_timing_read(uno_ctx* ctx, int32_t cls, int64_t* launches, double* total_ms,
                            double* bytes, double* flops);
 

@@ -135,3 +135,29 @@ def test_state_errors(w_np):
         eng.draft([0, 0])                    # duplicate id
     assert e.value.status == 1
     eng.sync()
+
+
+def test_timing_records_every_nth_call(w_np):
+    """Kernel timing: every call of an enabled class is recorded by default; with
+    a period n only the first of every n calls is, and the untimed calls still
+    run (same tokens)."""
+    S = 2
+    prompts = list(synth.prompts(TINY, 2300, S))
+    counts, outs = {}, {}
+    for every in (1, 3):
+        eng = engine(TINY, w_np, max_seqs=S, seed=11)
+        eng.prefill([0, 1], prompts)
+        eng.timing(["linear", "attention"], every=every)
+        o, n = eng.step([0, 1])
+        outs[every] = (host(o).copy(), host(n).copy())
+        counts[every] = {c: eng.timing_read(c) for c in ("linear", "attention", "lm_head")}
+        eng.timing([])
+        eng.sync()
+    calls = 2 * TINY.n_layers * 3                     # q|k|v, o, down per forward
+    assert counts[1]["linear"][0] == calls
+    assert counts[3]["linear"][0] == (calls + 2) // 3
+    assert counts[1]["attention"][0] == 2 * TINY.n_layers
+    assert counts[3]["attention"][0] == (2 * TINY.n_layers + 2) // 3
+    assert counts[1]["lm_head"][0] == 0                # class not enabled
+    assert counts[1]["linear"][1] > 0 and counts[3]["linear"][1] > 0
+    assert np.array_equal(outs[1][0], outs[3][0]) and np.array_equal(outs[1][1], outs[3][1])
