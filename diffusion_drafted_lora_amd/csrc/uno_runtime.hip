@@ -24,6 +24,14 @@ template <typename T> size_t attn_smem_bytes(int G, int hd);
 namespace {
 
 constexpr int kMaxChunks = 64;        // context chunks per (row, head) in attention
+#ifndef UNO_ATTN_TARGET_WG
+#define UNO_ATTN_TARGET_WG 1024
+#endif
+#ifndef UNO_ATTN_MIN_CHUNK
+#define UNO_ATTN_MIN_CHUNK 64
+#endif
+constexpr int kAttnTargetWG = UNO_ATTN_TARGET_WG;   // workgroups the context split aims at
+constexpr int kAttnMinChunk = UNO_ATTN_MIN_CHUNK;   // keys per chunk, at least (a multiple of 64)
 constexpr size_t kAlign = 256;
 
 thread_local std::string g_last_error = "";
@@ -485,9 +493,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // multiples, at most kMaxChunks chunks
   const int row_tiles = (f.rows_per_seq + 15) / 16;
   const int groups = f.n * Hkv * row_tiles;
-  int target = std::max(1, std::min(kMaxChunks, (1024 + groups - 1) / groups));
+  int target = std::max(1, std::min(kMaxChunks, (kAttnTargetWG + groups - 1) / groups));
   int chunk = (f.ctx_bound + target - 1) / target;
-  chunk = std::max(64, (chunk + 63) / 64 * 64);
+  chunk = std::max(kAttnMinChunk, (chunk + 63) / 64 * 64);
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
   if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
 
