@@ -67,7 +67,7 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   const int si = blockIdx.z / row_tiles, rt = blockIdx.z % row_tiles;
   const int Hkv = kv.n_kv_heads, hd = kv.head_dim, G = a.n_q_heads / Hkv;
-  const int seq = a.call_seq[si];
+  const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[si];
   const int r0 = si * a.rows_per_seq + rt * 16;
   const int nrows = min(16, a.rows_per_seq - rt * 16);
   const int NQ = 16 * G;               // query vectors of this block
@@ -188,48 +188,59 @@ k_attn_partial(AttnArgs a, KvLayout kv) {
   }
 }
 
-// Merge the chunk partials of one (row, head) in chunk order: one thread per
-// chunk loads its (max, sum) at once, thread 0 forms the weights in chunk order,
-// then every thread accumulates its output dimensions with unrolled loads.
+// Merge the chunk partials of one (row, head) in chunk order.  Every load goes
+// out at once: wave 0 lane c takes chunk c's (max, sum), thread (half, d) takes
+// dimension d of chunks 32 half .. 32 half + 31; wave 0 then forms the chunk
+// weights (max and sum by a fixed shuffle tree), each thread sums its chunks in
+// order and the two halves are added in LDS (half 0 + half 1).
 template <typename T>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 k_attn_combine(AttnArgs a, int hd) {
-  __shared__ float sm[kMaxCombine], ssum[kMaxCombine], sf[kMaxCombine];
+  static_assert(kMaxCombine == 64, "one wave lane per chunk, two halves of 32");
+  __shared__ float sf[kMaxCombine];
   __shared__ float sL;
+  __shared__ float sh[128];
   const int r = blockIdx.x / a.n_q_heads, h = blockIdx.x % a.n_q_heads;
   const int nc = a.row_nc[r];
   const size_t ph0 = ((size_t)r * a.n_q_heads + h) * a.n_chunks;
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-    sm[c] = a.part_ml[(ph0 + c) * 2];
-    ssum[c] = a.part_ml[(ph0 + c) * 2 + 1];
+  const int lane = threadIdx.x & 63, half = threadIdx.x >> 7, dl = threadIdx.x & 127;
+  float mc = -INFINITY, sc = 0.0f;
+  if (threadIdx.x < 64 && lane < nc) {
+    mc = a.part_ml[(ph0 + lane) * 2];
+    sc = a.part_ml[(ph0 + lane) * 2 + 1];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, sm[c]);
-    float L = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-      const float f = (sm[c] == -INFINITY) ? 0.0f : expf(sm[c] - M);
-      sf[c] = f;
-      L += ssum[c] * f;
+  for (int d0 = 0; d0 < hd; d0 += 128) {
+    const int d = d0 + dl, c0 = half * 32;
+    const float* po = a.part_o + (ph0 + c0) * hd + d;
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v[c] = (c0 + c < nc && d < hd) ? po[(size_t)c * hd] : 0.0f;
+    if (d0 == 0) {
+      if (threadIdx.x < 64) {
+        float M = mc;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float f = (mc == -INFINITY) ? 0.0f : expf(mc - M);
+        float L = sc * f;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+        sf[lane] = f;
+        if (lane == 0) sL = L;
+      }
+      __syncthreads();
     }
-    sL = L;
-  }
-  __syncthreads();
-  const float inv = sL > 0.0f ? 1.0f / sL : 0.0f;
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    const float* po = a.part_o + ph0 * hd + d;
     float acc = 0.0f;
-    int c = 0;
-    for (; c + 8 <= nc; c += 8) {
-      float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(c + u) * hd];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += v[u] * sf[c + u];
+    for (int c = 0; c < 32; ++c)
+      if (c0 + c < nc) acc += v[c] * sf[c0 + c];
+    if (half == 1) sh[dl] = acc;
+    __syncthreads();
+    if (half == 0 && d < hd) {
+      const float inv = sL > 0.0f ? 1.0f / sL : 0.0f;
+      reinterpret_cast<T*>(a.out)[act_off<T>(r, h * hd + d, a.n_q_heads * hd)] =
+          from_f<T>((acc + sh[dl]) * inv);
     }
-    for (; c < nc; ++c) acc += po[(size_t)c * hd] * sf[c];
-    reinterpret_cast<T*>(a.out)[act_off<T>(r, h * hd + d, a.n_q_heads * hd)] = from_f<T>(acc * inv);
+    __syncthreads();
   }
 }
 
@@ -261,7 +272,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   const int si = blockIdx.z / row_tiles, rt = blockIdx.z % row_tiles;
   const int Hkv = kv.n_kv_heads, G = a.n_q_heads / Hkv;
-  const int seq = a.call_seq[si];
+  const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[si];
   const int r0 = si * a.rows_per_seq + rt * 16;
   const int nrows = min(16, a.rows_per_seq - rt * 16);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
@@ -545,8 +556,7 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_chunks == 1 && mfma) return hipSuccess;   // the MFMA kernel wrote the outputs directly
-  uno_launch(k_attn_combine<T>, R * a.n_q_heads, kv.head_dim < 256 ? kv.head_dim : 256, 0, s, 
-      a, kv.head_dim);
+  uno_launch(k_attn_combine<T>, R * a.n_q_heads, 256, 0, s, a, kv.head_dim);
   return hipGetLastError();
 }
 

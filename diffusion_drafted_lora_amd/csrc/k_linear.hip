@@ -152,7 +152,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       } else {
         const int which = head < Hq + Hkv ? 0 : 1;
         const int h = head - Hq - which * Hkv;
-        const int seq = a.call_seq[m / a.rows_per_seq];
+        const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[m / a.rows_per_seq];
         const int slot = a.row_slot ? a.row_slot[m] : pos;
         T* dst = kv_dst<T>(a.kv, a.layer, which, seq, slot, h, a.err);
         if (dst) dst[kv_elem(a.kv, which, slot % a.kv.page_size, dim)] = from_f<T>(val);
@@ -467,7 +467,7 @@ UNO_DEV float epilogue8(const GemmArgs& a, int m, int col, const float* v, const
     } else {
       const int which = head < Hq + Hkv ? 0 : 1;
       const int h = head - Hq - which * Hkv;
-      const int seq = a.call_seq[m / a.rows_per_seq];
+      const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[m / a.rows_per_seq];
       const int slot = a.row_slot ? a.row_slot[m] : pos;
       bf16* blk = kv_dst<bf16>(a.kv, a.layer, which, seq, slot, h, a.err);
       if (!blk) return 0.0f;

@@ -245,6 +245,7 @@ struct GemmArgs {
   const int32_t* row_pos;
   const int32_t* row_slot;
   const int32_t* call_seq;
+  int32_t seq_fixed;   // > 0: every row belongs to sequence seq_fixed - 1 (saves a load)
   int32_t rows_per_seq, n_q_heads;
   const float* rcos;
   const float* rsin;
@@ -327,6 +328,7 @@ struct AttnArgs {
   const int32_t* row_vis;    // [R][3] or null
   int32_t* row_nc;           // [R] context chunks that hold each row's partials
   const int32_t* call_seq;   // [n]
+  int32_t seq_fixed;         // > 0: every row belongs to sequence seq_fixed - 1
   int32_t n, rows_per_seq, n_q_heads, n_chunks, chunk;
   float scale;
   float* part_o;             // [R * Hq, n_chunks, hd]

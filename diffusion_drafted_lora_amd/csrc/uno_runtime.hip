@@ -491,6 +491,8 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // attention chunking: split the context until ~1024 workgroups exist (a large
   // batch provides them unsplit, which also saves the partial-merge pass), 64-key
   // multiples, at most kMaxChunks chunks
+  // a single-sequence call names its sequence in the kernel arguments
+  const int seq_fixed = (f.n == 1 && !c->uploaded_call.empty()) ? c->uploaded_call[0] + 1 : 0;
   const int row_tiles = (f.rows_per_seq + 15) / 16;
   const int groups = f.n * Hkv * row_tiles;
   int target = std::max(1, std::min(kMaxChunks, (kAttnTargetWG + groups - 1) / groups));
@@ -601,6 +603,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       norm_in(a, 2 * l);
       a.epi = EPI_QKV;
       a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
+      a.seq_fixed = seq_fixed;
       if (f.mode == 4) a.row_slot = rs.row_slot;
       a.n_q_heads = Hq; a.rcos = c->at<float>(c->L.rope_cos); a.rsin = c->at<float>(c->L.rope_sin);
       a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
@@ -609,6 +612,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     {
       AttnArgs a{};
       a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
+      a.seq_fixed = seq_fixed;
       a.row_vis = f.mode == 4 ? rs.row_vis : nullptr;
       a.row_nc = c->at<int32_t>(c->L.row_nc);
       a.err = err;
@@ -966,6 +970,7 @@ uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_
   uno_status st = check_seqs(c, n, seq_ids, seqs, true);
   if (st) return st;
   if (seqs != c->drafted_ids) return fail(c, UNO_ERR_STATE, "verify without a matching draft");
+  if ((st = upload_call(c, seqs))) return st;     // another call may have changed the list
   const int B = c->cfg.block_size, V = c->cfg.vocab;
   int bound = 0;
   for (int sq : seqs) bound = std::max(bound, c->len_hi[sq] + B + 1);
