@@ -203,7 +203,7 @@ k_gemm_bf16(GemmArgs a) {
   const bf16* Bp[NT];
   const long long* Up[NT];
   const bf16* Uu[NT];     // gated, scaled bf16 intermediate (large-M down-projection)
-  int ldu[NT];
+  int ldu[NT], ucol[NT];
   int tile0, col_paired = 0;
   if (a.paired) {
     col_paired = grp * 16;
@@ -217,6 +217,7 @@ k_gemm_bf16(GemmArgs a) {
       Up[t] = sg.Ufx;
       Uu[t] = reinterpret_cast<const bf16*>(sg.U);
       ldu[t] = sg.ldu;
+      ucol[t] = sg.ucol;
     }
   } else {
     tile0 = grp * NT;
@@ -230,6 +231,7 @@ k_gemm_bf16(GemmArgs a) {
       Up[t] = sg.Ufx;
       Uu[t] = reinterpret_cast<const bf16*>(sg.U);
       ldu[t] = sg.ldu;
+      ucol[t] = sg.ucol;
     }
   }
   // every workgroup clears its share of a fixed-point buffer a later kernel fills
@@ -363,7 +365,7 @@ k_gemm_bf16(GemmArgs a) {
         if ((Up[t] == nullptr && Uu[t] == nullptr) || Bp[t] == nullptr) continue;
         bf16x8 af = zero8;
         if (Uu[t]) {
-          if (row_ok) af = load8(Uu[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq);
+          if (row_ok) af = load8(Uu[t] + frag_off(m_lane, ucol[t] + jr * 32 + kq, ldu[t]));
         } else if (gate_on) {
           const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq;
 #pragma unroll
@@ -510,31 +512,52 @@ UNO_DEV float epilogue8(const GemmArgs& a, int m, int col, const float* v, const
 // ---------------------------------------------------------------------------
 // Large-M variant (prefill, large batch, the distillation forward): a BM x BN
 // output tile per workgroup of WM x WN wavefronts (each a (BM/WM) x (BN/WN) block
-// of 16 x 16 MFMA tiles), K in steps of 32 through double-buffered, padded
-// (bank-conflict-free) LDS tiles: step k+1 is fetched from HBM / L2 into
-// registers while step k is multiplied, then written to the other buffer, one
-// barrier per step.  A wavefront's 64 lanes fetch one 16 x 32 fragment block as
-// 1 KB contiguous.  The LoRA up-projection runs as extra K steps over the rank
-// (A = gate * bf16(scale * t) formed from the fixed-point intermediate, B = the
-// LoRA up rows of the tile's segment).  Paired (SwiGLU) tiles interleave 16 gate
+// of 16 x 16 MFMA tiles).  Operands move from HBM / L2 straight into LDS as whole
+// 16 x 32 fragment blocks (global_load_lds_dwordx4: lane l's 16 bytes land at
+// l * 16), so the LDS copy of a block is already in MFMA operand order and each
+// lane reads its fragment back with one conflict-free 16-byte load.  A stage
+// holds TKB consecutive 32-wide K blocks of the tile's BM / 16 activation blocks
+// and BN / 16 weight blocks; TS stages form a ring, so TS - 1 stages are in flight
+// while one is multiplied, with one barrier per stage.  The LoRA up-projection
+// runs as further stages over the rank (A = the gated, scaled bf16 intermediate,
+// fragment-tiled; B = the LoRA up rows).  Paired (SwiGLU) tiles interleave 16 gate
 // rows and the matching 16 up rows, so a wavefront holds both halves of its
 // outputs.  Workgroups of one column block are numbered onto one XCD (its L2 then
 // serves that W tile to every row block).  The epilogue runs from the
 // accumulators: in the MFMA layout the 16 lanes of a row group hold 16
 // consecutive columns of one row, which is the epilogue's row group.
-constexpr int TBK = 32, TBKP = TBK + 8;
+constexpr int TKB = 2;    // 32-wide K blocks per stage
 
-template <int BM, int BN, int WM, int WN, int EPI>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+UNO_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int TS>
+constexpr size_t tile_smem_bytes() {
+  const size_t ring = (size_t)TS * TKB * (BM + BN) / 16 * 1024;
+  const size_t epi = (size_t)BM * (BN / WN + 4) * 4;
+  return ring > epi ? ring : epi;
+}
+
+template <int BM, int BN, int WM, int WN, int TS, int EPI>
 __global__ void __launch_bounds__(64 * WM * WN)
 k_gemm_tile(GemmArgs a, int nbm, int nbn) {
-  constexpr int NTH = 64 * WM * WN, TM = BM / WM, TN = BN / WN;
-  constexpr int PA = BM * TBK / 8 / NTH, PB = BN * TBK / 8 / NTH;
-  static_assert(PA * NTH * 8 == BM * TBK && PB * NTH * 8 == BN * TBK, "piece split");
+  constexpr int NTH = 64 * WM * WN, TM = BM / WM, TN = BN / WN, NW = WM * WN;
+  constexpr int NBA = BM / 16, NBB = BN / 16, NBS = NBA + NBB;    // blocks per K block
+  constexpr int NB = NBS * TKB;                                   // blocks per stage
+  static_assert(NB % NW == 0, "every wave issues the same number of block loads");
+  constexpr int P = NB / NW;                                      // block loads per wave and stage
   static_assert(TN % 32 == 0, "paired wave tiles hold whole gate/up pairs");
   static_assert(NTH >= BM, "one thread per tile row computes its norm");
+  static_assert(TS >= 2 && TS <= 4, "ring depth");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16* sA = reinterpret_cast<bf16*>(smem_raw);       // [2][BM][TBKP]
-  bf16* sB = sA + 2 * BM * TBKP;                      // [2][BN][TBKP]
+  __shared__ float s_rs[BM];
 
   const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
   const int total = nbm * nbn * nsl, per = (total + 7) / 8;
@@ -545,9 +568,12 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   const int m0 = mb * BM;
   const int outc = a.paired ? BN / 2 : BN;
   const int c0 = nb * outc;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int nkb = a.K / 32 / nsl, kb0 = slice * nkb, nrb = a.r / 32;
+  // the wave index is uniform: as a scalar it keeps the block addressing in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int r16 = lane & 15;
+  const int nkb_all = a.K / 32, nkb = nkb_all / nsl, kb0 = slice * nkb, nrb = a.r / 32;
+  const int mblocks = (a.M + 15) / 16;
 
   // every workgroup clears its share of a fixed-point buffer a later kernel fills
   if (a.zero_ptr) {
@@ -555,91 +581,50 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
     const long z0 = (long)t * share, z1 = min((long)a.zero_n, z0 + share);
     for (long i = z0 + tid; i < z1; i += NTH) a.zero_ptr[i] = 0;
   }
+  // row norms of the tile (their loads complete before the block loads start, so
+  // the ring's vmcnt accounting below only ever sees block loads)
+  if (a.ss_in && tid < BM) s_rs[tid] = rs_of(a, m0 + tid);
 
-  // B tile row -> (segment, packed row in it); the non-paired tile lies in one segment
+  // weight row block of B block bi (16 rows) and its segment
   const int sg0 = a.paired ? 0 : find_seg(a, c0);
-  auto brow = [&](int r, int* sg) -> int {
-    if (a.paired) { *sg = (r >> 4) & 1; return c0 + (r >> 5) * 16 + (r & 15); }
-    *sg = sg0;
-    return c0 + r - a.seg[sg0].n0;
+  auto bseg = [&](int bi) { return a.paired ? (bi & 1) : sg0; };
+  auto brb = [&](int bi) {
+    return a.paired ? c0 / 16 + (bi >> 1) : (c0 - a.seg[sg0].n0) / 16 + bi;
   };
-  // piece p of a [R][32] step: fragment block p / 64, slot p % 64 -> row
-  // (p / 64) * 16 + p % 16, k offset ((p % 64) / 16) * 8
-  const bf16* X = reinterpret_cast<const bf16*>(a.X);
-  const bf16* srcA[PA];
-  const bf16* srcB[PB];
-  bool okA[PA];
-#pragma unroll
-  for (int q = 0; q < PA; ++q) {
-    const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-    okA[q] = m0 + row < a.M;
-    srcA[q] = X + frag_off(okA[q] ? m0 + row : 0, kb0 * 32 + ko, a.K);
-  }
-#pragma unroll
-  for (int q = 0; q < PB; ++q) {
-    const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-    int sg;
-    const int wr = brow(row, &sg);
-    srcB[q] = reinterpret_cast<const bf16*>(a.seg[sg].W) + frag_off(wr, kb0 * 32 + ko, a.K);
-  }
-  // LoRA steps: one pass over the rank per segment of the tile that has an adapter
-  int lseg[2], nls = 0;
+  // LoRA passes: one per segment of the tile that has an adapter
+  int lseg[2] = {0, 0}, nls = 0;
   if (a.r > 0) {
     const int s_lo = a.paired ? 0 : sg0, s_hi = a.paired ? 1 : sg0;
     for (int sgi = s_lo; sgi <= s_hi; ++sgi)
-      if ((a.seg[sgi].Ufx || a.seg[sgi].U) && a.seg[sgi].Bl) lseg[nls++] = sgi;
+      if (a.seg[sgi].U && a.seg[sgi].Bl) lseg[nls++] = sgi;
   }
+  const int n_base = nkb / TKB, spp = nrb / TKB;       // base stages, stages per LoRA pass
+  const int nst = n_base + nls * spp;
 
-  const bf16x8 zero8 = {};
-  bf16x8 ra[PA], rb[PB];
-  auto fetch = [&](int st) {
-    const size_t off = (size_t)st * 512;
+  // block loads of stage st into ring slot `slot`: wave w loads blocks w * P .. + P - 1
+  auto issue = [&](int st, int slot) {
+    const int ls = st - n_base, pass = ls >= 0 ? ls / spp : 0;
+    const int sgl = lseg[pass];
 #pragma unroll
-    for (int q = 0; q < PA; ++q) ra[q] = okA[q] ? load8(srcA[q] + off) : zero8;
-#pragma unroll
-    for (int q = 0; q < PB; ++q) rb[q] = load8(srcB[q] + off);
-  };
-  // LoRA step jr of segment sgi: A = gate * bf16(scale * t), B = that segment's rows
-  auto fetch_lora = [&](int sgi, int jr) {
-    const GemmSeg& S = a.seg[sgi];
-#pragma unroll
-    for (int q = 0; q < PA; ++q) {
-      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-      const int m = m0 + row;
-      bf16x8 v = zero8;
-      if (S.U) {
-        // already gated and scaled (the large-M LoRA down-projection's output)
-        if (okA[q]) v = load8(reinterpret_cast<const bf16*>(S.U) + (size_t)m * S.ldu + jr * 32 + ko);
-      } else if (okA[q] && (a.gate == nullptr || a.gate[m] != 0)) {
-        const i64x2* tp = reinterpret_cast<const i64x2*>(S.Ufx + (size_t)m * S.ldu + jr * 32 + ko);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const i64x2 tv = tp[e];
-          v[2 * e] = (bf16)(a.scale * fx_to_float(tv.x));
-          v[2 * e + 1] = (bf16)(a.scale * fx_to_float(tv.y));
-        }
+    for (int q = 0; q < P; ++q) {
+      const int bb = w * P + q, kk = bb / NBS, b = bb % NBS;
+      const int mrow = min(m0 / 16 + b, mblocks - 1);
+      const bf16* src;
+      if (ls < 0) {
+        const int kb = kb0 + st * TKB + kk;
+        if (b < NBA) src = reinterpret_cast<const bf16*>(a.X) + ((size_t)mrow * nkb_all + kb) * 512;
+        else src = reinterpret_cast<const bf16*>(a.seg[bseg(b - NBA)].W) +
+                   ((size_t)brb(b - NBA) * nkb_all + kb) * 512;
+      } else {
+        const int jr = (ls % spp) * TKB + kk;
+        const GemmSeg& S = a.seg[sgl];
+        if (b < NBA) src = reinterpret_cast<const bf16*>(S.U) +
+                           ((size_t)mrow * (S.ldu / 32) + S.ucol / 32 + jr) * 512;
+        else src = reinterpret_cast<const bf16*>(a.seg[bseg(b - NBA)].Bl) +
+                   ((size_t)brb(b - NBA) * nrb + jr) * 512;
       }
-      ra[q] = v;
-    }
-#pragma unroll
-    for (int q = 0; q < PB; ++q) {
-      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-      int sg;
-      const int wr = brow(row, &sg);
-      rb[q] = sg == sgi ? load8(reinterpret_cast<const bf16*>(S.Bl) + frag_off(wr, jr * 32 + ko, a.r))
-                        : zero8;
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < PA; ++q) {
-      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-      *reinterpret_cast<bf16x8*>(sA + (buf * BM + row) * TBKP + ko) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < PB; ++q) {
-      const int p = tid + NTH * q, row = (p >> 6) * 16 + (p & 15), ko = ((p & 63) >> 4) * 8;
-      *reinterpret_cast<bf16x8*>(sB + (buf * BN + row) * TBKP + ko) = rb[q];
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + lane * 8),
+                                       (lds_void_t*)(smem_raw + (slot * NB + bb) * 1024), 16, 0, 0);
     }
   };
 
@@ -648,36 +633,9 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
     for (int j = 0; j < TN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int buf) {
-    bf16x8 af[TM / 16], bfr[TN / 16];
-#pragma unroll
-    for (int i = 0; i < TM / 16; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(sA + (buf * BM + wm * TM + i * 16 + r16) * TBKP + kq);
-#pragma unroll
-    for (int j = 0; j < TN / 16; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (buf * BN + wn * TN + j * 16 + r16) * TBKP + kq);
-#pragma unroll
-    for (int i = 0; i < TM / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < TN / 16; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  };
-  // base K loop (the first step's loads are in flight while the row norms of the
-  // tile go to LDS; the loop's barriers publish them before their use)
-  __shared__ float s_rs[BM];
-  fetch(0);
-  if (a.ss_in && tid < BM) s_rs[tid] = rs_of(a, m0 + tid);
-  stage(0);
-  __syncthreads();
-  for (int st = 0; st < nkb; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nkb) fetch(st + 1);
-    mma(buf);
-    if (st + 1 < nkb) stage(buf ^ 1);
-    __syncthreads();
-  }
-  // RMSNorm: the base product's rows scale by 1 / rms(x) before the LoRA steps
-  if (a.ss_in) {
+  // RMSNorm: the base product's rows scale by 1 / rms(x) before the LoRA stages
+  auto scale_rows = [&]() {
+    if (!a.ss_in) return;
 #pragma unroll
     for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
@@ -686,21 +644,43 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
 #pragma unroll
         for (int j = 0; j < TN / 16; ++j) acc[i][j][e] *= rs;
       }
-  }
-  // LoRA steps over the rank, one pass per segment of the tile with an adapter
-  const int nl = nls * nrb;
-  if (nl > 0) {
-    fetch_lora(lseg[0], 0);
-    stage(0);
-    __syncthreads();
-    for (int st = 0; st < nl; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < nl) fetch_lora(lseg[(st + 1) / nrb], (st + 1) % nrb);
-      mma(buf);
-      if (st + 1 < nl) stage(buf ^ 1);
-      __syncthreads();
+  };
+
+#pragma unroll
+  for (int s = 0; s < TS - 1; ++s)
+    if (s < nst) issue(s, s);
+  for (int st = 0; st < nst; ++st) {
+    // this wave's loads of stage st are done once at most the later stages' remain
+    const int newer = min(TS - 2, nst - 1 - st);
+    if (newer >= TS - 2) wait_vmcnt<(TS - 2) * P>();
+    else if (newer == 2) wait_vmcnt<2 * P>();
+    else if (newer == 1) wait_vmcnt<P>();
+    else wait_vmcnt<0>();
+    __syncthreads();          // every wave's loads of stage st landed; stage st - 1 consumed
+    if (st + TS - 1 < nst) issue(st + TS - 1, (st + TS - 1) % TS);
+    if (st == n_base) scale_rows();
+    // in a paired LoRA pass only the wave's column blocks of that segment take part
+    const int lsg = st >= n_base ? lseg[(st - n_base) / spp] : -1;
+#pragma unroll
+    for (int kk = 0; kk < TKB; ++kk) {
+      const char* base = smem_raw + ((st % TS) * NB + kk * NBS) * 1024 + lane * 16;
+      bf16x8 af[TM / 16], bfr[TN / 16];
+#pragma unroll
+      for (int i = 0; i < TM / 16; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(base + (wm * (TM / 16) + i) * 1024);
+#pragma unroll
+      for (int j = 0; j < TN / 16; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(base + (NBA + wn * (TN / 16) + j) * 1024);
+#pragma unroll
+      for (int i = 0; i < TM / 16; ++i)
+#pragma unroll
+        for (int j = 0; j < TN / 16; ++j)
+          if (lsg < 0 || !a.paired || ((wn * (TN / 16) + j) & 1) == lsg)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
+  if (nst == n_base) scale_rows();
+  __syncthreads();            // the ring is free for the epilogue
 
   // epilogue: one column slice of BN / WN at a time is staged in LDS (fp32) by the
   // wavefronts that own it; then each thread finishes items of 8 consecutive
@@ -932,7 +912,7 @@ k_lora_u(const long long* __restrict__ t, int n_slices, long long stride, int M,
       o[2 * e + 1] = (bf16)(scale * fx_to_float(acc[e].y));
     }
   }
-  *reinterpret_cast<bf16x8*>(u + off) = o;
+  *reinterpret_cast<bf16x8*>(u + frag_off(m, c, ncols)) = o;
 }
 
 __global__ void k_zero_i64(long long* p, size_t n) {
@@ -995,20 +975,19 @@ hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s) {
 // Large-M tile choice: the biggest tile that still gives every CU a workgroup and
 // whose column blocks do not straddle a segment boundary.  Returns false when no
 // tile fits (the skinny kernel then runs).
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int TS, int EPI>
 hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int outc = a.paired ? BN / 2 : BN;
   const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
   const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
   const int grid = (nbm * nbn * nsl + 7) / 8 * 8;
-  const size_t smem = std::max((size_t)2 * (BM + BN) * TBKP * sizeof(bf16),
-                               (size_t)BM * (BN / WN + 4) * sizeof(float));
+  constexpr size_t smem = tile_smem_bytes<BM, BN, WM, WN, TS>();
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tile<BM, BN, WM, WN, EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tile<BM, BN, WM, WN, TS, EPI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  uno_launch(k_gemm_tile<BM, BN, WM, WN, EPI>, grid, 64 * WM * WN, (uint32_t)smem, s, a, nbm, nbn);
+  uno_launch(k_gemm_tile<BM, BN, WM, WN, TS, EPI>, grid, 64 * WM * WN, (uint32_t)smem, s, a, nbm, nbn);
   return hipGetLastError();
 }
 
@@ -1021,37 +1000,51 @@ bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
   return true;
 }
 
+#ifndef UNO_TILE_MIN_WG
+#define UNO_TILE_MIN_WG 128
+#endif
+#ifndef UNO_TILE_TS1
+#define UNO_TILE_TS1 3
+#endif
+#ifndef UNO_TILE_TS3
+#define UNO_TILE_TS3 2
+#endif
+constexpr int kTileMinWG = UNO_TILE_MIN_WG;   // workgroups a larger tile must still give
+constexpr int kTileTS1 = UNO_TILE_TS1;        // ring depth of the 256 x 128 tile
+constexpr int kTileTS3 = UNO_TILE_TS3;        // ring depth of the 128 x 128 tile
+
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
   if (a.K % 32 || a.r % 32) return false;
-  const long cu = 256;
   const int nsl = (a.epi == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
-  if (a.K % (32 * nsl)) return false;
+  if (a.K % (32 * nsl) || (a.K / 32 / nsl) % TKB || (a.r / 32) % TKB) return false;
+  // the tile kernel takes its LoRA intermediate as fragment-tiled bf16 only
+  for (int i = 0; i < a.nseg; ++i)
+    if (a.seg[i].Ufx && a.seg[i].Bl) return false;
+  if (a.paired != (a.epi == EPI_SWIGLU)) return false;
   auto blocks = [&](int BM, int BN) {
     const int outc = a.paired ? BN / 2 : BN;
     return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc) * nsl;
   };
-  // prefer two workgroups per CU (one's epilogue overlaps the other's K loop),
-  // then one, then the smallest tile
+  // the largest tile that still gives half the CUs a workgroup (the 256-row tiles
+  // fill a CU's LDS alone), else the 128 x 128 tile, whose two-stage ring lets two
+  // workgroups share a CU (measured at batch 128 and in the distillation forward)
+  const long want = kTileMinWG;
   const bool f256 = tile_fits(a, n_cols_total, 256), f128 = tile_fits(a, n_cols_total, 128);
   int cfg = -1;
-  for (const long want : {2 * cu, cu}) {
-    if (f256 && blocks(256, 256) >= want) cfg = 0;
-    else if (f256 && blocks(128, 256) >= want) cfg = 1;
-    else if (f128 && blocks(256, 128) >= want) cfg = 2;
-    else if (f128 && blocks(128, 128) >= want) cfg = 3;
-    if (cfg >= 0) break;
-  }
-  if (cfg < 0 && f128) cfg = 3;
+  if (f256 && blocks(256, 256) >= want) cfg = 0;
+  else if (f128 && blocks(256, 128) >= want) cfg = 1;
+  else if (f256 && blocks(128, 256) >= want) cfg = 2;
+  else if (f128) cfg = 3;
+  else if (f256) cfg = 2;
   if (cfg < 0) return false;
-  if (a.paired != (a.epi == EPI_SWIGLU)) return false;
-#define UNO_TILE_EPI(E)                                                        \
-  case E:                                                                      \
-    switch (cfg) {                                                             \
-      case 0: *err = run_tile<256, 256, 4, 4, E>(a, n_cols_total, s); break;   \
-      case 1: *err = run_tile<128, 256, 2, 4, E>(a, n_cols_total, s); break;   \
-      case 2: *err = run_tile<256, 128, 4, 2, E>(a, n_cols_total, s); break;   \
-      default: *err = run_tile<128, 128, 2, 2, E>(a, n_cols_total, s); break;  \
-    }                                                                          \
+#define UNO_TILE_EPI(E)                                                          \
+  case E:                                                                        \
+    switch (cfg) {                                                               \
+      case 0: *err = run_tile<256, 256, 4, 4, 2, E>(a, n_cols_total, s); break;  \
+      case 1: *err = run_tile<256, 128, 4, 2, kTileTS1, E>(a, n_cols_total, s); break; \
+      case 2: *err = run_tile<128, 256, 2, 4, 3, E>(a, n_cols_total, s); break;  \
+      default: *err = run_tile<128, 128, 2, 2, kTileTS3, E>(a, n_cols_total, s); break; \
+    }                                                                            \
     return true;
   switch (a.epi) {
     UNO_TILE_EPI(EPI_STORE_F32)

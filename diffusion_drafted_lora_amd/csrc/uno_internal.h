@@ -206,12 +206,15 @@ UNO_DEV void ss_add(long long* ss, int m, int bank, float sq) {
 struct GemmSeg {
   const void* W;     // [N, K] of the storage type
   const void* Bl;    // LoRA up [N, r] (or null)
-  const void* U;     // gated, scaled LoRA intermediate [M, ldu] of the storage type (or null)
+  const void* U;     // gated, scaled LoRA intermediate of the storage type (or null):
+                     // float32 row-major at column 0 of the segment; bf16 the whole
+                     // fragment-tiled [M, ldu] buffer (segment at column ucol)
   const long long* Ufx;  // bf16 path: fixed-point t [M, ldu] (u = gate * bf16(scale * t))
   int32_t n0;        // first output column of this segment
   int32_t N;         // columns of this segment
   int32_t ldu;
-  int32_t pad;
+  int32_t ucol;      // bf16 U: first column of this segment's intermediate in the
+                     // fragment-tiled [M, ldu] buffer U points at
 };
 
 struct GemmArgs {
@@ -278,7 +281,8 @@ bool lora_down_tile_fits(int M, int K, int ncols, int k_slices);
 int lora_down_tile_slices(int M, int K, int ncols);
 hipError_t launch_lora_down_tile(const GemmArgs& a, int ncols, hipStream_t s);
 // u[m, c] = gate[m] ? bf16(scale * sum_s t[s][m, c] * 2^-32) : 0 over the K-slice
-// partials of the large-M down-projection ([M, ncols] each, `stride` apart)
+// partials of the large-M down-projection ([M, ncols] each, `stride` apart); u is
+// fragment-tiled [round16(M), ncols]
 hipError_t launch_lora_u(const long long* t, int n_slices, long long stride, int M, int ncols,
                          const uint8_t* gate, float scale, bf16* u, hipStream_t s);
 hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s);

@@ -88,7 +88,7 @@ Layout make_layout(const uno_config& c) {
   L.qbuf = take(R * q * ts);
   L.obuf = take(round16(R) * q * ts);
   L.hbuf = take(round16(R) * F * ts);
-  L.ubuf = take(R * 3 * r * ts + 16);
+  L.ubuf = take(round16(R) * 3 * r * ts + 16);
   // four fixed-point LoRA intermediates, each with room for up to TFX_SLICES
   // K-slice partials of the large-M down-projection
   L.tfx = take(4 * R * 3 * r * tfx_slices(R) * 8 + 16);
@@ -574,8 +574,14 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // attach the LoRA up-projection of segment `i` reading group buffer `buf`
   auto lora_up = [&](GemmArgs& a, int i, int proj, int l, int buf, int col, int ld) {
     a.seg[i].Bl = c->lb[proj][l];
-    if (c->bf16 && !tile_lora) a.seg[i].Ufx = Bfx[buf] + col;
-    else a.seg[i].U = ubuf + col;
+    if (c->bf16 && !tile_lora) {
+      a.seg[i].Ufx = Bfx[buf] + col;
+    } else if (c->bf16) {
+      a.seg[i].U = ubuf;          // fragment-tiled [R, ld], this segment at column col
+      a.seg[i].ucol = col;
+    } else {
+      a.seg[i].U = ubuf + col;
+    }
     a.seg[i].ldu = ld;
     a.gate = gate;
     a.scale = sc;
