@@ -259,7 +259,14 @@ constexpr int VPAD = MK + 8;      // LDS row of V^T (bf16)
 constexpr int PPAD = MK + 8;      // LDS row of P (bf16)
 constexpr int PGC = 1024;         // block-table entries cached per workgroup
 
-__global__ void __launch_bounds__(512)
+// WIN: rows carry visibility windows (keys map to slots through two ranges);
+// without, rows are plain causal and key p is slot p, so a V piece of eight
+// aligned keys always lies in one page and needs no per-element path.
+#ifndef UNO_ATTN_MIN_WAVES
+#define UNO_ATTN_MIN_WAVES 2
+#endif
+template <bool WIN>
+__global__ void __launch_bounds__(256, UNO_ATTN_MIN_WAVES)
 k_attn_mfma(AttnArgs a, KvLayout kv) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   bf16* sK = reinterpret_cast<bf16*>(smem_raw);                 // [MK][KPAD]
@@ -308,15 +315,16 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   for (int d = 0; d < HD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   bf16* myP = sP + w * 16 * PPAD;
-  // K / V of a 64-key sub-chunk in 16-byte pieces, prefetched into registers one
-  // sub-chunk ahead.  K piece e: key e / 16, dims (e % 16) * 8 .. +7 (a token row).
+  // K / V of a 64-key sub-chunk in 16-byte pieces, prefetched into registers two
+  // sub-chunks ahead.  K piece e: key e / 16, dims (e % 16) * 8 .. +7 (a token row).
   // V piece e: dim (e % 256) / 2, keys ((e / 256) * 2 + e % 2) * 8 .. +7 (the V block
   // is dim-major, so eight consecutive tokens of one dim are 16 contiguous bytes;
   // pieces whose eight keys are not eight aligned slots of one page go by element).
   constexpr int PF_MAX = MK * (HD / 8) / 256;          // 4 for >= 256 threads
   const int npf = (MK * (HD / 8) + nthr - 1) / nthr;
   const int ps = kv.page_size;
-  bf16x8 pk[PF_MAX], pv[PF_MAX];
+  // two register sets in turn: sub-chunk i + 2 is fetched while i is multiplied
+  bf16x8 pkA[PF_MAX], pvA[PF_MAX], pkB[PF_MAX], pvB[PF_MAX];
   // page of a slot: from the LDS copy of the chunk's block-table entries once it
   // is published (pages pl .. pl + npg - 1), else from the block table
   int pl = 0, npg = 0;
@@ -324,7 +332,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
     const int pi = sl / ps - pl;
     return (pi >= 0 && pi < npg) ? sPg[pi] : kv_page(kv, seq, sl);
   };
-  auto fetch = [&](int k0) {
+  auto fetch = [&](int k0, bf16x8 (&pk)[PF_MAX], bf16x8 (&pv)[PF_MAX]) {
 #pragma unroll
     for (int q = 0; q < PF_MAX; ++q) {
       const int e = tid + q * nthr;
@@ -338,7 +346,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
                                                 kv_elem(kv, 0, sl % ps, d8));
         const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1, p0 = k0 + jj * 8;
         const int s0 = vslot(p0, At, Ct);
-        if (p0 + 7 < kend && s0 % 8 == 0 && vslot(p0 + 7, At, Ct) == s0 + 7) {
+        if (!WIN || (p0 + 7 < kend && s0 % 8 == 0 && vslot(p0 + 7, At, Ct) == s0 + 7)) {
           const int pg = page_of(s0);
           if (pg >= 0)
             vv = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 1, pg, kvh) +
@@ -358,7 +366,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   };
   // Keys at or beyond kend are staged as zeros: masked keys get probability 0, and
   // 0 * V must stay 0 (a slot that was never written may hold a NaN pattern).
-  auto stage = [&](int k0) {
+  auto stage = [&](int k0, const bf16x8 (&pk)[PF_MAX], const bf16x8 (&pv)[PF_MAX]) {
 #pragma unroll
     for (int q = 0; q < PF_MAX; ++q) {
       const int e = tid + q * nthr;
@@ -377,8 +385,8 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   // first sub-chunk of plain causal rows: slots beyond the rows are read (from
   // reserved pages only) and zeroed at staging; this keeps the window reads off
   // the critical path
-  const bool causal = a.row_vis == nullptr;
-  if (causal) fetch(kbeg);
+  const bool causal = !WIN;
+  if (causal) fetch(kbeg, pkA, pvA);
   __syncthreads();
   int nv;
   tile_window(sW, &At, &Ct, &nv);
@@ -403,7 +411,8 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
     }
     for (int i = tid; i < npg_all; i += nthr) sPg[i] = kv_page(kv, seq, (pl + i) * ps);
   }
-  if (!causal) fetch(kbeg);
+  if (!causal) fetch(kbeg, pkA, pvA);
+  if (kbeg + MK < kend) fetch(kbeg + MK, pkB, pvB);
   npg = npg_all;
   int ra[4], rc[4], rd[4];
 #pragma unroll
@@ -412,10 +421,15 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
     rc[i] = sW[16 + grp * 4 + i];
     rd[i] = sW[32 + grp * 4 + i];
   }
-  for (int k0 = kbeg; k0 < kend; k0 += MK) {
+  for (int k0 = kbeg, it = 0; k0 < kend; k0 += MK, ++it) {
     __syncthreads();               // previous sub-chunk fully consumed
-    stage(k0);
-    if (k0 + MK < kend) fetch(k0 + MK);
+    if (it & 1) {
+      stage(k0, pkB, pvB);
+      if (k0 + 2 * MK < kend) fetch(k0 + 2 * MK, pkB, pvB);
+    } else {
+      stage(k0, pkA, pvA);
+      if (k0 + 2 * MK < kend) fetch(k0 + 2 * MK, pkA, pvA);
+    }
     __syncthreads();
     // S = Q K^T for 4 key tiles of 16
     f32x4 s[MK / 16];
@@ -527,16 +541,19 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   if (R <= 0) return hipSuccess;
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   dim3 grid(a.n_chunks, kv.n_kv_heads, a.n * row_tiles);
-  const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G >= 4 && G <= 8 && a.chunk % MK == 0 &&
+  const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G == 4 && a.chunk % MK == 0 &&
                     kv.page_size % 8 == 0;
   if (mfma) {
     const size_t smem = (size_t)(MK * KPAD + HD * VPAD + G * 16 * PPAD) * 2;
     if (smem > 64 * 1024) {
-      hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      if (ea != hipSuccess) return ea;
+      for (const void* f : {reinterpret_cast<const void*>(&k_attn_mfma<false>),
+                            reinterpret_cast<const void*>(&k_attn_mfma<true>)}) {
+        hipError_t ea = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (ea != hipSuccess) return ea;
+      }
     }
-    uno_launch(k_attn_mfma, grid, 64 * G, smem, s, a, kv);
+    if (a.row_vis) uno_launch(k_attn_mfma<true>, grid, 64 * G, smem, s, a, kv);
+    else uno_launch(k_attn_mfma<false>, grid, 64 * G, smem, s, a, kv);
   } else {
     const size_t smem = attn_smem_bytes<T>(G, kv.head_dim);
     const int nown = (16 * G * kv.head_dim + 255) / 256;
