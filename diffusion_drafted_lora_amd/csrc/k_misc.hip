@@ -80,13 +80,15 @@ __global__ void k_rows_setup(RowsSetup a) {
 }
 
 // x[r] = E[tok[r]] (or the given hidden row); also the first RMSNorm's input
-// xg = T(x * g) and the fixed-point sum of x^2 (2^-32 units).
+// xg = T(x * g) and the fixed-point sum of x^2 (2^-32 units).  Each thread takes
+// groups of eight consecutive columns (16-byte loads of the table row and the
+// gains; eight consecutive columns are also eight consecutive elements of the
+// fragment-tiled xg).
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
         const float* __restrict__ hidden_in, int d, int V, float* x, const T* g, T* xg,
         long long* ss, int32_t* err) {
-  __shared__ float sh[4];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * d;
   const T* er = nullptr;
@@ -99,11 +101,19 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
     er = E + (size_t)t * d;
   }
   float sq = 0.0f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const float v = hidden_in ? hidden_in[(size_t)r * d + c] : to_f(er[c]);
-    xr[c] = v;
-    if (xg) xg[act_off<T>(r, c, d)] = from_f<T>(v * to_f(g[c]));
-    sq += v * v;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8], gv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = hidden_in ? hidden_in[(size_t)r * d + c + e] : to_f(er[c + e]);
+      gv[e] = xg ? to_f(g[c + e]) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xr[c + e] = v[e];
+      if (xg) xg[act_off<T>(r, c + e, d)] = from_f<T>(v[e] * gv[e]);
+      sq += v[e] * v[e];
+    }
   }
   if (ss) {
     // per-wave partials in fixed point, so the total does not depend on order
@@ -111,7 +121,6 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
     for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
     if ((threadIdx.x & 63) == 0) ss_add(ss, r, threadIdx.x >> 6, sq);
   }
-  (void)sh;
 }
 
 
@@ -250,6 +259,7 @@ template <typename T>
 hipError_t launch_embed(const T* E, const int32_t* tok, const float* hidden_in, int R, int d,
                         int V, float* x, const T* g, T* xg, long long* ss, int32_t* err,
                         hipStream_t s) {
+  if (d % 8) return hipErrorInvalidValue;
   uno_launch(k_embed<T>, R, 256, 0, s, E, tok, hidden_in, d, V, x, g, xg, ss, err);
   return hipGetLastError();
 }
