@@ -423,7 +423,7 @@ def main():
         "hbm_frac_step": total_bytes / 1e9 / sec / HBM_PEAK_GBS,
         "prefill_s": t_prefill,
         "roofline": {
-            "kernel": "gated-LoRA gate/up linear + SwiGLU (k_gemm_bf16<2,16,4>)",
+            "kernel": "gated-LoRA gate/up linear + SwiGLU (k_gemm_bf16<2,4,4>)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
             "bytes_per_launch": sw_bytes_per_launch, "us_per_launch": 1e3 * sw_ms,
