@@ -1072,7 +1072,7 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   dim3 grid(n_cols_total / 16, mtiles);
   // Launch shapes measured at the 8B decode shapes (one MI355X): many small
   // workgroups beat few large ones -- the paired gate/up tiles at 4 waves of 4
-  // blocks in flight (5.6 TB/s), q|k|v, o and down at 12 waves of 2, the LM head
+  // blocks in flight (5.6 TB/s), o and down at 12 waves of 2, q|k|v at 8 of 2, the LM head
   // at two 16-column tiles per workgroup of 8 waves of 8.
   if (a.paired) {
     if (nkb >= 64) uno_launch(k_gemm_bf16<2, 4, 4>, grid, 256, 0, s, a);
@@ -1081,7 +1081,8 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
     if (a.epi == EPI_LOGITS && n_cols_total % 32 == 0 && a.nseg == 1 && nkb >= 32) {
       uno_launch(k_gemm_bf16<2, 8, 8>, dim3(n_cols_total / 32, mtiles), 512, 0, s, a);
     } else if (nkb >= 64) {
-      uno_launch(k_gemm_bf16<1, 12, 2>, grid, 768, 0, s, a);
+      if (a.epi == EPI_QKV) uno_launch(k_gemm_bf16<1, 8, 2>, grid, 512, 0, s, a);
+      else uno_launch(k_gemm_bf16<1, 12, 2>, grid, 768, 0, s, a);
     } else {
       uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
     }
