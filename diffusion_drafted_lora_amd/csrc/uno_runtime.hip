@@ -497,7 +497,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   const int groups = f.n * Hkv * row_tiles;
   int target = std::max(1, std::min(kMaxChunks, (kAttnTargetWG + groups - 1) / groups));
   int chunk = (f.ctx_bound + target - 1) / target;
-  chunk = std::max(kAttnMinChunk, (chunk + 63) / 64 * 64);
+  chunk = std::max(kAttnMinChunk, (chunk + kAttnMinChunk - 1) / kAttnMinChunk * kAttnMinChunk);
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
   if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
 
