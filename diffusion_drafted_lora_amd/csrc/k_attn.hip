@@ -282,7 +282,9 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[si];
   const int r0 = si * a.rows_per_seq + rt * 16;
   const int nrows = min(16, a.rows_per_seq - rt * 16);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
+  // one wave per query head of the KV head's group: G = 4 waves (checked at launch)
+  constexpr int nthr = 256;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
 
   // Loads that do not depend on each other go out together: row windows, the Q
@@ -322,15 +324,29 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   // pieces whose eight keys are not eight aligned slots of one page go by element).
   constexpr int PF_MAX = MK * (HD / 8) / 256;          // 4 for >= 256 threads
   const int npf = (MK * (HD / 8) + nthr - 1) / nthr;
-  const int ps = kv.page_size;
+  // pages are a power of two of slots (checked at launch): slot sl lies in page
+  // entry sl >> psh at offset sl & pmask; a page's block of this layer and KV head
+  // is pstride elements after the previous page's
+  const int psh = kv.page_shift, pmask = kv.page_size - 1;
+  const size_t pstride = (size_t)kv.n_kv_heads * kv.page_size * HD;
+  const bf16* kb0 = kv_block<const bf16>(kv, a.layer, 0, 0, kvh);
+  const bf16* vb0 = kv_block<const bf16>(kv, a.layer, 1, 0, kvh);
+  const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
+  // block-table entry of slot sl, or -1 outside the sequence's reserved pages
+  auto bt_page = [&](int sl) {
+    const int pi = sl >> psh;
+    if (sl < 0 || pi >= kv.max_pages_per_seq) return -1;
+    const int page = bt[pi];
+    return (page >= 0 && page < kv.n_pages) ? page : -1;
+  };
   // two register sets in turn: sub-chunk i + 2 is fetched while i is multiplied
   bf16x8 pkA[PF_MAX], pvA[PF_MAX], pkB[PF_MAX], pvB[PF_MAX];
   // page of a slot: from the LDS copy of the chunk's block-table entries once it
   // is published (pages pl .. pl + npg - 1), else from the block table
   int pl = 0, npg = 0;
   auto page_of = [&](int sl) {
-    const int pi = sl / ps - pl;
-    return (pi >= 0 && pi < npg) ? sPg[pi] : kv_page(kv, seq, sl);
+    const int pi = (sl >> psh) - pl;
+    return (pi >= 0 && pi < npg) ? sPg[pi] : bt_page(sl);
   };
   auto fetch = [&](int k0, bf16x8 (&pk)[PF_MAX], bf16x8 (&pv)[PF_MAX]) {
 #pragma unroll
@@ -342,21 +358,19 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
         const int sl = vslot(p, At, Ct);
         const int page = p < kend ? page_of(sl) : -1;
         if (page >= 0)
-          kk = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 0, page, kvh) +
-                                                kv_elem(kv, 0, sl % ps, d8));
+          kk = *reinterpret_cast<const bf16x8*>(kb0 + (size_t)page * pstride + (sl & pmask) * HD + d8);
         const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1, p0 = k0 + jj * 8;
         const int s0 = vslot(p0, At, Ct);
         if (!WIN || (p0 + 7 < kend && s0 % 8 == 0 && vslot(p0 + 7, At, Ct) == s0 + 7)) {
           const int pg = page_of(s0);
           if (pg >= 0)
-            vv = *reinterpret_cast<const bf16x8*>(kv_block<const bf16>(kv, a.layer, 1, pg, kvh) +
-                                                  kv_elem(kv, 1, s0 % ps, d));
+            vv = *reinterpret_cast<const bf16x8*>(vb0 + (size_t)pg * pstride + (d << psh) + (s0 & pmask));
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int pj = p0 + j, sj = vslot(pj, At, Ct);
             const int pg = pj < kend ? page_of(sj) : -1;
-            if (pg >= 0) vv[j] = kv_block<const bf16>(kv, a.layer, 1, pg, kvh)[kv_elem(kv, 1, sj % ps, d)];
+            if (pg >= 0) vv[j] = vb0[(size_t)pg * pstride + (d << psh) + (sj & pmask)];
           }
         }
       }
@@ -375,9 +389,11 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
         *reinterpret_cast<bf16x8*>(sK + key * KPAD + d8) = k0 + key < kend ? pk[q] : bf16x8{};
         const int jj = (e >> 8) * 2 + (e & 1), d = (e & 255) >> 1;
         bf16x8 vv = pv[q];
+        if (k0 + MK > kend) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (k0 + jj * 8 + j >= kend) vv[j] = (bf16)0.0f;
+          for (int j = 0; j < 8; ++j)
+            if (k0 + jj * 8 + j >= kend) vv[j] = (bf16)0.0f;
+        }
         *reinterpret_cast<bf16x8*>(sVt + d * VPAD + jj * 8) = vv;
       }
     }
@@ -405,21 +421,24 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       lo = min(lo, Ct + b - At);
       hi = max(hi, Ct + kend - 1 - At);
     }
-    if (hi >= lo && lo >= 0) {
-      const int p0 = lo / ps, p1 = hi / ps;
+    // (sub-chunks 0 and 1 are fetched below, before the copy is published, so
+    // a chunk of at most two sub-chunks never reads it)
+    if (hi >= lo && lo >= 0 && kend - kbeg > 2 * MK) {
+      const int p0 = lo >> psh, p1 = hi >> psh;
       if (p1 - p0 + 1 <= PGC) { pl = p0; npg_all = p1 - p0 + 1; }
     }
-    for (int i = tid; i < npg_all; i += nthr) sPg[i] = kv_page(kv, seq, (pl + i) * ps);
+    for (int i = tid; i < npg_all; i += nthr) sPg[i] = bt_page((pl + i) << psh);
   }
   if (!causal) fetch(kbeg, pkA, pvA);
   if (kbeg + MK < kend) fetch(kbeg + MK, pkB, pvB);
   npg = npg_all;
-  int ra[4], rc[4], rd[4];
+  int ra[4], rc[4], rd[4], lim[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     ra[i] = sW[grp * 4 + i];
     rc[i] = sW[16 + grp * 4 + i];
     rd[i] = sW[32 + grp * 4 + i];
+    lim[i] = min(kend, ra[i]);
   }
   for (int k0 = kbeg, it = 0; k0 < kend; k0 += MK, ++it) {
     __syncthreads();               // previous sub-chunk fully consumed
@@ -447,7 +466,7 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
 #pragma unroll
     for (int j = 0; j < MK / 16; ++j) {
       const int p = k0 + j * 16 + r16;
-      ksl[j] = p < kend ? vslot(p, At, Ct) : INT_MAX;
+      ksl[j] = WIN ? (p < kend ? vslot(p, At, Ct) : INT_MAX) : p;
     }
     float mt[4];
 #pragma unroll
@@ -456,7 +475,10 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
 #pragma unroll
       for (int j = 0; j < MK / 16; ++j) {
         float v = s[j][i] * sc;
-        if (ksl[j] == INT_MAX || !seen(ksl[j], ra[i], rc[i], rd[i])) v = -INFINITY;
+        // plain causal rows: keys are slots and row i sees slots below ra[i]
+        const bool vis = WIN ? (ksl[j] != INT_MAX && seen(ksl[j], ra[i], rc[i], rd[i]))
+                             : ksl[j] < lim[i];
+        if (!vis) v = -INFINITY;
         s[j][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -542,7 +564,7 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
   const int row_tiles = (a.rows_per_seq + 15) / 16;
   dim3 grid(a.n_chunks, kv.n_kv_heads, a.n * row_tiles);
   const bool mfma = sizeof(T) == 2 && kv.head_dim == HD && G == 4 && a.chunk % MK == 0 &&
-                    kv.page_size % 8 == 0;
+                    kv.page_shift >= 3;
   if (mfma) {
     const size_t smem = (size_t)(MK * KPAD + HD * VPAD + G * 16 * PPAD) * 2;
     if (smem > 64 * 1024) {

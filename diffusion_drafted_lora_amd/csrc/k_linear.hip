@@ -192,7 +192,8 @@ k_gemm_bf16(GemmArgs a) {
   static_assert(WAVES >= 4, "threads 0..255 own the 256 outputs of a tile");
   __shared__ float red[WAVES][NT][256];
   __shared__ float fin[256];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int mt = blockIdx.y;
   const int grp = blockIdx.x;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
@@ -302,31 +303,51 @@ k_gemm_bf16(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- base phase: this wave's share of the 32-wide K blocks
+  // ---- base phase: this wave's share of the 32-wide K blocks, streamed through
+  // a ring of KU register slots.  Slot u is refilled with the block KU ahead as
+  // soon as its MFMAs have issued, so KU blocks stay in flight up to the last
+  // round, whose refills bring in the (je - jb) % KU trailing blocks.
   const int jb = w * nkb / WAVES, je = (w + 1) * nkb / WAVES;
-  int j = jb;
+  const int nfull = (je - jb) / KU, rem = (je - jb) % KU;
   const bf16x8 zero8 = {};
-  for (; j + KU <= je; j += KU) {
-    bf16x8 af[KU], bfr[NT][KU];
+  bf16x8 ax[KU], bw[NT][KU];
+  // Activation rows past M are the padding of a whole 16-row tile: an MFMA output
+  // row depends on its own A row only, and those output rows are never stored.
+  auto fill = [&](int u, int j) {
+    ax[u] = load8(Xp + (size_t)j * 512);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) af[u] = row_ok ? load8(Xp + (size_t)(j + u) * 512) : zero8;
+    for (int t = 0; t < NT; ++t) bw[t][u] = load8_stream(Wp[t] + (size_t)j * 512);
+  };
+  auto consume = [&](int u) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u], bw[t][u], acc[t], 0, 0, 0);
+  };
+  int j = jb;
+  if (nfull > 0) {
 #pragma unroll
-      for (int u = 0; u < KU; ++u) bfr[t][u] = load8_stream(Wp[t] + (size_t)(j + u) * 512);
+    for (int u = 0; u < KU; ++u) fill(u, j + u);
+    for (int i = 1; i < nfull; ++i) {
+      j += KU;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        consume(u);
+        fill(u, j + u);
+      }
+    }
+    j += KU;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      consume(u);
+      if (u < rem) fill(u, j + u);
+    }
+  } else {
 #pragma unroll
     for (int u = 0; u < KU; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], bfr[t][u], acc[t], 0, 0, 0);
+      if (u < rem) fill(u, j + u);
   }
-  for (; j < je; ++j) {
-    const bf16x8 af = row_ok ? load8(Xp + (size_t)j * 512) : zero8;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8_stream(Wp[t] + (size_t)j * 512), acc[t],
-                                                       0, 0, 0);
-  }
+  for (int u = 0; u < KU; ++u)
+    if (u < rem) consume(u);
   // ---- RMSNorm: scale rows of the base product by 1 / rms(x)
   if (a.ss_in) {
     long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
@@ -1001,7 +1022,7 @@ bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
 }
 
 #ifndef UNO_TILE_MIN_WG
-#define UNO_TILE_MIN_WG 128
+#define UNO_TILE_MIN_WG 192
 #endif
 #ifndef UNO_TILE_TS1
 #define UNO_TILE_TS1 3
@@ -1012,6 +1033,10 @@ bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
 constexpr int kTileMinWG = UNO_TILE_MIN_WG;   // workgroups a larger tile must still give
 constexpr int kTileTS1 = UNO_TILE_TS1;        // ring depth of the 256 x 128 tile
 constexpr int kTileTS3 = UNO_TILE_TS3;        // ring depth of the 128 x 128 tile
+#ifndef UNO_TILE_TALL_FIRST
+#define UNO_TILE_TALL_FIRST 0
+#endif
+constexpr bool kTileTallFirst = UNO_TILE_TALL_FIRST;   // 128 x 256 before 256 x 128
 
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
   if (a.K % 32 || a.r % 32) return false;
@@ -1025,13 +1050,16 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
     const int outc = a.paired ? BN / 2 : BN;
     return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc) * nsl;
   };
-  // the largest tile that still gives half the CUs a workgroup (the 256-row tiles
-  // fill a CU's LDS alone), else the 128 x 128 tile, whose two-stage ring lets two
-  // workgroups share a CU (measured at batch 128 and in the distillation forward)
+  // the largest tile that still gives three quarters of the CUs a workgroup (the
+  // 256-row tiles fill a CU's LDS alone), else the 128 x 128 tile, whose two-stage
+  // ring lets two workgroups share a CU (measured at batch 128 and in the
+  // distillation forward: at 2048 rows q|k|v keeps 256 x 256 on 192 workgroups,
+  // o and down take 256 x 128 on 256 rather than 256 x 256 on 128)
   const long want = kTileMinWG;
   const bool f256 = tile_fits(a, n_cols_total, 256), f128 = tile_fits(a, n_cols_total, 128);
   int cfg = -1;
   if (f256 && blocks(256, 256) >= want) cfg = 0;
+  else if (kTileTallFirst && f256 && blocks(128, 256) >= want) cfg = 2;
   else if (f128 && blocks(256, 128) >= want) cfg = 1;
   else if (f256 && blocks(128, 256) >= want) cfg = 2;
   else if (f128) cfg = 3;
@@ -1058,6 +1086,30 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
 #undef UNO_TILE_EPI
 }
 
+#ifndef UNO_SK_GATEUP
+#define UNO_SK_GATEUP 2, 4, 4
+#endif
+#ifndef UNO_SK_QKV
+#define UNO_SK_QKV 1, 8, 2
+#endif
+#ifndef UNO_SK_O
+#define UNO_SK_O 1, 12, 2
+#endif
+#ifndef UNO_SK_DOWN
+#define UNO_SK_DOWN 1, 12, 2
+#endif
+
+// One skinny launch: WAVES waves splitting K, KU blocks in flight per wave; a
+// workgroup owns NT tiles of 16 columns (paired: the gate and up tiles of 16
+// output columns).
+template <int NT, int WAVES, int KU>
+hipError_t launch_skinny(const GemmArgs& a, int n_cols_total, int mtiles, hipStream_t s) {
+  const int per_wg = a.paired ? 16 : 16 * NT;
+  if (n_cols_total % per_wg) return hipErrorInvalidValue;
+  uno_launch(k_gemm_bf16<NT, WAVES, KU>, dim3(n_cols_total / per_wg, mtiles), WAVES * 64, 0, s, a);
+  return hipGetLastError();
+}
+
 template <>
 hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
@@ -1069,25 +1121,22 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   }
   const int mtiles = (a.M + 15) / 16;
   const int nkb = a.K / 32;
-  dim3 grid(n_cols_total / 16, mtiles);
   // Launch shapes measured at the 8B decode shapes (one MI355X): many small
   // workgroups beat few large ones -- the paired gate/up tiles at 4 waves of 4
-  // blocks in flight (5.6 TB/s), o and down at 12 waves of 2, q|k|v at 8 of 2, the LM head
-  // at two 16-column tiles per workgroup of 8 waves of 8.
+  // blocks in flight, q|k|v at 8 waves of 2, o at 12 of 2, down at 12 of 2, the LM
+  // head at two 16-column tiles per workgroup of 8 waves of 8.
   if (a.paired) {
-    if (nkb >= 64) uno_launch(k_gemm_bf16<2, 4, 4>, grid, 256, 0, s, a);
-    else uno_launch(k_gemm_bf16<2, 4, 1>, grid, 256, 0, s, a);
-  } else {
-    if (a.epi == EPI_LOGITS && n_cols_total % 32 == 0 && a.nseg == 1 && nkb >= 32) {
-      uno_launch(k_gemm_bf16<2, 8, 8>, dim3(n_cols_total / 32, mtiles), 512, 0, s, a);
-    } else if (nkb >= 64) {
-      if (a.epi == EPI_QKV) uno_launch(k_gemm_bf16<1, 8, 2>, grid, 512, 0, s, a);
-      else uno_launch(k_gemm_bf16<1, 12, 2>, grid, 768, 0, s, a);
-    } else {
-      uno_launch(k_gemm_bf16<1, 4, 1>, grid, 256, 0, s, a);
-    }
+    if (nkb >= 64) return launch_skinny<UNO_SK_GATEUP>(a, n_cols_total, mtiles, s);
+    return launch_skinny<2, 4, 1>(a, n_cols_total, mtiles, s);
   }
-  return hipGetLastError();
+  if (a.epi == EPI_LOGITS && n_cols_total % 32 == 0 && a.nseg == 1 && nkb >= 32)
+    return launch_skinny<2, 8, 8>(a, n_cols_total, mtiles, s);
+  if (nkb >= 64) {
+    if (a.epi == EPI_QKV) return launch_skinny<UNO_SK_QKV>(a, n_cols_total, mtiles, s);
+    if (nkb >= 256) return launch_skinny<UNO_SK_DOWN>(a, n_cols_total, mtiles, s);
+    return launch_skinny<UNO_SK_O>(a, n_cols_total, mtiles, s);
+  }
+  return launch_skinny<1, 4, 1>(a, n_cols_total, mtiles, s);
 }
 
 template <>

@@ -137,7 +137,7 @@ struct KvLayout {
   int32_t n_pages, n_kv_heads, page_size, head_dim, n_layers;
   const int32_t* block_table;   // [max_seqs, max_pages_per_seq]
   int32_t max_pages_per_seq;
-  int32_t pad;
+  int32_t page_shift;           // log2(page_size) for a power of two, else -1
 };
 
 // One (page, KV head) block of the pool holds page_size tokens x head_dim: K

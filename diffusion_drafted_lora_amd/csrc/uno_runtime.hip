@@ -276,6 +276,9 @@ KvLayout kv_layout(uno_ctx* c) {
   k.n_layers = c->cfg.n_layers;
   k.block_table = c->at<int32_t>(c->L.block_table);
   k.max_pages_per_seq = c->maxpp;
+  k.page_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if (k.page_size == (1 << b)) k.page_shift = b;
   return k;
 }
 
