@@ -957,10 +957,14 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
 // Large-M LoRA down-projection: the tile kernel with K split into k_slices
 // slices (a power of two up to 16, aiming at four workgroups per CU), each slice
 // storing its fixed-point partial; k_lora_u adds them.
+#ifndef UNO_LORA_TILE_TARGET
+#define UNO_LORA_TILE_TARGET 1024
+#endif
 int lora_down_tile_slices(int M, int K, int ncols) {
   const long tiles = (long)((M + 127) / 128) * (ncols / 128);
   int S = 1;
-  while (S < 16 && tiles * S < 1024 && (K / 32) % (2 * S) == 0 && K / 32 / (2 * S) >= 4) S *= 2;
+  while (S < 16 && tiles * S < UNO_LORA_TILE_TARGET && (K / 32) % (2 * S) == 0 && K / 32 / (2 * S) >= 4)
+    S *= 2;
   return S;
 }
 
