@@ -252,7 +252,11 @@ k_attn_combine(AttnArgs a, int hd) {
 // holds rows 4*(l/16)+i of column l%16); P goes through LDS to become the A
 // operand of P V.  Output accumulators share the row layout of S, so the
 // rescale by exp(m_old - m_new) needs no data movement.
-constexpr int MK = 64;            // keys per sub-chunk
+#ifndef UNO_ATTN_MK
+#define UNO_ATTN_MK 64
+#endif
+constexpr int MK = UNO_ATTN_MK;   // keys per sub-chunk
+static_assert(MK == 32 || MK == 64, "sub-chunks of 32 or 64 keys");
 constexpr int HD = 128;           // head dim of the MFMA path
 constexpr int KPAD = HD + 8;      // LDS row of K (bf16), 16-byte pad
 constexpr int VPAD = MK + 8;      // LDS row of V^T (bf16)

@@ -1037,6 +1037,13 @@ bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
 constexpr int kTileMinWG = UNO_TILE_MIN_WG;   // workgroups a larger tile must still give
 constexpr int kTileTS1 = UNO_TILE_TS1;        // ring depth of the 256 x 128 tile
 constexpr int kTileTS3 = UNO_TILE_TS3;        // ring depth of the 128 x 128 tile
+// template arguments <BM, BN, WM, WN, TS> of the 256 x 256 and 256 x 128 tiles
+#ifndef UNO_TILE_CFG0
+#define UNO_TILE_CFG0 256, 256, 4, 4, 2
+#endif
+#ifndef UNO_TILE_CFG1
+#define UNO_TILE_CFG1 256, 128, 4, 2, kTileTS1
+#endif
 #ifndef UNO_TILE_TALL_FIRST
 #define UNO_TILE_TALL_FIRST 0
 #endif
@@ -1055,25 +1062,28 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
     return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc) * nsl;
   };
   // the largest tile that still gives three quarters of the CUs a workgroup (the
-  // 256-row tiles fill a CU's LDS alone), else the 128 x 128 tile, whose two-stage
-  // ring lets two workgroups share a CU (measured at batch 128 and in the
+  // 256-row tiles fill a CU's LDS alone), else the largest that gives half of
+  // them one, else the 128 x 128 tile, whose two-stage ring lets two workgroups
+  // share a CU (measured at batch 128, in 1024-row prefill and in the
   // distillation forward: at 2048 rows q|k|v keeps 256 x 256 on 192 workgroups,
   // o and down take 256 x 128 on 256 rather than 256 x 256 on 128)
-  const long want = kTileMinWG;
   const bool f256 = tile_fits(a, n_cols_total, 256), f128 = tile_fits(a, n_cols_total, 128);
   int cfg = -1;
-  if (f256 && blocks(256, 256) >= want) cfg = 0;
-  else if (kTileTallFirst && f256 && blocks(128, 256) >= want) cfg = 2;
-  else if (f128 && blocks(256, 128) >= want) cfg = 1;
-  else if (f256 && blocks(128, 256) >= want) cfg = 2;
-  else if (f128) cfg = 3;
-  else if (f256) cfg = 2;
+  for (const long want : {(long)kTileMinWG, 128L}) {
+    if (f256 && blocks(256, 256) >= want) cfg = 0;
+    else if (kTileTallFirst && f256 && blocks(128, 256) >= want) cfg = 2;
+    else if (f128 && blocks(256, 128) >= want) cfg = 1;
+    else if (f256 && blocks(128, 256) >= want) cfg = 2;
+    if (cfg >= 0) break;
+  }
+  if (cfg < 0 && f128) cfg = 3;
+  else if (cfg < 0 && f256) cfg = 2;
   if (cfg < 0) return false;
 #define UNO_TILE_EPI(E)                                                          \
   case E:                                                                        \
     switch (cfg) {                                                               \
-      case 0: *err = run_tile<256, 256, 4, 4, 2, E>(a, n_cols_total, s); break;  \
-      case 1: *err = run_tile<256, 128, 4, 2, kTileTS1, E>(a, n_cols_total, s); break; \
+      case 0: *err = run_tile<UNO_TILE_CFG0, E>(a, n_cols_total, s); break;     \
+      case 1: *err = run_tile<UNO_TILE_CFG1, E>(a, n_cols_total, s); break;     \
       case 2: *err = run_tile<128, 256, 2, 4, 3, E>(a, n_cols_total, s); break;  \
       default: *err = run_tile<128, 128, 2, 2, kTileTS3, E>(a, n_cols_total, s); break; \
     }                                                                            \

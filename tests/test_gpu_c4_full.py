@@ -1,13 +1,17 @@
-"""The distillation forward at its full size: the 36-layer Qwen3-8B-shaped model
-(bf16, LoRA r 128, vocabulary 151936), one sequence of L = 2048 clean tokens plus
-2048 MASK rows -- the launch configuration the throughput measurement uses, per
-sequence.
+"""The full-size 36-layer Qwen3-8B-shaped model (bf16, LoRA r 128, vocabulary
+151936) in two launch configurations the throughput measurement uses: the
+distillation forward over one sequence of L = 2048 clean tokens plus 2048 MASK
+rows (per sequence), and one batch-1 decode forward of 16 draft rows at a
+1024-token context.
 
 * Sampled outputs against the oracle: the first 8 teacher rows (an AR forward of
   x[0..7]) and the first 8 student rows of block 0 (no clean context: 8 MASK rows
   with the adapter on), the oracle run layer by layer over weights copied from
   the device.  Tolerance as in the one-layer test: the bf16 oracle's own distance
   to the unrounded result sets the bound.
+* Decode: all 16 rows' 151936 logits against the oracle run layer by layer over
+  the same weights and the imported context (the skinny kernels at 16 rows and
+  the two-tile LM head with its logits epilogue), same tolerance.
 * Properties that hold exactly at any size (bitwise, since every row's arithmetic
   is independent of the other rows): teacher rows do not depend on B; student
   rows never see x[L-1]; with B = L the student rows do not depend on x at all;
@@ -130,3 +134,63 @@ def test_c4_full_size_exact_properties(full):
     tvr, tvb = host(tv16)[0], host(tvb16)[0]
     assert np.all(np.isfinite(tvr)) and tvr.min() >= 0.0 and tvr.max() <= 1.0
     assert np.abs(tvb - tvr.astype(np.float64).reshape(-1, 16).mean(-1)).max() <= 1e-6
+
+
+def test_decode_full_size_logits_match_oracle(full):
+    torch, w, _, _ = full
+    dev = torch.device("cuda", 0)
+    ctx, rows = 1024, 16
+    log("decode full: importing a 1024-token context into all 36 layers")
+    eng = uno.Engine(CFG, w, max_seqs=1, max_seq_len=ctx + 64, max_rows=rows, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(7501)
+    shape = (CFG.n_layers, ctx, CFG.n_kv_heads, CFG.head_dim)
+    k = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    eng.kv_import(0, k, v, pending=0)
+    toks = np.full(rows, CFG.mask_id, dtype=np.int32)
+    toks[0] = 1234                       # the pending token, then MASK rows
+    pos = np.arange(ctx, ctx + rows, dtype=np.int32)
+    gate = np.ones(rows, dtype=np.uint8)
+    gate[0] = 0                          # slot 0 is AR-only
+    t = lambda a: torch.from_numpy(a).to(dev)
+    log("decode full: GPU forward")
+    _, lg = eng.forward([0], rows, t(pos), t(gate), tokens=t(toks), want_logits=True)
+    got = host(lg)
+    eng.close()
+    kh, vh = _f64(k), _f64(v)
+    del k, v
+    log("decode full: oracle")
+    one = CFG.with_(n_layers=1)
+    one_exact = one.with_(dtype="f32")
+    E = w["embed"]
+    h0 = _f64(E[torch.as_tensor(toks, device=E.device).long()])[None]
+    h = {"bf16": h0, "exact": h0.copy()}
+    fn = _f64(w["final_norm"])
+    for l, lw in enumerate(w["layers"]):
+        lw64 = {"attn_norm": _f64(lw["attn_norm"]), "mlp_norm": _f64(lw["mlp_norm"]),
+                "w": {p: _f64(q) for p, q in lw["w"].items()},
+                "la": {p: _f64(q) for p, q in lw["la"].items()},
+                "lb": {p: _f64(q) for p, q in lw["lb"].items()}}
+        wl = {"final_norm": fn, "layers": [lw64]}
+        for key, cfg in (("bf16", one), ("exact", one_exact)):
+            cache = model.new_cache(cfg, 1, ctx + rows)
+            cache["k"][0, 0, :ctx] = kh[l]
+            cache["v"][0, 0, :ctx] = vh[l]
+            _, h[key] = model.forward(cfg, wl, None, pos[None], gate[None], cache, hidden_in=h[key],
+                                      want_logits=False)
+        if l % 6 == 5:
+            log(f"  oracle layer {l + 1}/{CFG.n_layers}")
+    head = {"final_norm": fn, "lm_head": _f64(w["lm_head"])}
+    ref = model.lm_logits(one, head, h["bf16"])[0]
+    ex = model.lm_logits(one_exact, head, h["exact"])[0]
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin)
+    err = np.abs(got[fin] - ref[fin])
+    noise = np.abs(ref[fin] - ex[fin])
+    gex = np.abs(got[fin] - ex[fin])
+    tol = max(3e-2, 2.0 * float(noise.max()))
+    log(f"  logits: max |gpu-oracle| {err.max():.3e} (bound {tol:.3e}); mean {err.mean():.2e}, "
+        f"|gpu-exact| {gex.mean():.2e}, |oracle-exact| {noise.mean():.2e}")
+    assert err.max() <= tol
+    assert err.mean() <= 1.5 * noise.mean()
+    assert gex.mean() <= 1.25 * noise.mean()

@@ -146,3 +146,46 @@ def test_large_m_rows_two_sequences():
         o = cache["k"][:, s, ctxs[s]:ctxs[s] + rows]
         assert np.all(np.abs(k - o) <= 2.0 ** -7 * np.abs(o) + 2e-3)
     eng.sync()
+
+
+def test_batch128_rows_sampled_sequences():
+    """2048 rows, the batch-128 decode launch configuration: 128 sequences of 16
+    rows against their own contexts (1024 down to 1024 - 7 * 127 keys), gates as
+    in a draft (slot 0 off).  At this height q|k|v runs 256 x 256 tiles, o and
+    down 256 x 128, gate/up paired 256 x 256, and the LoRA down-projections the
+    sliced large-M path.  A row's arithmetic does not depend on the other
+    sequences' rows, so the oracle runs on sampled sequences only."""
+    import torch
+    log("layer8b: 128 sequences x 16 rows")
+    w = synth.weights_numpy(CFG, 1001, with_embed=False)
+    n, rows = 128, 16
+    eng = engine(CFG, w, max_seqs=n, max_seq_len=CTX + 64, max_rows=n * rows)
+    ctxs = [CTX - 7 * s for s in range(n)]
+    sample = (0, 45, 127)
+    gen = torch.Generator(device="cuda").manual_seed(7301)
+    kept = {}
+    for s in range(n):
+        shape = (1, ctxs[s], CFG.n_kv_heads, CFG.head_dim)
+        kc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        vc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        eng.kv_import(s, kc, vc, pending=0)
+        if s in sample:
+            kept[s] = (host(kc.float())[0], host(vc.float())[0])
+    pos = np.stack([np.arange(c, c + rows) for c in ctxs]).astype(np.int32)
+    gate = (np.arange(n * rows).reshape(n, rows) % rows != 0).astype(np.uint8)
+    x = synth.normal(7401, (n, rows, CFG.d_model))
+    hid, _ = eng.forward(list(range(n)), rows, dev(pos.ravel()), dev(gate.ravel()),
+                         hidden_in=dev(x.reshape(-1, CFG.d_model)), want_hidden=True)
+    got = host(hid).reshape(n, rows, -1)
+    idx = list(sample)
+    cache = model.new_cache(CFG, len(idx), CTX + rows)
+    for i, s in enumerate(idx):
+        cache["k"][0, i, :ctxs[s]] = kept[s][0]
+        cache["v"][0, i, :ctxs[s]] = kept[s][1]
+    ex_cache = {"k": cache["k"].copy(), "v": cache["v"].copy()}
+    _, ref = model.forward(CFG, w, None, pos[idx], gate[idx], cache, hidden_in=x[idx],
+                           want_logits=False)
+    _, ex = model.forward(CFG.with_(dtype="f32"), w, None, pos[idx], gate[idx], ex_cache,
+                          hidden_in=x[idx], want_logits=False)
+    _check(got[idx], ref, ex, "128 x 16 rows")
+    eng.sync()
