@@ -580,7 +580,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   __shared__ float s_rs[BM];
 
-  const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  const int nsl = ((EPI == EPI_TFX || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
   const int total = nbm * nbn * nsl, per = (total + 7) / 8;
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= total) return;
@@ -614,7 +614,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   };
   // LoRA passes: one per segment of the tile that has an adapter
   int lseg[2] = {0, 0}, nls = 0;
-  if (a.r > 0) {
+  if (a.r > 0 && slice == 0) {
     const int s_lo = a.paired ? 0 : sg0, s_hi = a.paired ? 1 : sg0;
     for (int sgi = s_lo; sgi <= s_hi; ++sgi)
       if (a.seg[sgi].U && a.seg[sgi].Bl) lseg[nls++] = sgi;
@@ -753,6 +753,13 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
           for (int e = 0; e < 8; ++e) o[e] = (bf16)(g[e] / (1.0f + expf(-g[e])) * u[e]);
           const int col = c0 + (pass * TN) / 2 + cl;
           *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.out) + frag_off(m, col, a.ldo)) = o;
+        }
+      } else if (EPI == EPI_STORE_F32) {
+        if (m < a.M) {
+          float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)slice * a.slice_stride +
+                                                (size_t)m * a.ldo + c0 + pass * TN + cl);
+          o[0] = make_float4(fr[cl], fr[cl + 1], fr[cl + 2], fr[cl + 3]);
+          o[1] = make_float4(fr[cl + 4], fr[cl + 5], fr[cl + 6], fr[cl + 7]);
         }
       } else {
 #pragma unroll
@@ -944,6 +951,57 @@ __global__ void k_zero_i64(long long* p, size_t n) {
 
 }  // namespace
 
+// The residual epilogue of a K-split large-M product: row m, eight columns per
+// thread, x_new = resid + the slices' partial sums added in slice order; stores
+// x_new, the next norm's input bf16(x_new * g) (fragment-tiled) and adds the
+// workgroup's share of the row's x_new^2 to one bank of its fixed-point sum.
+__global__ void __launch_bounds__(256)
+k_resid_slices(const float* __restrict__ part, int n_slices, long long stride, int N,
+               float* __restrict__ resid, bf16* __restrict__ xg_out, const bf16* __restrict__ g_next,
+               long long* __restrict__ ss_out) {
+  __shared__ float s_sq[4];
+  const int m = blockIdx.y, col = (blockIdx.x * 256 + threadIdx.x) * 8;
+  float sq = 0.0f;
+  if (col < N) {
+    const size_t off = (size_t)m * N + col;
+    float4* r = reinterpret_cast<float4*>(resid + off);
+    const float4 r0 = r[0], r1 = r[1];
+    float xn[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    float v[8];
+    {
+      const float4* p = reinterpret_cast<const float4*>(part + off);
+      const float4 p0 = p[0], p1 = p[1];
+      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+    }
+    for (int sl = 1; sl < n_slices; ++sl) {
+      const float4* p = reinterpret_cast<const float4*>(part + (size_t)sl * stride + off);
+      const float4 p0 = p[0], p1 = p[1];
+      v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
+      v[4] += p1.x; v[5] += p1.y; v[6] += p1.z; v[7] += p1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xn[e] += v[e];
+    r[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
+    r[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += xn[e] * xn[e];
+    if (xg_out) {
+      const bf16x8 gg = load8(g_next + col);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)(xn[e] * (float)gg[e]);
+      *reinterpret_cast<bf16x8*>(xg_out + frag_off(m, col, N)) = o;
+    }
+  }
+  if (ss_out == nullptr) return;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+  if ((threadIdx.x & 63) == 0) s_sq[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0) ss_add(ss_out, m, blockIdx.x, s_sq[0] + s_sq[1] + s_sq[2] + s_sq[3]);
+}
+
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.kchunk <= 0 || a.K % a.kchunk || a.kchunk % 32 || a.r % 16) return hipErrorInvalidValue;
@@ -1004,7 +1062,7 @@ template <int BM, int BN, int WM, int WN, int TS, int EPI>
 hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int outc = a.paired ? BN / 2 : BN;
   const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
-  const int nsl = (EPI == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  const int nsl = ((EPI == EPI_TFX || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
   const int grid = (nbm * nbn * nsl + 7) / 8 * 8;
   constexpr size_t smem = tile_smem_bytes<BM, BN, WM, WN, TS>();
   if (smem > 64 * 1024) {
@@ -1048,6 +1106,38 @@ constexpr int kTileTS3 = UNO_TILE_TS3;        // ring depth of the 128 x 128 til
 #define UNO_TILE_TALL_FIRST 0
 #endif
 constexpr bool kTileTallFirst = UNO_TILE_TALL_FIRST;   // 128 x 256 before 256 x 128
+
+// A residual product whose 256 x 256 tiles number at least 128 but fewer than
+// kTileMinWG: two K slices of those tiles store float partials in the caller's
+// workspace (twice the workgroups), then k_resid_slices adds them and runs the
+// residual epilogue (measured at 2048 rows, the o and down projections of the 8B
+// shape: faster than 256 x 128 tiles without a split).  False: not applicable.
+bool launch_resid_split(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
+  constexpr int S = 2;
+  if (a.epi != EPI_RESID || !a.split_ws || a.paired || a.nseg != 1) return false;
+  if ((a.K / 32) % (S * TKB) || (a.r / 32) % TKB || a.ldo != n_cols_total || n_cols_total % 8) return false;
+  if (a.seg[0].Ufx && a.seg[0].Bl) return false;
+  if (!tile_fits(a, n_cols_total, 256)) return false;
+  const long tiles = (long)((a.M + 255) / 256) * (n_cols_total / 256);
+  if (tiles < 128 || tiles >= kTileMinWG) return false;
+  const long long stride = (long long)a.M * n_cols_total;
+  if (S * stride > a.split_cap) return false;
+  GemmArgs b = a;
+  b.epi = EPI_STORE_F32;
+  b.out = a.split_ws;
+  b.k_slices = S;
+  b.slice_stride = stride;
+  b.resid = nullptr;
+  b.xg_out = nullptr;
+  b.ss_out = nullptr;
+  *err = run_tile<UNO_TILE_CFG0, EPI_STORE_F32>(b, n_cols_total, s);
+  if (*err != hipSuccess) return true;
+  uno_launch(k_resid_slices, dim3((n_cols_total / 8 + 255) / 256, a.M), 256, 0, s, a.split_ws, S, stride,
+             n_cols_total, a.resid, reinterpret_cast<bf16*>(a.xg_out), reinterpret_cast<const bf16*>(a.g_next),
+             a.ss_out);
+  *err = hipGetLastError();
+  return true;
+}
 
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
   if (a.K % 32 || a.r % 32) return false;
@@ -1131,6 +1221,7 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   if (a.epi == EPI_QKV && (a.kv.head_dim % 16 != 0)) return hipErrorInvalidValue;
   if (a.M >= 64) {
     hipError_t e;
+    if (launch_resid_split(a, n_cols_total, s, &e)) return e;
     if (launch_tile(a, n_cols_total, s, &e)) return e;
   }
   const int mtiles = (a.M + 15) / 16;

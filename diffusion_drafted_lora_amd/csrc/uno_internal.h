@@ -256,10 +256,15 @@ struct GemmArgs {
   KvLayout kv;
   int32_t layer;
   int32_t* err;
-  // EPI_TFX (large-M kernel): K is split into k_slices equal slices, slice s
-  // storing its partial sum at out + s * slice_stride (int64 elements)
+  // EPI_TFX / EPI_STORE_F32 (large-M kernel): K is split into k_slices equal
+  // slices, slice s storing its partial sum at out + s * slice_stride (int64 /
+  // float elements); only slice 0 adds the LoRA stages
   int32_t k_slices;
   long long slice_stride;
+  // EPI_RESID at large M: float workspace of split_cap elements that a K-split
+  // launch may use for its partial sums (null: never split)
+  float* split_ws;
+  long long split_cap;
 };
 
 // LoRA down-projection of a group of projections sharing one input:

@@ -511,6 +511,12 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     UNO_HIP(c, launch_gemm<T>(a, ncols, s));
     return UNO_OK;
   };
+  // the attention partials are free between a layer's combine and the next
+  // layer's attention: the o and down products may split K into them
+  auto split_ws = [&](GemmArgs& a) {
+    a.split_ws = c->at<float>(c->L.part_o);
+    a.split_cap = (long long)R * Hq * kMaxChunks * hd;
+  };
   auto norm_in = [&](GemmArgs& a, int ss_idx) {
     a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
   };
@@ -653,6 +659,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       clear(a, 0, 3 * r);
       a.epi = EPI_RESID; a.ldo = d; a.resid = x;
       a.xg_out = xg; a.g_next = c->mlp_norm[l]; a.ss_out = SS(2 * l + 1);
+      split_ws(a);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
     // --- MLP block
@@ -684,6 +691,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.xg_out = xg;
       a.g_next = (l + 1 < L) ? c->attn_norm[l + 1] : c->final_norm;
       a.ss_out = SS(2 * l + 2);
+      split_ws(a);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
   }
