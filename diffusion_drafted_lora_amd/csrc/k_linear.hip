@@ -609,8 +609,9 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   // weight row block of B block bi (16 rows) and its segment
   const int sg0 = a.paired ? 0 : find_seg(a, c0);
   auto bseg = [&](int bi) { return a.paired ? (bi & 1) : sg0; };
+  const int last_rb = (a.paired ? a.seg[0].N : a.seg[sg0].N) / 16 - 1;
   auto brb = [&](int bi) {
-    return a.paired ? c0 / 16 + (bi >> 1) : (c0 - a.seg[sg0].n0) / 16 + bi;
+    return min(a.paired ? c0 / 16 + (bi >> 1) : (c0 - a.seg[sg0].n0) / 16 + bi, last_rb);
   };
   // LoRA passes: one per segment of the tile that has an adapter
   int lseg[2] = {0, 0}, nls = 0;
@@ -764,7 +765,9 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) { v[e] = fr[cl + e]; vp[e] = fr[(cl ^ 8) + e]; }
-        rsq[k] += epilogue8<EPI>(a, m, c0 + pass * TN + cl, v, vp, m < a.M);
+        const int col = c0 + pass * TN + cl;
+        const bool in_cols = EPI != EPI_LOGITS || col < a.n_tiles * 16;
+        rsq[k] += epilogue8<EPI>(a, m, col, v, vp, m < a.M && in_cols);
       }
     }
     __syncthreads();
@@ -1061,7 +1064,7 @@ hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s) {
 template <int BM, int BN, int WM, int WN, int TS, int EPI>
 hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int outc = a.paired ? BN / 2 : BN;
-  const int nbm = (a.M + BM - 1) / BM, nbn = n_cols_total / outc;
+  const int nbm = (a.M + BM - 1) / BM, nbn = (n_cols_total + outc - 1) / outc;
   const int nsl = ((EPI == EPI_TFX || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
   const int grid = (nbm * nbn * nsl + 7) / 8 * 8;
   constexpr size_t smem = tile_smem_bytes<BM, BN, WM, WN, TS>();
@@ -1076,6 +1079,11 @@ hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
 
 bool tile_fits(const GemmArgs& a, int n_cols_total, int BN) {
   const int outc = a.paired ? BN / 2 : BN;
+  // logits of one segment may end in a ragged tile (its missing weight rows are
+  // never stored: the kernel re-reads the last row block and drops the columns)
+  if (a.epi == EPI_LOGITS && !a.paired && a.nseg == 1 && a.seg[0].n0 == 0 &&
+      a.seg[0].N == n_cols_total && n_cols_total % 16 == 0)
+    return true;
   if (n_cols_total % outc) return false;
   if (!a.paired)
     for (int i = 0; i < a.nseg; ++i)
@@ -1149,7 +1157,7 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
   if (a.paired != (a.epi == EPI_SWIGLU)) return false;
   auto blocks = [&](int BM, int BN) {
     const int outc = a.paired ? BN / 2 : BN;
-    return (long)((a.M + BM - 1) / BM) * (n_cols_total / outc) * nsl;
+    return (long)((a.M + BM - 1) / BM) * ((n_cols_total + outc - 1) / outc) * nsl;
   };
   // the largest tile that still gives three quarters of the CUs a workgroup (the
   // 256-row tiles fill a CU's LDS alone), else the largest that gives half of
