@@ -570,6 +570,9 @@ template <int BM, int BN, int WM, int WN, int TS, int EPI>
 __global__ void __launch_bounds__(64 * WM * WN)
 k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   constexpr int NTH = 64 * WM * WN, TM = BM / WM, TN = BN / WN, NW = WM * WN;
+  // gate/up pairs are interleaved in exactly the SwiGLU instantiations (the
+  // launcher rejects any other combination)
+  constexpr bool PAIRED = EPI == EPI_SWIGLU;
   constexpr int NBA = BM / 16, NBB = BN / 16, NBS = NBA + NBB;    // blocks per K block
   constexpr int NB = NBS * TKB;                                   // blocks per stage
   static_assert(NB % NW == 0, "every wave issues the same number of block loads");
@@ -587,7 +590,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   const int slice = t / (nbm * nbn), tt = t % (nbm * nbn);
   const int nb = tt / nbm, mb = tt % nbm;
   const int m0 = mb * BM;
-  const int outc = a.paired ? BN / 2 : BN;
+  const int outc = PAIRED ? BN / 2 : BN;
   const int c0 = nb * outc;
   // the wave index is uniform: as a scalar it keeps the block addressing in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -607,18 +610,33 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   if (a.ss_in && tid < BM) s_rs[tid] = rs_of(a, m0 + tid);
 
   // weight row block of B block bi (16 rows) and its segment
-  const int sg0 = a.paired ? 0 : find_seg(a, c0);
-  auto bseg = [&](int bi) { return a.paired ? (bi & 1) : sg0; };
-  const int last_rb = (a.paired ? a.seg[0].N : a.seg[sg0].N) / 16 - 1;
+  const int sg0 = PAIRED ? 0 : find_seg(a, c0);
+  const int last_rb = (PAIRED ? a.seg[0].N : a.seg[sg0].N) / 16 - 1;
   auto brb = [&](int bi) {
-    return min(a.paired ? c0 / 16 + (bi >> 1) : (c0 - a.seg[sg0].n0) / 16 + bi, last_rb);
+    return min(PAIRED ? c0 / 16 + (bi >> 1) : (c0 - a.seg[sg0].n0) / 16 + bi, last_rb);
   };
-  // LoRA passes: one per segment of the tile that has an adapter
-  int lseg[2] = {0, 0}, nls = 0;
+  // Operand pointers as scalars (segments 0 and 1 when paired, the tile's segment
+  // otherwise): nothing below indexes a.seg with a runtime value, which would make
+  // the compiler copy the argument block into scratch.
+  const bf16* const W0 = reinterpret_cast<const bf16*>(a.seg[sg0].W);
+  const bf16* const W1 = PAIRED ? reinterpret_cast<const bf16*>(a.seg[1].W) : W0;
+  const bf16* const B0 = reinterpret_cast<const bf16*>(a.seg[sg0].Bl);
+  const bf16* const B1 = PAIRED ? reinterpret_cast<const bf16*>(a.seg[1].Bl) : B0;
+  // LoRA passes: one per segment of the tile that has an adapter (pass p reads the
+  // intermediate U_p at block column ucol_p of a row of ldu_p blocks)
+  int lseg0 = 0, lseg1 = 0, nls = 0;
+  const bf16 *U0 = nullptr, *U1 = nullptr;
+  int ldu0 = 0, ldu1 = 0, uc0 = 0, uc1 = 0;
   if (a.r > 0 && slice == 0) {
-    const int s_lo = a.paired ? 0 : sg0, s_hi = a.paired ? 1 : sg0;
-    for (int sgi = s_lo; sgi <= s_hi; ++sgi)
-      if (a.seg[sgi].U && a.seg[sgi].Bl) lseg[nls++] = sgi;
+#pragma unroll
+    for (int k = 0; k < (PAIRED ? 2 : 1); ++k) {
+      const GemmSeg& g = PAIRED ? a.seg[k] : a.seg[sg0];
+      if (g.U && g.Bl) {
+        if (nls == 0) { lseg0 = PAIRED ? k : sg0; U0 = reinterpret_cast<const bf16*>(g.U); ldu0 = g.ldu / 32; uc0 = g.ucol / 32; }
+        else { lseg1 = k; U1 = reinterpret_cast<const bf16*>(g.U); ldu1 = g.ldu / 32; uc1 = g.ucol / 32; }
+        ++nls;
+      }
+    }
   }
   const int n_base = nkb / TKB, spp = nrb / TKB;       // base stages, stages per LoRA pass
   const int nst = n_base + nls * spp;
@@ -626,24 +644,22 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   // block loads of stage st into ring slot `slot`: wave w loads blocks w * P .. + P - 1
   auto issue = [&](int st, int slot) {
     const int ls = st - n_base, pass = ls >= 0 ? ls / spp : 0;
-    const int sgl = lseg[pass];
+    const bf16* const Up = pass == 0 ? U0 : U1;
+    const int ldu = pass == 0 ? ldu0 : ldu1, uc = pass == 0 ? uc0 : uc1;
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       const int bb = w * P + q, kk = bb / NBS, b = bb % NBS;
       const int mrow = min(m0 / 16 + b, mblocks - 1);
+      const bool odd = PAIRED && ((b - NBA) & 1);      // the up half of a gate/up pair
       const bf16* src;
       if (ls < 0) {
         const int kb = kb0 + st * TKB + kk;
         if (b < NBA) src = reinterpret_cast<const bf16*>(a.X) + ((size_t)mrow * nkb_all + kb) * 512;
-        else src = reinterpret_cast<const bf16*>(a.seg[bseg(b - NBA)].W) +
-                   ((size_t)brb(b - NBA) * nkb_all + kb) * 512;
+        else src = (odd ? W1 : W0) + ((size_t)brb(b - NBA) * nkb_all + kb) * 512;
       } else {
         const int jr = (ls % spp) * TKB + kk;
-        const GemmSeg& S = a.seg[sgl];
-        if (b < NBA) src = reinterpret_cast<const bf16*>(S.U) +
-                           ((size_t)mrow * (S.ldu / 32) + S.ucol / 32 + jr) * 512;
-        else src = reinterpret_cast<const bf16*>(a.seg[bseg(b - NBA)].Bl) +
-                   ((size_t)brb(b - NBA) * nrb + jr) * 512;
+        if (b < NBA) src = Up + ((size_t)mrow * ldu + uc + jr) * 512;
+        else src = (odd ? B1 : B0) + ((size_t)brb(b - NBA) * nrb + jr) * 512;
       }
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + lane * 8),
                                        (lds_void_t*)(smem_raw + (slot * NB + bb) * 1024), 16, 0, 0);
@@ -682,7 +698,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
     if (st + TS - 1 < nst) issue(st + TS - 1, (st + TS - 1) % TS);
     if (st == n_base) scale_rows();
     // in a paired LoRA pass only the wave's column blocks of that segment take part
-    const int lsg = st >= n_base ? lseg[(st - n_base) / spp] : -1;
+    const int lsg = st < n_base ? -1 : (st - n_base) / spp == 0 ? lseg0 : lseg1;
 #pragma unroll
     for (int kk = 0; kk < TKB; ++kk) {
       const char* base = smem_raw + ((st % TS) * NB + kk * NBS) * 1024 + lane * 16;
@@ -693,12 +709,19 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
 #pragma unroll
       for (int j = 0; j < TN / 16; ++j)
         bfr[j] = *reinterpret_cast<const bf16x8*>(base + (NBA + wn * (TN / 16) + j) * 1024);
+      // a paired LoRA pass adds its intermediate times the LoRA-up rows of its own
+      // segment only: the other segment's column blocks (odd / even j, TN / 16 is
+      // even) multiply a zero fragment, so the MFMA block stays branch-free
+      if (PAIRED && lsg >= 0) {
+#pragma unroll
+        for (int j = 0; j < TN / 16; ++j)
+          if ((j & 1) != lsg) bfr[j] = bf16x8{};
+      }
 #pragma unroll
       for (int i = 0; i < TM / 16; ++i)
 #pragma unroll
         for (int j = 0; j < TN / 16; ++j)
-          if (lsg < 0 || !a.paired || ((wn * (TN / 16) + j) & 1) == lsg)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
   if (nst == n_base) scale_rows();
