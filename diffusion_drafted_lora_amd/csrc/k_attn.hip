@@ -257,6 +257,11 @@ k_attn_combine(AttnArgs a, int hd) {
 #endif
 constexpr int MK = UNO_ATTN_MK;   // keys per sub-chunk
 static_assert(MK == 32 || MK == 64, "sub-chunks of 32 or 64 keys");
+#ifndef UNO_ATTN_PF
+#define UNO_ATTN_PF 2
+#endif
+constexpr int PFD = UNO_ATTN_PF;  // sub-chunks fetched ahead (register sets in turn)
+static_assert(PFD == 1 || PFD == 2, "prefetch one or two sub-chunks ahead");
 constexpr int HD = 128;           // head dim of the MFMA path
 constexpr int KPAD = HD + 8;      // LDS row of K (bf16), 16-byte pad
 constexpr int VPAD = MK + 8;      // LDS row of V^T (bf16)
@@ -425,16 +430,16 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
       lo = min(lo, Ct + b - At);
       hi = max(hi, Ct + kend - 1 - At);
     }
-    // (sub-chunks 0 and 1 are fetched below, before the copy is published, so
-    // a chunk of at most two sub-chunks never reads it)
-    if (hi >= lo && lo >= 0 && kend - kbeg > 2 * MK) {
+    // (the first PFD sub-chunks are fetched below, before the copy is published,
+    // so a chunk of at most PFD sub-chunks never reads it)
+    if (hi >= lo && lo >= 0 && kend - kbeg > PFD * MK) {
       const int p0 = lo >> psh, p1 = hi >> psh;
       if (p1 - p0 + 1 <= PGC) { pl = p0; npg_all = p1 - p0 + 1; }
     }
     for (int i = tid; i < npg_all; i += nthr) sPg[i] = bt_page((pl + i) << psh);
   }
   if (!causal) fetch(kbeg, pkA, pvA);
-  if (kbeg + MK < kend) fetch(kbeg + MK, pkB, pvB);
+  if (PFD == 2 && kbeg + MK < kend) fetch(kbeg + MK, pkB, pvB);
   npg = npg_all;
   int ra[4], rc[4], rd[4], lim[4];
 #pragma unroll
@@ -446,7 +451,10 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   }
   for (int k0 = kbeg, it = 0; k0 < kend; k0 += MK, ++it) {
     __syncthreads();               // previous sub-chunk fully consumed
-    if (it & 1) {
+    if (PFD == 1) {
+      stage(k0, pkA, pvA);
+      if (k0 + MK < kend) fetch(k0 + MK, pkA, pvA);
+    } else if (it & 1) {
       stage(k0, pkB, pvB);
       if (k0 + 2 * MK < kend) fetch(k0 + 2 * MK, pkB, pvB);
     } else {

@@ -547,7 +547,10 @@ UNO_DEV float epilogue8(const GemmArgs& a, int m, int col, const float* v, const
 // serves that W tile to every row block).  The epilogue runs from the
 // accumulators: in the MFMA layout the 16 lanes of a row group hold 16
 // consecutive columns of one row, which is the epilogue's row group.
-constexpr int TKB = 2;    // 32-wide K blocks per stage
+#ifndef UNO_TILE_TKB
+#define UNO_TILE_TKB 2
+#endif
+constexpr int TKB = UNO_TILE_TKB;    // 32-wide K blocks per stage
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
