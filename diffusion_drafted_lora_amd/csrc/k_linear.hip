@@ -1042,7 +1042,7 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s) {
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err);
 
 // Large-M LoRA down-projection: the tile kernel with K split into k_slices
-// slices (a power of two up to 16, aiming at four workgroups per CU), each slice
+// slices (a power of two up to 8, aiming at four workgroups per CU), each slice
 // storing its fixed-point partial; k_lora_u adds them.
 #ifndef UNO_LORA_TILE_TARGET
 #define UNO_LORA_TILE_TARGET 1024
@@ -1050,7 +1050,9 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
 int lora_down_tile_slices(int M, int K, int ncols) {
   const long tiles = (long)((M + 127) / 128) * (ncols / 128);
   int S = 1;
-  while (S < 16 && tiles * S < UNO_LORA_TILE_TARGET && (K / 32) % (2 * S) == 0 && K / 32 / (2 * S) >= 4)
+  // at most 8 slices: at 2048 rows 16 slices of int64 partials cost more traffic
+  // than their extra workgroups gain
+  while (S < 8 && tiles * S < UNO_LORA_TILE_TARGET && (K / 32) % (2 * S) == 0 && K / 32 / (2 * S) >= 4)
     S *= 2;
   return S;
 }
