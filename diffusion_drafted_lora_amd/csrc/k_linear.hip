@@ -1235,6 +1235,9 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
 #ifndef UNO_SK_O
 #define UNO_SK_O 1, 12, 2
 #endif
+#ifndef UNO_SK_LMHEAD
+#define UNO_SK_LMHEAD 2, 4, 8
+#endif
 #ifndef UNO_SK_DOWN
 #define UNO_SK_DOWN 1, 12, 2
 #endif
@@ -1265,13 +1268,13 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   // Launch shapes measured at the 8B decode shapes (one MI355X): many small
   // workgroups beat few large ones -- the paired gate/up tiles at 4 waves of 4
   // blocks in flight, q|k|v at 8 waves of 2, o at 12 of 2, down at 12 of 2, the LM
-  // head at two 16-column tiles per workgroup of 8 waves of 8.
+  // head at two 16-column tiles per workgroup of 4 waves of 8.
   if (a.paired) {
     if (nkb >= 64) return launch_skinny<UNO_SK_GATEUP>(a, n_cols_total, mtiles, s);
     return launch_skinny<2, 4, 1>(a, n_cols_total, mtiles, s);
   }
   if (a.epi == EPI_LOGITS && n_cols_total % 32 == 0 && a.nseg == 1 && nkb >= 32)
-    return launch_skinny<2, 8, 8>(a, n_cols_total, mtiles, s);
+    return launch_skinny<UNO_SK_LMHEAD>(a, n_cols_total, mtiles, s);
   if (nkb >= 64) {
     if (a.epi == EPI_QKV) return launch_skinny<UNO_SK_QKV>(a, n_cols_total, mtiles, s);
     if (nkb >= 256) return launch_skinny<UNO_SK_DOWN>(a, n_cols_total, mtiles, s);
