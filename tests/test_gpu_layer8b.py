@@ -148,20 +148,23 @@ def test_large_m_rows_two_sequences():
     eng.sync()
 
 
-def test_batch128_rows_sampled_sequences():
+@pytest.mark.parametrize("n", [128, 125])
+def test_batch128_rows_sampled_sequences(n):
     """2048 rows, the batch-128 decode launch configuration: 128 sequences of 16
     rows against their own contexts (1024 down to 1024 - 7 * 127 keys), gates as
     in a draft (slot 0 off).  At this height q|k|v runs 256 x 256 tiles, o and
-    down 256 x 128, gate/up paired 256 x 256, and the LoRA down-projections the
-    sliced large-M path.  A row's arithmetic does not depend on the other
-    sequences' rows, so the oracle runs on sampled sequences only."""
+    down split K in two over 256 x 256 tiles (then the slice-sum residual pass),
+    gate/up paired 256 x 256, and the LoRA down-projections the sliced large-M
+    path.  125 sequences (2000 rows) take the same paths with a ragged last
+    256-row tile.  A row's arithmetic does not depend on the other sequences'
+    rows, so the oracle runs on sampled sequences only."""
     import torch
-    log("layer8b: 128 sequences x 16 rows")
+    log(f"layer8b: {n} sequences x 16 rows")
     w = synth.weights_numpy(CFG, 1001, with_embed=False)
-    n, rows = 128, 16
+    rows = 16
     eng = engine(CFG, w, max_seqs=n, max_seq_len=CTX + 64, max_rows=n * rows)
     ctxs = [CTX - 7 * s for s in range(n)]
-    sample = (0, 45, 127)
+    sample = (0, 45, n - 1)
     gen = torch.Generator(device="cuda").manual_seed(7301)
     kept = {}
     for s in range(n):
@@ -187,5 +190,5 @@ def test_batch128_rows_sampled_sequences():
                            want_logits=False)
     _, ex = model.forward(CFG.with_(dtype="f32"), w, None, pos[idx], gate[idx], ex_cache,
                           hidden_in=x[idx], want_logits=False)
-    _check(got[idx], ref, ex, "128 x 16 rows")
+    _check(got[idx], ref, ex, f"{n} x 16 rows")
     eng.sync()
