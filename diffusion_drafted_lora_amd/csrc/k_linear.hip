@@ -586,7 +586,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   __shared__ float s_rs[BM];
 
-  const int nsl = ((EPI == EPI_TFX || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
+  const int nsl = ((EPI == EPI_TSLICE || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
   const int total = nbm * nbn * nsl, per = (total + 7) / 8;
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= total) return;
@@ -758,15 +758,12 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
       const int it = tid + NTH * k, row = it / IPR, cl = (it % IPR) * 8, m = m0 + row;
       const float* fr = sC + row * TNP;
       float v[8], vp[8];
-      if (EPI == EPI_TFX) {
+      if (EPI == EPI_TSLICE || EPI == EPI_STORE_F32) {
         if (m < a.M) {
-          i64x2* o = reinterpret_cast<i64x2*>(reinterpret_cast<long long*>(a.out) +
-                                              (size_t)slice * a.slice_stride + (size_t)m * a.ldo +
-                                              c0 + pass * TN + cl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = i64x2{(long long)llrintf(fr[cl + 2 * e] * LORA_FX_SCALE),
-                         (long long)llrintf(fr[cl + 2 * e + 1] * LORA_FX_SCALE)};
+          float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)slice * a.slice_stride +
+                                                (size_t)m * a.ldo + c0 + pass * TN + cl);
+          o[0] = make_float4(fr[cl], fr[cl + 1], fr[cl + 2], fr[cl + 3]);
+          o[1] = make_float4(fr[cl + 4], fr[cl + 5], fr[cl + 6], fr[cl + 7]);
         }
       } else if (EPI == EPI_SWIGLU) {
         // slice column pairs: 16 gate | 16 up per 16 outputs
@@ -780,13 +777,6 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
           for (int e = 0; e < 8; ++e) o[e] = (bf16)(g[e] / (1.0f + expf(-g[e])) * u[e]);
           const int col = c0 + (pass * TN) / 2 + cl;
           *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.out) + frag_off(m, col, a.ldo)) = o;
-        }
-      } else if (EPI == EPI_STORE_F32) {
-        if (m < a.M) {
-          float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)slice * a.slice_stride +
-                                                (size_t)m * a.ldo + c0 + pass * TN + cl);
-          o[0] = make_float4(fr[cl], fr[cl + 1], fr[cl + 2], fr[cl + 3]);
-          o[1] = make_float4(fr[cl + 4], fr[cl + 5], fr[cl + 6], fr[cl + 7]);
         }
       } else {
 #pragma unroll
@@ -945,7 +935,7 @@ k_lora_down(LoraDownArgs a) {
 // Sum of the K-slice partials of the large-M down-projection, gated and scaled to
 // the bf16 operand of the LoRA up-projection: eight columns per thread.
 __global__ void __launch_bounds__(256)
-k_lora_u(const long long* __restrict__ t, int n_slices, long long stride, int M, int ncols,
+k_lora_u(const float* __restrict__ t, int n_slices, long long stride, int M, int ncols,
          const uint8_t* __restrict__ gate, float scale, bf16* __restrict__ u) {
   const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
   const int per_row = ncols / 8;
@@ -954,20 +944,19 @@ k_lora_u(const long long* __restrict__ t, int n_slices, long long stride, int M,
   const size_t off = (size_t)m * ncols + c;
   bf16x8 o = {};
   if (gate == nullptr || gate[m] != 0) {
-    i64x2 acc[4];
-    const i64x2* p = reinterpret_cast<const i64x2*>(t + off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = p[e];
+    float acc[8];
+    const float4* p = reinterpret_cast<const float4*>(t + off);
+    const float4 p0 = p[0], p1 = p[1];
+    acc[0] = p0.x; acc[1] = p0.y; acc[2] = p0.z; acc[3] = p0.w;
+    acc[4] = p1.x; acc[5] = p1.y; acc[6] = p1.z; acc[7] = p1.w;
     for (int sl = 1; sl < n_slices; ++sl) {
-      const i64x2* q = reinterpret_cast<const i64x2*>(t + (size_t)sl * stride + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += q[e];
+      const float4* q = reinterpret_cast<const float4*>(t + (size_t)sl * stride + off);
+      const float4 q0 = q[0], q1 = q[1];
+      acc[0] += q0.x; acc[1] += q0.y; acc[2] += q0.z; acc[3] += q0.w;
+      acc[4] += q1.x; acc[5] += q1.y; acc[6] += q1.z; acc[7] += q1.w;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (bf16)(scale * fx_to_float(acc[e].x));
-      o[2 * e + 1] = (bf16)(scale * fx_to_float(acc[e].y));
-    }
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)(scale * acc[e]);
   }
   *reinterpret_cast<bf16x8*>(u + frag_off(m, c, ncols)) = o;
 }
@@ -1057,7 +1046,7 @@ int lora_down_tile_slices(int M, int K, int ncols) {
   return S;
 }
 
-hipError_t launch_lora_u(const long long* t, int n_slices, long long stride, int M, int ncols,
+hipError_t launch_lora_u(const float* t, int n_slices, long long stride, int M, int ncols,
                          const uint8_t* gate, float scale, bf16* u, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (ncols % 8 || n_slices < 1) return hipErrorInvalidValue;
@@ -1072,7 +1061,7 @@ bool lora_down_tile_fits(int M, int K, int ncols, int k_slices) {
 }
 
 hipError_t launch_lora_down_tile(const GemmArgs& a, int ncols, hipStream_t s) {
-  if (a.epi != EPI_TFX || a.r != 0 || !lora_down_tile_fits(a.M, a.K, ncols, a.k_slices))
+  if (a.epi != EPI_TSLICE || a.r != 0 || !lora_down_tile_fits(a.M, a.K, ncols, a.k_slices))
     return hipErrorInvalidValue;
   hipError_t e;
   if (!launch_tile(a, ncols, s, &e)) return hipErrorInvalidValue;
@@ -1093,7 +1082,7 @@ template <int BM, int BN, int WM, int WN, int TS, int EPI>
 hipError_t run_tile(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   const int outc = a.paired ? BN / 2 : BN;
   const int nbm = (a.M + BM - 1) / BM, nbn = (n_cols_total + outc - 1) / outc;
-  const int nsl = ((EPI == EPI_TFX || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
+  const int nsl = ((EPI == EPI_TSLICE || EPI == EPI_STORE_F32) && a.k_slices > 1) ? a.k_slices : 1;
   const int grid = (nbm * nbn * nsl + 7) / 8 * 8;
   constexpr size_t smem = tile_smem_bytes<BM, BN, WM, WN, TS>();
   if (smem > 64 * 1024) {
@@ -1177,7 +1166,7 @@ bool launch_resid_split(const GemmArgs& a, int n_cols_total, hipStream_t s, hipE
 
 bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
   if (a.K % 32 || a.r % 32) return false;
-  const int nsl = (a.epi == EPI_TFX && a.k_slices > 1) ? a.k_slices : 1;
+  const int nsl = (a.epi == EPI_TSLICE && a.k_slices > 1) ? a.k_slices : 1;
   if (a.K % (32 * nsl) || (a.K / 32 / nsl) % TKB || (a.r / 32) % TKB) return false;
   // the tile kernel takes its LoRA intermediate as fragment-tiled bf16 only
   for (int i = 0; i < a.nseg; ++i)
@@ -1220,7 +1209,7 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
     UNO_TILE_EPI(EPI_SWIGLU)
     UNO_TILE_EPI(EPI_LOGITS)
     UNO_TILE_EPI(EPI_QKV)
-    UNO_TILE_EPI(EPI_TFX)
+    UNO_TILE_EPI(EPI_TSLICE)
     default: return false;
   }
 #undef UNO_TILE_EPI

@@ -169,7 +169,7 @@ enum GemmEpi : int32_t {
   EPI_RESID = 2,       // resid[m, n] += acc
   EPI_SWIGLU = 3,      // out_t[m, n] = T(silu(acc_gate) * acc_up)    (paired segments)
   EPI_LOGITS = 4,      // out_f32[m, n] = acc (MASK column -inf) + per-tile max / sum-exp
-  EPI_TFX = 6,         // out_i64[slice][m, n] = acc in 2^-32 fixed point (LoRA down, large M)
+  EPI_TSLICE = 6,      // out_f32[slice][m, n] = acc of K slice `slice` (LoRA down, large M)
 };
 
 // LoRA intermediates accumulated in fixed point: t = sum x*A in units of 2^-32
@@ -256,9 +256,9 @@ struct GemmArgs {
   KvLayout kv;
   int32_t layer;
   int32_t* err;
-  // EPI_TFX / EPI_STORE_F32 (large-M kernel): K is split into k_slices equal
-  // slices, slice s storing its partial sum at out + s * slice_stride (int64 /
-  // float elements); only slice 0 adds the LoRA stages
+  // EPI_TSLICE / EPI_STORE_F32 (large-M kernel): K is split into k_slices equal
+  // slices, slice s storing its float partial sum at out + s * slice_stride
+  // elements; only slice 0 adds the LoRA stages
   int32_t k_slices;
   long long slice_stride;
   // EPI_RESID at large M: float workspace of split_cap elements that a K-split
@@ -280,7 +280,7 @@ struct LoraDownArgs {
   float inv_d, eps;
 };
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
-// Large-M LoRA down-projection on the tile kernel (EPI_TFX, no atomics): false
+// Large-M LoRA down-projection on the tile kernel (EPI_TSLICE, no atomics): false
 // when no tile shape fits the problem (the atomic kernel then serves it).
 bool lora_down_tile_fits(int M, int K, int ncols, int k_slices);
 int lora_down_tile_slices(int M, int K, int ncols);
@@ -288,7 +288,7 @@ hipError_t launch_lora_down_tile(const GemmArgs& a, int ncols, hipStream_t s);
 // u[m, c] = gate[m] ? bf16(scale * sum_s t[s][m, c] * 2^-32) : 0 over the K-slice
 // partials of the large-M down-projection ([M, ncols] each, `stride` apart); u is
 // fragment-tiled [round16(M), ncols]
-hipError_t launch_lora_u(const long long* t, int n_slices, long long stride, int M, int ncols,
+hipError_t launch_lora_u(const float* t, int n_slices, long long stride, int M, int ncols,
                          const uint8_t* gate, float scale, bf16* u, hipStream_t s);
 hipError_t launch_zero_i64(long long* p, size_t n, hipStream_t s);
 

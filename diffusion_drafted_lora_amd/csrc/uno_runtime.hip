@@ -89,8 +89,8 @@ Layout make_layout(const uno_config& c) {
   L.obuf = take(round16(R) * q * ts);
   L.hbuf = take(round16(R) * F * ts);
   L.ubuf = take(round16(R) * 3 * r * ts + 16);
-  // four fixed-point LoRA intermediates, each with room for up to TFX_SLICES
-  // K-slice partials of the large-M down-projection
+  // four LoRA intermediates: fixed-point words (few rows, atomics) or room for
+  // up to tfx_slices float K-slice partials each (the large-M down-projection)
   L.tfx = take(4 * R * 3 * r * tfx_slices(R) * 8 + 16);
   static_assert(sizeof(long long) == 8, "fixed-point words");
   L.ss = take((size_t)(2 * c.n_layers + 1) * R * SS_BANKS * 8);   // fixed-point sums of x^2
@@ -462,9 +462,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   long long* ssb = c->at<long long>(c->L.ss);
   auto SS = [&](int i) { return ssb + (size_t)i * R * SS_BANKS; };
   // LoRA down-projection of each group (buffer b): qkv, o, gate/up, down.  Large M
-  // (every group fits the tile kernel): tsl[b] K-slice partials stored into the
-  // tfx region, summed, gated and scaled into ubuf -- no atomics, nothing to
-  // clear.  Few rows: integer atomics into buffer b, cleared by a later kernel.
+  // (every group fits the tile kernel): tsl[b] K-slice float partials stored into
+  // the tfx region, summed in slice order, gated and scaled into ubuf -- no
+  // atomics, nothing to clear.  Few rows: integer atomics into buffer b, cleared by a later kernel.
   const int gK[4] = {d, qd, d, F}, gN[4] = {3 * r, r, 2 * r, r};
   long long* tfx = c->at<long long>(c->L.tfx);
   const size_t tcap = (size_t)c->cfg.max_rows * 3 * r * tfx_slices(c->cfg.max_rows) * 4;
@@ -538,15 +538,15 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       }
       if (ss_idx >= 0) norm_in(a, ss_idx);
       const int nc = nproj * r;
-      a.epi = EPI_TFX; a.ldo = nc; a.out = tfx;
+      a.epi = EPI_TSLICE; a.ldo = nc; a.out = tfx;
       a.k_slices = tsl[buf]; a.slice_stride = (long long)R * nc;
       double b, fl;
       gemm_cost(a, nc, sizeof(T), &b, &fl);
       // slices written, then read back with the gates; u written
-      b += (double)R * nc * 8 * tsl[buf] * 2 + (double)R + (double)R * nc * sizeof(T);
+      b += (double)R * nc * 4 * tsl[buf] * 2 + (double)R + (double)R * nc * sizeof(T);
       Timed t(c, UNO_KC_LORA_DOWN, b, fl);
       UNO_HIP(c, launch_lora_down_tile(a, nc, s));
-      UNO_HIP(c, launch_lora_u(tfx, tsl[buf], a.slice_stride, R, nc, gate, sc,
+      UNO_HIP(c, launch_lora_u(reinterpret_cast<const float*>(tfx), tsl[buf], a.slice_stride, R, nc, gate, sc,
                                reinterpret_cast<bf16*>(ubuf), s));
       return UNO_OK;
     }
