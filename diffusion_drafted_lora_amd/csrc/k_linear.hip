@@ -1032,7 +1032,7 @@ bool launch_tile(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t*
 
 // Large-M LoRA down-projection: the tile kernel with K split into k_slices
 // slices (a power of two up to 8, aiming at four workgroups per CU), each slice
-// storing its fixed-point partial; k_lora_u adds them.
+// storing its float partial; k_lora_u adds them in slice order.
 #ifndef UNO_LORA_TILE_TARGET
 #define UNO_LORA_TILE_TARGET 1024
 #endif
