@@ -1132,19 +1132,20 @@ constexpr int kTileTS3 = UNO_TILE_TS3;        // ring depth of the 128 x 128 til
 #endif
 constexpr bool kTileTallFirst = UNO_TILE_TALL_FIRST;   // 128 x 256 before 256 x 128
 
-// A residual product whose 256 x 256 tiles number at least 128 but fewer than
-// kTileMinWG: two K slices of those tiles store float partials in the caller's
-// workspace (twice the workgroups), then k_resid_slices adds them and runs the
-// residual epilogue (measured at 2048 rows, the o and down projections of the 8B
-// shape: faster than 256 x 128 tiles without a split).  False: not applicable.
+// A residual product whose 256 x 256 tiles number at least 64 but fewer than
+// kTileMinWG: S K slices of those tiles (S = 2 from 128 tiles, else 4) store float
+// partials in the caller's workspace, then k_resid_slices adds them and runs the
+// residual epilogue (measured on the o and down projections of the 8B shape at
+// 2048 rows and in 1024-row prefill: faster than 256 x 128 tiles without a
+// split).  False: not applicable.
 bool launch_resid_split(const GemmArgs& a, int n_cols_total, hipStream_t s, hipError_t* err) {
-  constexpr int S = 2;
   if (a.epi != EPI_RESID || !a.split_ws || a.paired || a.nseg != 1) return false;
-  if ((a.K / 32) % (S * TKB) || (a.r / 32) % TKB || a.ldo != n_cols_total || n_cols_total % 8) return false;
   if (a.seg[0].Ufx && a.seg[0].Bl) return false;
   if (!tile_fits(a, n_cols_total, 256)) return false;
   const long tiles = (long)((a.M + 255) / 256) * (n_cols_total / 256);
-  if (tiles < 128 || tiles >= kTileMinWG) return false;
+  if (tiles < 64 || tiles >= kTileMinWG) return false;
+  const int S = tiles >= 128 ? 2 : 4;
+  if ((a.K / 32) % (S * TKB) || (a.r / 32) % TKB || a.ldo != n_cols_total || n_cols_total % 8) return false;
   const long long stride = (long long)a.M * n_cols_total;
   if (S * stride > a.split_cap) return false;
   GemmArgs b = a;

@@ -148,7 +148,7 @@ def test_large_m_rows_two_sequences():
     eng.sync()
 
 
-@pytest.mark.parametrize("n", [128, 125])
+@pytest.mark.parametrize("n", [128, 125, 64])
 def test_batch128_rows_sampled_sequences(n):
     """2048 rows, the batch-128 decode launch configuration: 128 sequences of 16
     rows against their own contexts (1024 down to 1024 - 7 * 127 keys), gates as
@@ -156,7 +156,8 @@ def test_batch128_rows_sampled_sequences(n):
     down split K in two over 256 x 256 tiles (then the slice-sum residual pass),
     gate/up paired 256 x 256, and the LoRA down-projections the sliced large-M
     path.  125 sequences (2000 rows) take the same paths with a ragged last
-    256-row tile.  A row's arithmetic does not depend on the other sequences'
+    256-row tile; 64 sequences (1024 rows, the height of a prefill chunk) split
+    o and down into four K slices.  A row's arithmetic does not depend on the other sequences'
     rows, so the oracle runs on sampled sequences only."""
     import torch
     log(f"layer8b: {n} sequences x 16 rows")
