@@ -307,8 +307,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the Psi-Spec step is data parallel over sequences "
-              "with no cross-GPU exchange, and this build runs on a single MI355X; "
-              "run it with --gpus 1.", file=sys.stderr)
+              "with no cross-GPU exchange, and it runs on one MI355X: use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -69,7 +69,7 @@ typedef enum {
   UNO_ERR_STATE = 3,         /* call out of order (e.g. verify without a draft)       */
   UNO_ERR_NUMERIC = 4,       /* NaN / negative probability or a row with no mass      */
   UNO_ERR_DEVICE = 5,        /* a HIP call failed, or a device bounds check tripped   */
-  UNO_ERR_UNSUPPORTED = 6    /* a shape this build does not implement                 */
+  UNO_ERR_UNSUPPORTED = 6    /* a shape the library does not implement                */
 } uno_status;
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
