@@ -238,7 +238,123 @@ __global__ void k_accept_commit(int B, const int32_t* draft, const int32_t* k_in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-p (nucleus) truncation of probability rows, in place or out of place: one
+// workgroup of 1024 threads per row.  The evaluations of the pages sample with
+// top-p 0.95 and losslessness holds for that filtered law ([blog] "我的判断");
+// the same truncation is applied to the AR and the draft laws.  Made exact so
+// that it is reproducible bit for bit: masses are floor(p * 2^40) in int64 (exact
+// and order-free sums), the target is max(1, ceil(top_p * W)) in double, the
+// threshold is the largest value whose upper set {p >= tau} holds the target
+// (found by a radix descent over the float bit pattern, which orders like the
+// value for p >= 0: four passes of 8 bits, per-wave int64 histograms in LDS),
+// and kept values are divided by float(W_kept * 2^-40).  top_p >= 1, or a row
+// without fixed-point mass, is copied unchanged.
+constexpr int TP_THREADS = 1024, TP_WAVES = TP_THREADS / 64;
+
+UNO_DEV long long tp_mass(float p) {
+  return p > 0.0f ? (long long)floor((double)p * 0x1p40) : 0;
+}
+
+// sum of v over the workgroup (every thread returns it)
+UNO_DEV long long tp_block_sum(long long v, long long* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int i = 0; i < TP_WAVES; ++i) t += red[i];
+  return t;
+}
+
+__global__ void __launch_bounds__(TP_THREADS)
+k_top_p(const float* in, float* out, int V, float top_p) {
+  __shared__ long long hist[TP_WAVES][256];
+  __shared__ long long red[TP_WAVES];
+  __shared__ long long suf[256];
+  __shared__ unsigned s_prefix;
+  __shared__ long long s_above;
+  const float* p = in + (size_t)blockIdx.x * V;
+  float* o = out + (size_t)blockIdx.x * V;
+  const int tid = threadIdx.x, w = tid >> 6;
+
+  long long mine = 0;
+  for (int i = tid; i < V; i += TP_THREADS) mine += tp_mass(p[i]);
+  const long long W = tp_block_sum(mine, red);
+  if (top_p >= 1.0f || W == 0) {
+    for (int i = tid; i < V; i += TP_THREADS) o[i] = p[i];
+    return;
+  }
+  long long target = (long long)ceil((double)top_p * (double)W);
+  if (target < 1) target = 1;
+
+  // radix descent: after pass k the top 8(k+1) bits of tau are fixed
+  unsigned prefix = 0, mask = 0;
+  long long above = 0;                      // mass strictly above the prefix range
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < TP_WAVES * 256; b += TP_THREADS) (&hist[0][0])[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < V; i += TP_THREADS) {
+      const float v = p[i];
+      const unsigned bits = __float_as_uint(v);
+      if (v > 0.0f && (bits & mask) == prefix)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[w][(bits >> shift) & 255]),
+                  (unsigned long long)tp_mass(v));
+    }
+    __syncthreads();
+    // suffix sums over the bins (highest bin first): suf[b] = sum of bins >= b
+    if (tid < 256) {
+      long long t = 0;
+#pragma unroll
+      for (int i = 0; i < TP_WAVES; ++i) t += hist[i][tid];
+      suf[tid] = t;
+    }
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      long long add = 0;
+      if (tid < 256 && tid + d < 256) add = suf[tid + d];
+      __syncthreads();
+      if (tid < 256) suf[tid] += add;
+      __syncthreads();
+    }
+    // the bin where the running mass from the top first reaches the target
+    if (tid < 256) {
+      const long long hi = tid < 255 ? suf[tid + 1] : 0;
+      if (above + suf[tid] >= target && above + hi < target) {
+        s_prefix = prefix | ((unsigned)tid << shift);
+        s_above = above + hi;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    above = s_above;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+
+  // kept mass and the renormalised row
+  mine = 0;
+  for (int i = tid; i < V; i += TP_THREADS)
+    if (p[i] > 0.0f && __float_as_uint(p[i]) >= prefix) mine += tp_mass(p[i]);
+  const long long kept = tp_block_sum(mine, red);
+  const float z = (float)((double)kept * 0x1p-40);
+  for (int i = tid; i < V; i += TP_THREADS) {
+    const float v = p[i];
+    o[i] = (v > 0.0f && __float_as_uint(v) >= prefix) ? v / z : 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_top_p(const float* in, float* out, int rows, int V, float top_p, hipStream_t s) {
+  if (rows <= 0 || V <= 0) return hipSuccess;
+  uno_launch(k_top_p, rows, TP_THREADS, 0, s, in, out, V, top_p);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_cdf(const RowDesc* desc, int rows, int V, uint64_t* chunk_tot, int32_t* err,
                       hipStream_t s) {

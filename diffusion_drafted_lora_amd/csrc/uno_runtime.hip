@@ -770,6 +770,9 @@ uno_status set_state(uno_ctx* c, int seq, int len, int pending, int iter) {
 }  // namespace
 
 // ====================================================================== C ABI
+// top-p truncation of `rows` probability rows of V (k_sample.hip; in place when in == out)
+hipError_t launch_top_p(const float* in, float* out, int rows, int V, float top_p, hipStream_t s);
+
 extern "C" {
 
 uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t cols,
@@ -782,6 +785,16 @@ uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t
   hipError_t e = launch_pack(static_cast<const bf16*>(d_src), static_cast<bf16*>(d_dst), rows, cols,
                              pair_hd, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(nullptr, UNO_ERR_DEVICE, std::string("pack: ") + hipGetErrorString(e));
+  return UNO_OK;
+}
+
+uno_status uno_top_p(const float* d_in, float* d_out, int32_t rows, int32_t vocab, float top_p,
+                     void* stream) {
+  if (!d_in || !d_out) return fail(nullptr, UNO_ERR_INVALID_ARG, "top_p: null buffer");
+  if (rows < 0 || vocab <= 0 || !(top_p > 0.0f))
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "top_p: rows >= 0, vocab > 0 and top_p > 0 required");
+  hipError_t e = launch_top_p(d_in, d_out, rows, vocab, top_p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, UNO_ERR_DEVICE, std::string("top_p: ") + hipGetErrorString(e));
   return UNO_OK;
 }
 

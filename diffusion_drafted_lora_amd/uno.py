@@ -23,7 +23,7 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
             "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_every", "uno_timing_read",
-            "uno_distill_forward", "uno_pack_weight")
+            "uno_distill_forward", "uno_pack_weight", "uno_top_p")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -347,6 +347,22 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+def top_p(probs, p, out=None):
+    """Top-p truncation of the rows of a float32 device tensor [..., V] (see
+    uno_top_p); in place when out is probs."""
+    import torch
+    if not (probs.is_cuda and probs.is_contiguous() and probs.dtype == torch.float32):
+        raise ValueError("top_p needs a contiguous float32 device tensor")
+    if out is None:
+        out = torch.empty_like(probs)
+    V = probs.shape[-1]
+    st = lib().uno_top_p(_ptr(probs), _ptr(out), probs.numel() // V, V, C.c_float(p),
+                         C.c_void_p(torch.cuda.current_stream(probs.device).cuda_stream))
+    if st != UNO_OK:
+        raise UnoError(st, lib().uno_last_error(None).decode())
+    return out
 
 
 def pack_weights(cfg, w):

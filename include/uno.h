@@ -122,6 +122,21 @@ typedef struct {
 uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t cols,
                            int32_t pair_hd, void* stream);
 
+/* Top-p (nucleus) truncation of probability rows.  The pages' evaluations sample
+ * at temperature 1 with top-p 0.95, and losslessness holds for that filtered law
+ * (shibing624 reading notes, "我的判断"); applying the same truncation to the AR
+ * law p and the draft law q keeps speculative rejection exact for it.  Row r of
+ * d_in [rows, vocab] (float32 probabilities, >= 0) becomes row r of d_out: with
+ * masses w_i = floor(p_i * 2^40) (int64), W = sum w_i and the target mass
+ * T = max(1, ceil(top_p * W)) (double), tau is the largest value whose upper set
+ * {p >= tau} holds at least T (ties kept); kept entries become p_i / Z with
+ * Z = float(W_kept * 2^-40), the others 0.  top_p >= 1, or a row with W == 0, is
+ * copied unchanged.  d_out may equal d_in (in place); device pointers; one
+ * workgroup per row, enqueued on stream (a hipStream_t); no context needed.
+ * UNO_ERR_INVALID_ARG for null buffers, rows < 0, vocab <= 0 or top_p <= 0. */
+uno_status uno_top_p(const float* d_in, float* d_out, int32_t rows, int32_t vocab, float top_p,
+                     void* stream);
+
 /* Sizes of the caller-allocated KV pool and workspace for a config.
  * KV pool layout (exposed for inspection only; use uno_kv_import/export):
  * [layer][K|V][page][kv_head] blocks of page_size x head_dim of the storage type,

@@ -124,3 +124,45 @@ def test_accept_nan_sets_numeric_flag():
     eng.accept(dev(p), dev(q), dev(y), dev(z), dev(z), dev(z))
     with pytest.raises(Exception, match="NUMERIC"):
         eng.sync()
+
+
+@pytest.mark.parametrize("V", [32, 2080, 151936])
+def test_top_p_bit_exact(V):
+    """Top-p truncation (uno_top_p) against the oracle's exact reading, bit for bit:
+    softmax rows of several temperatures, rows with many tied values, rows with
+    zero entries, and top-p from 0.05 to 1 (identity)."""
+    import torch
+    from diffusion_drafted_lora_amd import uno
+    from oracle import nucleus
+    rng = np.random.default_rng(V)
+    rows = []
+    for scale in (0.5, 2.0, 6.0):
+        lg = rng.normal(0.0, scale, size=(3, V))
+        p = np.exp(lg - lg.max(-1, keepdims=True))
+        rows.append(p / p.sum(-1, keepdims=True))
+    ties = np.exp(rng.integers(-4, 3, size=(2, V)) * 0.9)        # heavy ties
+    rows.append(ties / ties.sum(-1, keepdims=True))
+    sparse = rng.random((2, V)) * (rng.random((2, V)) < 0.3)       # zeros
+    sparse[:, 0] = 1.0
+    rows.append(sparse / sparse.sum(-1, keepdims=True))
+    P = np.concatenate(rows).astype(np.float32)
+    for top_p in (0.05, 0.5, 0.9, 0.95, 0.999, 1.0):
+        got = host(uno.top_p(dev(P), top_p))
+        want = nucleus.filter_rows(P, top_p)
+        assert np.array_equal(got, want), f"V={V} top_p={top_p}"
+    # in place
+    t = dev(P)
+    uno.top_p(t, 0.95, out=t)
+    assert np.array_equal(host(t), nucleus.filter_rows(P, 0.95))
+
+
+def test_top_p_exact_boundary_and_errors():
+    import torch
+    from diffusion_drafted_lora_amd import uno
+    from oracle import nucleus
+    d = np.array([[0.5, 0.25, 0.125, 0.125], [0.25, 0.25, 0.25, 0.25]], dtype=np.float32)
+    got = host(uno.top_p(dev(d), 0.75))
+    assert np.array_equal(got, nucleus.filter_rows(d, 0.75))
+    assert np.flatnonzero(got[0]).tolist() == [0, 1]
+    with pytest.raises(uno.UnoError):
+        uno.top_p(dev(d), 0.0)
