@@ -258,8 +258,12 @@ uno_status check_config(const uno_config* c) {
     return fail(nullptr, UNO_ERR_UNSUPPORTED, "lora rank");
   if (c->max_rows < c->max_seqs * c->block_size)
     return fail(nullptr, UNO_ERR_INVALID_ARG, "max_rows < max_seqs * block_size");
+  if (!(c->top_p >= 0.0f)) return fail(nullptr, UNO_ERR_INVALID_ARG, "top_p < 0 or NaN");
   return UNO_OK;
 }
+
+// Nucleus truncation of a block of probability rows in place, when the config asks.
+bool top_p_on(const uno_config& c) { return c.top_p > 0.0f && c.top_p < 1.0f; }
 
 size_t kv_bytes(const uno_config& c) {
   const size_t ts = c.dtype == UNO_BF16 ? 2 : 4;
@@ -979,6 +983,8 @@ uno_status uno_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_d
   hipStream_t s = c->stream;
   RowDesc* desc = c->at<RowDesc>(c->L.desc);
   Timed tsm(c, UNO_KC_SAMPLING, (double)n * B * V * 8, 0);
+  if (top_p_on(c->cfg))
+    UNO_HIP(c, launch_top_p(f.probs_out, f.probs_out, n * B, V, c->cfg.top_p, s));
   UNO_HIP(c, launch_draft_desc(f.probs_out, n, B, V, c->cfg.seed, c->at<int32_t>(c->L.call_seq),
                                c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
                                c->at<int32_t>(c->L.draft_tok), desc, s));
@@ -1015,6 +1021,8 @@ uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_
   int32_t* err = c->at<int32_t>(c->L.err);
   const float* pd = c->at<float>(c->L.probs_d);
   Timed tsm(c, UNO_KC_SAMPLING, (double)n * V * 8 * 2, 0);
+  if (top_p_on(c->cfg))
+    UNO_HIP(c, launch_top_p(f.probs_out, f.probs_out, n * B, V, c->cfg.top_p, s));
   UNO_HIP(c, launch_accept_test(c->cfg.seed, n, B, V, f.probs_out, pd + V, B,
                                 c->at<int32_t>(c->L.draft_tok), c->at<int32_t>(c->L.call_seq),
                                 c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),

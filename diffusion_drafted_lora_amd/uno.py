@@ -43,7 +43,7 @@ class UnoConfigC(C.Structure):
                [("lora_alpha", C.c_float), ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + \
                [(n, C.c_int32) for n in ("block_size", "page_size", "max_seqs", "max_seq_len",
                                          "n_pages", "max_rows", "dtype")] + \
-               [("seed", C.c_uint64)]
+               [("seed", C.c_uint64), ("top_p", C.c_float)]
 
 
 PP = C.POINTER(C.c_void_p)
@@ -100,7 +100,8 @@ def lib():
     return _lib
 
 
-def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, seed=0):
+def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, seed=0,
+                top_p=0.0):
     """uno_config for a configs.UnoConfig plus decoding limits."""
     max_seq_len = max_seq_len or cfg.max_len
     pages_per_seq = -(-max_seq_len // cfg.page_size)
@@ -116,6 +117,7 @@ def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, 
     c.max_rows = max_rows or max_seqs * cfg.block_size
     c.dtype = 1 if cfg.dtype == "bf16" else 0
     c.seed = seed
+    c.top_p = top_p
     return c
 
 
@@ -140,14 +142,14 @@ class Engine:
     """A libuno context over torch-allocated device memory."""
 
     def __init__(self, cfg, weights, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None,
-                 seed=0, device="cuda", stream=None):
+                 seed=0, device="cuda", stream=None, top_p=0.0):
         import torch
         self.torch = torch
         self.cfg = cfg
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed)
+        self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed, top_p)
         self.n_pages = self.ccfg.n_pages
         kv_bytes, ws_bytes = query_sizes(self.ccfg)
         self.kv = torch.empty(max(kv_bytes, 1), dtype=torch.uint8, device=self.device)

@@ -87,6 +87,10 @@ typedef struct {
   int32_t max_rows;         /* rows one forward may carry (>= max_seqs*block_size)   */
   int32_t dtype;            /* uno_dtype                                             */
   uint64_t seed;            /* Philox key word 0                                     */
+  float top_p;              /* nucleus truncation of the draft and verify laws (the
+                               uno_top_p rule, applied right after each softmax):
+                               0 (the zero-initialised default) or >= 1 turns it off;
+                               negative or NaN is UNO_ERR_INVALID_ARG              */
 } uno_config;
 
 /* Weights: host arrays of device pointers, copied at uno_init (the device memory

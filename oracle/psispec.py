@@ -26,11 +26,15 @@ Readings where the pages are silent (each listed in the design notes):
 * emitted tokens are y_1..y_{k-1}, z (k of them); the cache keeps positions
   n..n+k-1; then n <- n+k, t <- z, iteration += 1;
 * prefill runs the AR forward over prompt[0..P-2] and leaves prompt[P-1] pending;
-* random draws use rng.draw_word with the (position, stream, iteration) counter.
+* random draws use rng.draw_word with the (position, stream, iteration) counter;
+* with top-p on, the nucleus truncation (nucleus.filter_row) is applied to every
+  draft and verify row right after the softmax, so q and p above are the filtered
+  laws and the output distribution is the filtered AR law.
 """
 import numpy as np
 
 from . import model
+from . import nucleus
 from . import rng
 
 
@@ -101,8 +105,9 @@ def accept_block(p_rows, q_rows, drafts, seed, seq_ids, n, it,
 class Decoder:
     """Psi-Spec decoding state of S sequences against one contiguous KV cache."""
 
-    def __init__(self, cfg, weights, seq_ids, seed, max_len):
+    def __init__(self, cfg, weights, seq_ids, seed, max_len, top_p=1.0):
         self.cfg = cfg
+        self.top_p = top_p
         self.w = weights
         self.seq_ids = np.asarray(seq_ids, dtype=np.int64)
         self.seed = int(seed)
@@ -112,6 +117,14 @@ class Decoder:
         self.t = np.zeros(S, dtype=np.int64)
         self.it = np.zeros(S, dtype=np.int64)
         self.forwards = 0
+
+    def _law(self, logits):
+        """Softmax of the logits, then (0 < top_p < 1) the nucleus truncation of
+        each row: the same filter on the draft and the AR law."""
+        P = model.probs(logits)
+        if 0.0 < self.top_p < 1.0:
+            P = nucleus.filter_rows(P, self.top_p)
+        return P
 
     @property
     def S(self):
@@ -146,7 +159,7 @@ class Decoder:
         gate = np.ones((S, B))
         gate[:, 0] = 0.0
         logits, _ = model.forward(cfg, self.w, toks, pos, gate, self.cache)
-        P_d = model.probs(logits)
+        P_d = self._law(logits)
         y = np.empty((S, B), dtype=np.int64)
         for j in range(1, B + 1):
             word = rng.draw_word(self.seed, self.seq_ids, self.n + j, rng.STREAM_DRAFT, self.it)
@@ -161,7 +174,7 @@ class Decoder:
         cfg, B, S = self.cfg, self.cfg.block_size, self.S
         pos = self.n[:, None] + 1 + np.arange(B)[None, :]
         logits, _ = model.forward(cfg, self.w, y, pos, np.zeros((S, B)), self.cache)
-        return model.probs(logits)
+        return self._law(logits)
 
     def step(self, broken=None):
         """One Psi-Spec iteration.  Returns dict with out, n_out, y, P_d, P_v."""
@@ -180,7 +193,7 @@ class Decoder:
         cfg, S = self.cfg, self.S
         logits, _ = model.forward(cfg, self.w, self.t[:, None], self.n[:, None],
                                   np.zeros((S, 1)), self.cache)
-        P = model.probs(logits)[:, 0]
+        P = self._law(logits)[:, 0]
         word = rng.draw_word(self.seed, self.seq_ids, self.n + 1, rng.STREAM_DRAFT, self.it)
         idx, total = rng.sample_icdf(P, word)
         self.forwards += 1
@@ -228,7 +241,7 @@ class Decoder:
     # -- helpers that run a subset of the sequences against views of the cache --
     def _subdecoder(self, rows):
         sub = Decoder.__new__(Decoder)
-        sub.cfg, sub.w, sub.seed = self.cfg, self.w, self.seed
+        sub.cfg, sub.w, sub.seed, sub.top_p = self.cfg, self.w, self.seed, self.top_p
         sub.seq_ids = self.seq_ids[rows]
         sub.cache = {"k": self.cache["k"][:, rows], "v": self.cache["v"][:, rows]}
         sub.n, sub.t, sub.it = self.n[rows].copy(), self.t[rows].copy(), self.it[rows].copy()

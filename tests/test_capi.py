@@ -58,6 +58,13 @@ def test_invalid_configs_rejected():
     bad = uno.make_config(configs.TINY, max_rows=1)
     with pytest.raises(uno.UnoError):
         uno.query_sizes(bad)
+    for tp in (-0.1, float("nan")):
+        bad = uno.make_config(configs.TINY, top_p=tp)
+        with pytest.raises(uno.UnoError) as e:
+            uno.query_sizes(bad)
+        assert e.value.status == 1
+    for tp in (0.0, 0.95, 1.0, 2.0):              # off, on, off, off
+        uno.query_sizes(uno.make_config(configs.TINY, top_p=tp))
 
 
 def test_init_rejects_null_buffers_before_touching_the_device():

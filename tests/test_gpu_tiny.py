@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from diffusion_drafted_lora_amd import configs, synth
-from oracle import model, psispec
+from oracle import model, nucleus, psispec
 from tests.gpu_util import dev, engine, host, log
 
 pytestmark = pytest.mark.gpu
@@ -58,20 +58,22 @@ def test_forward_logits_hidden_and_cache(w_np):
     eng.sync()
 
 
-@pytest.mark.parametrize("stress", [False, True])
-def test_decode_iterations_match_oracle(stress):
+@pytest.mark.parametrize("stress,top_p", [(False, 0.0), (True, 0.0), (True, 0.9)])
+def test_decode_iterations_match_oracle(stress, top_p):
     """prefill + 8 iterations of draft / verify / accept / commit on 5 sequences with
-    ragged prompt lengths; every intermediate checked against the oracle."""
-    log(f"tiny decode stress={stress}")
+    ragged prompt lengths; every intermediate checked against the oracle (with top_p,
+    both sides truncate the draft and verify laws to their nuclei)."""
+    log(f"tiny decode stress={stress} top_p={top_p}")
     w = synth.weights_numpy(TINY, 1001, lm_head_std=0.35, lora_b_std=0.6) if stress \
         else synth.weights_numpy(TINY, 1000)
     S, seed = 5, 3000
     lens = [16, 9, 1, 16, 4]
     prompts = [synth.prompts(TINY, 2000 + i, 1, L)[0] for i, L in enumerate(lens)]
     seq_ids = [4, 0, 2, 1, 3]
-    eng = engine(TINY, w, max_seqs=S, max_seq_len=TINY.max_len + 40, seed=seed)
+    eng = engine(TINY, w, max_seqs=S, max_seq_len=TINY.max_len + 40, seed=seed, top_p=top_p)
     eng.prefill(seq_ids, prompts)
-    dec = psispec.Decoder(TINY, w, seq_ids, seed, TINY.max_len + 40)
+    dec = psispec.Decoder(TINY, w, seq_ids, seed, TINY.max_len + 40,
+                          top_p=top_p if top_p > 0 else 1.0)
     dec.prefill(prompts)
     hist = []
     for step in range(8):
@@ -95,6 +97,35 @@ def test_decode_iterations_match_oracle(stress):
     assert min(hist) >= 2 and max(hist) <= TINY.block_size + 1
     log(f"accept lengths {sorted(set(hist))}")
     eng.sync()
+
+
+def test_top_p_config_filters_draft_bit_exact():
+    """The top_p config field applies exactly the nucleus rule to the softmax rows:
+    two contexts on the same weights and seed, one with top_p 0.9, give draft laws
+    that the oracle's filter maps one onto the other bit for bit; the draws stay
+    inside the nuclei, and the verify rows are truncated too (zeros beyond the mask
+    column, unit mass).  The verify laws themselves are checked against the oracle
+    by the decode test with top_p."""
+    w = synth.weights_numpy(TINY, 1001, lm_head_std=0.35, lora_b_std=0.6)
+    S = 3
+    prompts = list(synth.prompts(TINY, 2200, S))
+    ids = [0, 1, 2]
+    res = []
+    for tp in (0.0, 0.9):
+        log(f"tiny top_p config {tp}")
+        eng = engine(TINY, w, max_seqs=S, seed=77, top_p=tp)
+        eng.prefill(ids, prompts)
+        y, pd = eng.draft(ids, want_probs=True)
+        _, _, pv = eng.verify(ids, want_probs=True)
+        res.append((host(y).copy(), host(pd).copy(), host(pv).copy()))
+        eng.sync()
+    (_, pd0, pv0), (y1, pd1, pv1) = res
+    assert np.array_equal(nucleus.filter_rows(pd0, 0.9), pd1)
+    assert ((pd1 == 0).sum(-1) > (pd0 == 0).sum(-1)).all()
+    drawn = np.take_along_axis(pd1, y1[..., None].astype(np.int64), -1)[..., 0]
+    assert (drawn > 0).all()
+    assert ((pv1 == 0).sum(-1) > (pv0 == 0).sum(-1).min()).all()
+    assert np.abs(pv1.astype(np.float64).sum(-1) - 1).max() <= 1e-5
 
 
 def test_step_equals_draft_then_verify_and_release(w_np):

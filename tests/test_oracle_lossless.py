@@ -11,7 +11,7 @@ import pytest
 from scipy import stats
 
 from diffusion_drafted_lora_amd import configs, synth
-from oracle import model, psispec
+from oracle import model, nucleus, psispec
 
 TINY = configs.TINY
 STRESS = dict(lm_head_std=0.35, lora_b_std=0.6)
@@ -41,7 +41,7 @@ def _exact_joint2(cfg, w, prompt):
     return joint
 
 
-def _sample_first_two(cfg, w, prompt, N, seed, broken=None):
+def _sample_first_two(cfg, w, prompt, N, seed, broken=None, top_p=1.0):
     """Run one Psi-Spec iteration for N sequences (seq ids 0..N-1) sharing a prompt."""
     one = psispec.Decoder(cfg, w, [0], seed, len(prompt) + cfg.block_size + 2)
     one.prefill([prompt])
@@ -49,7 +49,8 @@ def _sample_first_two(cfg, w, prompt, N, seed, broken=None):
     chunk = 20_000
     for a in range(0, N, chunk):
         b = min(N, a + chunk)
-        dec = psispec.Decoder(cfg, w, np.arange(a, b), seed, len(prompt) + cfg.block_size + 2)
+        dec = psispec.Decoder(cfg, w, np.arange(a, b), seed, len(prompt) + cfg.block_size + 2,
+                              top_p=top_p)
         dec.cache["k"][:] = one.cache["k"]
         dec.cache["v"][:] = one.cache["v"]
         dec.n[:], dec.t[:] = one.n[0], one.t[0]
@@ -90,6 +91,46 @@ def test_lossless_first_two_tokens_tiny(tiny_w):
     joint = _exact_joint2(TINY, tiny_w, prompt)
     obs = _sample_first_two(TINY, tiny_w, prompt, 60_000, 3000)
     assert _chi2_pvalue(obs, joint) > 0.01
+
+
+def _filtered_joint2(cfg, w, prompt, top_p):
+    """Exact law of (t1, t2) when every AR conditional is truncated to its top-p
+    nucleus: filter(p(t1 | prompt)) filter(p(t2 | prompt, t1)), the float32 laws the
+    sampler draws from."""
+    V = cfg.vocab
+    P = len(prompt)
+    cache = model.new_cache(cfg, 1, P + 2)
+    lg, _ = model.forward(cfg, w, np.asarray(prompt)[None], np.arange(P)[None],
+                          np.zeros((1, P)), cache)
+    p1 = nucleus.filter_row(model.probs(lg[0, -1]), top_p).astype(np.float64)
+    toks = np.tile(np.concatenate([prompt, [0]]), (V, 1))
+    toks[:, -1] = np.arange(V)
+    cache = model.new_cache(cfg, V, P + 2)
+    lg, _ = model.forward(cfg, w, toks, np.tile(np.arange(P + 1), (V, 1)),
+                          np.zeros((V, P + 1)), cache)
+    p2 = nucleus.filter_rows(model.probs(lg[:, -1]), top_p).astype(np.float64)
+    joint = p1[:, None] * p2
+    return joint / joint.sum()
+
+
+def test_lossless_first_two_tokens_top_p_stress(stress_w):
+    """With top-p 0.9 the output law is the filtered AR law: no sample outside the
+    nuclei, chi^2 against the filtered joint passes, and against the unfiltered
+    joint (what a sampler that skipped the filter would follow) it fails."""
+    prompt = synth.prompts(TINY, 2003, 1)[0]
+    joint_f = _filtered_joint2(TINY, stress_w, prompt, 0.9)
+    joint = _exact_joint2(TINY, stress_w, prompt)
+    assert (joint_f > 0).sum() < 0.8 * (joint > 0).sum()      # the filter bites
+    obs = _sample_first_two(TINY, stress_w, prompt, 30_000, 3005, top_p=0.9)
+    assert _chi2_pvalue(obs, joint_f) > 0.01
+    N = len(obs)
+    counts = np.zeros_like(joint)
+    np.add.at(counts, (obs[:, 0], obs[:, 1]), 1)
+    e = joint.ravel() * N
+    big = e >= 5
+    o = counts.ravel()
+    eb, ob = np.append(e[big], e[~big].sum()), np.append(o[big], o[~big].sum())
+    assert stats.chisquare(ob, eb * ob.sum() / eb.sum()).pvalue < 1e-6
 
 
 def _tv_draft_vs_ar(cfg, w, prompt):
