@@ -12,7 +12,8 @@ resample test and the commit.  W untimed steps, then exactly K timed steps.
 Reported: accepted tokens/s (value), positions/s, tokens per forward, whole-step
 algorithmic HBM GB/s, the roofline of the dominant kernel (the gate/up
 gated-LoRA linear, timed with HIP events on the library's stream), a per-class
-kernel time breakdown, and the CPU oracle timed on a bounded sample on the host.
+kernel time breakdown, the nucleus (top-p) truncation kernel at the batch-1 and
+batch-128 row counts, and the CPU oracle timed on a bounded sample on the host.
 """
 import argparse
 import json
@@ -212,6 +213,39 @@ def run_distill(cfg, w, dev, batch, L, B, reps):
             "rows_per_s": R / sec, "mean_tv_block": tvb, "breakdown": breakdown}
 
 
+def run_top_p(V, rows_list, top_p=0.95, reps=20):
+    """Nucleus truncation (uno_top_p) on float32 probability rows of the model's
+    vocabulary: softmax rows of N(0, 3^2) logits, out of place.  Timed with HIP
+    events on the stream the kernel runs on; algorithmic bytes are one read and one
+    write of every row (8 V bytes per row)."""
+    import torch
+    from diffusion_drafted_lora_amd import uno
+    out = []
+    st = torch.cuda.current_stream()
+    for rows in rows_list:
+        g = torch.Generator(device="cuda:0").manual_seed(4000 + rows)
+        probs = torch.softmax(torch.randn(rows, V, device="cuda:0", generator=g) * 3.0, -1)
+        dst = torch.empty_like(probs)
+        for _ in range(3):
+            uno.top_p(probs, top_p, out=dst)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            uno.top_p(probs, top_p, out=dst)
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        kept = float((dst > 0).sum(-1).float().mean())
+        byts = 8.0 * rows * V
+        out.append({"rows": rows, "vocab": V, "top_p": top_p, "us_per_launch": us,
+                    "bytes_per_launch": byts, "GB/s": byts / 1e3 / us,
+                    "frac_hbm": byts / 1e3 / us / HBM_PEAK_GBS, "mean_kept": kept})
+        log(f"top-p rows {rows}: {us:.1f} us per launch")
+        del probs, dst
+    return out
+
+
 def cpu_sample_weights(cfg, w):
     """Host float32 copies of what the CPU baseline runs on: layer 0 and the first
     eighth of the LM head (row-major, before packing)."""
@@ -301,6 +335,8 @@ def main():
     ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
                     help="distillation-forward leg (batch, L, block size); 'none' skips it")
     ap.add_argument("--distill-reps", type=int, default=2)
+    ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
+                    help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy of MIB MiB (HBM counter scale)")
     args = ap.parse_args()
@@ -440,6 +476,9 @@ def main():
     if args.distill != "none":
         db, dl, dbs = (int(v) for v in args.distill.split(","))
         result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)
+    if args.top_p_leg:
+        # one launch filters the B draft (or verify) rows of every sequence
+        result["top_p"] = run_top_p(cfg.vocab, [B, 128 * B])
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(cfg, sample_w, tokens / K)

@@ -245,106 +245,137 @@ __global__ void k_accept_commit(int B, const int32_t* draft, const int32_t* k_in
 // the same truncation is applied to the AR and the draft laws.  Made exact so
 // that it is reproducible bit for bit: masses are floor(p * 2^40) in int64 (exact
 // and order-free sums), the target is max(1, ceil(top_p * W)) in double, the
-// threshold is the largest value whose upper set {p >= tau} holds the target
-// (found by a radix descent over the float bit pattern, which orders like the
-// value for p >= 0: four passes of 8 bits, per-wave int64 histograms in LDS),
+// threshold is the largest value whose upper set {p >= tau} holds the target,
 // and kept values are divided by float(W_kept * 2^-40).  top_p >= 1, or a row
 // without fixed-point mass, is copied unchanged.
+//
+// The threshold comes from a radix descent over the bit pattern, which orders
+// like the value for p > 0: three passes over bits 30..20, 19..9 and 8..0 (2048,
+// 2048 and 512 bins of int64 mass in LDS, two copies split by wave parity).  The
+// first histogram holds every positive entry, so its sum is W; the last pass
+// yields the mass at or above tau, W_kept.  The row is read four times (three
+// histograms and the output pass) and written once; fine bins keep the LDS
+// atomics of neighbouring lanes on different addresses for most rows.
 constexpr int TP_THREADS = 1024, TP_WAVES = TP_THREADS / 64;
+constexpr int TP_BINS = 2048, TP_COPIES = 2;
 
 UNO_DEV long long tp_mass(float p) {
   return p > 0.0f ? (long long)floor((double)p * 0x1p40) : 0;
 }
 
-// sum of v over the workgroup (every thread returns it)
-UNO_DEV long long tp_block_sum(long long v, long long* red) {
+// f(index, value) over the row, with 16-byte loads when the row allows them
+template <class F>
+UNO_DEV void tp_each(const float* p, int V, F&& f) {
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    const float4* p4 = reinterpret_cast<const float4*>(p);
+    for (int i = threadIdx.x; i < (V >> 2); i += TP_THREADS) {
+      const float4 v = p4[i];
+      f(4 * i, v.x);
+      f(4 * i + 1, v.y);
+      f(4 * i + 2, v.z);
+      f(4 * i + 3, v.w);
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += TP_THREADS) f(i, p[i]);
+  }
+}
+
+// Sum of v over the threads >= threadIdx.x (a suffix over the workgroup);
+// *total receives the sum over all threads.
+UNO_DEV long long tp_block_suffix(long long v, long long* red, long long* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int w = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long y = __shfl_down(v, d);
+    if (lane + d < 64) v += y;
+  }
+  __syncthreads();                        // the previous use of red[] is over
+  if (lane == 0) red[w] = v;              // lane 0 holds the wave's total
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  long long t = 0;
+  long long hi = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < TP_WAVES; ++i) t += red[i];
-  return t;
+  for (int i = 0; i < TP_WAVES; ++i) {
+    const long long t = red[i];
+    all += t;
+    if (i > w) hi += t;
+  }
+  *total = all;
+  return v + hi;
 }
 
 __global__ void __launch_bounds__(TP_THREADS)
 k_top_p(const float* in, float* out, int V, float top_p) {
-  __shared__ long long hist[TP_WAVES][256];
+  __shared__ long long hist[TP_COPIES][TP_BINS];
   __shared__ long long red[TP_WAVES];
-  __shared__ long long suf[256];
   __shared__ unsigned s_prefix;
-  __shared__ long long s_above;
+  __shared__ long long s_above, s_kept;
   const float* p = in + (size_t)blockIdx.x * V;
   float* o = out + (size_t)blockIdx.x * V;
-  const int tid = threadIdx.x, w = tid >> 6;
-
-  long long mine = 0;
-  for (int i = tid; i < V; i += TP_THREADS) mine += tp_mass(p[i]);
-  const long long W = tp_block_sum(mine, red);
-  if (top_p >= 1.0f || W == 0) {
-    for (int i = tid; i < V; i += TP_THREADS) o[i] = p[i];
+  const int tid = threadIdx.x;
+  long long* h = hist[(tid >> 6) & (TP_COPIES - 1)];
+  auto copy_row = [&] { tp_each(p, V, [&](int i, float v) { o[i] = v; }); };
+  if (top_p >= 1.0f) {
+    copy_row();
     return;
   }
-  long long target = (long long)ceil((double)top_p * (double)W);
-  if (target < 1) target = 1;
 
-  // radix descent: after pass k the top 8(k+1) bits of tau are fixed
   unsigned prefix = 0, mask = 0;
-  long long above = 0;                      // mass strictly above the prefix range
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < TP_WAVES * 256; b += TP_THREADS) (&hist[0][0])[b] = 0;
+  long long above = 0, target = 0, kept = 0;   // above: mass strictly above the prefix group
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : pass == 1 ? 9 : 0;
+    const unsigned nb = pass == 2 ? 512u : 2048u;
+    for (int b = tid; b < TP_COPIES * TP_BINS; b += TP_THREADS) (&hist[0][0])[b] = 0;
     __syncthreads();
-    for (int i = tid; i < V; i += TP_THREADS) {
-      const float v = p[i];
+    tp_each(p, V, [&](int, float v) {
       const unsigned bits = __float_as_uint(v);
       if (v > 0.0f && (bits & mask) == prefix)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[w][(bits >> shift) & 255]),
+        atomicAdd(reinterpret_cast<unsigned long long*>(&h[(bits >> shift) & (nb - 1)]),
                   (unsigned long long)tp_mass(v));
-    }
+    });
     __syncthreads();
-    // suffix sums over the bins (highest bin first): suf[b] = sum of bins >= b
-    if (tid < 256) {
-      long long t = 0;
+    // this thread's bins 2t and 2t+1, summed over the copies (bins >= nb are empty)
+    long long h0 = 0, h1 = 0;
 #pragma unroll
-      for (int i = 0; i < TP_WAVES; ++i) t += hist[i][tid];
-      suf[tid] = t;
+    for (int c = 0; c < TP_COPIES; ++c) {
+      h0 += hist[c][2 * tid];
+      h1 += hist[c][2 * tid + 1];
     }
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-      long long add = 0;
-      if (tid < 256 && tid + d < 256) add = suf[tid + d];
-      __syncthreads();
-      if (tid < 256) suf[tid] += add;
-      __syncthreads();
-    }
-    // the bin where the running mass from the top first reaches the target
-    if (tid < 256) {
-      const long long hi = tid < 255 ? suf[tid + 1] : 0;
-      if (above + suf[tid] >= target && above + hi < target) {
-        s_prefix = prefix | ((unsigned)tid << shift);
-        s_above = above + hi;
+    long long total;
+    const long long s0 = tp_block_suffix(h0 + h1, red, &total);   // mass of bins >= 2t
+    if (pass == 0) {
+      if (total == 0) {                    // W == 0: the same in every thread
+        copy_row();
+        return;
       }
+      target = (long long)ceil((double)top_p * (double)total);
+      if (target < 1) target = 1;
+    }
+    const long long s1 = s0 - h0;          // bins >= 2t+1
+    const long long s2 = s1 - h1;          // bins >= 2t+2
+    // the one bin where the running mass from the top first reaches the target
+    if (above + s0 >= target && above + s1 < target) {
+      s_prefix = prefix | ((2u * tid) << shift);
+      s_above = above + s1;
+      s_kept = above + s0;
+    } else if (above + s1 >= target && above + s2 < target) {
+      s_prefix = prefix | ((2u * tid + 1) << shift);
+      s_above = above + s2;
+      s_kept = above + s1;
     }
     __syncthreads();
     prefix = s_prefix;
     above = s_above;
-    mask |= 255u << shift;
-    __syncthreads();
+    kept = s_kept;
+    mask |= (nb - 1) << shift;
+    __syncthreads();                       // s_* and hist are rewritten by the next pass
   }
 
-  // kept mass and the renormalised row
-  mine = 0;
-  for (int i = tid; i < V; i += TP_THREADS)
-    if (p[i] > 0.0f && __float_as_uint(p[i]) >= prefix) mine += tp_mass(p[i]);
-  const long long kept = tp_block_sum(mine, red);
+  // prefix is now tau's bit pattern and kept the mass of {p >= tau}
   const float z = (float)((double)kept * 0x1p-40);
-  for (int i = tid; i < V; i += TP_THREADS) {
-    const float v = p[i];
+  tp_each(p, V, [&](int i, float v) {
     o[i] = (v > 0.0f && __float_as_uint(v) >= prefix) ? v / z : 0.0f;
-  }
+  });
 }
 
 }  // namespace
