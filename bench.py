@@ -12,7 +12,8 @@ resample test and the commit.  W untimed steps, then exactly K timed steps.
 Reported: accepted tokens/s (value), positions/s, tokens per forward, whole-step
 algorithmic HBM GB/s, the roofline of the dominant kernel (the gate/up
 gated-LoRA linear, timed with HIP events on the library's stream), a per-class
-kernel time breakdown, the nucleus (top-p) truncation kernel at the batch-1 and
+kernel time breakdown, batch-128 windows at contexts 1024, 5120 and 9216 with their
+integral over the 1K-in / 8K-out run, the nucleus (top-p) truncation kernel at the batch-1 and
 batch-128 row counts, and the CPU oracle timed on a bounded sample on the host.
 """
 import argparse
@@ -159,6 +160,26 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
         "gemm_mfma_tflops": mfma_tflops, "gemm_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
         "fill_s": t_fill, "breakdown": breakdown,
     }
+
+
+def integrate_windows(windows, batch, B):
+    """Whole-run figures of a batch leg measured in windows at several contexts: the
+    iteration time is taken piecewise linear in the context between the windows
+    (trapezoid rule), and every iteration emits batch * 2 * TPF tokens, so the
+    run's rate is tokens per iteration over the mean iteration time."""
+    if len(windows) < 2:
+        return None
+    ws = sorted(windows, key=lambda d: d["context_start"])
+    span = ws[-1]["context_start"] - ws[0]["context_start"]
+    if span <= 0:
+        return None
+    mean_ms = sum((b["context_start"] - a["context_start"]) * (a["ms_per_step"] + b["ms_per_step"]) / 2
+                  for a, b in zip(ws, ws[1:])) / span
+    tpf = sum(d["tokens_per_forward"] for d in ws) / len(ws)
+    return {"contexts": [d["context_start"] for d in ws], "method": "trapezoid over the windows",
+            "mean_ms_per_step": mean_ms, "tokens_per_forward": tpf,
+            "accepted_tokens_per_s": batch * 2 * tpf / (mean_ms / 1e3),
+            "positions_per_s": batch * 2 * B / (mean_ms / 1e3)}
 
 
 def run_distill(cfg, w, dev, batch, L, B, reps):
@@ -330,8 +351,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--bs128-steps", type=int, default=6,
                     help="timed iterations of the batch-128 leg (0 skips it)")
-    ap.add_argument("--bs128-ctx", type=str, default="1024",
-                    help="comma-separated starting contexts of the batch-128 leg")
+    ap.add_argument("--bs128-ctx", type=str, default="1024,5120,9216",
+                    help="comma-separated starting contexts of the batch-128 leg (windows "
+                         "over the 1K-in / 8K-out run)")
     ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
                     help="distillation-forward leg (batch, L, block size); 'none' skips it")
     ap.add_argument("--distill-reps", type=int, default=2)
@@ -473,6 +495,7 @@ def main():
     if args.bs128_steps > 0:
         result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
                            for c in args.bs128_ctx.split(",")]
+        result["bs128_run"] = integrate_windows(result["bs128"], 128, B)
     if args.distill != "none":
         db, dl, dbs = (int(v) for v in args.distill.split(","))
         result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)
