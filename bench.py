@@ -357,6 +357,9 @@ def main():
     ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
                     help="distillation-forward leg (batch, L, block size); 'none' skips it")
     ap.add_argument("--distill-reps", type=int, default=2)
+    ap.add_argument("--distill-b-sweep", type=str, default="4,8,32",
+                    help="further block sizes of the distillation leg, one timed forward "
+                         "each ('none' skips them)")
     ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
                     help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -499,6 +502,12 @@ def main():
     if args.distill != "none":
         db, dl, dbs = (int(v) for v in args.distill.split(","))
         result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)
+        if args.distill_b_sweep != "none":
+            keys = ("B", "ms_per_forward", "tflops", "mfma_frac", "rows_per_s", "mean_tv_block")
+            result["distill_b_sweep"] = [
+                {k: d[k] for k in keys}
+                for d in (run_distill(cfg, w, dev, db, dl, int(b), 1)
+                          for b in args.distill_b_sweep.split(","))]
     if args.top_p_leg:
         # one launch filters the B draft (or verify) rows of every sequence
         result["top_p"] = run_top_p(cfg.vocab, [B, 128 * B])

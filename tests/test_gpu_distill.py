@@ -122,10 +122,11 @@ def w8():
     return synth.weights_numpy(CFG8, 1001, with_embed=True)
 
 
-@pytest.mark.parametrize("L,B", [(48, 8), (64, 16), (64, 4)])
+@pytest.mark.parametrize("L,B", [(48, 8), (64, 16), (64, 4), (64, 32)])
 def test_layer8b_distill_forward(w8, L, B):
     """L = 48: the LM head runs on the skinny kernel (48 rows); L = 64: the large-M
-    kernels; B = 4 and 8: one 16-row attention tile spans several blocks."""
+    kernels; B = 4 and 8: one 16-row attention tile spans several blocks; B = 32: a
+    block spans two tiles."""
     log(f"layer8b distill L={L} B={B}")
     eng = engine(CFG8, w8, max_seqs=1, max_seq_len=2 * L + 16, max_rows=2 * L)
     x = synth.prompts(CFG8, 7300 + L + B, 1, L).astype(np.int32)
