@@ -26,6 +26,7 @@ Citations name the web page and its section.  The pages are:
 Modules:
   rng      Philox4x64-10, the 24-bit uniform, the integer inverse-CDF sampler.
   model    the decoder forward with gated LoRA, RoPE, GQA and a KV cache.
-  psispec  prefill, draft, verify, accept/resample, commit, generation loop.
+  psispec  prefill, draft, verify, accept/resample, commit, generation loop (top-p optional).
   distill  the [x, z1] block-causal forward with teacher/student logits and TV.
+  nucleus  the top-p truncation of a probability row (exact fixed-point reading).
 """
