@@ -166,7 +166,9 @@ uno_status uno_prefill(uno_ctx* ctx, int32_t n, const int32_t* seq_ids,
 /* Draft forward [blog Psi-Spec sampler]: rows [t, MASK x (B-1)] at n..n+B-1 with
  * gate [0,1,...,1]; samples y_1 from row 0 (AR) and y_i from row i-1 (q_i).
  * d_draft: device int32 [n, B] (y_1..y_B), may be NULL.  d_probs: device float32
- * [n, B, vocab] (row 0 = p(y_1), rows 1.. = q_2..q_B), may be NULL. */
+ * [n, B, vocab] (row 0 = p(y_1), rows 1.. = q_2..q_B), may be NULL.  With
+ * config.top_p in (0, 1) every row is first truncated to its nucleus (the
+ * uno_top_p rule): the draws and d_probs use the truncated laws. */
 uno_status uno_draft(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_draft,
                      float* d_probs);
 
@@ -175,8 +177,10 @@ uno_status uno_draft(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d
  * first rejected slot from max(0, p_k - q_k) (bonus row p_{B+1} if none fails),
  * commits positions n..n+k-1 and makes z pending.  d_out: device int32 [n, B+1]
  * (k tokens, then -1); d_n_out: device int32 [n] (k in [2, B+1]).  d_probs: device
- * float32 [n, B, vocab] (p_2..p_{B+1}), may be NULL.  Needs a preceding uno_draft
- * of exactly these sequences. */
+ * float32 [n, B, vocab] (p_2..p_{B+1}), may be NULL.  With config.top_p in (0, 1)
+ * the p rows are truncated to their nuclei before the accept test, like the draft
+ * laws, so the emitted tokens follow the truncated AR law.  Needs a preceding
+ * uno_draft of exactly these sequences. */
 uno_status uno_verify(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
                       int32_t* d_n_out, float* d_probs);
 
