@@ -390,3 +390,8 @@ hipError_t launch_set_list(const SetList& l, hipStream_t s);
 template <typename T>
 hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,
                           hipStream_t s);
+
+// Records msg as the context-free last error (uno_last_error(NULL)); returns status.
+int32_t uno_fail_global(int32_t status, const char* msg);
+// Looks up the current device's address of the no-allocation scratch array.
+hipError_t noalloc_prime();

@@ -177,6 +177,11 @@ constexpr int kTimedLaunches = 32768;
 
 thread_local KernelTimer* g_kernel_timer = nullptr;
 
+int32_t uno_fail_global(int32_t status, const char* msg) {
+  g_last_error = msg;
+  return status;
+}
+
 namespace {
 
 // Arms the kernel timer for the launches of one call of a timed class: each of
@@ -881,6 +886,8 @@ uno_status uno_init(const uno_config* cfg, const uno_weights* wts, void* d_kv_po
     return s2;
   };
   hipError_t e;
+  // the current device's no-allocation scratch is looked up once, at set-up
+  if ((e = noalloc_prime())) return bad(e, "no-allocation scratch lookup");
   if ((e = hipHostMalloc((void**)&c->snap_host, sizeof(int32_t) * cfg->max_seqs, hipHostMallocDefault)))
     return bad(e, "hipHostMalloc");
   if ((e = hipEventCreateWithFlags(&c->snap_event, hipEventDisableTiming))) return bad(e, "hipEventCreate");

@@ -23,7 +23,7 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
             "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_every", "uno_timing_read",
-            "uno_distill_forward", "uno_pack_weight", "uno_top_p")
+            "uno_distill_forward", "uno_pack_weight", "uno_top_p", "uno_accept_noalloc")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -77,6 +77,8 @@ def lib():
         L.uno_step.argtypes = [vp, i32, P(i32), vp, vp]
         L.uno_accept.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.uno_sample.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
+        L.uno_accept_noalloc.argtypes = [u64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp]
         L.uno_forward.argtypes = [vp, i32, P(i32), i32, vp, vp, vp, vp, vp, vp]
         L.uno_kv_import.argtypes = [vp, i32, i32, vp, vp, i32, i32]
         L.uno_kv_export.argtypes = [vp, i32, i32, vp, vp]
@@ -365,6 +367,23 @@ def top_p(probs, p, out=None):
     if st != UNO_OK:
         raise UnoError(st, lib().uno_last_error(None).decode())
     return out
+
+
+def accept_noalloc(seed, p, q, draft, seq_ids, pos, iters, out, n_out, err=None, stream=None):
+    """uno_accept_noalloc on device tensors: p [n,B,V], q [n,B-1,V] (or None when B
+    is 1), draft [n,B]; seq_ids, pos, iters int32 [n]; outputs out [n,B+1] and n_out
+    [n] are caller-allocated, err an optional int32 [1] that receives the device
+    error bits.  Enqueued on `stream` (default: the current torch stream)."""
+    import torch
+    n, B = draft.shape
+    V = p.shape[-1]
+    s = stream or torch.cuda.current_stream(p.device)
+    st = lib().uno_accept_noalloc(C.c_uint64(seed), n, B, V, _ptr(p), _ptr(q), _ptr(draft),
+                                  _ptr(seq_ids), _ptr(pos), _ptr(iters), _ptr(out), _ptr(n_out),
+                                  _ptr(err), C.c_void_p(s.cuda_stream))
+    if st != UNO_OK:
+        raise UnoError(st, lib().uno_last_error(None).decode())
+    return out, n_out
 
 
 def pack_weights(cfg, w):

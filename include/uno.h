@@ -199,6 +199,30 @@ uno_status uno_accept(uno_ctx* ctx, int32_t n, const float* d_p, const float* d_
                       const int32_t* d_draft, const int32_t* d_seq_ids, const int32_t* d_pos,
                       const int32_t* d_iter, int32_t* d_out, int32_t* d_n_out);
 
+/* Accept/resample without a context and without allocating anything, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same kernels and the same results as
+ * uno_accept on a context whose seed, block_size and vocab are these: d_p
+ * [n, block_size, vocab] = p_2..p_{B+1}, d_q [n, block_size-1, vocab] = q_2..q_B
+ * (may be NULL when block_size is 1), d_draft [n, block_size], d_seq_ids / d_pos /
+ * d_iter [n] (device int32: Philox key word 1, the pending position, the
+ * iteration); outputs d_out [n, block_size+1] and d_n_out [n] as uno_verify.
+ * d_err (device int32, may be NULL): the call ORs its device error bits into it
+ * (1: a NaN / negative / > 1 probability, a draft id outside the vocabulary, or a
+ * row without integer mass), so the caller clears it beforehand.  Enqueued on
+ * stream (a hipStream_t) on the current device; calls neither hipMalloc nor
+ * hipFree.  Its working memory (row descriptors, CDF chunk sums, accept lengths,
+ * drawn tokens) is one static device array of 1.05 MiB per GPU, kept until the
+ * process ends and shared by every call on that GPU: calls that overlap on one
+ * GPU race.  Limits: n <= 1024 and vocab <= 262144 (128 CDF chunks of 2048);
+ * larger sizes, block_size outside 1..64 or a null required buffer give
+ * UNO_ERR_INVALID_ARG before anything is enqueued (text in uno_last_error(NULL)). */
+uno_status uno_accept_noalloc(uint64_t seed, int32_t n, int32_t block_size, int32_t vocab,
+                              const float* d_p, const float* d_q, const int32_t* d_draft,
+                              const int32_t* d_seq_ids, const int32_t* d_pos,
+                              const int32_t* d_iter, int32_t* d_out, int32_t* d_n_out,
+                              int32_t* d_err, void* stream);
+
 /* Categorical draws on caller-given rows (the parity entry of the sampler):
  * row r of d_w [rows, V] (float32 weights in [0, 1]) is drawn with
  * Philox(key = (seed, d_seq_ids[r]), counter = (d_pos[r], stream_id, d_iter[r], 0)).

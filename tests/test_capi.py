@@ -74,3 +74,17 @@ def test_init_rejects_null_buffers_before_touching_the_device():
                             C.byref(h))
     assert st == 1 and not h.value
     assert b"null" in uno.lib().uno_last_error(None)
+
+
+def test_accept_noalloc_rejects_sizes_beyond_its_scratch():
+    """Host-side checks of uno_accept_noalloc run before any device call."""
+    lib = uno.lib()
+    nz = C.c_void_p(16)          # never dereferenced: validation fails first
+    for n, B, V in ((1025, 16, 151936), (0, 16, 32), (4, 65, 32), (4, 16, 262145), (4, 16, 1)):
+        st = lib.uno_accept_noalloc(C.c_uint64(1), n, B, V, nz, nz, nz, nz, nz, nz, nz, nz,
+                                    None, None)
+        assert st == 1, (n, B, V)
+        assert b"accept_noalloc" in lib.uno_last_error(None)
+    st = lib.uno_accept_noalloc(C.c_uint64(1), 4, 16, 32, nz, None, nz, nz, nz, nz, nz, nz,
+                                None, None)
+    assert st == 1 and b"null" in lib.uno_last_error(None)
