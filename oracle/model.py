@@ -135,6 +135,46 @@ def new_cache(cfg, n_seqs, max_len):
     return {"k": np.zeros(shape), "v": np.zeros(shape)}
 
 
+def _proj(cfg, lw, name, h, gate):
+    la, lb = lw.get("la", {}), lw.get("lb", {})
+    return gated_lora_linear(cfg, h, lw["w"][name], la.get(name), lb.get(name), gate)
+
+
+# A layer as five stages.  Each stage returns its result before the storage
+# rounding of its output (``_store``), so a stage can be evaluated on its own from
+# given inputs; ``layer_forward`` chains them with the rounding in place.
+
+def qkv_stage(cfg, lw, x, pos, gate):
+    """Attention inputs of rows x [S, R, d]: q [S, R, Hq, hd] and k [S, R, Hkv, hd]
+    after RoPE at positions ``pos``, and v, from the pre-attention RMSNorm and the
+    gated q / k / v projections."""
+    S, R, _ = x.shape
+    Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    h = norm_input(cfg, x, lw["attn_norm"], cfg.rms_eps)
+    q = _proj(cfg, lw, "q", h, gate).reshape(S, R, Hq, hd)
+    k = _proj(cfg, lw, "k", h, gate).reshape(S, R, Hkv, hd)
+    v = _proj(cfg, lw, "v", h, gate).reshape(S, R, Hkv, hd)
+    return rope(q, pos, cfg.rope_theta), rope(k, pos, cfg.rope_theta), v
+
+
+def o_stage(cfg, lw, x, o, gate):
+    """Residual stream after the attention block: x + o_proj(o), o [S, R, Hq * hd]."""
+    return x + _proj(cfg, lw, "o", o, gate)
+
+
+def mlp_act_stage(cfg, lw, x, gate):
+    """SwiGLU product silu(gate(h2)) * up(h2) of the pre-MLP RMSNorm h2 of x."""
+    h2 = norm_input(cfg, x, lw["mlp_norm"], cfg.rms_eps)
+    g = _proj(cfg, lw, "gate", h2, gate)
+    u = _proj(cfg, lw, "up", h2, gate)
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def down_stage(cfg, lw, x, a, gate):
+    """Residual stream after the MLP: x + down(a)."""
+    return x + _proj(cfg, lw, "down", a, gate)
+
+
 def layer_forward(cfg, lw, x, pos, gate, kcache, vcache, visible, slots=None):
     """One pre-norm decoder layer on rows x [S, R, d] (float64, updated copy returned).
 
@@ -145,31 +185,16 @@ def layer_forward(cfg, lw, x, pos, gate, kcache, vcache, visible, slots=None):
     if slots is None:
         slots = pos
     S, R, d = x.shape
-    Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    w, la, lb = lw["w"], lw.get("la", {}), lw.get("lb", {})
-
-    def proj(name, h):
-        return gated_lora_linear(cfg, h, w[name], la.get(name), lb.get(name), gate)
-
-    h = norm_input(cfg, x, lw["attn_norm"], cfg.rms_eps)
-    q = proj("q", h).reshape(S, R, Hq, hd)
-    k = proj("k", h).reshape(S, R, Hkv, hd)
-    v = proj("v", h).reshape(S, R, Hkv, hd)
-    q = _store(cfg, rope(q, pos, cfg.rope_theta))
-    k = _store(cfg, rope(k, pos, cfg.rope_theta))
-    v = _store(cfg, v)
+    Hq, hd = cfg.n_q_heads, cfg.head_dim
+    q, k, v = qkv_stage(cfg, lw, x, pos, gate)
+    q, k, v = _store(cfg, q), _store(cfg, k), _store(cfg, v)
     sidx = np.arange(S)[:, None]
     kcache[sidx, slots] = k
     vcache[sidx, slots] = v
-    o = attention(q, kcache, vcache, visible)
-    o = _store(cfg, o.reshape(S, R, Hq * hd))
-    x = x + proj("o", o)
-    h2 = norm_input(cfg, x, lw["mlp_norm"], cfg.rms_eps)
-    g = proj("gate", h2)
-    u = proj("up", h2)
-    a = _store(cfg, g / (1.0 + np.exp(-g)) * u)
-    x = x + proj("down", a)
-    return x
+    o = _store(cfg, attention(q, kcache, vcache, visible).reshape(S, R, Hq * hd))
+    x = o_stage(cfg, lw, x, o, gate)
+    a = _store(cfg, mlp_act_stage(cfg, lw, x, gate))
+    return down_stage(cfg, lw, x, a, gate)
 
 
 def lm_logits(cfg, weights, x):

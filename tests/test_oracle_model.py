@@ -112,11 +112,20 @@ def test_gated_lora_special_cases():
     assert np.allclose(y[gate == 1], merged[gate == 1], rtol=1e-12, atol=1e-12)
 
 
-def _torch_forward(cfg, w, tokens, gate):
+STORE_POINTS = ("norm", "lora", "q", "k", "v", "attn", "act")
+
+
+def _torch_forward(cfg, w, tokens, gate, store=()):
     """Independent float64 causal forward from torch library routines (linear,
-    rms_norm, scaled_dot_product_attention with is_causal, silu)."""
+    rms_norm, scaled_dot_product_attention with is_causal, silu).  ``store`` names
+    the values rounded to bfloat16 (torch's conversion) as a bf16 configuration
+    stores them: "norm" the gain-scaled RMSNorm input x * g (times the exact
+    1 / rms), "lora" the scaled LoRA intermediate, "q" / "k" after RoPE, "v", "attn"
+    the attention output and "act" the SwiGLU product."""
     F = torch.nn.functional
     T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    st = {p: (lambda t: t.to(torch.bfloat16).to(torch.float64)) if p in store else (lambda t: t)
+          for p in STORE_POINTS}
     x = T(w["embed"])[torch.from_numpy(np.asarray(tokens))]            # [R, d]
     R = x.shape[0]
     g = T(gate)[:, None]
@@ -131,21 +140,27 @@ def _torch_forward(cfg, w, tokens, gate):
         a, b = t[..., :half], t[..., half:]
         return torch.cat([a * cos - b * sin, b * cos + a * sin], -1)
 
+    def norm(xx, gain):
+        if "norm" not in store:
+            return F.rms_norm(xx, (cfg.d_model,), T(gain), cfg.rms_eps)
+        rs = torch.rsqrt(xx.pow(2).mean(-1, keepdim=True) + cfg.rms_eps)
+        return st["norm"](xx * T(gain)) * rs
+
     for lw in w["layers"]:
         def lin(p, hh):
-            return F.linear(hh, T(lw["w"][p])) + g * F.linear(s * F.linear(hh, T(lw["la"][p])),
-                                                              T(lw["lb"][p]))
-        h = F.rms_norm(x, (cfg.d_model,), T(lw["attn_norm"]), cfg.rms_eps)
-        q = rot(lin("q", h).view(R, Hq, hd)).transpose(0, 1)
-        k = rot(lin("k", h).view(R, Hkv, hd)).transpose(0, 1)
-        v = lin("v", h).view(R, Hkv, hd).transpose(0, 1)
+            u = st["lora"](s * F.linear(hh, T(lw["la"][p])))
+            return F.linear(hh, T(lw["w"][p])) + g * F.linear(u, T(lw["lb"][p]))
+        h = norm(x, lw["attn_norm"])
+        q = st["q"](rot(lin("q", h).view(R, Hq, hd))).transpose(0, 1)
+        k = st["k"](rot(lin("k", h).view(R, Hkv, hd))).transpose(0, 1)
+        v = st["v"](lin("v", h).view(R, Hkv, hd)).transpose(0, 1)
         k = k.repeat_interleave(Hq // Hkv, 0)
         v = v.repeat_interleave(Hq // Hkv, 0)
         o = F.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)[0]
-        x = x + lin("o", o.transpose(0, 1).reshape(R, Hq * hd))
-        h2 = F.rms_norm(x, (cfg.d_model,), T(lw["mlp_norm"]), cfg.rms_eps)
-        x = x + lin("down", F.silu(lin("gate", h2)) * lin("up", h2))
-    hf = F.rms_norm(x, (cfg.d_model,), T(w["final_norm"]), cfg.rms_eps)
+        x = x + lin("o", st["attn"](o.transpose(0, 1).reshape(R, Hq * hd)))
+        h2 = norm(x, lw["mlp_norm"])
+        x = x + lin("down", st["act"](F.silu(lin("gate", h2)) * lin("up", h2)))
+    hf = norm(x, w["final_norm"])
     logits = F.linear(hf, T(w["lm_head"]))
     logits[:, cfg.mask_id] = -float("inf")
     return logits.numpy()
@@ -234,3 +249,37 @@ def test_norm_input_is_rms_norm():
     y = model.norm_input(cfg, x, g, 1e-6)
     assert np.allclose(y, ref, rtol=2.0 ** -8, atol=1e-12)
     assert not np.allclose(y, ref, rtol=1e-9, atol=0)
+
+
+def _bf16_case():
+    cfg = TINY.with_(dtype="bf16")
+    w = synth.weights_numpy(cfg, 1000, lm_head_std=0.35, lora_b_std=0.6)
+    r = np.random.default_rng(10)
+    R = 12
+    toks = r.integers(0, cfg.vocab - 1, size=R)
+    gate = (r.random(R) < 0.5).astype(np.float64)
+    cache = model.new_cache(cfg, 1, R)
+    logits, _ = model.forward(cfg, w, toks[None], np.arange(R)[None], gate[None], cache)
+    return cfg, w, toks, gate, logits[0]
+
+
+def test_bf16_storage_points_match_torch_library_forward():
+    """The bf16 oracle rounds exactly at the storage points of the bf16 reading
+    (gain-scaled norm input, LoRA intermediate, q, k, v, attention output, SwiGLU
+    product): it equals an independent torch forward that rounds there by torch's
+    own bfloat16 conversion."""
+    cfg, w, toks, gate, got = _bf16_case()
+    ref = _torch_forward(cfg, w, toks, gate, store=STORE_POINTS)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.allclose(got[fin], ref[fin], rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("skip", STORE_POINTS)
+def test_bf16_storage_pin_has_power(skip):
+    """Leaving out any one rounding point moves the logits far beyond the pin's
+    tolerance, so an oracle that forgot (or misplaced) one would fail the pin."""
+    cfg, w, toks, gate, got = _bf16_case()
+    ref = _torch_forward(cfg, w, toks, gate, store=tuple(p for p in STORE_POINTS if p != skip))
+    fin = np.isfinite(ref)
+    assert np.abs(got[fin] - ref[fin]).max() > 1e-5
