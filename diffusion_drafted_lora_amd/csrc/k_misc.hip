@@ -225,6 +225,18 @@ __global__ void k_pack(const bf16* __restrict__ src, bf16* __restrict__ dst, int
       *reinterpret_cast<const uint4*>(src + (size_t)sr * cols + c);
 }
 
+// Row-major copy of a fragment-tiled bf16 activation, eight columns per thread
+// (eight consecutive columns of a row are eight consecutive elements of a block).
+__global__ void __launch_bounds__(256)
+k_untile(const bf16* __restrict__ src, bf16* __restrict__ dst, int R, int C) {
+  const long i = blockIdx.x * 256L + threadIdx.x;
+  const int per = C / 8;
+  if (i >= (long)R * per) return;
+  const int r = (int)(i / per), c = (int)(i % per) * 8;
+  *reinterpret_cast<bf16x8*>(dst + (size_t)r * C + c) =
+      *reinterpret_cast<const bf16x8*>(src + frag_off(r, c, C));
+}
+
 __global__ void k_set_list(SetList l) {
   for (int i = threadIdx.x; i < l.count; i += blockDim.x) l.dst[l.idx[i]] = l.val[i];
 }
@@ -297,6 +309,20 @@ hipError_t launch_pack(const bf16* src, bf16* dst, int rows, int cols, int pair_
   const size_t n = (size_t)rows * cols / 8;
   uno_launch(k_pack, (unsigned)((n + 255) / 256), 256, 0, s, src, dst, rows, cols, pair_hd);
   return hipGetLastError();
+}
+
+template <>
+hipError_t launch_untile<bf16>(const bf16* src, bf16* dst, int R, int C, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (C % 32) return hipErrorInvalidValue;
+  const long n = (long)R * (C / 8);
+  uno_launch(k_untile, (unsigned)((n + 255) / 256), 256, 0, s, src, dst, R, C);
+  return hipGetLastError();
+}
+template <>
+hipError_t launch_untile<float>(const float* src, float* dst, int R, int C, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  return hipMemcpyAsync(dst, src, sizeof(float) * (size_t)R * C, hipMemcpyDeviceToDevice, s);
 }
 
 hipError_t launch_set_list(const SetList& l, hipStream_t s) {

@@ -391,6 +391,13 @@ template <typename T>
 hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,
                           hipStream_t s);
 
+// Row-major copy [R, C] of an activation buffer of the linear kernels' layout
+// (fragment-tiled bf16, row-major float32).
+template <typename T>
+hipError_t launch_untile(const T* src, T* dst, int R, int C, hipStream_t s);
+template <> hipError_t launch_untile<bf16>(const bf16* src, bf16* dst, int R, int C, hipStream_t s);
+template <> hipError_t launch_untile<float>(const float* src, float* dst, int R, int C, hipStream_t s);
+
 // Records msg as the context-free last error (uno_last_error(NULL)); returns status.
 int32_t uno_fail_global(int32_t status, const char* msg);
 // Looks up the current device's address of the no-allocation scratch array.

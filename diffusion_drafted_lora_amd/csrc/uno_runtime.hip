@@ -142,6 +142,9 @@ struct uno_ctx {
   hipEvent_t snap_event = nullptr;
   bool snap_inflight = false;
   std::vector<int> snap_base;
+  // stage capture
+  bool trace_on = false;
+  uno_trace trace{};
   // kernel timing
   uint32_t tmask = 0;
   int32_t tperiod = 1;                  // record every tperiod-th call of a class
@@ -470,6 +473,22 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // before its MLP, [2L] before the LM head; SS_BANKS words per row
   long long* ssb = c->at<long long>(c->L.ss);
   auto SS = [&](int i) { return ssb + (size_t)i * R * SS_BANKS; };
+  // stage capture of the armed trace (row-major copies into caller buffers)
+  auto traced = [&](int l) -> const uno_trace_layer* {
+    if (!c->trace_on) return nullptr;
+    for (int i = 0; i < c->trace.n; ++i)
+      if (c->trace.layer[i].layer == l) return &c->trace.layer[i];
+    return nullptr;
+  };
+  auto cap_x = [&](float* dst) -> uno_status {
+    if (dst) UNO_HIP(c, hipMemcpyAsync(dst, c->at<float>(c->L.x), sizeof(float) * R * d,
+                                       hipMemcpyDeviceToDevice, s));
+    return UNO_OK;
+  };
+  auto cap_act = [&](void* dst, const T* src, int cols) -> uno_status {
+    if (dst) UNO_HIP(c, launch_untile<T>(src, reinterpret_cast<T*>(dst), R, cols, s));
+    return UNO_OK;
+  };
   // LoRA down-projection of each group (buffer b): qkv, o, gate/up, down.  Large M
   // (every group fits the tile kernel): tsl[b] K-slice float partials stored into
   // the tfx region, summed in slice order, gated and scaled into ubuf -- no
@@ -609,6 +628,8 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   };
 
   for (int l = 0; l < L; ++l) {
+    const uno_trace_layer* tr = traced(l);
+    if (tr) { if (uno_status st = cap_x(tr->x_in)) return st; }
     // --- attention block: q|k|v (+LoRA) with RoPE and the paged K/V write
     static const int pqkv[3] = {0, 1, 2};
     if (lora) { uno_status st = lora_down(xg, d, 3, pqkv, l, 0, 2 * l); if (st) return st; }
@@ -633,6 +654,8 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
       if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
     }
+    if (tr && tr->q)
+      UNO_HIP(c, hipMemcpyAsync(tr->q, qbuf, sizeof(T) * R * qd, hipMemcpyDeviceToDevice, s));
     {
       AttnArgs a{};
       a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
@@ -657,6 +680,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       Timed t(c, UNO_KC_ATTENTION, kvb + pb + io, fl);
       UNO_HIP(c, launch_attention<T>(a, kv, s));
     }
+    if (tr) { if (uno_status st = cap_act(tr->attn, obuf, qd)) return st; }
     static const int po[1] = {3};
     if (lora) { uno_status st = lora_down(obuf, qd, 1, po, l, 1, -1); if (st) return st; }
     {
@@ -671,6 +695,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       split_ws(a);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
+    if (tr) { if (uno_status st = cap_x(tr->x_mid)) return st; }
     // --- MLP block
     static const int pgu[2] = {4, 5};
     if (lora) { uno_status st = lora_down(xg, d, 2, pgu, l, 2, 2 * l + 1); if (st) return st; }
@@ -687,6 +712,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       a.epi = EPI_SWIGLU; a.ldo = F; a.out = hbuf;
       if (uno_status st = run_gemm(a, F, UNO_KC_LINEAR_SWIGLU)) return st;
     }
+    if (tr) { if (uno_status st = cap_act(tr->act, hbuf, F)) return st; }
     static const int pd[1] = {6};
     if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l, 3, -1); if (st) return st; }
     {
@@ -703,6 +729,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       split_ws(a);
       if (uno_status st = run_gemm(a, d, UNO_KC_LINEAR)) return st;
     }
+    if (tr) { if (uno_status st = cap_x(tr->x_out)) return st; }
   }
   if (f.hidden_out)
     UNO_HIP(c, hipMemcpyAsync(f.hidden_out, x, sizeof(float) * R * d, hipMemcpyDeviceToDevice, s));
@@ -752,6 +779,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     a.epi = EPI_LOGITS; a.ldo = V; a.out = c->at<float>(c->L.logits);
     a.mask_col = g.mask_id; a.tile_stats = c->at<float>(c->L.tile_stats); a.n_tiles = V / 16;
     if (uno_status st = run_gemm(a, V, UNO_KC_LM_HEAD)) return st;
+    if (c->trace_on && c->trace.logits)
+      UNO_HIP(c, hipMemcpyAsync(c->trace.logits, c->at<float>(c->L.logits), sizeof(float) * R * V,
+                                hipMemcpyDeviceToDevice, s));
     if (f.probs_out) {
       Timed t(c, UNO_KC_SAMPLING, (double)R * V * 8 + (double)R * (V / 16) * 8, 0);
       UNO_HIP(c, launch_row_stats(a.tile_stats, R, V / 16, c->at<float>(c->L.row_ml), s));
@@ -1182,6 +1212,22 @@ uno_status uno_distill_forward(uno_ctx* c, int32_t batch, int32_t L, int32_t B, 
     if (st) return st;
     if (st2) return st2;
   }
+  return UNO_OK;
+}
+
+uno_status uno_set_trace(uno_ctx* c, const uno_trace* t) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (!t) {
+    c->trace_on = false;
+    c->trace = uno_trace{};
+    return UNO_OK;
+  }
+  if (t->n < 0 || t->n > 4) return fail(c, UNO_ERR_INVALID_ARG, "trace: n must be 0..4");
+  for (int i = 0; i < t->n; ++i)
+    if (t->layer[i].layer >= c->cfg.n_layers)
+      return fail(c, UNO_ERR_INVALID_ARG, "trace: layer index >= n_layers");
+  c->trace = *t;
+  c->trace_on = true;
   return UNO_OK;
 }
 

@@ -23,7 +23,8 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_step", "uno_accept", "uno_sample", "uno_forward", "uno_kv_import",
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
             "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_every", "uno_timing_read",
-            "uno_distill_forward", "uno_pack_weight", "uno_top_p", "uno_accept_noalloc")
+            "uno_distill_forward", "uno_pack_weight", "uno_top_p", "uno_accept_noalloc",
+            "uno_set_trace")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -47,6 +48,18 @@ class UnoConfigC(C.Structure):
 
 
 PP = C.POINTER(C.c_void_p)
+
+
+class UnoTraceLayerC(C.Structure):
+    _fields_ = [("layer", C.c_int32), ("x_in", C.c_void_p), ("q", C.c_void_p),
+                ("attn", C.c_void_p), ("x_mid", C.c_void_p), ("act", C.c_void_p),
+                ("x_out", C.c_void_p)]
+
+
+class UnoTraceC(C.Structure):
+    _fields_ = [("n", C.c_int32), ("layer", UnoTraceLayerC * 4), ("logits", C.c_void_p)]
+
+TRACE_FIELDS = ("x_in", "q", "attn", "x_mid", "act", "x_out")
 
 
 class UnoWeightsC(C.Structure):
@@ -80,6 +93,7 @@ def lib():
         L.uno_accept_noalloc.argtypes = [u64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp]
         L.uno_forward.argtypes = [vp, i32, P(i32), i32, vp, vp, vp, vp, vp, vp]
+        L.uno_set_trace.argtypes = [vp, P(UnoTraceC)]
         L.uno_kv_import.argtypes = [vp, i32, i32, vp, vp, i32, i32]
         L.uno_kv_export.argtypes = [vp, i32, i32, vp, vp]
         L.uno_seq_state.argtypes = [vp, i32, P(i32), P(i32), P(i32)]
@@ -297,6 +311,40 @@ class Engine:
         self._check(lib().uno_distill_forward(self.h, batch, L, B, _ptr(x), _ptr(teacher),
                                               _ptr(student), _ptr(tv_row), _ptr(tv_block)))
         return teacher, student, tv_row, tv_block
+
+    def set_trace(self, rows, layers=(), logits=False):
+        """Arm the stage capture for forwards of `rows` rows: for each layer index
+        in `layers` (at most four) device buffers for x_in, q, attn, x_mid, act and
+        x_out, plus the logits when asked; returns {layer: {field: tensor}} and
+        (under the key "logits") the logits tensor.  rows=None disarms."""
+        torch = self.torch
+        if rows is None:
+            self._check(lib().uno_set_trace(self.h, None))
+            self._trace = None
+            return None
+        cfg = self.cfg
+        st = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        f32 = torch.float32
+        shapes = {"x_in": (cfg.d_model, f32), "q": (cfg.q_dim, st), "attn": (cfg.q_dim, st),
+                  "x_mid": (cfg.d_model, f32), "act": (cfg.ffn_dim, st),
+                  "x_out": (cfg.d_model, f32)}
+        tc = UnoTraceC()
+        tc.n = len(layers)
+        bufs = {}
+        for i, l in enumerate(layers):
+            tc.layer[i].layer = l
+            bufs[l] = {}
+            for f in TRACE_FIELDS:
+                cols, dt = shapes[f]
+                t = self._empty((rows, cols), dt)
+                bufs[l][f] = t
+                setattr(tc.layer[i], f, t.data_ptr())
+        if logits:
+            bufs["logits"] = self._empty((rows, cfg.vocab), f32)
+            tc.logits = bufs["logits"].data_ptr()
+        self._check(lib().uno_set_trace(self.h, C.byref(tc)))
+        self._trace = bufs          # the library writes into these: keep them alive
+        return bufs
 
     def kv_import(self, seq_id, k, v, pending, iteration=0):
         """k, v: device tensors [layers, len, Hkv, hd] of the storage dtype."""

@@ -267,6 +267,37 @@ uno_status uno_distill_forward(uno_ctx* ctx, int32_t batch, int32_t L, int32_t B
                                const int32_t* d_x, float* d_teacher, float* d_student,
                                float* d_tv_row, float* d_tv_block);
 
+/* Stage capture (parity instrumentation).  While a trace is armed, every forward
+ * of the context (draft, verify, uno_forward, prefill chunks, the distillation
+ * forward) copies, on its stream, the intermediates of up to four layers and its
+ * logits into caller-owned device buffers, so each stage of the layer can be
+ * checked on its own against a reference fed the same inputs.  R is the number
+ * of rows of that forward, in call order (draft / verify: n * block_size; the
+ * distillation forward: 2L per sequence; every prefill chunk overwrites the
+ * previous one's).  Each pointer may be NULL (not captured).  Matrices are
+ * row-major; "storage type" means bfloat16 or float32 as the config says.  The
+ * KV cache itself is read with uno_kv_export.  Disarm before timing: the copies
+ * are enqueued between the kernels. */
+typedef struct {
+  int32_t layer;     /* layer index; an entry with layer < 0 is ignored              */
+  float* x_in;       /* [R, d_model] float32 residual stream entering the layer      */
+  void* q;           /* [R, n_q_heads * head_dim] storage type: queries after RoPE    */
+  void* attn;        /* [R, n_q_heads * head_dim] storage type: attention output      */
+  float* x_mid;      /* [R, d_model] float32 residual after the o projection         */
+  void* act;         /* [R, ffn_dim] storage type: SwiGLU product silu(g) * u         */
+  float* x_out;      /* [R, d_model] float32 residual after the down projection      */
+} uno_trace_layer;
+typedef struct {
+  int32_t n;                 /* entries of layer[] in use, 0..4                     */
+  uno_trace_layer layer[4];
+  float* logits;             /* [R, vocab] float32 logits (MASK column -inf) of the
+                                forwards that run the LM head (draft, verify,
+                                uno_forward with logits), or NULL                  */
+} uno_trace;
+/* Arm (trace != NULL; the struct is copied) or disarm (NULL) the capture.
+ * UNO_ERR_INVALID_ARG when n is outside 0..4 or a layer index is >= n_layers. */
+uno_status uno_set_trace(uno_ctx* ctx, const uno_trace* trace);
+
 /* Copy a sequence's K/V for positions [0, len) in from / out to contiguous device
  * buffers [n_layers][len][n_kv_heads][head_dim] of the storage type.  Import
  * reserves pages, sets the committed length to len and the pending token and
