@@ -37,7 +37,7 @@ UNO_DEV bf16x8 load8_stream(const bf16* p) {
 
 UNO_DEV float rs_of(const GemmArgs& a, int m) {
   if (!a.ss_in || m >= a.M) return 1.0f;
-  const float ms = fx_to_float(ss_row(a.ss_in, m)) * a.inv_d;
+  const float ms = fx_to_float(ss_row(a.ss_in, m, a.err)) * a.inv_d;
   return 1.0f / sqrtf(ms + a.eps);
 }
 
@@ -118,7 +118,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       if (a.ss_out) {
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 16);
-        if (ok && c == 0) ss_add(a.ss_out, m, blockIdx.x, sq);
+        if (ok && c == 0) ss_add(a.ss_out, m, blockIdx.x, sq, a.err);
       }
       break;
     }
@@ -351,6 +351,7 @@ k_gemm_bf16(GemmArgs a) {
   // ---- RMSNorm: scale rows of the base product by 1 / rms(x)
   if (a.ss_in) {
     long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
+    if (w == 0) ss_check(ssq0.x | ssq0.y | ssq1.x | ssq1.y, a.err);
     sq += __shfl_xor(sq, 1);
     sq += __shfl_xor(sq, 2);
 #pragma unroll
@@ -795,7 +796,7 @@ k_gemm_tile(GemmArgs a, int nbm, int nbn) {
 #pragma unroll
       for (int off = IPR / 2; off > 0; off >>= 1) sq += __shfl_xor(sq, off, IPR);
       const int it = tid + NTH * k, m = m0 + it / IPR;
-      if (it % IPR == 0 && m < a.M) ss_add(a.ss_out, m, blockIdx.x, sq);
+      if (it % IPR == 0 && m < a.M) ss_add(a.ss_out, m, blockIdx.x, sq, a.err);
     }
   }
 }
@@ -912,6 +913,7 @@ k_lora_down(LoraDownArgs a) {
   for (int i = 0; i < 4; ++i) red[w][((lane >> 4) * 4 + i) * 16 + r16] = acc[i];
   if (w == 0) {
     long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
+    ss_check(ssq0.x | ssq0.y | ssq1.x | ssq1.y, a.err);
     sq += __shfl_xor(sq, 1);
     sq += __shfl_xor(sq, 2);
     if ((lane & 3) == 0)
@@ -976,7 +978,7 @@ __global__ void k_zero_i64(long long* p, size_t n) {
 __global__ void __launch_bounds__(256)
 k_resid_slices(const float* __restrict__ part, int n_slices, long long stride, int N,
                float* __restrict__ resid, bf16* __restrict__ xg_out, const bf16* __restrict__ g_next,
-               long long* __restrict__ ss_out) {
+               long long* __restrict__ ss_out, int32_t* err) {
   __shared__ float s_sq[4];
   const int m = blockIdx.y, col = (blockIdx.x * 256 + threadIdx.x) * 8;
   float sq = 0.0f;
@@ -1017,7 +1019,7 @@ k_resid_slices(const float* __restrict__ part, int n_slices, long long stride, i
   for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
   if ((threadIdx.x & 63) == 0) s_sq[threadIdx.x >> 6] = sq;
   __syncthreads();
-  if (threadIdx.x == 0) ss_add(ss_out, m, blockIdx.x, s_sq[0] + s_sq[1] + s_sq[2] + s_sq[3]);
+  if (threadIdx.x == 0) ss_add(ss_out, m, blockIdx.x, s_sq[0] + s_sq[1] + s_sq[2] + s_sq[3], err);
 }
 
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s) {
@@ -1160,7 +1162,7 @@ bool launch_resid_split(const GemmArgs& a, int n_cols_total, hipStream_t s, hipE
   if (*err != hipSuccess) return true;
   uno_launch(k_resid_slices, dim3((n_cols_total / 8 + 255) / 256, a.M), 256, 0, s, a.split_ws, S, stride,
              n_cols_total, a.resid, reinterpret_cast<bf16*>(a.xg_out), reinterpret_cast<const bf16*>(a.g_next),
-             a.ss_out);
+             a.ss_out, a.err);
   *err = hipGetLastError();
   return true;
 }

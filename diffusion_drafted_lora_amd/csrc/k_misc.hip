@@ -119,7 +119,7 @@ k_embed(const T* __restrict__ E, const int32_t* __restrict__ tok,
     // per-wave partials in fixed point, so the total does not depend on order
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-    if ((threadIdx.x & 63) == 0) ss_add(ss, r, threadIdx.x >> 6, sq);
+    if ((threadIdx.x & 63) == 0) ss_add(ss, r, threadIdx.x >> 6, sq, err);
   }
 }
 

@@ -188,17 +188,35 @@ UNO_DEV float fx_to_float(long long t) {
 // consumer adds the banks (integer sums: exact in any order).
 constexpr int SS_BANKS = 16;
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
-UNO_DEV long long ss_row(const long long* ss, int m) {
+// Range: a producer's partial must stay below 2^25 and a bank below 2^26 (2^58
+// fixed-point units), so a row's sum of squares is exact below 2^30 (an rms of 512
+// at d 4096).  At most 32 partials reach one bank, so clamping each partial to
+// 2^25 keeps every bank below 2^62: nothing wraps silently -- a producer whose
+// partial is out of range (or NaN) and a consumer that reads a bank of 2^58 or
+// more set the numeric flag.
+constexpr float SS_PART_MAX = 33554432.0f;          // 2^25
+constexpr long long SS_BANK_MAX = 1LL << 58;
+// A consumer's check of the banks it read (OR of the bank words).
+UNO_DEV void ss_check(long long banks_or, int32_t* err) {
+  if ((banks_or & ~(SS_BANK_MAX - 1)) != 0 && err) atomicOr(err, UNO_DEVERR_NUMERIC);
+}
+UNO_DEV long long ss_row(const long long* ss, int m, int32_t* err) {
   const i64x2* p = reinterpret_cast<const i64x2*>(ss + (size_t)m * SS_BANKS);
-  long long t = 0;
+  long long t = 0, o = 0;
 #pragma unroll
   for (int i = 0; i < SS_BANKS / 2; ++i) {
     const i64x2 v = p[i];
     t += v.x + v.y;
+    o |= v.x | v.y;
   }
+  ss_check(o, err);
   return t;
 }
-UNO_DEV void ss_add(long long* ss, int m, int bank, float sq) {
+UNO_DEV void ss_add(long long* ss, int m, int bank, float sq, int32_t* err) {
+  if (!(sq < SS_PART_MAX)) {                         // out of range, or NaN
+    if (err) atomicOr(err, UNO_DEVERR_NUMERIC);
+    sq = SS_PART_MAX;
+  }
   atomicAdd(reinterpret_cast<unsigned long long*>(ss + (size_t)m * SS_BANKS + (bank & (SS_BANKS - 1))),
             (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
 }
@@ -278,6 +296,7 @@ struct LoraDownArgs {
   long long* t;      // [M, nproj * r]
   const long long* ss_in;   // RMSNorm input (see GemmArgs), or null
   float inv_d, eps;
+  int32_t* err;             // device error flags (sum-of-squares range)
 };
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
 // Large-M LoRA down-projection on the tile kernel (EPI_TSLICE, no atomics): false

@@ -43,6 +43,7 @@ struct Layout {
   size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate, row_slot, row_vis, row_nc;
   size_t x, xn, qbuf, obuf, hbuf, ubuf, tfx, ss;
   size_t part_o, part_ml;
+  size_t part_o_floats, part_rows;   // capacities: float words, (row, head, chunk) triples / Hq
   size_t logits, tile_stats, row_ml, probs_d, probs_v;
   size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32, tv;
   size_t total;
@@ -94,8 +95,16 @@ Layout make_layout(const uno_config& c) {
   L.tfx = take(4 * R * 3 * r * tfx_slices(R) * 8 + 16);
   static_assert(sizeof(long long) == 8, "fixed-point words");
   L.ss = take((size_t)(2 * c.n_layers + 1) * R * SS_BANKS * 8);   // fixed-point sums of x^2
-  L.part_o = take(R * c.n_q_heads * kMaxChunks * c.head_dim * 4);
-  L.part_ml = take(R * c.n_q_heads * kMaxChunks * 2 * 4);
+  // Attention partials: a call splits the context into n_chunks <= target chunks,
+  // target = ceil(kAttnTargetWG / groups) with groups = n * Hkv * ceil(rows / 16), so
+  // rows * n_chunks <= 16 * kAttnTargetWG / Hkv + rows (and <= 64 * rows).  The
+  // same buffer holds the K-split slices of the residual products (<= 4 * R * d
+  // floats) between a layer's attention and the next.
+  L.part_rows = std::min(R * kMaxChunks,
+                         (size_t)16 * ((kAttnTargetWG + c.n_kv_heads - 1) / c.n_kv_heads) + 16 + R);
+  L.part_o_floats = std::max(L.part_rows * c.n_q_heads * c.head_dim, (size_t)4 * R * d);
+  L.part_o = take(L.part_o_floats * 4);
+  L.part_ml = take(L.part_rows * c.n_q_heads * 2 * 4);
   L.logits = take(R * V * 4);
   L.tile_stats = take(R * (V / 16) * 2 * 4);
   L.row_ml = take(R * 2 * 4);
@@ -133,6 +142,7 @@ struct uno_ctx {
   std::vector<std::vector<int>> seq_pages;
   std::vector<int> len_hi;          // upper bound of each committed length
   std::vector<char> live;           // sequence has been prefilled / imported
+  std::vector<uint32_t> epoch;      // bumped when a slot's sequence is replaced
   std::vector<int> pt_idx, pt_val;  // pending block-table writes
   std::vector<int> uploaded_call;   // call_seq contents on the device
   // draft bookkeeping
@@ -142,6 +152,7 @@ struct uno_ctx {
   hipEvent_t snap_event = nullptr;
   bool snap_inflight = false;
   std::vector<int> snap_base;
+  std::vector<uint32_t> snap_epoch;
   // stage capture
   bool trace_on = false;
   uno_trace trace{};
@@ -354,14 +365,20 @@ uno_status upload_call(uno_ctx* c, const std::vector<int>& seqs) {
   return scatter(c, c->at<int32_t>(c->L.call_seq), idx, val);
 }
 
-// Fold a finished length snapshot into the host bounds.
+// Fold a finished length snapshot into the host bounds.  A slot whose sequence
+// was released, prefilled or imported after the snapshot was taken (its epoch
+// moved on) keeps its bound: the snapshot describes the previous sequence.
 void poll_snapshot(uno_ctx* c) {
   if (!c->snap_inflight) return;
   if (hipEventQuery(c->snap_event) != hipSuccess) return;
   for (int s = 0; s < c->cfg.max_seqs; ++s)
-    if (c->live[s]) c->len_hi[s] = c->snap_host[s] + (c->len_hi[s] - c->snap_base[s]);
+    if (c->live[s] && c->epoch[s] == c->snap_epoch[s])
+      c->len_hi[s] = c->snap_host[s] + (c->len_hi[s] - c->snap_base[s]);
   c->snap_inflight = false;
 }
+
+// The slot's sequence is replaced (release, prefill, import).
+void new_epoch(uno_ctx* c, int s) { ++c->epoch[s]; }
 
 uno_status start_snapshot(uno_ctx* c) {
   if (c->snap_inflight) return UNO_OK;
@@ -369,6 +386,7 @@ uno_status start_snapshot(uno_ctx* c) {
                             sizeof(int32_t) * c->cfg.max_seqs, hipMemcpyDeviceToHost, c->stream));
   UNO_HIP(c, hipEventRecord(c->snap_event, c->stream));
   c->snap_base = c->len_hi;
+  c->snap_epoch = c->epoch;
   c->snap_inflight = true;
   return UNO_OK;
 }
@@ -530,9 +548,12 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   int chunk = (f.ctx_bound + target - 1) / target;
   chunk = std::max(kAttnMinChunk, (chunk + kAttnMinChunk - 1) / kAttnMinChunk * kAttnMinChunk);
   const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
-  if (n_chunks > kMaxChunks) return fail(c, UNO_ERR_INVALID_ARG, "attention chunking");
+  if (n_chunks > kMaxChunks || (size_t)R * n_chunks > c->L.part_rows)
+    return fail(c, UNO_ERR_INVALID_ARG, "attention chunking exceeds the partial buffers");
 
-  auto run_gemm = [&](const GemmArgs& a, int ncols, int cls) -> uno_status {
+  auto run_gemm = [&](const GemmArgs& a0, int ncols, int cls) -> uno_status {
+    GemmArgs a = a0;
+    a.err = err;
     double b, fl;
     gemm_cost(a, ncols, sizeof(T), &b, &fl);
     Timed t(c, cls, b, fl);
@@ -543,7 +564,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   // layer's attention: the o and down products may split K into them
   auto split_ws = [&](GemmArgs& a) {
     a.split_ws = c->at<float>(c->L.part_o);
-    a.split_cap = (long long)R * Hq * kMaxChunks * hd;
+    a.split_cap = (long long)c->L.part_o_floats;
   };
   auto norm_in = [&](GemmArgs& a, int ss_idx) {
     a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps;
@@ -559,6 +580,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       GemmArgs a{};
       a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = 0;
       a.nseg = nproj;
+      a.err = err;
       for (int i = 0; i < nproj; ++i) {
         a.seg[i].W = c->la[pidx[i]][l];
         a.seg[i].n0 = i * r;
@@ -581,6 +603,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     if (c->bf16) {
       LoraDownArgs a{};
       a.X = X; a.ldx = K; a.M = R; a.K = K; a.r = r; a.nproj = nproj; a.t = Bfx[buf];
+      a.err = err;
       if (ss_idx >= 0) { a.ss_in = SS(ss_idx); a.inv_d = 1.0f / (float)d; a.eps = g.rms_eps; }
       for (int i = 0; i < nproj; ++i) a.A[i] = c->la[pidx[i]][l];
       // about 128 workgroups: K chunks of whole 32-wide blocks
@@ -906,7 +929,9 @@ uno_status uno_init(const uno_config* cfg, const uno_weights* wts, void* d_kv_po
   c->seq_pages.assign(cfg->max_seqs, {});
   c->len_hi.assign(cfg->max_seqs, 0);
   c->live.assign(cfg->max_seqs, 0);
+  c->epoch.assign(cfg->max_seqs, 0);
   c->snap_base.assign(cfg->max_seqs, 0);
+  c->snap_epoch.assign(cfg->max_seqs, 0);
 
   auto bad = [&](hipError_t e, const char* w) {
     uno_status s2 = hip_fail(nullptr, e, w);
@@ -983,6 +1008,7 @@ uno_status uno_prefill(uno_ctx* c, int32_t n, const int32_t* seq_ids, const int3
                               sizeof(int32_t), hipMemcpyDeviceToDevice, c->stream));
     c->len_hi[seqs[i]] = P - 1;
     c->live[seqs[i]] = 1;
+    new_epoch(c, seqs[i]);
     off += P;
   }
   c->drafted_ids.clear();
@@ -1250,6 +1276,7 @@ uno_status uno_kv_import(uno_ctx* c, int32_t seq_id, int32_t len, const void* d_
   if ((st = set_state(c, seq_id, len, pending, iter))) return st;
   c->len_hi[seq_id] = len;
   c->live[seq_id] = 1;
+  new_epoch(c, seq_id);
   return UNO_OK;
 }
 
@@ -1293,6 +1320,7 @@ uno_status uno_release(uno_ctx* c, int32_t seq_id) {
   pg.clear();
   c->live[seq_id] = 0;
   c->len_hi[seq_id] = 0;
+  new_epoch(c, seq_id);
   if (std::find(c->drafted_ids.begin(), c->drafted_ids.end(), seq_id) != c->drafted_ids.end())
     c->drafted_ids.clear();
   uno_status st = flush_pages(c);

@@ -184,12 +184,17 @@ uno_status uno_draft(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d
 uno_status uno_verify(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
                       int32_t* d_n_out, float* d_probs);
 
-/* One Psi-Spec iteration: uno_draft followed by uno_verify. */
+/* One Psi-Spec iteration [blog Psi-Spec sampler: a draft forward proposes the block,
+ * one verify forward checks it, so every iteration costs two forwards and emits
+ * between 2 and B+1 tokens]: uno_draft followed by uno_verify. */
 uno_status uno_step(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
                     int32_t* d_n_out);
 
 /* Accept/resample on caller-given probabilities (the parity entry of the accept
- * kernel), using the context's seed and workspace; the sequence state is not
+ * kernel) [blog Psi-Spec sampler: keep the longest prefix the AR law accepts,
+ * resample the first rejected slot from max(0, p - q) renormalised; blog
+ * distillation section: the standard speculative rejection of Leviathan et al.,
+ * Cor. 3.6], using the context's seed and workspace; the sequence state is not
  * touched.  d_p: [n, B, V] = p_2..p_{B+1}; d_q: [n, B-1, V] = q_2..q_B; d_draft:
  * [n, B] = y_1..y_B; d_seq_ids, d_pos, d_iter: device int32 [n] (Philox key word 1,
  * the pending position n, the iteration).  Outputs as uno_verify.  A NaN /
@@ -232,9 +237,12 @@ uno_status uno_sample(uno_ctx* ctx, int32_t rows, const float* d_w, const int32_
                       const int32_t* d_pos, const int32_t* d_iter, int32_t stream_id,
                       int32_t* d_idx);
 
-/* Raw forward (parity entry): rows_per_seq rows for each listed sequence, row
- * inputs either tokens (d_tokens [n*rows]) or hidden states (d_hidden_in float32
- * [n*rows, d]); positions d_pos [n*rows] and gates d_gate (uint8) [n*rows].  Each
+/* Raw forward (parity entry) of the one decoder with its gated LoRA [blog method
+ * core: one model holds the AR weights and the LoRA; summary, method key points:
+ * the gate switches the adapter per row]: rows_per_seq rows for each listed
+ * sequence, row inputs either tokens (d_tokens [n*rows]) or hidden states
+ * (d_hidden_in float32 [n*rows, d]); positions d_pos [n*rows] and gates d_gate
+ * (uint8, 1 = LoRA on) [n*rows].  Each
  * row's K/V is written at its position (pages reserved as needed) and a row at
  * position m attends to its sequence's positions 0..m.  Committed lengths and
  * pending tokens are not changed.  Outputs (each may be NULL): the final residual

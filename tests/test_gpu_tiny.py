@@ -192,3 +192,14 @@ def test_timing_records_every_nth_call(w_np):
     assert counts[1]["lm_head"][0] == 0                # class not enabled
     assert counts[1]["linear"][1] > 0 and counts[3]["linear"][1] > 0
     assert np.array_equal(outs[1][0], outs[3][0]) and np.array_equal(outs[1][1], outs[3][1])
+
+
+def test_huge_activations_set_numeric_flag(w_np):
+    """Rows whose sum of squares leaves the exact fixed-point range (here x ~ 1e5,
+    sum ~ 6e11) set the numeric flag instead of wrapping silently."""
+    eng = engine(TINY, w_np, max_seqs=1, max_rows=8)
+    pos = np.arange(4, dtype=np.int32)
+    x = np.full((4, TINY.d_model), 1e5, dtype=np.float32)
+    eng.forward([0], 4, dev(pos), dev(np.zeros(4, np.uint8)), hidden_in=dev(x), want_hidden=True)
+    with pytest.raises(Exception, match="NUMERIC"):
+        eng.sync()
