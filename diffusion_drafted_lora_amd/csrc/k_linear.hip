@@ -186,6 +186,77 @@ UNO_DEV void logits_epilogue(const GemmArgs& a, int m, int c, int tile0, const f
   }
 }
 
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+UNO_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One piece of a LoRA down-projection for a few rows: rank tile ct (16 columns of
+// the nproj * r intermediate), K chunk kc, row tile mt.  The NW waves split the
+// chunk's 32-wide K blocks; their partials are summed in LDS in wave order (red:
+// NW rows of 256 floats, red_stride apart), scaled by the row's 1 / rms, and added
+// to t in fixed point with one 64-bit integer atomic per element, so the total is
+// exact and independent of the order the pieces land in.
+template <int NW>
+UNO_DEV void lora_down_piece(const LoraDownArgs& a, int ct, int kc, int mt, float* red,
+                             int red_stride, float* s_rs) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r16 = lane & 15;
+  const int col0 = ct * 16, p = col0 / a.r, lc = col0 % a.r, nkb = a.K / 32;
+  // fragment-tiled operands: block (row block, k / 32), this lane's 16 bytes
+  const bf16* Ap = reinterpret_cast<const bf16*>(a.A[p]) + (size_t)(lc / 16) * nkb * 512 + lane * 8;
+  const int m_lane = mt * 16 + r16;
+  const bool row_ok = m_lane < a.M;
+  const bf16* Xp = reinterpret_cast<const bf16*>(a.X) + (size_t)mt * nkb * 512 + lane * 8;
+  // row sums of x^2 (wave 0): lane l holds banks 4 (l % 4) .. +3 of row l / 4
+  i64x2 ssq0 = {0, 0}, ssq1 = {0, 0};
+  if (a.ss_in && w == 0 && mt * 16 + (lane >> 2) < a.M) {
+    const i64x2* sp = reinterpret_cast<const i64x2*>(
+        a.ss_in + (size_t)(mt * 16 + (lane >> 2)) * SS_BANKS + (lane & 3) * 4);
+    ssq0 = sp[0];
+    ssq1 = sp[1];
+  }
+  // this wave's share of the chunk's 32-wide K blocks, loaded four at a time
+  const int cb = a.kchunk / 32, jb = kc * cb + w * cb / NW, je = kc * cb + (w + 1) * cb / NW;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero8 = {};
+  for (int j = jb; j < je; j += 4) {
+    bf16x8 x[4], wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = j + u < je;
+      x[u] = (in && row_ok) ? load8(Xp + (size_t)(j + u) * 512) : zero8;
+      wv[u] = in ? load8(Ap + (size_t)(j + u) * 512) : zero8;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[u], wv[u], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w * red_stride + ((lane >> 4) * 4 + i) * 16 + r16] = acc[i];
+  if (w == 0) {
+    long long sq = ssq0.x + ssq0.y + ssq1.x + ssq1.y;
+    ss_check(ssq0.x | ssq0.y | ssq1.x | ssq1.y, a.err);
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((lane & 3) == 0)
+      s_rs[lane >> 2] = a.ss_in ? 1.0f / sqrtf(fx_to_float(sq) * a.inv_d + a.eps) : 1.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x, row = e >> 4, m = mt * 16 + row;
+    if (m < a.M) {
+      float v = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) v += red[ww * red_stride + e];
+      v *= s_rs[row];
+      const long long q = (long long)llrintf(v * LORA_FX_SCALE);
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.t + (size_t)m * (a.nproj * a.r) + col0 + (e & 15)),
+                (unsigned long long)q);
+    }
+  }
+}
+
 template <int NT, int WAVES, int KU>
 __global__ void __launch_bounds__(WAVES * 64)
 k_gemm_bf16(GemmArgs a) {
@@ -195,7 +266,22 @@ k_gemm_bf16(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int mt = blockIdx.y;
-  const int grp = blockIdx.x;
+  // fused LoRA down-projection: the first n_prod workgroups of the row tile produce
+  // the intermediate, then publish it (release) by adding 1 to the launch counter
+  // (The producers' only global writes are device-scope atomic adds, which the
+  // device performs at its point of coherence across all XCDs -- the property every
+  // multi-workgroup fixed-point sum of this library relies on.  Waiting for their
+  // completion before the counter add orders them before it; no L2 write-back
+  // fence is taken, which would stall the L2 the consumers are streaming through.)
+  if ((int)blockIdx.x < a.n_prod) {
+    const int nct = a.ld.nproj * a.ld.r / 16;
+    lora_down_piece<WAVES>(a.ld, blockIdx.x % nct, blockIdx.x / nct, mt, &red[0][0][0], NT * 256, fin);
+    wait_vmcnt<0>();                    // this thread's atomics are performed
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(a.sync + mt, 1u);
+    return;
+  }
+  const int grp = blockIdx.x - a.n_prod;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int nkb = a.K / 32, nrb = a.r / 32;
 
@@ -237,7 +323,8 @@ k_gemm_bf16(GemmArgs a) {
   }
   // every workgroup clears its share of a fixed-point buffer a later kernel fills
   if (a.zero_ptr) {
-    const long nwg = (long)gridDim.x * gridDim.y, wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    const long ncons = (long)gridDim.x - a.n_prod;
+    const long nwg = ncons * gridDim.y, wg = (long)blockIdx.y * ncons + grp;
     const long share = ((long)a.zero_n + nwg - 1) / nwg;
     const long z0 = wg * share, z1 = min((long)a.zero_n, z0 + share);
     for (long i = z0 + threadIdx.x; i < z1; i += WAVES * 64) a.zero_ptr[i] = 0;
@@ -261,6 +348,9 @@ k_gemm_bf16(GemmArgs a) {
   // the up-projection fragment
   // (four-tile LM-head instances have no adapter and keep their registers)
   constexpr bool kPreLora = NT <= 2;
+  // (a fused launch's intermediate is only ready after the wait below: then just the
+  // up-projection fragment is loaded here)
+  const bool fused = a.sync != nullptr;
   const bool lora_pre = kPreLora && a.r > 0 && w < nrb && Uu[0] == nullptr;
   i64x2 tq[NT][4];
   bf16x8 bq[NT];
@@ -273,7 +363,7 @@ k_gemm_bf16(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) tq[t][q] = i64x2{0, 0};
       if (Up[t] == nullptr || Bp[t] == nullptr) continue;
-      if (row_ok) {
+      if (row_ok && !fused) {
         const i64x2* tp = reinterpret_cast<const i64x2*>(Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq);
 #pragma unroll
         for (int q = 0; q < 4; ++q) tq[t][q] = tp[q];
@@ -363,6 +453,36 @@ k_gemm_bf16(GemmArgs a) {
     }
   }
 
+  // ---- fused LoRA down-projection: wait until every producer of this row tile has
+  // published its piece (bounded: a wait that runs out flags the context).  The
+  // intermediate is then read with device-scope loads (below) rather than after an
+  // acquire fence, which would invalidate the L2 lines other workgroups reuse.
+  if (fused) {
+    if (threadIdx.x == 0) {
+      int spins = 0;
+      while ((int)(__hip_atomic_load(a.sync + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                   a.sync_target[mt]) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 24)) {
+          if (a.err) atomicOr(a.err, UNO_DEVERR_SYNC);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (lora_pre && gate_on) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (Up[t] == nullptr || Bp[t] == nullptr) continue;
+        const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          tq[t][q].x = __hip_atomic_load(tp + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          tq[t][q].y = __hip_atomic_load(tp + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
   // ---- LoRA phase: k over the rank, A = gate * bf16(scale * t), B = LoRA up
   if (a.r > 0 && !lora_pre) gate_on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
   if (lora_pre) {
@@ -390,8 +510,15 @@ k_gemm_bf16(GemmArgs a) {
           if (row_ok) af = load8(Uu[t] + frag_off(m_lane, ucol[t] + jr * 32 + kq, ldu[t]));
         } else if (gate_on) {
           const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + jr * 32 + kq;
+          if (fused) {          // published by this launch's producers
 #pragma unroll
-          for (int e = 0; e < 8; ++e) af[e] = (bf16)(a.scale * fx_to_float(tp[e]));
+            for (int e = 0; e < 8; ++e)
+              af[e] = (bf16)(a.scale * fx_to_float(__hip_atomic_load(
+                                  tp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) af[e] = (bf16)(a.scale * fx_to_float(tp[e]));
+          }
         }
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, load8(Bp[t] + (size_t)jr * 512),
                                                          acc[t], 0, 0, 0);
@@ -556,12 +683,6 @@ constexpr int TKB = UNO_TILE_TKB;    // 32-wide K blocks per stage
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-UNO_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <int BM, int BN, int WM, int WN, int TS>
 constexpr size_t tile_smem_bytes() {
@@ -1241,7 +1362,15 @@ template <int NT, int WAVES, int KU>
 hipError_t launch_skinny(const GemmArgs& a, int n_cols_total, int mtiles, hipStream_t s) {
   const int per_wg = a.paired ? 16 : 16 * NT;
   if (n_cols_total % per_wg) return hipErrorInvalidValue;
-  uno_launch(k_gemm_bf16<NT, WAVES, KU>, dim3(n_cols_total / per_wg, mtiles), WAVES * 64, 0, s, a);
+  if (a.n_prod > 0) {
+    // the producers' pieces must tile the intermediate and the chunks whole K blocks
+    const LoraDownArgs& l = a.ld;
+    if (!a.sync || l.r % 16 || l.kchunk <= 0 || l.kchunk % 32 || l.K % l.kchunk ||
+        a.n_prod != l.nproj * l.r / 16 * (l.K / l.kchunk) || l.M != a.M || mtiles > 4)
+      return hipErrorInvalidValue;
+  }
+  uno_launch(k_gemm_bf16<NT, WAVES, KU>, dim3(a.n_prod + n_cols_total / per_wg, mtiles),
+             WAVES * 64, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1250,6 +1379,7 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   if (a.M <= 0) return hipSuccess;
   if (a.K % 32 != 0 || (a.r % 32) != 0 || n_cols_total % 16 != 0) return hipErrorInvalidValue;
   if (a.epi == EPI_QKV && (a.kv.head_dim % 16 != 0)) return hipErrorInvalidValue;
+  if (a.n_prod > 0 && a.M >= 64) return hipErrorInvalidValue;   // fused producers: skinny only
   if (a.M >= 64) {
     hipError_t e;
     if (launch_resid_split(a, n_cols_total, s, &e)) return e;

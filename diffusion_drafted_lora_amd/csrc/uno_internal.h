@@ -65,6 +65,7 @@ hipError_t launch_pack(const bf16* src, bf16* dst, int rows, int cols, int pair_
 enum : int32_t {
   UNO_DEVERR_NUMERIC = 1,   // NaN / negative / >1 probability, or a row without mass
   UNO_DEVERR_BOUNDS = 2,    // a KV position outside the sequence's reserved pages
+  UNO_DEVERR_SYNC = 4,      // a workgroup's bounded wait for another's result ran out
 };
 
 // ------------------------------------------------------------- Philox4x64-10
@@ -221,6 +222,20 @@ UNO_DEV void ss_add(long long* ss, int m, int bank, float sq, int32_t* err) {
             (unsigned long long)(long long)llrintf(sq * LORA_FX_SCALE));
 }
 
+// LoRA down-projection of a group of projections sharing one input:
+// t[m, p*r + j] += sum_k X[m, k] * A_p[j, k] (fixed point, int64 atomics).
+struct LoraDownArgs {
+  const void* X;
+  int32_t ldx, M, K, r;
+  const void* A[4];
+  int32_t nproj;
+  int32_t kchunk;
+  long long* t;      // [M, nproj * r]
+  const long long* ss_in;   // RMSNorm input (see GemmArgs), or null
+  float inv_d, eps;
+  int32_t* err;             // device error flags (sum-of-squares range)
+};
+
 struct GemmSeg {
   const void* W;     // [N, K] of the storage type
   const void* Bl;    // LoRA up [N, r] (or null)
@@ -283,21 +298,20 @@ struct GemmArgs {
   // launch may use for its partial sums (null: never split)
   float* split_ws;
   long long split_cap;
+  // Fused LoRA down-projection (few rows, skinny kernel): the first n_prod
+  // workgroups of row tile mt compute pieces of the intermediate described by
+  // `ld` (rank tile p % (ld.nproj * ld.r / 16), K chunk p / that) and then add 1 to
+  // sync[mt]; the tile's other workgroups stream their base product meanwhile and
+  // wait for sync[mt] to reach sync_target[mt] before the LoRA phase.  A tile's
+  // producers are dispatched before its consumers (lower workgroup ids), so the
+  // wait always ends; the counters only grow (each launch raises a tile's target
+  // by n_prod).
+  int32_t n_prod;
+  uint32_t sync_target[4];
+  uint32_t* sync;
+  LoraDownArgs ld;
 };
 
-// LoRA down-projection of a group of projections sharing one input:
-// t[m, p*r + j] += sum_k X[m, k] * A_p[j, k] (fixed point, int64 atomics).
-struct LoraDownArgs {
-  const void* X;
-  int32_t ldx, M, K, r;
-  const void* A[4];
-  int32_t nproj;
-  int32_t kchunk;
-  long long* t;      // [M, nproj * r]
-  const long long* ss_in;   // RMSNorm input (see GemmArgs), or null
-  float inv_d, eps;
-  int32_t* err;             // device error flags (sum-of-squares range)
-};
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
 // Large-M LoRA down-projection on the tile kernel (EPI_TSLICE, no atomics): false
 // when no tile shape fits the problem (the atomic kernel then serves it).

@@ -33,13 +33,14 @@ constexpr int kMaxChunks = 64;        // context chunks per (row, head) in atten
 constexpr int kAttnTargetWG = UNO_ATTN_TARGET_WG;   // workgroups the context split aims at
 constexpr int kAttnMinChunk = UNO_ATTN_MIN_CHUNK;   // keys per chunk, at least (a multiple of 64)
 constexpr size_t kAlign = 256;
+constexpr int kSyncCounters = 16;     // per LoRA group (q|k|v, o, gate/up, down) and row tile
 
 thread_local std::string g_last_error = "";
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t len, pending, iter, err, block_table, rope_cos, rope_sin;
+  size_t len, pending, iter, err, sync, block_table, rope_cos, rope_sin;
   size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate, row_slot, row_vis, row_nc;
   size_t x, xn, qbuf, obuf, hbuf, ubuf, tfx, ss;
   size_t part_o, part_ml;
@@ -70,6 +71,7 @@ Layout make_layout(const uno_config& c) {
   L.pending = take(S * 4);
   L.iter = take(S * 4);
   L.err = take(4);
+  L.sync = take(kSyncCounters * 4);      // hand-off counters of fused launches (zeroed at init)
   L.block_table = take(S * pages_per_seq(c) * 4);
   const size_t rope_rows = (size_t)pages_per_seq(c) * c.page_size;
   L.rope_cos = take(rope_rows * (c.head_dim / 2) * 4);
@@ -153,6 +155,8 @@ struct uno_ctx {
   bool snap_inflight = false;
   std::vector<int> snap_base;
   std::vector<uint32_t> snap_epoch;
+  // producer counts issued so far on each hand-off counter (their targets)
+  uint32_t sync_issued[kSyncCounters] = {};   // [group][row tile]
   // stage capture
   bool trace_on = false;
   uno_trace trace{};
@@ -237,6 +241,11 @@ void gemm_cost(const GemmArgs& a, int ncols, size_t ts, double* bytes, double* f
     const double lcols = a.paired ? 2.0 * ncols : (double)ncols;
     b += lcols * r * ts + M * r * nl * ts;
     f += 2.0 * M * lcols * r;
+  }
+  if (a.n_prod > 0) {   // fused LoRA down-projection: its A, the input and the atomics
+    const double nc = (double)a.ld.nproj * a.ld.r;
+    b += nc * a.ld.K * ts + M * nc * 8;
+    f += 2.0 * M * nc * a.ld.K;
   }
   switch (a.epi) {
     case EPI_STORE_F32: b += M * ncols * 4; break;
@@ -631,6 +640,31 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     a.epi = EPI_LORA_U; a.ldo = nproj * r; a.out = ubuf; a.gate = gate; a.scale = sc;
     return run_gemm(a, nproj * r, UNO_KC_LORA_DOWN);
   };
+  // Few rows (the skinny kernel): the group's LoRA down-projection runs inside the
+  // consumer launch as its first workgroups (GemmArgs::n_prod), which saves a
+  // launch per group; the consumers wait for it only before their LoRA phase.
+  const bool fuse_lora = lora && c->bf16 && !tile_lora && R < 64;
+  auto fuse_down = [&](GemmArgs& a, const T* X, int K, int nproj, const int* pidx, int l, int buf,
+                       int ss_idx) {
+    LoraDownArgs& d2 = a.ld;
+    d2.X = X; d2.ldx = K; d2.M = R; d2.K = K; d2.r = r; d2.nproj = nproj; d2.t = Bfx[buf];
+    d2.err = err;
+    if (ss_idx >= 0) { d2.ss_in = SS(ss_idx); d2.inv_d = 1.0f / (float)d; d2.eps = g.rms_eps; }
+    for (int i = 0; i < nproj; ++i) d2.A[i] = c->la[pidx[i]][l];
+    // about 128 producer workgroups per row tile: K chunks of whole 32-wide blocks
+    const int tiles = nproj * r / 16;
+    const int tgt = std::max(1, (128 + tiles - 1) / tiles);
+    int ks = 1;
+    for (int cand = 1; cand <= K / 32; ++cand)
+      if ((K / 32) % cand == 0 && cand <= tgt) ks = cand;
+    d2.kchunk = K / ks;
+    a.n_prod = tiles * ks;
+    a.sync = c->at<uint32_t>(c->L.sync) + 4 * buf;
+    for (int mt = 0; mt < (R + 15) / 16; ++mt) {
+      c->sync_issued[4 * buf + mt] += (uint32_t)a.n_prod;
+      a.sync_target[mt] = c->sync_issued[4 * buf + mt];
+    }
+  };
   // attach the LoRA up-projection of segment `i` reading group buffer `buf`
   auto lora_up = [&](GemmArgs& a, int i, int proj, int l, int buf, int col, int ld) {
     a.seg[i].Bl = c->lb[proj][l];
@@ -655,9 +689,10 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     if (tr) { if (uno_status st = cap_x(tr->x_in)) return st; }
     // --- attention block: q|k|v (+LoRA) with RoPE and the paged K/V write
     static const int pqkv[3] = {0, 1, 2};
-    if (lora) { uno_status st = lora_down(xg, d, 3, pqkv, l, 0, 2 * l); if (st) return st; }
+    if (lora && !fuse_lora) { uno_status st = lora_down(xg, d, 3, pqkv, l, 0, 2 * l); if (st) return st; }
     {
       GemmArgs a{};
+      if (fuse_lora) fuse_down(a, xg, d, 3, pqkv, l, 0, 2 * l);
       a.X = xg; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
       a.nseg = 3;
       const int n0s[3] = {0, qd, qd + kvd}, Ns[3] = {qd, kvd, kvd};
@@ -705,9 +740,10 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     }
     if (tr) { if (uno_status st = cap_act(tr->attn, obuf, qd)) return st; }
     static const int po[1] = {3};
-    if (lora) { uno_status st = lora_down(obuf, qd, 1, po, l, 1, -1); if (st) return st; }
+    if (lora && !fuse_lora) { uno_status st = lora_down(obuf, qd, 1, po, l, 1, -1); if (st) return st; }
     {
       GemmArgs a{};
+      if (fuse_lora) fuse_down(a, obuf, qd, 1, po, l, 1, -1);
       a.X = obuf; a.ldx = qd; a.M = R; a.K = qd; a.r = lora ? r : 0;
       a.nseg = 1;
       a.seg[0].W = c->w[3][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
@@ -721,9 +757,10 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     if (tr) { if (uno_status st = cap_x(tr->x_mid)) return st; }
     // --- MLP block
     static const int pgu[2] = {4, 5};
-    if (lora) { uno_status st = lora_down(xg, d, 2, pgu, l, 2, 2 * l + 1); if (st) return st; }
+    if (lora && !fuse_lora) { uno_status st = lora_down(xg, d, 2, pgu, l, 2, 2 * l + 1); if (st) return st; }
     {
       GemmArgs a{};
+      if (fuse_lora) fuse_down(a, xg, d, 2, pgu, l, 2, 2 * l + 1);
       a.X = xg; a.ldx = d; a.M = R; a.K = d; a.r = lora ? r : 0;
       a.nseg = 2; a.paired = 1;
       for (int i = 0; i < 2; ++i) {
@@ -737,9 +774,10 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     }
     if (tr) { if (uno_status st = cap_act(tr->act, hbuf, F)) return st; }
     static const int pd[1] = {6};
-    if (lora) { uno_status st = lora_down(hbuf, F, 1, pd, l, 3, -1); if (st) return st; }
+    if (lora && !fuse_lora) { uno_status st = lora_down(hbuf, F, 1, pd, l, 3, -1); if (st) return st; }
     {
       GemmArgs a{};
+      if (fuse_lora) fuse_down(a, hbuf, F, 1, pd, l, 3, -1);
       a.X = hbuf; a.ldx = F; a.M = R; a.K = F; a.r = lora ? r : 0;
       a.nseg = 1;
       a.seg[0].W = c->w[6][l]; a.seg[0].n0 = 0; a.seg[0].N = d;
@@ -1335,6 +1373,7 @@ uno_status uno_sync(uno_ctx* c) {
   UNO_HIP(c, hipMemcpy(&e, c->at<int32_t>(c->L.err), 4, hipMemcpyDeviceToHost));
   poll_snapshot(c);
   if (e & UNO_DEVERR_BOUNDS) return fail(c, UNO_ERR_DEVICE, "device bounds check tripped");
+  if (e & UNO_DEVERR_SYNC) return fail(c, UNO_ERR_DEVICE, "a workgroup's wait for another's result ran out");
   if (e & UNO_DEVERR_NUMERIC) return fail(c, UNO_ERR_NUMERIC, "NaN / negative probability or empty row");
   return UNO_OK;
 }

@@ -69,6 +69,40 @@ def test_layer_stages_batch1(ctx):
     eng.sync()
 
 
+def test_layer_stages_three_sequences():
+    """48 rows (three row tiles of the few-row kernels, each with its own LoRA
+    down-projection producers): three sequences of 16 draft rows at contexts 1024,
+    700 and 3000."""
+    import torch
+    ctxs, rows = [1024, 700, 3000], 16
+    n = len(ctxs)
+    log("stages 3 sequences x 16 rows")
+    w = synth.weights_numpy(CFG, 1001, with_embed=False)
+    lw = w["layers"][0]
+    eng = engine(CFG, w, max_seqs=n, max_seq_len=3000 + 64, max_rows=n * rows)
+    gen = torch.Generator(device="cuda").manual_seed(7321)
+    for s_, c in enumerate(ctxs):
+        shape = (1, c, CFG.n_kv_heads, CFG.head_dim)
+        kc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        vc = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        eng.kv_import(s_, kc, vc, pending=0)
+    pos = np.stack([np.arange(c, c + rows) for c in ctxs]).astype(np.int32)
+    gate = (np.arange(n * rows).reshape(n, rows) % rows != 0).astype(np.uint8)
+    x = synth.normal(7421, (n * rows, CFG.d_model))
+    for rep in range(2):         # twice: the hand-off counters carry over between launches
+        bufs = eng.set_trace(n * rows, [0])
+        eng.forward(list(range(n)), rows, dev(pos.ravel()), dev(gate.ravel()), hidden_in=dev(x))
+        tr = _trace_np(bufs[0])
+        eng.set_trace(None)
+    for s_ in range(n):
+        k, v = eng.kv_export(s_, ctxs[s_] + rows)
+        K = host(k.float()).astype(np.float64)[0]
+        V = host(v.float()).astype(np.float64)[0]
+        sc.layer_stages(CFG, lw, tr, np.arange(s_ * rows, (s_ + 1) * rows), pos[s_], gate[s_], K,
+                        V, f"seq {s_} ctx {ctxs[s_]}")
+    eng.sync()
+
+
 def test_layer_stages_batch128_long_context():
     """2048 rows: 128 sequences x 16 draft rows, sequence 0 at context 9216."""
     import torch
