@@ -12,9 +12,10 @@ resample test and the commit.  W untimed steps, then exactly K timed steps.
 Reported: accepted tokens/s (value), positions/s, tokens per forward, whole-step
 algorithmic HBM GB/s, the roofline of the dominant kernel (the gate/up
 gated-LoRA linear, timed with HIP events on the library's stream), a per-class
-kernel time breakdown, batch-128 windows at contexts 1024, 5120 and 9216 with their
-integral over the 1K-in / 8K-out run, the nucleus (top-p) truncation kernel at the batch-1 and
-batch-128 row counts, and the CPU oracle timed on a bounded sample on the host.
+kernel time breakdown, batch-1 and batch-128 windows at contexts 1024, 5120 and 9216
+with their integrals over the 1K-in / 8K-out run, the nucleus (top-p) truncation
+kernel at the batch-1 and batch-128 row counts, and the CPU oracle timed on a
+bounded sample on the host (with its thread counts and a one-thread figure).
 """
 import argparse
 import json
@@ -103,7 +104,7 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     from diffusion_drafted_lora_amd import synth, uno
 
     B = cfg.block_size
-    max_len = ctx + (warmup + steps + 2) * (B + 1) + B + 2
+    max_len = ctx + (warmup + steps + 6) * (B + 1) + B + 2
     eng = uno.Engine(cfg, w, max_seqs=batch, max_seq_len=max_len, max_rows=batch * B,
                      seed=3003, device=dev)
     ids = list(range(batch))
@@ -125,12 +126,19 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     eng.sync()
     t_fill = time.perf_counter() - t0
     outs = torch.empty((batch, B + 1), dtype=torch.int32, device=dev)
-    nouts = torch.empty((warmup + steps, batch), dtype=torch.int32, device=dev)
+    nouts = torch.empty((warmup, batch), dtype=torch.int32, device=dev)
     for i in range(warmup):
         eng.step(ids, out=outs, n_out=nouts[i])
     eng.sync()
     cls = ["linear", "linear_swiglu", "lora_down", "lm_head", "attention"]
-    eng.timing(cls)
+    # Few sequences: hundreds of short kernels per iteration, whose event pairs would
+    # lengthen the timed iterations, so the class breakdown comes from a few extra
+    # iterations after them.  Large batch: kernels are long, the same iterations serve.
+    separate = batch < 8
+    extra = min(4, steps) if separate else 0
+    nouts = torch.empty((warmup + steps + extra, batch), dtype=torch.int32, device=dev)
+    if not separate:
+        eng.timing(cls)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(warmup, warmup + steps):
@@ -138,12 +146,18 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
     eng.sync()
-    tok = int(nouts[warmup:].sum().item())
+    tok = int(nouts[warmup:warmup + steps].sum().item())
+    if separate:
+        eng.timing(cls)
+        for i in range(warmup + steps, warmup + steps + extra):
+            eng.step(ids, out=outs, n_out=nouts[i])
+        eng.sync()
+    nb = extra if separate else steps
     gemm_ms = gemm_fl = 0.0
     breakdown = {}
     for c in cls:
         n, ms, b, f = eng.timing_read(c)
-        breakdown[c] = {"ms_per_step": ms / steps, "TFLOP/s": f / 1e12 / (ms / 1e3) if ms else None,
+        breakdown[c] = {"ms_per_step": ms / nb, "TFLOP/s": f / 1e12 / (ms / 1e3) if ms else None,
                         "GB/s": b / 1e9 / (ms / 1e3) if ms else None}
         if c != "attention":
             gemm_ms += ms
@@ -153,13 +167,29 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     del eng
     torch.cuda.empty_cache()
     mfma_tflops = gemm_fl / 1e12 / (gemm_ms / 1e3)
+    # algorithmic HBM bytes of the timed iterations: both forwards' weights, the
+    # draft's LoRA, and every sequence's context K/V read by both forwards
+    fixed, lora = model_bytes(cfg)
+    ctx_mid = ctx + (warmup + steps / 2.0) * tok / max(1, batch * steps)
+    it_bytes = 2 * fixed + lora + batch * kv_bytes_per_pos(cfg) * (2 * ctx_mid + 2 * B)
+    hbm = it_bytes / 1e9 / (sec / steps)
     return {
         "batch": batch, "context_start": ctx, "steps": steps, "warmup": warmup,
         "accepted_tokens_per_s": tok / sec, "positions_per_s": 2 * B * batch * steps / sec,
         "ms_per_step": 1e3 * sec / steps, "tokens_per_forward": tok / (2.0 * batch * steps),
         "gemm_mfma_tflops": mfma_tflops, "gemm_mfma_frac": mfma_tflops / BF16_PEAK_TFLOPS,
+        "hbm_gbs_algorithmic": hbm, "hbm_frac": hbm / HBM_PEAK_GBS,
         "fill_s": t_fill, "breakdown": breakdown,
     }
+
+
+def run_bytes_per_iteration(cfg, contexts):
+    """Mean algorithmic bytes of a batch-1 iteration over contexts [c0, c_last]: both
+    forwards' weights, the draft's LoRA and the K/V of the context read twice (the
+    context grows linearly, so its mean is the midpoint)."""
+    fixed, lora = model_bytes(cfg)
+    mid = (contexts[0] + contexts[-1]) / 2.0
+    return 2 * fixed + lora + kv_bytes_per_pos(cfg) * (2 * mid + 2 * cfg.block_size)
 
 
 def integrate_windows(windows, batch, B):
@@ -327,8 +357,20 @@ def cpu_baseline(cfg, sample_w, tokens_per_iter, ctx=1024):
     t_samp = time.perf_counter() - t0
     t_iter = cfg.n_layers * t_layer + t_lm + t_samp
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    # one BLAS thread: the draft forward of the sampled layer, once
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        model.forward(one, w1, None, np.arange(ctx, ctx + B)[None], gate, cache, hidden_in=xd,
+                      want_logits=False)
+        t_draft1 = time.perf_counter() - t0
+    t_iter1 = t_iter * (t_draft1 / (t_layer / 2.0))
     return {
         "value": tokens_per_iter / t_iter, "unit": "tokens/s", "cores": int(threads),
+        "host_cpus": os.cpu_count(), "blas_threads": int(threads),
+        "one_thread": {"value": tokens_per_iter / t_iter1, "seconds_per_iteration": t_iter1,
+                       "sample": "the draft forward of the sampled layer with one BLAS thread, "
+                                 "scaled by the multi-threaded iteration's layer share"},
         "kind": "oracle",
         "sample": (f"float64 numpy oracle with bf16 storage rounding: 1 of {cfg.n_layers} layers "
                    f"(16 draft rows + 16 verify rows at context {ctx}) timed {reps}x, the LM head "
@@ -354,6 +396,11 @@ def main():
     ap.add_argument("--bs128-ctx", type=str, default="1024,5120,9216",
                     help="comma-separated starting contexts of the batch-128 leg (windows "
                          "over the 1K-in / 8K-out run)")
+    ap.add_argument("--bs1-window-steps", type=int, default=40,
+                    help="timed iterations of each batch-1 window (0 skips the windows)")
+    ap.add_argument("--bs1-ctx", type=str, default="1024,5120,9216",
+                    help="comma-separated starting contexts of the batch-1 windows over the "
+                         "1K-in / 8K-out run")
     ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
                     help="distillation-forward leg (batch, L, block size); 'none' skips it")
     ap.add_argument("--distill-reps", type=int, default=2)
@@ -495,6 +542,16 @@ def main():
     eng.close()
     del eng
     torch.cuda.empty_cache()
+    if args.bs1_window_steps > 0:
+        result["bs1_windows"] = [run_batch(cfg, w, dev, 1, int(c), args.bs1_window_steps, 4,
+                                           args.prompt, log_prefix="bs1")
+                                 for c in args.bs1_ctx.split(",")]
+        result["bs1_run"] = integrate_windows(result["bs1_windows"], 1, B)
+        if result["bs1_run"]:
+            run = result["bs1_run"]
+            run["hbm_gbs_algorithmic"] = run_bytes_per_iteration(cfg, run["contexts"]) / 1e9 / \
+                (run["mean_ms_per_step"] / 1e3)
+            run["hbm_frac"] = run["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
     if args.bs128_steps > 0:
         result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
                            for c in args.bs128_ctx.split(",")]

@@ -35,3 +35,15 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     f.write_text(f"traffic_bytes_per_launch: 123456\n"
                  f"kernel_source_sha256: {bench.kernel_source_hash()}\n")
     assert bench.measured_traffic() == 123456.0
+
+
+def test_run_bytes_per_iteration_counts_weights_lora_and_mean_context():
+    from diffusion_drafted_lora_amd import configs
+    cfg = configs.MODEL8B
+    fixed, lora = bench.model_bytes(cfg)
+    # the 8B shape: 15.136 GB of weights per forward, 0.698 GB of LoRA, 147,456 B of K/V
+    # per position over 36 layers
+    assert abs(fixed / 1e9 - 15.136) < 1e-3 and abs(lora / 1e9 - 0.698) < 1e-3
+    assert bench.kv_bytes_per_pos(cfg) == 147456
+    b = bench.run_bytes_per_iteration(cfg, [1024, 5120, 9216])
+    assert abs(b - (2 * fixed + lora + 147456 * (2 * 5120 + 32))) < 1
