@@ -17,6 +17,16 @@
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+UNO_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 constexpr int SUB = 32;   // keys per LDS sub-chunk
 constexpr int kMaxCombine = 64;   // chunk partials merged per (row, head)
 
@@ -559,6 +569,244 @@ k_attn_mfma(AttnArgs a, KvLayout kv) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Plain-causal bf16 attention (head_dim 128, four query heads per KV head,
+// 16-token pages) that streams K and V straight from the pages into a ring of
+// RNS LDS stages with global_load_lds -- no register staging -- so RNS - 1
+// sub-chunks of RMK keys are in flight while one is multiplied, with one barrier
+// per sub-chunk.  Each 1 KB load instruction fills 64 16-byte LDS slots; the
+// lanes pick their global chunks so that the stage is XOR-swizzled and every
+// MFMA fragment read is free of bank conflicts:
+//   K, key t of the sub-chunk, dims 8c..8c+7:  t * 256 + ((c ^ (t & 15)) * 16)
+//   V, page p of the sub-chunk, dim d, tokens 8h..8h+7 of the page:
+//                                              RMK * 256 + p * 4096 + d * 32 + ((h ^ ((d >> 3) & 1)) * 16)
+// Keys at or past the chunk end are loaded from page 0 (in bounds, never seen):
+// their scores are masked, and their V entries are zeroed in LDS before P.V (a
+// slot that was never written may hold a NaN pattern, and 0 * NaN is NaN).
+#ifndef UNO_ATTN_RING
+#define UNO_ATTN_RING 2
+#endif
+#ifndef UNO_ATTN_RING_KEYS
+#define UNO_ATTN_RING_KEYS 64
+#endif
+constexpr int RNS = UNO_ATTN_RING;              // ring stages
+constexpr int RMK = UNO_ATTN_RING_KEYS;         // keys per stage
+static_assert(RMK == 32 || RMK == 64, "stages of 32 or 64 keys");
+constexpr int RPG = RMK / 16;                   // pages per stage
+constexpr int RPPAD = RMK + 8;                  // LDS row of P (bf16)
+#ifndef UNO_ATTN_RING_MIN_CHUNK
+#define UNO_ATTN_RING_MIN_CHUNK 64
+#endif
+constexpr int kAttnRingMinChunk = UNO_ATTN_RING_MIN_CHUNK;   // shorter chunks: register staging
+static_assert(RNS >= 2 && RNS <= 4, "ring depth");
+constexpr int RSTAGE = RMK * HD * 2 * 2;        // one stage: K and V of RMK keys
+constexpr int RVOFF = RMK * HD * 2;             // V part of a stage
+constexpr int RLOADS = RSTAGE / 1024 / 4;       // 1 KB load instructions per wave and stage
+
+__global__ void __launch_bounds__(256, 1)
+k_attn_ring(AttnArgs a, KvLayout kv) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  bf16* sP = reinterpret_cast<bf16*>(smem_raw + (size_t)RNS * RSTAGE);   // [4][16][RPPAD]
+  __shared__ int sW[48];
+  __shared__ int sPg[PGC];
+
+  const int c = blockIdx.x, kvh = blockIdx.y;
+  const int row_tiles = (a.rows_per_seq + 15) / 16;
+  const int si = blockIdx.z / row_tiles, rt = blockIdx.z % row_tiles;
+  const int G = 4;
+  const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[si];
+  const int r0 = si * a.rows_per_seq + rt * 16;
+  const int nrows = min(16, a.rows_per_seq - rt * 16);
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, grp = lane >> 4;
+
+  if (tid < 16) row_window(a, r0 + tid, tid < nrows, sW + tid, sW + 16 + tid, sW + 32 + tid);
+  const int head = kvh * G + w;
+  const bf16* Q = reinterpret_cast<const bf16*>(a.q);
+  bf16x8 qf[HD / 32];
+  {
+    const bool ok = r16 < nrows;
+    const bf16* qr = Q + (size_t)(r0 + (ok ? r16 : 0)) * a.n_q_heads * HD + head * HD;
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + ks * 32 + grp * 8);
+      qf[ks] = ok ? v : bf16x8{};
+    }
+  }
+  const float sc = a.scale * 1.4426950408889634f;    // scores in the exp2 domain
+  __syncthreads();
+  int At, Ct, nv;
+  tile_window(sW, &At, &Ct, &nv);
+  publish_nc(a, c, kvh, tid, r0, nrows, nv);
+  const int kbeg = c * a.chunk;
+  if (kbeg >= nv) return;
+  const int kend = min(kbeg + a.chunk, nv);
+  const int nsub = (kend - kbeg + RMK - 1) / RMK;
+
+  // pages of the chunk's keys (kbeg is a multiple of 64, so of the page size);
+  // entries outside the sequence's pages read page 0 (masked / zeroed below)
+  const int p0 = kbeg >> 4, npg = nsub * RPG;
+  const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
+  for (int i = tid; i < npg; i += 256) {
+    const int pi = p0 + i;
+    int page = (pi < kv.max_pages_per_seq && (pi << 4) < kend) ? bt[pi] : 0;
+    sPg[i] = (page >= 0 && page < kv.n_pages) ? page : 0;
+  }
+  const size_t pstride = (size_t)kv.n_kv_heads * 16 * HD;
+  const bf16* kb0 = kv_block<const bf16>(kv, a.layer, 0, 0, kvh);
+  const bf16* vb0 = kv_block<const bf16>(kv, a.layer, 1, 0, kvh);
+  __syncthreads();
+
+  // wave w issues the stage's load instructions w * RLOADS .. + RLOADS - 1: first
+  // the K pages (four instructions of four tokens each), then the V pages (four
+  // instructions of 32 dims each)
+  auto issue = [&](int sub, int slot) {
+#pragma unroll
+    for (int q = 0; q < RLOADS; ++q) {
+      const int ins = w * RLOADS + q, kind = ins / (4 * RPG), pg = (ins % (4 * RPG)) >> 2,
+                part = ins & 3;
+      const int page = sPg[sub * RPG + pg];
+      const bf16* src;
+      if (kind == 0) {
+        const int tl = part * 4 + grp, cq = r16 ^ tl;      // token of the page, its data chunk
+        src = kb0 + (size_t)page * pstride + tl * HD + cq * 8;
+      } else {
+        const int d = part * 32 + (lane >> 1), h = (lane & 1) ^ ((d >> 3) & 1);
+        src = vb0 + (size_t)page * pstride + d * 16 + h * 8;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (glb_void_t*)src,
+          (lds_void_t*)(smem_raw + (size_t)slot * RSTAGE + kind * RVOFF + pg * 4096 + part * 1024),
+          16, 0, 0);
+    }
+  };
+
+  float m[4], l[4];
+  f32x4 o[HD / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+#pragma unroll
+  for (int d = 0; d < HD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int lim[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lim[i] = min(kend, sW[grp * 4 + i]);
+  bf16* myP = sP + w * 16 * RPPAD;
+
+#pragma unroll
+  for (int st = 0; st < RNS - 1; ++st)
+    if (st < nsub) issue(st, st);
+  for (int it = 0; it < nsub; ++it) {
+    // this wave's loads of sub-chunk it are done once at most the later ones remain
+    const int newer = min(RNS - 2, nsub - 1 - it);
+    if (newer >= 2) wait_vmcnt<2 * RLOADS>();
+    else if (newer == 1) wait_vmcnt<RLOADS>();
+    else wait_vmcnt<0>();
+    __syncthreads();                 // every wave's loads landed; sub-chunk it - 1 consumed
+    if (it + RNS - 1 < nsub) issue(it + RNS - 1, (it + RNS - 1) % RNS);
+    const int k0 = kbeg + it * RMK;
+    const char* stK = smem_raw + (size_t)(it % RNS) * RSTAGE;
+    const char* stV = stK + RVOFF;
+    if (k0 + RMK > kend) {
+      // zero the V entries of keys at or past the chunk end (tokens of this stage)
+      bf16* zV = reinterpret_cast<bf16*>(const_cast<char*>(stV));
+      for (int e = tid; e < (k0 + RMK - kend) * HD; e += 256) {
+        const int kk = kend - k0 + e / HD, d = e % HD;
+        const int pg = kk >> 4, tk = kk & 15, h = (tk >> 3) ^ ((d >> 3) & 1);
+        zV[(pg * 4096 + d * 32 + h * 16) / 2 + (tk & 7)] = (bf16)0.0f;
+      }
+      __syncthreads();
+    }
+    // S = Q K^T over RMK / 16 key tiles of 16
+    constexpr int NJ = RMK / 16;
+    f32x4 s[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int t = j * 16 + r16;
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        const int cq = (ks * 4 + grp) ^ r16;
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(stK + t * 256 + cq * 16);
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[j], 0, 0, 0);
+      }
+    }
+    // mask (row grp*4+i sees keys below lim[i]) and the online softmax
+    float mt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float v = s[j][i] * sc;
+        if (k0 + j * 16 + r16 >= lim[i]) v = -INFINITY;
+        s[j][i] = v;
+        mx = fmaxf(mx, v);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+      mt[i] = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(m[i], mt[i]);
+      const float f = (m[i] == -INFINITY) ? 0.0f : exp2f(m[i] - mn);
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float pv = (s[j][i] == -INFINITY) ? 0.0f : exp2f(s[j][i] - mn);
+        s[j][i] = pv;
+        ps += pv;
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 16);
+      l[i] = l[i] * f + ps;
+      m[i] = mn;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) o[d][i] *= f;
+    }
+    // P to this wave's LDS rows (bf16, row-major [16][RMK]), then O += P V
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) myP[(grp * 4 + i) * RPPAD + j * 16 + r16] = (bf16)s[j][i];
+#pragma unroll
+    for (int ks = 0; ks < RMK / 32; ++ks) {
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(myP + r16 * RPPAD + ks * 32 + grp * 8);
+      const int pg = ks * 2 + (grp >> 1), h = grp & 1;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) {
+        const int dim = d * 16 + r16;
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(
+            stV + pg * 4096 + dim * 32 + ((h ^ ((dim >> 3) & 1)) * 16));
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[d], 0, 0, 0);
+      }
+    }
+  }
+  // partials (or the final output when the context has one chunk)
+  const bool single = a.n_chunks == 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = grp * 4 + i;
+    if (row >= nrows) continue;
+    const size_t rr = (size_t)(r0 + row);
+    if (single) {
+      const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
+      bf16* out = reinterpret_cast<bf16*>(a.out);
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d)
+        out[frag_off((int)rr, head * HD + d * 16 + r16, a.n_q_heads * HD)] = (bf16)(o[d][i] * inv);
+    } else {
+      const size_t ph = (rr * a.n_q_heads + head) * a.n_chunks + c;
+#pragma unroll
+      for (int d = 0; d < HD / 16; ++d) a.part_o[ph * HD + d * 16 + r16] = o[d][i];
+      if (r16 == 0) {
+        a.part_ml[ph * 2] = m[i] * 0.6931471805599453f;
+        a.part_ml[ph * 2 + 1] = l[i];
+      }
+    }
+  }
+}
 }  // namespace
 
 template <typename T>
@@ -586,8 +834,19 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
         if (ea != hipSuccess) return ea;
       }
     }
-    if (a.row_vis) uno_launch(k_attn_mfma<true>, grid, 64 * G, smem, s, a, kv);
-    else uno_launch(k_attn_mfma<false>, grid, 64 * G, smem, s, a, kv);
+    const bool ring = !a.row_vis && kv.page_size == 16 && a.chunk % 64 == 0 &&
+                      a.chunk >= kAttnRingMinChunk && a.chunk <= PGC * 16;
+    if (ring) {
+      const size_t rsmem = (size_t)RNS * RSTAGE + (size_t)G * 16 * RPPAD * 2;
+      hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_ring),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)rsmem);
+      if (ea != hipSuccess) return ea;
+      uno_launch(k_attn_ring, grid, 256, (uint32_t)rsmem, s, a, kv);
+    } else if (a.row_vis) {
+      uno_launch(k_attn_mfma<true>, grid, 64 * G, smem, s, a, kv);
+    } else {
+      uno_launch(k_attn_mfma<false>, grid, 64 * G, smem, s, a, kv);
+    }
   } else {
     const size_t smem = attn_smem_bytes<T>(G, kv.head_dim);
     const int nown = (16 * G * kv.head_dim + 255) / 256;
