@@ -29,4 +29,6 @@ Modules:
   psispec  prefill, draft, verify, accept/resample, commit, generation loop (top-p optional).
   distill  the [x, z1] block-causal forward with teacher/student logits and TV.
   nucleus  the top-p truncation of a probability row (exact fixed-point reading).
+  distill_grad  the block-wise TV loss and its gradient with respect to the LoRA
+           (base frozen), layer by layer over the z1 rows.
 """
