@@ -435,3 +435,71 @@ template <> hipError_t launch_untile<float>(const float* src, float* dst, int R,
 int32_t uno_fail_global(int32_t status, const char* msg);
 // Looks up the current device's address of the no-allocation scratch array.
 hipError_t noalloc_prime();
+
+// ------------------------------------------------------ distillation backward
+// Index map of a strided axis: i -> (i >> sh) * hi + (i & (2^sh - 1)) * lo (a
+// plain stride is {0, ld, 0}; sh > 0 walks rows i * G + g of G query heads).
+struct Idx2 {
+  int sh;
+  long hi, lo;
+};
+inline Idx2 idx_ld(long ld) { return Idx2{0, ld, 0}; }
+
+// Operand layouts of the backward GEMM C[m, n] = sum_k A(m, k) B(n, k).
+enum : int {
+  BW_A_K16 = 0,   // bf16, A(m, k) at A[ai(m) + k]
+  BW_A_K32 = 1,   // float32 (two bf16 terms), A(m, k) at A[ai(m) + k]
+  BW_A_M32 = 2,   // float32 (two bf16 terms), A(m, k) at A[ai(k) + m], times kscale[k]
+};
+enum : int {
+  BW_B_TN = 0,    // fragment-tiled weight [N, K] (b_cols = K): B(n, k) = W[n][k]
+  BW_B_TT = 1,    // fragment-tiled weight [K, N] (b_cols = N): B(n, k) = W[k][n]
+  BW_B_K16 = 2,   // bf16, B(n, k) at B[bi(n) + k]
+  BW_B_N16 = 3,   // bf16, B(n, k) at B[bi(k) + n]
+  BW_B_N32 = 4,   // float32 (two bf16 terms), B(n, k) at B[bi(k) + n]
+};
+struct BwGemm {
+  int amode, bmode;
+  const void* A;
+  Idx2 ai;
+  long a_bs;                 // batch strides in elements (blockIdx.z)
+  const void* B;
+  Idx2 bi;
+  long b_bs;
+  int b_cols;                // columns of a tiled weight
+  void* C;                   // C[ci(row) + col], float32 or bf16
+  Idx2 ci;
+  long c_bs;
+  int M, N, K, batch, splits;
+  float alpha;               // C = alpha * row_scale[m] * sum (+ C when accumulate)
+  const float* row_scale;
+  const float* kscale;
+  int accumulate, out_bf16;
+  int perm_hd;               // > 0: output rows are in the RoPE pair order of heads of
+                             // perm_hd rows and are written to their head-order rows
+  float* part;               // splits > 1: float32 [splits, M, N] partials
+};
+hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t s);
+template <typename T>
+hipError_t launch_bw_rmsprep(const float* x, const T* gain, float eps, int rows, int d, bf16* hg,
+                             float* rs, hipStream_t s);
+template <typename T>
+hipError_t launch_bw_rmsback(const float* x, const bf16* hg, const float* rs, const T* gain,
+                             const float* dh, const float* dres, float* dx, int rows, int d,
+                             hipStream_t s);
+hipError_t launch_bw_qkv_post(const float* Yq, const float* Yk, const float* Yv, const float* rcos,
+                              const float* rsin, int rows, int L, int Hq, int Hkv, int hd, bf16* Q,
+                              bf16* Ka, bf16* Va, hipStream_t s);
+hipError_t launch_bw_qkv_back(const float* dq, const float* dk, const float* dv, const float* rcos,
+                              const float* rsin, int rows, int L, int Hq, int Hkv, int hd, float* dYq,
+                              float* dYk, float* dYv, hipStream_t s);
+hipError_t launch_bw_ctx_copy(const bf16* k, const bf16* v, long seq_stride, int S, int L, int Hkv,
+                              int hd, bf16* Ka, bf16* Va, hipStream_t s);
+hipError_t launch_bw_softmax(float* S, int L, int G, int Hkv, int B, float scale, hipStream_t s);
+hipError_t launch_bw_softmax_back(const float* P, float* dP, int L, int G, int Hkv, float scale,
+                                  hipStream_t s);
+hipError_t launch_bw_swiglu(const float* Yg, const float* Yu, bf16* a, long n, hipStream_t s);
+hipError_t launch_bw_swiglu_back(const float* da, float* Yg, float* Yu, long n, hipStream_t s);
+hipError_t launch_tv_grad(const float* T, const float* S, int rows, int V, float inv2n, float* dz,
+                          float* tv_row, hipStream_t s);
+hipError_t launch_tv_mean(const float* tv_row, int rows, float* loss, hipStream_t s);

@@ -157,6 +157,11 @@ struct uno_ctx {
   std::vector<uint32_t> snap_epoch;
   // producer counts issued so far on each hand-off counter (their targets)
   uint32_t sync_issued[kSyncCounters] = {};   // [group][row tile]
+  // activation checkpoint of the distillation forward (uno_set_distill_checkpoint)
+  float* ck_x = nullptr;
+  void* ck_k = nullptr;
+  void* ck_v = nullptr;
+  int ck_batch = 0, ck_L = 0;
   // stage capture
   bool trace_on = false;
   uno_trace trace{};
@@ -447,6 +452,11 @@ struct FwdIn {
   float* student;
   float* tv_row;
   float* tv_block;
+  // activation checkpoint of the distillation forward: the z1 rows' residual
+  // stream entering layer l goes to ck_x + l * ck_stride (rows of the group's
+  // sequences in order, [n * L, d]); slot n_layers takes the stream before the LM head
+  float* ck_x;
+  size_t ck_stride;
 };
 
 template <typename T>
@@ -684,9 +694,20 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
     if (lora && c->bf16 && !tile_lora) { a.zero_ptr = Bfx[buf]; a.zero_n = R * cols; }
   };
 
+  // z1 rows of every sequence of the group into checkpoint slot i
+  auto cap_ck = [&](int i) -> uno_status {
+    if (f.mode != 4 || !f.ck_x) return UNO_OK;
+    const size_t Lx = f.rows_per_seq / 2;
+    UNO_HIP(c, hipMemcpy2DAsync(f.ck_x + (size_t)i * f.ck_stride, Lx * d * sizeof(float),
+                                x + Lx * d, (size_t)f.rows_per_seq * d * sizeof(float),
+                                Lx * d * sizeof(float), f.n, hipMemcpyDeviceToDevice, s));
+    return UNO_OK;
+  };
+
   for (int l = 0; l < L; ++l) {
     const uno_trace_layer* tr = traced(l);
     if (tr) { if (uno_status st = cap_x(tr->x_in)) return st; }
+    if (uno_status st = cap_ck(l)) return st;
     // --- attention block: q|k|v (+LoRA) with RoPE and the paged K/V write
     static const int pqkv[3] = {0, 1, 2};
     if (lora && !fuse_lora) { uno_status st = lora_down(xg, d, 3, pqkv, l, 0, 2 * l); if (st) return st; }
@@ -795,6 +816,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   if (f.hidden_out)
     UNO_HIP(c, hipMemcpyAsync(f.hidden_out, x, sizeof(float) * R * d, hipMemcpyDeviceToDevice, s));
   if (f.mode == 4) {
+    if (uno_status st = cap_ck(L)) return st;
     // teacher = x-row logits (AR weights), student = z1-row logits (AR + LoRA)
     if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
     const int Lx = f.rows_per_seq / 2, nt = V / 16;
@@ -872,6 +894,271 @@ uno_status set_state(uno_ctx* c, int seq, int len, int pending, int iter) {
 // ====================================================================== C ABI
 // top-p truncation of `rows` probability rows of V (k_sample.hip; in place when in == out)
 hipError_t launch_top_p(const float* in, float* out, int rows, int V, float top_p, hipStream_t s);
+
+// ------------------------------------------------------ distillation backward
+namespace {
+
+// Projection shapes (out, in) in the order q, k, v, o, gate, up, down.
+void proj_shape(const uno_config& g, int p, int* out, int* in) {
+  const int d = g.d_model, qd = g.n_q_heads * g.head_dim, kvd = g.n_kv_heads * g.head_dim;
+  const int F = g.ffn_dim;
+  const int o[7] = {qd, kvd, kvd, d, F, F, d}, i[7] = {d, d, d, qd, d, d, F};
+  *out = o[p];
+  *in = i[p];
+}
+
+// Scratch of the backward over S sequences of L z1 rows (N = S * L), bytes from 0.
+struct BwLayout {
+  size_t hg1, rs1, hg2, rs2, x2, t[7], Yq, Yk, Yv, Q, Ka, Va, P, dP, o, Yg, Yu, a, da, dt;
+  size_t dx2, dh, dq, dk, dv, part, dy, tv, dz, lm_hg, lm_rs, lm_dh;
+  size_t part_floats;
+  int lm_rows;            // rows of one LM-head backward chunk
+  size_t total;
+};
+
+constexpr int kBwMaxSplits = 16;
+
+BwLayout bw_layout(const uno_config& g, size_t S, size_t L) {
+  BwLayout W{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  const size_t N = S * L, d = g.d_model, r = g.lora_rank, F = g.ffn_dim;
+  const size_t qd = (size_t)g.n_q_heads * g.head_dim, kvd = (size_t)g.n_kv_heads * g.head_dim;
+  const size_t wide = std::max({d, qd, F});
+  W.hg1 = take(N * d * 2); W.rs1 = take(N * 4);
+  W.hg2 = take(N * d * 2); W.rs2 = take(N * 4);
+  W.x2 = take(N * d * 4);
+  for (int p = 0; p < 7; ++p) W.t[p] = take(N * r * 2);
+  W.Yq = take(N * qd * 4); W.Yk = take(N * kvd * 4); W.Yv = take(N * kvd * 4);
+  W.Q = take(N * qd * 2);
+  W.Ka = take(S * 2 * L * kvd * 2); W.Va = take(S * 2 * L * kvd * 2);
+  W.P = take(N * g.n_q_heads * 2 * L * 4);          // [S][Hkv][L * G][2L]
+  W.dP = take(L * g.n_q_heads * 2 * L * 4);         // one sequence
+  W.o = take(N * qd * 2);
+  W.Yg = take(N * F * 4); W.Yu = take(N * F * 4); W.a = take(N * F * 2);
+  W.da = take(N * F * 4); W.dt = take(N * r * 4);
+  W.dx2 = take(N * d * 4); W.dh = take(N * std::max(d, qd) * 4);
+  W.dq = take(N * qd * 4); W.dk = take(N * kvd * 4); W.dv = take(N * kvd * 4);
+  W.part_floats = std::max((size_t)kBwMaxSplits * r * wide, (size_t)4 * N * r);
+  W.part = take(W.part_floats * 4);
+  W.dy = take(N * d * 4);
+  W.tv = take(N * 4);
+  W.lm_rows = (int)std::min<size_t>(N, 2048);
+  W.dz = take((size_t)W.lm_rows * g.vocab * 4);
+  W.lm_hg = take((size_t)W.lm_rows * d * 2); W.lm_rs = take((size_t)W.lm_rows * 4);
+  W.lm_dh = take((size_t)W.lm_rows * d * 4);
+  W.total = o;
+  return W;
+}
+
+int ilog2(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
+
+// Splits of the k range for a GEMM with few output tiles and a long k: enough
+// workgroups for the chip, at least four k steps each.
+int bw_splits(int M, int N, int K, size_t part_floats) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int s = std::min(kBwMaxSplits, std::max(1, 512 / tiles));
+  s = std::min(s, std::max(1, K / 128));
+  while (s > 1 && (size_t)s * M * N > part_floats) --s;
+  return s;
+}
+
+uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes) {
+  const uno_config& g = c->cfg;
+  if (!c->bf16) return fail(c, UNO_ERR_UNSUPPORTED, "the backward runs in bf16 contexts");
+  if (!c->has_lora) return fail(c, UNO_ERR_INVALID_ARG, "the context has no LoRA");
+  const int G = g.n_q_heads / g.n_kv_heads;
+  if (G & (G - 1)) return fail(c, UNO_ERR_UNSUPPORTED, "backward: query group must be a power of 2");
+  if (S < 1 || L < 16 || L % 16 || B < 1 || L % B)
+    return fail(c, UNO_ERR_INVALID_ARG, "backward: batch >= 1, L a multiple of 16 and of B");
+  if (L > c->maxpp * g.page_size) return fail(c, UNO_ERR_INVALID_ARG, "backward: L beyond the RoPE table");
+  if (!scratch || bytes < bw_layout(g, S, L).total)
+    return fail(c, UNO_ERR_INVALID_ARG, "backward: scratch smaller than uno_query_backward_bytes");
+  return UNO_OK;
+}
+
+BwGemm bw_mk(int am, int bm, const void* A, Idx2 ai, const void* B, Idx2 bi, int b_cols, void* C,
+             Idx2 ci, int M, int N, int K) {
+  BwGemm x{};
+  x.amode = am; x.bmode = bm;
+  x.A = A; x.ai = ai; x.B = B; x.bi = bi; x.b_cols = b_cols; x.C = C; x.ci = ci;
+  x.M = M; x.N = N; x.K = K; x.batch = 1; x.splits = 1; x.alpha = 1.0f;
+  return x;
+}
+
+// One layer of the backward over the z1 rows of S sequences (N = S * L rows, row
+// s * L + i at position i): recompute the gate-on forward from the layer input
+// xin [N, d] and the x rows' K/V (kc / vc: sequence s at kc + s * kv_seq_stride,
+// [L][Hkv][hd]), then propagate dy [N, d] to dx [N, d] and form the LoRA
+// gradients ga[p] [r, in] and gb[p] [out, r] (overwritten).
+uno_status layer_backward(uno_ctx* c, int l, int S, int L, int B, const float* xin, const bf16* kc,
+                          const bf16* vc, long kv_seq_stride, const float* dy, float* dx,
+                          float* const* ga, float* const* gb, char* ws, const BwLayout& W) {
+  const uno_config& g = c->cfg;
+  hipStream_t st = c->stream;
+  const int N = S * L, d = g.d_model, r = g.lora_rank, F = g.ffn_dim, hd = g.head_dim;
+  const int Hq = g.n_q_heads, Hkv = g.n_kv_heads, G = Hq / Hkv, LG = L * G;
+  const int qd = Hq * hd, kvd = Hkv * hd, sh = ilog2(G);
+  const float sc = g.lora_alpha / (float)r, ascale = 1.0f / std::sqrt((float)hd);
+  auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto BF = [&](size_t off) { return reinterpret_cast<bf16*>(ws + off); };
+  auto Wt = [&](int p) { return c->w[p][l]; };
+  auto At = [&](int p) { return c->la[p][l]; };
+  auto Bt = [&](int p) { return c->lb[p][l]; };
+  const bf16* g1 = static_cast<const bf16*>(c->attn_norm[l]);
+  const bf16* g2 = static_cast<const bf16*>(c->mlp_norm[l]);
+  const float* rcos = c->at<float>(c->L.rope_cos);
+  const float* rsin = c->at<float>(c->L.rope_sin);
+  auto gemm = [&](const BwGemm& x) -> uno_status {
+    UNO_HIP(c, launch_bw_gemm(x, st));
+    return UNO_OK;
+  };
+#define BW_DO(expr) do { if (uno_status s_ = (expr)) return s_; } while (0)
+  // gated-LoRA projection recompute: t = bf16(s * rs * (h A^T)), y = rs * (h W^T) + t B^T
+  auto proj_fwd = [&](int p, const bf16* h, const float* rs, void* y, bool y_acc) -> uno_status {
+    int out, in;
+    proj_shape(g, p, &out, &in);
+    BwGemm a = bw_mk(BW_A_K16, BW_B_TN, h, idx_ld(in), At(p), {}, in, BF(W.t[p]), idx_ld(r), N, r, in);
+    a.alpha = sc; a.row_scale = rs; a.out_bf16 = 1;
+    BW_DO(gemm(a));
+    BwGemm b = bw_mk(BW_A_K16, BW_B_TN, h, idx_ld(in), Wt(p), {}, in, y, idx_ld(out), N, out, in);
+    b.row_scale = rs; b.accumulate = y_acc;
+    BW_DO(gemm(b));
+    BwGemm u = bw_mk(BW_A_K16, BW_B_TN, BF(W.t[p]), idx_ld(r), Bt(p), {}, r, y, idx_ld(out), N, out, r);
+    u.accumulate = 1;
+    return gemm(u);
+  };
+  // projection backward: dB = dY^T t, dt = dY B, dA = s (dt * ks)^T h, dh (+)= dY W + s dt A
+  auto proj_back = [&](int p, const float* dY, const bf16* h, const float* ks, float* dh,
+                       bool dh_acc, int perm) -> uno_status {
+    int out, in;
+    proj_shape(g, p, &out, &in);
+    float* dt = F32(W.dt);
+    BwGemm gB = bw_mk(BW_A_M32, BW_B_N16, dY, idx_ld(out), BF(W.t[p]), idx_ld(r), 0, gb[p], idx_ld(r), out, r, N);
+    gB.perm_hd = perm;
+    gB.splits = bw_splits(out, r, N, W.part_floats); gB.part = F32(W.part);
+    BW_DO(gemm(gB));
+    BwGemm gt = bw_mk(BW_A_K32, BW_B_TT, dY, idx_ld(out), Bt(p), {}, r, dt, idx_ld(r), N, r, out);
+    BW_DO(gemm(gt));
+    BwGemm gA = bw_mk(BW_A_M32, BW_B_N16, dt, idx_ld(r), h, idx_ld(in), 0, ga[p], idx_ld(in), r, in, N);
+    gA.alpha = sc; gA.kscale = ks;
+    gA.splits = bw_splits(r, in, N, W.part_floats); gA.part = F32(W.part);
+    BW_DO(gemm(gA));
+    BwGemm gh = bw_mk(BW_A_K32, BW_B_TT, dY, idx_ld(out), Wt(p), {}, in, dh, idx_ld(in), N, in, out);
+    gh.accumulate = dh_acc;
+    BW_DO(gemm(gh));
+    BwGemm gl = bw_mk(BW_A_K32, BW_B_TT, dt, idx_ld(r), At(p), {}, in, dh, idx_ld(in), N, in, r);
+    gl.alpha = sc; gl.accumulate = 1;
+    return gemm(gl);
+  };
+
+  // ---------------- recompute of the gate-on forward
+  UNO_HIP(c, launch_bw_rmsprep<bf16>(xin, g1, g.rms_eps, N, d, BF(W.hg1), F32(W.rs1), st));
+  BW_DO(proj_fwd(0, BF(W.hg1), F32(W.rs1), F32(W.Yq), false));
+  BW_DO(proj_fwd(1, BF(W.hg1), F32(W.rs1), F32(W.Yk), false));
+  BW_DO(proj_fwd(2, BF(W.hg1), F32(W.rs1), F32(W.Yv), false));
+  UNO_HIP(c, launch_bw_qkv_post(F32(W.Yq), F32(W.Yk), F32(W.Yv), rcos, rsin, N, L, Hq, Hkv, hd,
+                                BF(W.Q), BF(W.Ka), BF(W.Va), st));
+  UNO_HIP(c, launch_bw_ctx_copy(kc, vc, kv_seq_stride, S, L, Hkv, hd, BF(W.Ka), BF(W.Va), st));
+  const Idx2 qrow{sh, (long)qd, (long)hd};          // row i * G + g of KV head h
+  const long kv_seq = (long)Hkv * 2 * L * hd, p_seq = (long)Hkv * LG * 2 * L;
+  for (int s = 0; s < S; ++s) {
+    float* P = F32(W.P) + s * p_seq;
+    BwGemm sg = bw_mk(BW_A_K16, BW_B_K16, BF(W.Q) + (size_t)s * L * qd, qrow, BF(W.Ka) + s * kv_seq,
+                      idx_ld(hd), 0, P, idx_ld(2 * L), LG, 2 * L, hd);
+    sg.batch = Hkv; sg.a_bs = (long)G * hd; sg.b_bs = 2L * L * hd; sg.c_bs = (long)LG * 2 * L;
+    BW_DO(gemm(sg));
+    UNO_HIP(c, launch_bw_softmax(P, L, G, Hkv, B, ascale, st));
+    BwGemm og = bw_mk(BW_A_K32, BW_B_N16, P, idx_ld(2 * L), BF(W.Va) + s * kv_seq, idx_ld(hd), 0,
+                      BF(W.o) + (size_t)s * L * qd, qrow, LG, hd, 2 * L);
+    og.batch = Hkv; og.a_bs = (long)LG * 2 * L; og.b_bs = 2L * L * hd; og.c_bs = (long)G * hd;
+    og.out_bf16 = 1;
+    BW_DO(gemm(og));
+  }
+  UNO_HIP(c, hipMemcpyAsync(F32(W.x2), xin, sizeof(float) * N * d, hipMemcpyDeviceToDevice, st));
+  BW_DO(proj_fwd(3, BF(W.o), nullptr, F32(W.x2), true));
+  UNO_HIP(c, launch_bw_rmsprep<bf16>(F32(W.x2), g2, g.rms_eps, N, d, BF(W.hg2), F32(W.rs2), st));
+  BW_DO(proj_fwd(4, BF(W.hg2), F32(W.rs2), F32(W.Yg), false));
+  BW_DO(proj_fwd(5, BF(W.hg2), F32(W.rs2), F32(W.Yu), false));
+  UNO_HIP(c, launch_bw_swiglu(F32(W.Yg), F32(W.Yu), BF(W.a), (long)N * F, st));
+  {   // the down projection's LoRA intermediate (its output is not needed)
+    BwGemm a = bw_mk(BW_A_K16, BW_B_TN, BF(W.a), idx_ld(F), At(6), {}, F, BF(W.t[6]), idx_ld(r), N, r, F);
+    a.alpha = sc; a.out_bf16 = 1;
+    BW_DO(gemm(a));
+  }
+
+  // ---------------- backward
+  BW_DO(proj_back(6, dy, BF(W.a), nullptr, F32(W.da), false, 0));
+  UNO_HIP(c, launch_bw_swiglu_back(F32(W.da), F32(W.Yg), F32(W.Yu), (long)N * F, st));
+  BW_DO(proj_back(4, F32(W.Yg), BF(W.hg2), F32(W.rs2), F32(W.dh), false, 0));
+  BW_DO(proj_back(5, F32(W.Yu), BF(W.hg2), F32(W.rs2), F32(W.dh), true, 0));
+  UNO_HIP(c, launch_bw_rmsback<bf16>(F32(W.x2), BF(W.hg2), F32(W.rs2), g2, F32(W.dh), dy,
+                                     F32(W.dx2), N, d, st));
+  BW_DO(proj_back(3, F32(W.dx2), BF(W.o), nullptr, F32(W.dh), false, 0));   // dh = dO
+  for (int s = 0; s < S; ++s) {
+    const float* P = F32(W.P) + s * p_seq;
+    float* dP = F32(W.dP);
+    const float* dO = F32(W.dh) + (size_t)s * L * qd;
+    BwGemm pg = bw_mk(BW_A_K32, BW_B_K16, dO, qrow, BF(W.Va) + s * kv_seq, idx_ld(hd), 0, dP,
+                      idx_ld(2 * L), LG, 2 * L, hd);
+    pg.batch = Hkv; pg.a_bs = (long)G * hd; pg.b_bs = 2L * L * hd; pg.c_bs = (long)LG * 2 * L;
+    BW_DO(gemm(pg));
+    UNO_HIP(c, launch_bw_softmax_back(P, dP, L, G, Hkv, ascale, st));
+    BwGemm qg = bw_mk(BW_A_K32, BW_B_N16, dP, idx_ld(2 * L), BF(W.Ka) + s * kv_seq, idx_ld(hd), 0,
+                      F32(W.dq) + (size_t)s * L * qd, qrow, LG, hd, 2 * L);
+    qg.batch = Hkv; qg.a_bs = (long)LG * 2 * L; qg.b_bs = 2L * L * hd; qg.c_bs = (long)G * hd;
+    BW_DO(gemm(qg));
+    // the z1 keys (columns L..2L-1): dk = dS^T q, dv = P^T dO
+    BwGemm kg = bw_mk(BW_A_M32, BW_B_N16, dP + L, idx_ld(2 * L), BF(W.Q) + (size_t)s * L * qd, qrow,
+                      0, F32(W.dk) + (size_t)s * L * kvd, idx_ld(kvd), L, hd, LG);
+    kg.batch = Hkv; kg.a_bs = (long)LG * 2 * L; kg.b_bs = (long)G * hd; kg.c_bs = hd;
+    BW_DO(gemm(kg));
+    BwGemm vg = bw_mk(BW_A_M32, BW_B_N32, P + L, idx_ld(2 * L), dO, qrow, 0,
+                      F32(W.dv) + (size_t)s * L * kvd, idx_ld(kvd), L, hd, LG);
+    vg.batch = Hkv; vg.a_bs = (long)LG * 2 * L; vg.b_bs = (long)G * hd; vg.c_bs = hd;
+    BW_DO(gemm(vg));
+  }
+  UNO_HIP(c, launch_bw_qkv_back(F32(W.dq), F32(W.dk), F32(W.dv), rcos, rsin, N, L, Hq, Hkv, hd,
+                                F32(W.Yq), F32(W.Yk), F32(W.Yv), st));
+  BW_DO(proj_back(0, F32(W.Yq), BF(W.hg1), F32(W.rs1), F32(W.dh), false, hd));
+  BW_DO(proj_back(1, F32(W.Yk), BF(W.hg1), F32(W.rs1), F32(W.dh), true, hd));
+  BW_DO(proj_back(2, F32(W.Yv), BF(W.hg1), F32(W.rs1), F32(W.dh), true, hd));
+  UNO_HIP(c, launch_bw_rmsback<bf16>(xin, BF(W.hg1), F32(W.rs1), g1, F32(W.dh), F32(W.dx2), dx,
+                                     N, d, st));
+#undef BW_DO
+  return UNO_OK;
+}
+
+// LM-head backward of rows [0, rows) (chunked): dx = d/dx of rms_norm(x) W_lm^T
+// given dlogits; when teacher / student are given, dlogits are first formed from
+// them (the TV gradient, 1 / (2 n_total) scale) with the rows' TV in tv_row.
+uno_status lm_backward(uno_ctx* c, int rows, const float* xf, const float* dlogits,
+                       const float* teacher, const float* student, int n_total, float* tv_row,
+                       float* dx, char* ws, const BwLayout& W) {
+  const uno_config& g = c->cfg;
+  hipStream_t st = c->stream;
+  const int d = g.d_model, V = g.vocab;
+  const bf16* gf = static_cast<const bf16*>(c->final_norm);
+  for (int r0 = 0; r0 < rows; r0 += W.lm_rows) {
+    const int n = std::min(W.lm_rows, rows - r0);
+    const float* dz = dlogits ? dlogits + (size_t)r0 * V : reinterpret_cast<float*>(ws + W.dz);
+    if (!dlogits)
+      UNO_HIP(c, launch_tv_grad(teacher + (size_t)r0 * V, student + (size_t)r0 * V, n, V,
+                                0.5f / (float)n_total, reinterpret_cast<float*>(ws + W.dz),
+                                tv_row ? tv_row + r0 : nullptr, st));
+    bf16* hg = reinterpret_cast<bf16*>(ws + W.lm_hg);
+    float* rs = reinterpret_cast<float*>(ws + W.lm_rs);
+    float* dh = reinterpret_cast<float*>(ws + W.lm_dh);
+    UNO_HIP(c, launch_bw_rmsprep<bf16>(xf + (size_t)r0 * d, gf, g.rms_eps, n, d, hg, rs, st));
+    BwGemm h = bw_mk(BW_A_K32, BW_B_TT, dz, idx_ld(V), c->lm_head, {}, d, dh, idx_ld(d), n, d, V);
+    UNO_HIP(c, launch_bw_gemm(h, st));
+    UNO_HIP(c, launch_bw_rmsback<bf16>(xf + (size_t)r0 * d, hg, rs, gf, dh, nullptr,
+                                       dx + (size_t)r0 * d, n, d, st));
+  }
+  return UNO_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -1243,6 +1530,9 @@ uno_status uno_distill_forward(uno_ctx* c, int32_t batch, int32_t L, int32_t B, 
   nb = std::min(nb, batch);
   if (nb < 1) return fail(c, UNO_ERR_OUT_OF_PAGES, "no free sequence slot / pages for [x, z1]");
   const size_t V = c->cfg.vocab;
+  const bool ck = c->ck_x != nullptr;
+  if (ck && (c->ck_batch != batch || c->ck_L != L || !c->bf16))
+    return fail(c, UNO_ERR_INVALID_ARG, "the armed checkpoint is for another batch / L (or not bf16)");
   poll_snapshot(c);
   for (int g0 = 0; g0 < batch; g0 += nb) {
     const int n = std::min(nb, batch - g0);
@@ -1261,7 +1551,18 @@ uno_status uno_distill_forward(uno_ctx* c, int32_t batch, int32_t L, int32_t B, 
     f.student = d_student ? d_student + (size_t)g0 * L * V : nullptr;
     f.tv_row = d_tv_row ? d_tv_row + (size_t)g0 * L : nullptr;
     f.tv_block = d_tv_block ? d_tv_block + (size_t)g0 * (L / B) : nullptr;
+    if (ck) {
+      f.ck_x = c->ck_x + (size_t)g0 * L * c->cfg.d_model;
+      f.ck_stride = (size_t)batch * L * c->cfg.d_model;
+    }
     st = forward(c, f);
+    // the x rows' K/V of every layer (positions 0..L-1 of each borrowed slot)
+    for (int j = 0; ck && !st && j < n; ++j) {
+      const size_t o = (size_t)(g0 + j) * c->cfg.n_layers * L * c->cfg.n_kv_heads * c->cfg.head_dim;
+      hipError_t e = launch_kv_copy<bf16>(kv_layout(c), seqs[j], L, static_cast<bf16*>(c->ck_k) + o,
+                                          static_cast<bf16*>(c->ck_v) + o, 0, c->stream);
+      if (e != hipSuccess) st = hip_fail(c, e, "checkpoint K/V export");
+    }
     // the pages go back to the pool (stream-ordered after the forward)
     for (int s : seqs) {
       auto& pg = c->seq_pages[s];
@@ -1419,6 +1720,110 @@ uno_status uno_timing_read(uno_ctx* c, int32_t cls, int64_t* launches, double* t
   if (total_ms) *total_ms = ms;
   if (bytes) *bytes = b;
   if (flops) *flops = f;
+  return UNO_OK;
+}
+
+uno_status uno_query_backward_bytes(const uno_config* cfg, int32_t batch, int32_t L, size_t* bytes) {
+  uno_status s = check_config(cfg);
+  if (s) return s;
+  if (batch < 1 || L < 1 || !bytes) return fail(nullptr, UNO_ERR_INVALID_ARG, "backward bytes: batch, L >= 1");
+  *bytes = bw_layout(*cfg, batch, L).total;
+  return UNO_OK;
+}
+
+uno_status uno_set_distill_checkpoint(uno_ctx* c, float* d_x, void* d_k, void* d_v, int32_t batch,
+                                      int32_t L) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (!d_x) {
+    c->ck_x = nullptr; c->ck_k = c->ck_v = nullptr; c->ck_batch = c->ck_L = 0;
+    return UNO_OK;
+  }
+  if (!d_k || !d_v || batch < 1 || L < 1)
+    return fail(c, UNO_ERR_INVALID_ARG, "checkpoint: buffers and batch, L >= 1 required");
+  c->ck_x = d_x; c->ck_k = d_k; c->ck_v = d_v; c->ck_batch = batch; c->ck_L = L;
+  return UNO_OK;
+}
+
+uno_status uno_tv_backward(const float* d_teacher, const float* d_student, int32_t rows, int32_t vocab,
+                           int32_t n_rows_total, float* d_dlogits, float* d_tv_row, void* stream) {
+  if (!d_teacher || !d_student || !d_dlogits)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "tv_backward: null buffer");
+  if (rows < 0 || vocab <= 0 || n_rows_total < 1)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "tv_backward: rows >= 0, vocab > 0, n_rows_total >= 1");
+  hipError_t e = launch_tv_grad(d_teacher, d_student, rows, vocab, 0.5f / (float)n_rows_total,
+                                d_dlogits, d_tv_row, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, UNO_ERR_DEVICE, std::string("tv_backward: ") + hipGetErrorString(e));
+  return UNO_OK;
+}
+
+uno_status uno_lm_head_backward(uno_ctx* c, int32_t rows, const float* d_x_final,
+                                const float* d_dlogits, float* d_dx, void* d_scratch,
+                                size_t scratch_bytes) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (!d_x_final || !d_dlogits || !d_dx) return fail(c, UNO_ERR_INVALID_ARG, "lm_head_backward: null buffer");
+  if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
+  if (rows < 16 || rows % 16) return fail(c, UNO_ERR_INVALID_ARG, "lm_head_backward: rows a multiple of 16");
+  if (uno_status s = bw_check(c, 1, rows, 1, d_scratch, scratch_bytes)) return s;
+  return lm_backward(c, rows, d_x_final, d_dlogits, nullptr, nullptr, rows, nullptr, d_dx,
+                     static_cast<char*>(d_scratch), bw_layout(c->cfg, 1, rows));
+}
+
+uno_status uno_lora_layer_backward(uno_ctx* c, int32_t layer, int32_t batch, int32_t L, int32_t B,
+                                   const float* d_x_in, const void* d_k_ctx, const void* d_v_ctx,
+                                   const float* d_dy, float* d_dx, float* const* d_grad_a,
+                                   float* const* d_grad_b, void* d_scratch, size_t scratch_bytes) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, UNO_ERR_INVALID_ARG, "bad layer");
+  if (!d_x_in || !d_k_ctx || !d_v_ctx || !d_dy || !d_dx || !d_grad_a || !d_grad_b)
+    return fail(c, UNO_ERR_INVALID_ARG, "layer_backward: null buffer");
+  for (int p = 0; p < 7; ++p)
+    if (!d_grad_a[p] || !d_grad_b[p]) return fail(c, UNO_ERR_INVALID_ARG, "layer_backward: null gradient");
+  if (uno_status s = bw_check(c, batch, L, B, d_scratch, scratch_bytes)) return s;
+  const long kvd = (long)c->cfg.n_kv_heads * c->cfg.head_dim;
+  return layer_backward(c, layer, batch, L, B, d_x_in, static_cast<const bf16*>(d_k_ctx),
+                        static_cast<const bf16*>(d_v_ctx), (long)L * kvd, d_dy, d_dx, d_grad_a,
+                        d_grad_b, static_cast<char*>(d_scratch), bw_layout(c->cfg, batch, L));
+}
+
+uno_status uno_distill_backward(uno_ctx* c, int32_t batch, int32_t L, int32_t B,
+                                const float* d_teacher, const float* d_student,
+                                const float* d_x_ckpt, const void* d_k_ckpt, const void* d_v_ckpt,
+                                float* d_loss, float* d_tv_row, float* const* d_grad_a,
+                                float* const* d_grad_b, void* d_scratch, size_t scratch_bytes) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (!d_teacher || !d_student || !d_x_ckpt || !d_k_ckpt || !d_v_ckpt || !d_grad_a || !d_grad_b)
+    return fail(c, UNO_ERR_INVALID_ARG, "distill_backward: null buffer");
+  for (int p = 0; p < 7; ++p)
+    if (!d_grad_a[p] || !d_grad_b[p]) return fail(c, UNO_ERR_INVALID_ARG, "distill_backward: null gradient");
+  if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
+  if (uno_status s = bw_check(c, batch, L, B, d_scratch, scratch_bytes)) return s;
+  const uno_config& g = c->cfg;
+  const BwLayout W = bw_layout(g, batch, L);
+  char* ws = static_cast<char*>(d_scratch);
+  const size_t N = (size_t)batch * L, d = g.d_model, r = g.lora_rank, nl = g.n_layers;
+  const long kvd = (long)g.n_kv_heads * g.head_dim;
+  float* dy = reinterpret_cast<float*>(ws + W.dy);
+  float* tv = d_tv_row ? d_tv_row : reinterpret_cast<float*>(ws + W.tv);
+  if (uno_status s = lm_backward(c, (int)N, d_x_ckpt + nl * N * d, nullptr, d_teacher, d_student,
+                                 (int)N, tv, dy, ws, W))
+    return s;
+  if (d_loss) UNO_HIP(c, launch_tv_mean(tv, (int)N, d_loss, c->stream));
+  for (int l = (int)nl - 1; l >= 0; --l) {
+    float* ga[7];
+    float* gb[7];
+    for (int p = 0; p < 7; ++p) {
+      int out, in;
+      proj_shape(g, p, &out, &in);
+      ga[p] = d_grad_a[p] + (size_t)l * r * in;
+      gb[p] = d_grad_b[p] + (size_t)l * out * r;
+    }
+    // dx overwrites dy in place: a layer's last read of dy precedes its write of dx
+    const bf16* kc = static_cast<const bf16*>(d_k_ckpt) + (size_t)l * L * kvd;
+    const bf16* vc = static_cast<const bf16*>(d_v_ckpt) + (size_t)l * L * kvd;
+    if (uno_status s = layer_backward(c, l, batch, L, B, d_x_ckpt + l * N * d, kc, vc,
+                                      (long)nl * L * kvd, dy, dy, ga, gb, ws, W))
+      return s;
+  }
   return UNO_OK;
 }
 

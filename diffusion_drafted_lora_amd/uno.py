@@ -24,7 +24,9 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_kv_export", "uno_seq_state", "uno_release", "uno_sync", "uno_free_pages",
             "uno_last_error", "uno_destroy", "uno_timing", "uno_timing_every", "uno_timing_read",
             "uno_distill_forward", "uno_pack_weight", "uno_top_p", "uno_accept_noalloc",
-            "uno_set_trace")
+            "uno_set_trace", "uno_query_backward_bytes", "uno_set_distill_checkpoint",
+            "uno_tv_backward", "uno_lm_head_backward", "uno_lora_layer_backward",
+            "uno_distill_backward")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -105,6 +107,14 @@ def lib():
         L.uno_last_error.restype = C.c_char_p
         L.uno_destroy.argtypes = [vp]
         L.uno_destroy.restype = None
+        L.uno_query_backward_bytes.argtypes = [P(UnoConfigC), i32, i32, P(C.c_size_t)]
+        L.uno_set_distill_checkpoint.argtypes = [vp, vp, vp, vp, i32, i32]
+        L.uno_tv_backward.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.uno_lm_head_backward.argtypes = [vp, i32, vp, vp, vp, vp, C.c_size_t]
+        L.uno_lora_layer_backward.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                              P(vp), P(vp), vp, C.c_size_t]
+        L.uno_distill_backward.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                           P(vp), P(vp), vp, C.c_size_t]
         L.uno_timing.argtypes = [vp, C.c_uint32]
         L.uno_timing_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double), P(C.c_double),
                                       P(C.c_double)]
@@ -312,6 +322,84 @@ class Engine:
                                               _ptr(student), _ptr(tv_row), _ptr(tv_block)))
         return teacher, student, tv_row, tv_block
 
+    # ---- distillation backward (gradient of L_TV with respect to the LoRA)
+
+    def backward_scratch(self, batch, L):
+        """Device scratch for a backward over batch x L z1 rows (cached, grown)."""
+        n = C.c_size_t(0)
+        self._check(lib().uno_query_backward_bytes(C.byref(self.ccfg), batch, L, C.byref(n)))
+        cur = getattr(self, "_bw_scratch", None)
+        if cur is None or cur.numel() < n.value:
+            self._bw_scratch = None
+            self._bw_scratch = self._empty((n.value,), self.torch.uint8)
+        return self._bw_scratch
+
+    def set_distill_checkpoint(self, batch, L):
+        """Arm the activation checkpoint for distillation forwards of batch x L and
+        return its buffers {"x", "k", "v"}; batch None disarms."""
+        torch = self.torch
+        if batch is None:
+            self._check(lib().uno_set_distill_checkpoint(self.h, None, None, None, 0, 0))
+            self._ckpt = None
+            return None
+        cfg = self.cfg
+        ck = {"x": self._empty((cfg.n_layers + 1, batch * L, cfg.d_model), torch.float32),
+              "k": self._empty((batch, cfg.n_layers, L, cfg.n_kv_heads, cfg.head_dim), torch.bfloat16),
+              "v": self._empty((batch, cfg.n_layers, L, cfg.n_kv_heads, cfg.head_dim), torch.bfloat16)}
+        self._check(lib().uno_set_distill_checkpoint(self.h, _ptr(ck["x"]), _ptr(ck["k"]),
+                                                     _ptr(ck["v"]), batch, L))
+        self._ckpt = ck
+        return ck
+
+    def _grad_bufs(self, layers):
+        torch = self.torch
+        shapes = synth.proj_shapes(self.cfg)
+        r = self.cfg.lora_rank
+        lead = () if layers is None else (layers,)
+        ga = {p: self._empty(lead + (r, shapes[p][1]), torch.float32) for p in PROJ}
+        gb = {p: self._empty(lead + (shapes[p][0], r), torch.float32) for p in PROJ}
+        arr = lambda d: (C.c_void_p * 7)(*[C.c_void_p(d[p].data_ptr()) for p in PROJ])
+        return ga, gb, arr(ga), arr(gb)
+
+    def lm_head_backward(self, x_final, dlogits):
+        """uno_lm_head_backward: dx [rows, d] of the final residual stream."""
+        rows = x_final.shape[0]
+        dx = self._empty((rows, self.cfg.d_model), self.torch.float32)
+        sc = self.backward_scratch(1, rows)
+        self._check(lib().uno_lm_head_backward(self.h, rows, _ptr(x_final), _ptr(dlogits), _ptr(dx),
+                                               _ptr(sc), sc.numel()))
+        return dx
+
+    def lora_layer_backward(self, layer, B, x_in, k_ctx, v_ctx, dy, dx=None):
+        """uno_lora_layer_backward over the z1 rows of k_ctx.shape[0] sequences of
+        L = k_ctx.shape[1] rows.  Returns (dx, {proj: dA}, {proj: dB})."""
+        batch, L = k_ctx.shape[0], k_ctx.shape[1]
+        if dx is None:
+            dx = self._empty((batch * L, self.cfg.d_model), self.torch.float32)
+        ga, gb, pa, pb = self._grad_bufs(None)
+        sc = self.backward_scratch(batch, L)
+        self._check(lib().uno_lora_layer_backward(self.h, layer, batch, L, B, _ptr(x_in), _ptr(k_ctx),
+                                                  _ptr(v_ctx), _ptr(dy), _ptr(dx), pa, pb, _ptr(sc),
+                                                  sc.numel()))
+        return dx, ga, gb
+
+    def distill_backward(self, B, teacher, student, ckpt=None, tv_row=None):
+        """uno_distill_backward after a checkpointed distill_forward.  Returns
+        (loss [1], tv_row [batch * L], {proj: dA [layers, r, in]}, {proj: dB})."""
+        torch = self.torch
+        ckpt = ckpt or self._ckpt
+        batch, L = teacher.shape[0], teacher.shape[1]
+        loss = self._empty((1,), torch.float32)
+        if tv_row is None:
+            tv_row = self._empty((batch * L,), torch.float32)
+        ga, gb, pa, pb = self._grad_bufs(self.cfg.n_layers)
+        sc = self.backward_scratch(batch, L)
+        self._check(lib().uno_distill_backward(self.h, batch, L, B, _ptr(teacher), _ptr(student),
+                                               _ptr(ckpt["x"]), _ptr(ckpt["k"]), _ptr(ckpt["v"]),
+                                               _ptr(loss), _ptr(tv_row), pa, pb, _ptr(sc),
+                                               sc.numel()))
+        return loss, tv_row, ga, gb
+
     def set_trace(self, rows, layers=(), logits=False):
         """Arm the stage capture for forwards of `rows` rows: for each layer index
         in `layers` (at most four) device buffers for x_in, q, attn, x_mid, act and
@@ -415,6 +503,24 @@ def top_p(probs, p, out=None):
     if st != UNO_OK:
         raise UnoError(st, lib().uno_last_error(None).decode())
     return out
+
+
+def tv_backward(teacher, student, n_rows_total=None, dlogits=None, tv_row=None):
+    """uno_tv_backward on float32 device logits [rows, V] (no context): returns
+    (dL_TV/d student logits, per-row TV)."""
+    import torch
+    V = teacher.shape[-1]
+    rows = teacher.numel() // V
+    if dlogits is None:
+        dlogits = torch.empty_like(student)
+    if tv_row is None:
+        tv_row = torch.empty(rows, dtype=torch.float32, device=teacher.device)
+    st = lib().uno_tv_backward(_ptr(teacher), _ptr(student), rows, V, n_rows_total or rows,
+                               _ptr(dlogits), _ptr(tv_row),
+                               C.c_void_p(torch.cuda.current_stream(teacher.device).cuda_stream))
+    if st != UNO_OK:
+        raise UnoError(st, lib().uno_last_error(None).decode())
+    return dlogits, tv_row
 
 
 def accept_noalloc(seed, p, q, draft, seq_ids, pos, iters, out, n_out, err=None, stream=None):

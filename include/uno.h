@@ -275,6 +275,85 @@ uno_status uno_distill_forward(uno_ctx* ctx, int32_t batch, int32_t L, int32_t B
                                const int32_t* d_x, float* d_teacher, float* d_student,
                                float* d_tv_row, float* d_tv_block);
 
+/* ---- Distillation backward (the training side of the [x, z1] forward).
+ * The pages train only the LoRA of the diffusion path, with the AR weights frozen
+ * as the teacher, and the block-wise total variation between the diffusion and
+ * the AR distributions as the loss term that trained best (shibing624 reading
+ * notes, "Diffusion Distillation"; ai-papers-daily summary, method key points).
+ * The library reads the loss L_TV as the mean over sequences and blocks of the
+ * block TV, a block's TV being the mean over its rows of
+ * TV_i = 0.5 * sum_v |p_T,i(v) - p_S,i(v)| (so the mean of TV_i over all rows),
+ * with the teacher law a constant, d|u|/du = 0 at u = 0 and every bf16 storage
+ * rounding of the forward passed straight through.  Gradients are float32:
+ * dL/dA_p [r, in] and dL/dB_p [out, r] row-major in the uno_weights row order
+ * (q / k / v rows in head order, not the pair order of the packed weights).
+ * The z1 rows' forward is recomputed layer by layer from a checkpoint; every
+ * product runs on the bf16 matrix cores with float32 accumulation, a float32
+ * gradient operand entering as two bf16 terms (hi = bf16(g), lo = bf16(g - hi)).
+ * bf16 contexts with LoRA only (UNO_ERR_UNSUPPORTED otherwise); the query group
+ * n_q_heads / n_kv_heads must be a power of two.  Scratch memory is the caller's
+ * (uno_query_backward_bytes); all calls are asynchronous on the context's stream. */
+
+/* Scratch bytes for a backward over `batch` sequences of L z1 rows (also the
+ * bound of uno_lm_head_backward with batch 1 and L = rows). */
+uno_status uno_query_backward_bytes(const uno_config* cfg, int32_t batch, int32_t L,
+                                    size_t* bytes);
+
+/* Arm (d_x != NULL) or disarm the activation checkpoint that the next
+ * uno_distill_forward calls (of exactly this batch and L) fill:
+ *   d_x  float32 [n_layers + 1][batch * L][d_model]: slot l holds the z1 rows'
+ *        residual stream entering layer l, slot n_layers the stream entering the
+ *        final norm (sequence b's rows at b * L);
+ *   d_k, d_v  bf16 [batch][n_layers][L][n_kv_heads][head_dim]: the x rows' K
+ *        (after RoPE) and V of every layer.
+ * A distillation forward of another batch or L while armed is UNO_ERR_INVALID_ARG. */
+uno_status uno_set_distill_checkpoint(uno_ctx* ctx, float* d_x, void* d_k, void* d_v,
+                                      int32_t batch, int32_t L);
+
+/* Gradient of L_TV at the student logits (parity entry; no context): for each of
+ * `rows` rows of d_teacher / d_student [rows, vocab] (float32 logits, -inf
+ * allowed), with N = n_rows_total rows in the whole loss,
+ * g(v) = sign(p_S(v) - p_T(v)) / (2N) and d_dlogits(v) = p_S(v) (g(v) - sum_u p_S(u) g(u));
+ * d_tv_row [rows] (may be NULL) receives TV_i.  Softmaxes in float32. */
+uno_status uno_tv_backward(const float* d_teacher, const float* d_student, int32_t rows,
+                           int32_t vocab, int32_t n_rows_total, float* d_dlogits, float* d_tv_row,
+                           void* stream);
+
+/* LM-head backward (parity entry): d_dx [rows, d] = the gradient at the final
+ * residual stream d_x_final [rows, d] of logits = rms_norm(x) W_lm^T given
+ * d_dlogits [rows, vocab].  rows a multiple of 16. */
+uno_status uno_lm_head_backward(uno_ctx* ctx, int32_t rows, const float* d_x_final,
+                                const float* d_dlogits, float* d_dx, void* d_scratch,
+                                size_t scratch_bytes);
+
+/* One layer of the backward (parity entry).  Rows: the z1 rows of `batch`
+ * sequences of L rows (row b * L + i at position i, gate on), each block of B rows
+ * attending to the x rows' keys before the block and causally to its own.
+ *   d_x_in   float32 [batch * L, d]: the residual stream entering the layer;
+ *   d_k_ctx, d_v_ctx  bf16 [batch][L][n_kv_heads][head_dim]: the x rows' K (after
+ *            RoPE) and V of this layer;
+ *   d_dy     float32 [batch * L, d]: dL / d(layer output);
+ *   d_dx     float32 [batch * L, d]: dL / d(layer input) (may equal d_dy);
+ *   d_grad_a[7], d_grad_b[7]: this layer's dL/dA_p [r, in], dL/dB_p [out, r]
+ *            (overwritten). */
+uno_status uno_lora_layer_backward(uno_ctx* ctx, int32_t layer, int32_t batch, int32_t L,
+                                   int32_t B, const float* d_x_in, const void* d_k_ctx,
+                                   const void* d_v_ctx, const float* d_dy, float* d_dx,
+                                   float* const* d_grad_a, float* const* d_grad_b,
+                                   void* d_scratch, size_t scratch_bytes);
+
+/* The whole backward of one distillation forward: d_teacher / d_student [batch,
+ * L, vocab] and the checkpoint buffers as that forward left them;
+ * d_loss (float32 [1], may be NULL) = L_TV; d_tv_row [batch * L] (may be NULL);
+ * d_grad_a[p] -> float32 [n_layers][r][in_p], d_grad_b[p] -> [n_layers][out_p][r]
+ * (overwritten). */
+uno_status uno_distill_backward(uno_ctx* ctx, int32_t batch, int32_t L, int32_t B,
+                                const float* d_teacher, const float* d_student,
+                                const float* d_x_ckpt, const void* d_k_ckpt,
+                                const void* d_v_ckpt, float* d_loss, float* d_tv_row,
+                                float* const* d_grad_a, float* const* d_grad_b, void* d_scratch,
+                                size_t scratch_bytes);
+
 /* Stage capture (parity instrumentation).  While a trace is armed, every forward
  * of the context (draft, verify, uno_forward, prefill chunks, the distillation
  * forward) copies, on its stream, the intermediates of up to four layers and its
