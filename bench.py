@@ -264,6 +264,71 @@ def run_distill(cfg, w, dev, batch, L, B, reps):
             "rows_per_s": R / sec, "mean_tv_block": tvb, "breakdown": breakdown}
 
 
+def backward_flops(cfg, batch, L, B):
+    """Algorithmic flops of one distillation backward over batch x L z1 rows: the
+    gate-on forward recompute and the backward of every projection (base input
+    gradient, LoRA up / down and both LoRA gradients), attention over the visible
+    (z1 row, key) pairs only -- forward, the score / probability gradients, dq and
+    the z1 keys' dk, dv -- and the LM head's input gradient."""
+    from diffusion_drafted_lora_amd import synth
+    N = batch * L
+    r = cfg.lora_rank
+    shapes = synth.proj_shapes(cfg)
+    base = sum(o * i for o, i in shapes.values())
+    lora_fwd = sum(r * i + (o * r if p != "down" else 0) for p, (o, i) in shapes.items())
+    lora_bwd = sum(2 * r * i + 2 * o * r for o, i in shapes.values())
+    # visible keys of z1 row i: bB x keys and i - bB + 1 own keys
+    vis = sum((i // B) * B + (i - (i // B) * B + 1) for i in range(L)) * batch
+    own = sum(i - (i // B) * B + 1 for i in range(L)) * batch
+    hq, hd = cfg.n_q_heads, cfg.head_dim
+    attn = 2.0 * hq * hd * (2 * vis + 2 * vis + 2 * own)
+    per_layer = 2.0 * N * (2 * base + lora_fwd + lora_bwd) + attn
+    return cfg.n_layers * per_layer + 2.0 * N * cfg.vocab * cfg.d_model
+
+
+def run_distill_backward(cfg, w, dev, batch, L, B, reps):
+    """Backward of the distillation step: a checkpointed [x, z1] forward, then
+    uno_distill_backward (the L_TV gradient with respect to every LoRA matrix)
+    timed with HIP events on the engine's stream.  Returns ms per backward and the
+    algorithmic TFLOP/s against the bf16 matrix peak."""
+    import torch
+    from diffusion_drafted_lora_amd import synth, uno
+
+    rows = max(2 * L, min(batch, 2) * 2 * L)
+    eng = uno.Engine(cfg, w, max_seqs=batch, max_seq_len=2 * L + 16, max_rows=rows,
+                     seed=3005, device=dev)
+    x = torch.from_numpy(synth.prompts(cfg, 2005, batch, L)).to(torch.int32).to(dev)
+    V = cfg.vocab
+    teacher = torch.empty((batch, L, V), dtype=torch.float32, device=dev)
+    student = torch.empty((batch, L, V), dtype=torch.float32, device=dev)
+    ck = eng.set_distill_checkpoint(batch, L)
+    log(f"distill backward: checkpointed forward, batch {batch} x [{L} | {L}], B {B}")
+    eng.distill_forward(x, B, teacher, student)
+    eng.set_distill_checkpoint(None, L)
+    log("distill backward: warmup")
+    loss, tv, ga, gb = eng.distill_backward(B, teacher, student, ck)
+    eng.sync()
+    st = eng.stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        eng.distill_backward(B, teacher, student, ck)
+    e1.record(st)
+    eng.sync()
+    ms = e0.elapsed_time(e1) / reps
+    gnorm = float(sum(ga[p].double().norm() ** 2 + gb[p].double().norm() ** 2 for p in ga) ** 0.5)
+    lval = float(loss.item())
+    fl = backward_flops(cfg, batch, L, B)
+    eng.close()
+    del eng, teacher, student, ck, ga, gb
+    torch.cuda.empty_cache()
+    log(f"distill backward: {ms:.1f} ms, loss {lval:.4f}")
+    return {"batch": batch, "L": L, "B": B, "reps": reps, "ms_per_backward": ms,
+            "tflop_per_backward": fl / 1e12, "tflops": fl / 1e9 / ms,
+            "mfma_frac": fl / 1e9 / ms / BF16_PEAK_TFLOPS, "loss": lval, "grad_norm": gnorm}
+
+
 def run_top_p(V, rows_list, top_p=0.95, reps=20):
     """Nucleus truncation (uno_top_p) on float32 probability rows of the model's
     vocabulary: softmax rows of N(0, 3^2) logits, out of place.  Timed with HIP
@@ -404,6 +469,8 @@ def main():
     ap.add_argument("--distill", type=str, default="8,2048,16", metavar="BATCH,L,B",
                     help="distillation-forward leg (batch, L, block size); 'none' skips it")
     ap.add_argument("--distill-reps", type=int, default=2)
+    ap.add_argument("--distill-backward-reps", type=int, default=1,
+                    help="timed backward passes of the distillation leg (0 skips the backward)")
     ap.add_argument("--distill-b-sweep", type=str, default="4,8,32",
                     help="further block sizes of the distillation leg, one timed forward "
                          "each ('none' skips them)")
@@ -565,6 +632,9 @@ def main():
                 {k: d[k] for k in keys}
                 for d in (run_distill(cfg, w, dev, db, dl, int(b), 1)
                           for b in args.distill_b_sweep.split(","))]
+        if args.distill_backward_reps > 0:
+            result["distill_backward"] = run_distill_backward(cfg, w, dev, db, dl, dbs,
+                                                              args.distill_backward_reps)
     if args.top_p_leg:
         # one launch filters the B draft (or verify) rows of every sequence
         result["top_p"] = run_top_p(cfg.vocab, [B, 128 * B])

@@ -79,14 +79,21 @@ __global__ void __launch_bounds__(256) k_bw_gemm(BwGemm g) {
   const int tiles_n = (g.N + BT - 1) / BT, tiles = tiles_n * ((g.M + BT - 1) / BT);
   const int split = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int m0 = (tile / tiles_n) * BT, n0 = (tile % tiles_n) * BT;
-  const long z = blockIdx.z;
-  const char* Ab = reinterpret_cast<const char*>(g.A) + z * g.a_bs * (AM == BW_A_K16 ? 2 : 4);
-  const char* Bb = reinterpret_cast<const char*>(g.B) + z * g.b_bs * (BMD == BW_B_N32 ? 4 : 2);
-  const long cb = z * g.c_bs;
+  const long zo = blockIdx.z / g.bz, zi = blockIdx.z % g.bz;
+  const char* Ab = reinterpret_cast<const char*>(g.A) +
+                   (zo * g.a_bs + zi * g.a_bs2) * (AM == BW_A_K16 ? 2 : 4);
+  const char* Bb = reinterpret_cast<const char*>(g.B) +
+                   (zo * g.b_bs + zi * g.b_bs2) * (BMD == BW_B_N32 ? 4 : 2);
+  const long cb = zo * g.c_bs + zi * g.c_bs2;
   // this split's k range, whole steps
   const int nsteps = (g.K + BK - 1) / BK;
   const int per = (nsteps + g.splits - 1) / g.splits;
-  const int s0 = split * per, s1 = min(nsteps, s0 + per);
+  int s0 = split * per, s1 = min(nsteps, s0 + per);
+  if (g.lim_mode) {   // block-causal key limit of this tile's rows
+    const int lim = (((min(m0 + BT, g.M) - 1) / g.lim_G) / g.lim_B) * g.lim_B;
+    if (g.lim_mode == 1 && n0 >= lim) return;
+    if (g.lim_mode == 2) s1 = min(s1, (lim + BK - 1) / BK);
+  }
 
   // staged operands of one step: two 8-element chunks of A and of B per thread
   float ra[2][8], rb[2][8];
@@ -319,14 +326,14 @@ UNO_DEV int pair_pos(int c, int hd) {
   return c < half ? 16 * (c >> 3) + (c & 7) : 16 * ((c - half) >> 3) + 8 + ((c - half) & 7);
 }
 
-// q / k after RoPE and v, stored bf16 in head order: Q [N][Hq*hd]; the z1 rows'
-// K / V at key L + i of their sequence in Ka / Va [S][Hkv][2L][hd].  Y* are the
-// projections in the stored pair order; row n = s * L + i sits at position i.
+// q / k after RoPE and v, stored bf16 in head order: Q [N][Hq*hd], Ks / Vs
+// [N][Hkv*hd].  Y* are the projections in the stored pair order; row n = s * L + i
+// sits at position i.
 __global__ void k_bw_qkv_post(const float* Yq, const float* Yk, const float* Yv, const float* rcos,
                               const float* rsin, int L, int Hq, int Hkv, int hd, bf16* Q,
-                              bf16* Ka, bf16* Va) {
+                              bf16* Ks, bf16* Vs) {
   const long n = blockIdx.x;
-  const int i = (int)(n % L), s = (int)(n / L), half = hd / 2;
+  const int i = (int)(n % L), half = hd / 2;
   const int qd = Hq * hd, kvd = Hkv * hd;
   for (int e = threadIdx.x; e < (Hq + Hkv) * half; e += blockDim.x) {
     const int h = e / half, c = e % half;
@@ -340,11 +347,11 @@ __global__ void k_bw_qkv_post(const float* Yq, const float* Yk, const float* Yv,
       const int hk = h - Hq;
       const float* y = Yk + n * kvd + hk * hd;
       const float y1 = y[pair_pos(c, hd)], y2 = y[pair_pos(c + half, hd)];
-      bf16* kr = Ka + (((size_t)s * Hkv + hk) * 2 * L + L + i) * hd;
+      bf16* kr = Ks + n * kvd + hk * hd;
       kr[c] = (bf16)(y1 * cs - y2 * sn);
       kr[c + half] = (bf16)(y2 * cs + y1 * sn);
       const float* yv = Yv + n * kvd + hk * hd;
-      bf16* vr = Va + (((size_t)s * Hkv + hk) * 2 * L + L + i) * hd;
+      bf16* vr = Vs + n * kvd + hk * hd;
       vr[c] = (bf16)yv[pair_pos(c, hd)];
       vr[c + half] = (bf16)yv[pair_pos(c + half, hd)];
     }
@@ -381,52 +388,144 @@ __global__ void k_bw_qkv_back(const float* dq, const float* dk, const float* dv,
   }
 }
 
-// The x rows' K / V of one layer ([S] sequences of [L][Hkv][hd], sequence stride
-// seq_stride elements) into keys 0..L-1 of Ka / Va [S][Hkv][2L][hd].
-__global__ void k_bw_ctx_copy(const bf16* k, const bf16* v, long seq_stride, int L, int Hkv,
-                              int hd, bf16* Ka, bf16* Va) {
-  const int j = blockIdx.x, s = blockIdx.y;
-  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
-    const int h = e / hd, c = e % hd;
-    const size_t src = (size_t)s * seq_stride + ((size_t)j * Hkv + h) * hd + c;
-    const size_t dst = (((size_t)s * Hkv + h) * 2 * L + j) * hd + c;
-    Ka[dst] = k[src];
-    Va[dst] = v[src];
+// Keys of the x rows that the GEMMs of one BT-row tile of rows m = i * G + g read
+// (the tile's limit, rounded up to a k step): entries below it are written.
+UNO_DEV int tile_keys(long m, int M, int G, int B, int L) {
+  const long t0 = (m / BT) * BT;
+  const int lim = (int)((((min(t0 + BT, (long)M) - 1) / G) / B) * B);
+  return min(L, (lim + BK - 1) / BK * BK);
+}
+
+// Own-block scores of the z1 rows of block b (blockIdx.x) and KV head h
+// (blockIdx.y): So[h][i * G + g][j] = q_(i, g) . k_(bB + j) for j <= i - bB.
+__global__ void k_bw_own_scores(const bf16* Q, const bf16* Ks, int L, int Hq, int Hkv, int hd, int B,
+                                float* So) {
+  extern __shared__ float sk[];          // [B][hd] own keys
+  const int b = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, qd = Hq * hd, kvd = Hkv * hd;
+  for (int e = threadIdx.x; e < B * hd; e += blockDim.x)
+    sk[e] = (float)Ks[(size_t)(b * B + e / hd) * kvd + h * hd + e % hd];
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * G * B; e += blockDim.x) {
+    const int r = e / B, j = e % B, i = b * B + r / G, g = r % G;
+    float acc = 0.f;
+    if (j <= i - b * B) {
+      const bf16* q = Q + (size_t)i * qd + (h * G + g) * hd;
+      for (int d = 0; d < hd; ++d) acc += (float)q[d] * sk[j * hd + d];
+    }
+    So[((size_t)h * L * G + (size_t)i * G + g) * B + j] = acc;
   }
 }
 
-// Block-causal softmax of one sequence's scores, in place: row m = i * G + g of KV
-// head h (blockIdx.y) over keys [x 0..L-1 | z1 0..L-1]; z1 row i (block b = i / B)
-// sees x keys < bB and z1 keys bB..i.  P = softmax(scale * S) on the visible keys.
-__global__ void k_bw_softmax(float* S, int L, int G, int B, float scale) {
+// Block-causal softmax of one sequence, in place: row m = i * G + g of KV head h
+// (blockIdx.y) over the x keys < bB (St) and its own block's keys bB..i (So), with
+// P = softmax(scale * S).  Invisible entries the GEMMs read become 0.
+__global__ void k_bw_softmax(float* St, float* So, int L, int G, int B, float scale) {
   __shared__ float red[16];
   const long m = blockIdx.x, h = blockIdx.y;
-  const int i = (int)(m / G), b0 = (i / B) * B;
-  float* row = S + (h * (long)L * G + m) * 2 * L;
-  auto vis = [&](int j) { return j < L ? j < b0 : (j - L >= b0 && j - L <= i); };
+  const int M = L * G, i = (int)(m / G), b0 = (i / B) * B, no = i - b0 + 1;
+  const int lw = tile_keys(m, M, G, B, L);
+  float* t = St + (h * (long)M + m) * L;
+  float* o = So + (h * (long)M + m) * B;
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < 2 * L; j += blockDim.x)
-    if (vis(j)) mx = fmaxf(mx, scale * row[j]);
+  for (int j = threadIdx.x; j < b0; j += blockDim.x) mx = fmaxf(mx, scale * t[j]);
+  for (int j = threadIdx.x; j < no; j += blockDim.x) mx = fmaxf(mx, scale * o[j]);
   mx = block_max(mx, red);
   float sum = 0.f;
-  for (int j = threadIdx.x; j < 2 * L; j += blockDim.x)
-    if (vis(j)) sum += expf(scale * row[j] - mx);
+  for (int j = threadIdx.x; j < b0; j += blockDim.x) sum += expf(scale * t[j] - mx);
+  for (int j = threadIdx.x; j < no; j += blockDim.x) sum += expf(scale * o[j] - mx);
   sum = block_sum(sum, red);
   const float inv = 1.0f / sum;
-  for (int j = threadIdx.x; j < 2 * L; j += blockDim.x)
-    row[j] = vis(j) ? expf(scale * row[j] - mx) * inv : 0.f;
+  for (int j = threadIdx.x; j < lw; j += blockDim.x) t[j] = j < b0 ? expf(scale * t[j] - mx) * inv : 0.f;
+  for (int j = threadIdx.x; j < B; j += blockDim.x) o[j] = j < no ? expf(scale * o[j] - mx) * inv : 0.f;
 }
 
-// Softmax backward in place: dS = scale * P * (dP - sum_j P_j dP_j) (the scale of
-// the scores folded in, so that dq = dS K and dk = dS^T q).
-__global__ void k_bw_softmax_back(const float* P, float* dP, int L, int G, float scale) {
+// o = bf16(o32 + sum_j Po[., j] v_(bB + j)): the own block's share added to the x
+// keys' share o32 [L][Hq*hd] of the z1 rows of block b (blockIdx.x), KV head h.
+__global__ void k_bw_own_pv(const float* Po, const bf16* Vs, const float* o32, int L, int Hq, int Hkv,
+                            int hd, int B, bf16* o) {
+  extern __shared__ float sv[];          // [B][hd]
+  const int b = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, qd = Hq * hd, kvd = Hkv * hd;
+  for (int e = threadIdx.x; e < B * hd; e += blockDim.x)
+    sv[e] = (float)Vs[(size_t)(b * B + e / hd) * kvd + h * hd + e % hd];
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * G * hd; e += blockDim.x) {
+    const int r = e / hd, d = e % hd, i = b * B + r / G, g = r % G;
+    const float* p = Po + ((size_t)h * L * G + (size_t)i * G + g) * B;
+    const size_t oi = (size_t)i * qd + (h * G + g) * hd + d;
+    float acc = o32[oi];
+    for (int j = 0; j <= i - b * B; ++j) acc += p[j] * sv[j * hd + d];
+    o[oi] = (bf16)acc;
+  }
+}
+
+// dPo[., j] = dO . v_(bB + j) for the own block (j <= i - bB).
+__global__ void k_bw_own_dp(const float* dO, const bf16* Vs, int L, int Hq, int Hkv, int hd, int B,
+                            float* dPo) {
+  extern __shared__ float sv[];
+  const int b = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, qd = Hq * hd, kvd = Hkv * hd;
+  for (int e = threadIdx.x; e < B * hd; e += blockDim.x)
+    sv[e] = (float)Vs[(size_t)(b * B + e / hd) * kvd + h * hd + e % hd];
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * G * B; e += blockDim.x) {
+    const int r = e / B, j = e % B, i = b * B + r / G, g = r % G;
+    float acc = 0.f;
+    if (j <= i - b * B) {
+      const float* go = dO + (size_t)i * qd + (h * G + g) * hd;
+      for (int d = 0; d < hd; ++d) acc += go[d] * sv[j * hd + d];
+    }
+    dPo[((size_t)h * L * G + (size_t)i * G + g) * B + j] = acc;
+  }
+}
+
+// Softmax backward in place over the same entries: dS = scale * P * (dP - D),
+// D = sum over the visible keys of P dP (the scale of the scores folded in).
+__global__ void k_bw_softmax_back(const float* Pt, const float* Po, float* dPt, float* dPo, int L,
+                                  int G, int B, float scale) {
   __shared__ float red[16];
   const long m = blockIdx.x, h = blockIdx.y;
-  const long o = (h * (long)L * G + m) * 2 * L;
+  const int M = L * G, i = (int)(m / G), b0 = (i / B) * B, no = i - b0 + 1;
+  const int lw = tile_keys(m, M, G, B, L);
+  const long ot = (h * (long)M + m) * L, oo = (h * (long)M + m) * B;
   float s = 0.f;
-  for (int j = threadIdx.x; j < 2 * L; j += blockDim.x) s += P[o + j] * dP[o + j];
+  for (int j = threadIdx.x; j < b0; j += blockDim.x) s += Pt[ot + j] * dPt[ot + j];
+  for (int j = threadIdx.x; j < no; j += blockDim.x) s += Po[oo + j] * dPo[oo + j];
   s = block_sum(s, red);
-  for (int j = threadIdx.x; j < 2 * L; j += blockDim.x) dP[o + j] = scale * P[o + j] * (dP[o + j] - s);
+  for (int j = threadIdx.x; j < lw; j += blockDim.x)
+    dPt[ot + j] = j < b0 ? scale * Pt[ot + j] * (dPt[ot + j] - s) : 0.f;
+  for (int j = threadIdx.x; j < B; j += blockDim.x)
+    dPo[oo + j] = j < no ? scale * Po[oo + j] * (dPo[oo + j] - s) : 0.f;
+}
+
+// Own-block backward of block b (blockIdx.x), KV head h: dq += dSo K_own, and the
+// z1 keys' dk = dSo^T q, dv = Po^T dO (every (key, head) owned by one workgroup).
+__global__ void k_bw_own_back(const float* dSo, const float* Po, const bf16* Q, const bf16* Ks,
+                              const float* dO, int L, int Hq, int Hkv, int hd, int B, float* dq,
+                              float* dk, float* dv) {
+  extern __shared__ float sk[];
+  const int b = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, qd = Hq * hd, kvd = Hkv * hd;
+  const size_t rb = (size_t)h * L * G + (size_t)b * B * G;     // first row of the block
+  for (int e = threadIdx.x; e < B * hd; e += blockDim.x)
+    sk[e] = (float)Ks[(size_t)(b * B + e / hd) * kvd + h * hd + e % hd];
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * G * hd; e += blockDim.x) {
+    const int r = e / hd, d = e % hd, i = b * B + r / G, g = r % G;
+    const float* ds = dSo + (rb + r) * B;
+    float acc = 0.f;
+    for (int j = 0; j <= i - b * B; ++j) acc += ds[j] * sk[j * hd + d];
+    dq[(size_t)i * qd + (h * G + g) * hd + d] += acc;
+  }
+  for (int e = threadIdx.x; e < B * hd; e += blockDim.x) {
+    const int j = e / hd, d = e % hd;
+    float ak = 0.f, av = 0.f;
+    for (int r = j * G; r < B * G; ++r) {      // rows i >= bB + j see key bB + j
+      const int i = b * B + r / G, g = r % G;
+      const size_t qi = (size_t)i * qd + (h * G + g) * hd + d;
+      ak += dSo[(rb + r) * B + j] * (float)Q[qi];
+      av += Po[(rb + r) * B + j] * dO[qi];
+    }
+    dk[(size_t)(b * B + j) * kvd + h * hd + d] = ak;
+    dv[(size_t)(b * B + j) * kvd + h * hd + d] = av;
+  }
 }
 
 // SwiGLU product a = bf16(silu(g) * u).
@@ -510,7 +609,9 @@ hipError_t run_bw(const BwGemm& g, hipStream_t s) {
 
 hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
-  if (g.splits < 1 || g.batch < 1 || (g.splits > 1 && (g.batch != 1 || !g.part)))
+  if (g.splits < 1 || g.batch < 1 || g.bz < 1 || (g.splits > 1 && (g.batch != 1 || !g.part)))
+    return hipErrorInvalidValue;
+  if (g.lim_mode && (g.lim_G < 1 || g.lim_B < 1 || (g.lim_mode == 2 && g.splits != 1)))
     return hipErrorInvalidValue;
   // 16-byte operand chunks: the contiguous axis of every operand in whole 8s
   if (g.K % 8 || g.M % 8 || g.N % 8) return hipErrorInvalidValue;
@@ -525,7 +626,6 @@ hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t s) {
   BW_CASE(BW_A_K32, BW_B_K16)
   BW_CASE(BW_A_K32, BW_B_TT)
   BW_CASE(BW_A_M32, BW_B_N16)
-  BW_CASE(BW_A_M32, BW_B_N32)
 #undef BW_CASE
   return hipErrorInvalidValue;
 }
@@ -549,9 +649,9 @@ hipError_t launch_bw_rmsback(const float* x, const bf16* hg, const float* rs, co
 
 hipError_t launch_bw_qkv_post(const float* Yq, const float* Yk, const float* Yv, const float* rcos,
                               const float* rsin, int rows, int L, int Hq, int Hkv, int hd, bf16* Q,
-                              bf16* Ka, bf16* Va, hipStream_t s) {
+                              bf16* Ks, bf16* Vs, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  uno_launch(k_bw_qkv_post, dim3(rows), dim3(256), 0, s, Yq, Yk, Yv, rcos, rsin, L, Hq, Hkv, hd, Q, Ka, Va);
+  uno_launch(k_bw_qkv_post, dim3(rows), dim3(256), 0, s, Yq, Yk, Yv, rcos, rsin, L, Hq, Hkv, hd, Q, Ks, Vs);
   return hipGetLastError();
 }
 
@@ -563,21 +663,41 @@ hipError_t launch_bw_qkv_back(const float* dq, const float* dk, const float* dv,
   return hipGetLastError();
 }
 
-hipError_t launch_bw_ctx_copy(const bf16* k, const bf16* v, long seq_stride, int S, int L, int Hkv,
-                              int hd, bf16* Ka, bf16* Va, hipStream_t s) {
-  if (S <= 0 || L <= 0) return hipSuccess;
-  uno_launch(k_bw_ctx_copy, dim3(L, S), dim3(256), 0, s, k, v, seq_stride, L, Hkv, hd, Ka, Va);
+hipError_t launch_bw_own_scores(const bf16* Q, const bf16* Ks, int L, int Hq, int Hkv, int hd, int B,
+                                float* So, hipStream_t s) {
+  uno_launch(k_bw_own_scores, dim3(L / B, Hkv), dim3(256), (uint32_t)(B * hd * 4), s, Q, Ks, L, Hq, Hkv, hd, B, So);
   return hipGetLastError();
 }
 
-hipError_t launch_bw_softmax(float* S, int L, int G, int Hkv, int B, float scale, hipStream_t s) {
-  uno_launch(k_bw_softmax, dim3(L * G, Hkv), dim3(256), 0, s, S, L, G, B, scale);
+hipError_t launch_bw_softmax(float* St, float* So, int L, int G, int Hkv, int B, float scale,
+                             hipStream_t s) {
+  uno_launch(k_bw_softmax, dim3(L * G, Hkv), dim3(256), 0, s, St, So, L, G, B, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bw_softmax_back(const float* P, float* dP, int L, int G, int Hkv, float scale,
-                                  hipStream_t s) {
-  uno_launch(k_bw_softmax_back, dim3(L * G, Hkv), dim3(256), 0, s, P, dP, L, G, scale);
+hipError_t launch_bw_own_pv(const float* Po, const bf16* Vs, const float* o32, int L, int Hq, int Hkv,
+                            int hd, int B, bf16* o, hipStream_t s) {
+  uno_launch(k_bw_own_pv, dim3(L / B, Hkv), dim3(256), (uint32_t)(B * hd * 4), s, Po, Vs, o32, L, Hq, Hkv, hd, B, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_own_dp(const float* dO, const bf16* Vs, int L, int Hq, int Hkv, int hd, int B,
+                            float* dPo, hipStream_t s) {
+  uno_launch(k_bw_own_dp, dim3(L / B, Hkv), dim3(256), (uint32_t)(B * hd * 4), s, dO, Vs, L, Hq, Hkv, hd, B, dPo);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_softmax_back(const float* Pt, const float* Po, float* dPt, float* dPo, int L,
+                                  int G, int Hkv, int B, float scale, hipStream_t s) {
+  uno_launch(k_bw_softmax_back, dim3(L * G, Hkv), dim3(256), 0, s, Pt, Po, dPt, dPo, L, G, B, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_own_back(const float* dSo, const float* Po, const bf16* Q, const bf16* Ks,
+                              const float* dO, int L, int Hq, int Hkv, int hd, int B, float* dq,
+                              float* dk, float* dv, hipStream_t s) {
+  uno_launch(k_bw_own_back, dim3(L / B, Hkv), dim3(256), (uint32_t)(B * hd * 4), s, dSo, Po, Q, Ks, dO, L,
+             Hq, Hkv, hd, B, dq, dk, dv);
   return hipGetLastError();
 }
 

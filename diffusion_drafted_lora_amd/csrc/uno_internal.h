@@ -478,6 +478,14 @@ struct BwGemm {
   int perm_hd;               // > 0: output rows are in the RoPE pair order of heads of
                              // perm_hd rows and are written to their head-order rows
   float* part;               // splits > 1: float32 [splits, M, N] partials
+  // two-level batch: z -> (z / bz, z % bz) with strides (a_bs, a_bs2) etc.
+  int bz;
+  long a_bs2, b_bs2, c_bs2;
+  // block-causal key limit over rows m = i * G + g: the rows of an output tile see
+  // keys below lim = (i_last / lim_B) * lim_B, i_last the tile's last row position.
+  // lim_mode 1: the N axis is keys, tiles at or past lim are skipped (not written);
+  // lim_mode 2: the K axis is keys, the k loop stops at lim (rounded up to a step)
+  int lim_mode, lim_G, lim_B;
 };
 hipError_t launch_bw_gemm(const BwGemm& g, hipStream_t s);
 template <typename T>
@@ -489,15 +497,27 @@ hipError_t launch_bw_rmsback(const float* x, const bf16* hg, const float* rs, co
                              hipStream_t s);
 hipError_t launch_bw_qkv_post(const float* Yq, const float* Yk, const float* Yv, const float* rcos,
                               const float* rsin, int rows, int L, int Hq, int Hkv, int hd, bf16* Q,
-                              bf16* Ka, bf16* Va, hipStream_t s);
+                              bf16* Ks, bf16* Vs, hipStream_t s);
 hipError_t launch_bw_qkv_back(const float* dq, const float* dk, const float* dv, const float* rcos,
                               const float* rsin, int rows, int L, int Hq, int Hkv, int hd, float* dYq,
                               float* dYk, float* dYv, hipStream_t s);
-hipError_t launch_bw_ctx_copy(const bf16* k, const bf16* v, long seq_stride, int S, int L, int Hkv,
-                              int hd, bf16* Ka, bf16* Va, hipStream_t s);
-hipError_t launch_bw_softmax(float* S, int L, int G, int Hkv, int B, float scale, hipStream_t s);
-hipError_t launch_bw_softmax_back(const float* P, float* dP, int L, int G, int Hkv, float scale,
-                                  hipStream_t s);
+// Attention of one sequence's z1 rows (rows m = i * G + g of each KV head h):
+// St [Hkv][L*G][L] scores / probabilities over the x keys, So [Hkv][L*G][B] over
+// the row's own block (key bB + j at column j); Q [L][Hq*hd] bf16, own K / V
+// [L][Hkv*hd] bf16 (this sequence's rows).
+hipError_t launch_bw_own_scores(const bf16* Q, const bf16* Ks, int L, int Hq, int Hkv, int hd, int B,
+                                float* So, hipStream_t s);
+hipError_t launch_bw_softmax(float* St, float* So, int L, int G, int Hkv, int B, float scale,
+                             hipStream_t s);
+hipError_t launch_bw_own_pv(const float* Po, const bf16* Vs, const float* o32, int L, int Hq, int Hkv,
+                            int hd, int B, bf16* o, hipStream_t s);
+hipError_t launch_bw_own_dp(const float* dO, const bf16* Vs, int L, int Hq, int Hkv, int hd, int B,
+                            float* dPo, hipStream_t s);
+hipError_t launch_bw_softmax_back(const float* Pt, const float* Po, float* dPt, float* dPo, int L,
+                                  int G, int Hkv, int B, float scale, hipStream_t s);
+hipError_t launch_bw_own_back(const float* dSo, const float* Po, const bf16* Q, const bf16* Ks,
+                              const float* dO, int L, int Hq, int Hkv, int hd, int B, float* dq,
+                              float* dk, float* dv, hipStream_t s);
 hipError_t launch_bw_swiglu(const float* Yg, const float* Yu, bf16* a, long n, hipStream_t s);
 hipError_t launch_bw_swiglu_back(const float* da, float* Yg, float* Yu, long n, hipStream_t s);
 hipError_t launch_tv_grad(const float* T, const float* S, int rows, int V, float inv2n, float* dz,

@@ -909,7 +909,8 @@ void proj_shape(const uno_config& g, int p, int* out, int* in) {
 
 // Scratch of the backward over S sequences of L z1 rows (N = S * L), bytes from 0.
 struct BwLayout {
-  size_t hg1, rs1, hg2, rs2, x2, t[7], Yq, Yk, Yv, Q, Ka, Va, P, dP, o, Yg, Yu, a, da, dt;
+  size_t hg1, rs1, hg2, rs2, x2, t[7], Yq, Yk, Yv, Q, Ks, Vs, Pt, Po, dPt, dPo, o32, o;
+  size_t Yg, Yu, a, da, dt;
   size_t dx2, dh, dq, dk, dv, part, dy, tv, dz, lm_hg, lm_rs, lm_dh;
   size_t part_floats;
   int lm_rows;            // rows of one LM-head backward chunk
@@ -917,6 +918,7 @@ struct BwLayout {
 };
 
 constexpr int kBwMaxSplits = 16;
+constexpr int kBwMaxB = 64;          // block sizes the own-block buffers hold
 
 BwLayout bw_layout(const uno_config& g, size_t S, size_t L) {
   BwLayout W{};
@@ -931,9 +933,12 @@ BwLayout bw_layout(const uno_config& g, size_t S, size_t L) {
   for (int p = 0; p < 7; ++p) W.t[p] = take(N * r * 2);
   W.Yq = take(N * qd * 4); W.Yk = take(N * kvd * 4); W.Yv = take(N * kvd * 4);
   W.Q = take(N * qd * 2);
-  W.Ka = take(S * 2 * L * kvd * 2); W.Va = take(S * 2 * L * kvd * 2);
-  W.P = take(N * g.n_q_heads * 2 * L * 4);          // [S][Hkv][L * G][2L]
-  W.dP = take(L * g.n_q_heads * 2 * L * 4);         // one sequence
+  W.Ks = take(N * kvd * 2); W.Vs = take(N * kvd * 2);
+  W.Pt = take(N * g.n_q_heads * L * 4);             // [S][Hkv][L * G][L]: x keys
+  W.Po = take(N * g.n_q_heads * kBwMaxB * 4);       // [S][Hkv][L * G][B]: own block
+  W.dPt = take(L * g.n_q_heads * L * 4);            // one sequence
+  W.dPo = take(L * g.n_q_heads * kBwMaxB * 4);
+  W.o32 = take(L * qd * 4);                         // one sequence
   W.o = take(N * qd * 2);
   W.Yg = take(N * F * 4); W.Yu = take(N * F * 4); W.a = take(N * F * 2);
   W.da = take(N * F * 4); W.dt = take(N * r * 4);
@@ -969,7 +974,7 @@ uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes
   if (!c->has_lora) return fail(c, UNO_ERR_INVALID_ARG, "the context has no LoRA");
   const int G = g.n_q_heads / g.n_kv_heads;
   if (G & (G - 1)) return fail(c, UNO_ERR_UNSUPPORTED, "backward: query group must be a power of 2");
-  if (S < 1 || L < 16 || L % 16 || B < 1 || L % B)
+  if (S < 1 || L < 16 || L % 16 || B < 1 || B > kBwMaxB || L % B)
     return fail(c, UNO_ERR_INVALID_ARG, "backward: batch >= 1, L a multiple of 16 and of B");
   if (L > c->maxpp * g.page_size) return fail(c, UNO_ERR_INVALID_ARG, "backward: L beyond the RoPE table");
   if (!scratch || bytes < bw_layout(g, S, L).total)
@@ -982,7 +987,7 @@ BwGemm bw_mk(int am, int bm, const void* A, Idx2 ai, const void* B, Idx2 bi, int
   BwGemm x{};
   x.amode = am; x.bmode = bm;
   x.A = A; x.ai = ai; x.B = B; x.bi = bi; x.b_cols = b_cols; x.C = C; x.ci = ci;
-  x.M = M; x.N = N; x.K = K; x.batch = 1; x.splits = 1; x.alpha = 1.0f;
+  x.M = M; x.N = N; x.K = K; x.batch = 1; x.splits = 1; x.alpha = 1.0f; x.bz = 1;
   return x;
 }
 
@@ -1058,22 +1063,33 @@ uno_status layer_backward(uno_ctx* c, int l, int S, int L, int B, const float* x
   BW_DO(proj_fwd(1, BF(W.hg1), F32(W.rs1), F32(W.Yk), false));
   BW_DO(proj_fwd(2, BF(W.hg1), F32(W.rs1), F32(W.Yv), false));
   UNO_HIP(c, launch_bw_qkv_post(F32(W.Yq), F32(W.Yk), F32(W.Yv), rcos, rsin, N, L, Hq, Hkv, hd,
-                                BF(W.Q), BF(W.Ka), BF(W.Va), st));
-  UNO_HIP(c, launch_bw_ctx_copy(kc, vc, kv_seq_stride, S, L, Hkv, hd, BF(W.Ka), BF(W.Va), st));
-  const Idx2 qrow{sh, (long)qd, (long)hd};          // row i * G + g of KV head h
-  const long kv_seq = (long)Hkv * 2 * L * hd, p_seq = (long)Hkv * LG * 2 * L;
+                                BF(W.Q), BF(W.Ks), BF(W.Vs), st));
+  // attention per sequence and KV head: rows m = i * G + g against the x keys (GEMMs
+  // that skip the keys no row of a tile sees) and the own block (small kernels)
+  const Idx2 qrow{sh, (long)qd, (long)hd};
+  const long pt_seq = (long)Hkv * LG * L, po_seq = (long)Hkv * LG * B;
+  auto attn_gemm = [&](BwGemm x, int mode) {
+    x.batch = Hkv; x.lim_mode = mode; x.lim_G = G; x.lim_B = B;
+    return x;
+  };
   for (int s = 0; s < S; ++s) {
-    float* P = F32(W.P) + s * p_seq;
-    BwGemm sg = bw_mk(BW_A_K16, BW_B_K16, BF(W.Q) + (size_t)s * L * qd, qrow, BF(W.Ka) + s * kv_seq,
-                      idx_ld(hd), 0, P, idx_ld(2 * L), LG, 2 * L, hd);
-    sg.batch = Hkv; sg.a_bs = (long)G * hd; sg.b_bs = 2L * L * hd; sg.c_bs = (long)LG * 2 * L;
+    const bf16* Qs = BF(W.Q) + (size_t)s * L * qd;
+    const bf16* Kt = kc + s * kv_seq_stride;
+    const bf16* Vt = vc + s * kv_seq_stride;
+    float* Pt = F32(W.Pt) + s * pt_seq;
+    float* Po = F32(W.Po) + s * po_seq;
+    BwGemm sg = attn_gemm(bw_mk(BW_A_K16, BW_B_K16, Qs, qrow, Kt, idx_ld(kvd), 0, Pt, idx_ld(L),
+                                LG, L, hd), 1);
+    sg.a_bs = (long)G * hd; sg.b_bs = hd; sg.c_bs = (long)LG * L;
     BW_DO(gemm(sg));
-    UNO_HIP(c, launch_bw_softmax(P, L, G, Hkv, B, ascale, st));
-    BwGemm og = bw_mk(BW_A_K32, BW_B_N16, P, idx_ld(2 * L), BF(W.Va) + s * kv_seq, idx_ld(hd), 0,
-                      BF(W.o) + (size_t)s * L * qd, qrow, LG, hd, 2 * L);
-    og.batch = Hkv; og.a_bs = (long)LG * 2 * L; og.b_bs = 2L * L * hd; og.c_bs = (long)G * hd;
-    og.out_bf16 = 1;
+    UNO_HIP(c, launch_bw_own_scores(Qs, BF(W.Ks) + (size_t)s * L * kvd, L, Hq, Hkv, hd, B, Po, st));
+    UNO_HIP(c, launch_bw_softmax(Pt, Po, L, G, Hkv, B, ascale, st));
+    BwGemm og = attn_gemm(bw_mk(BW_A_K32, BW_B_N16, Pt, idx_ld(L), Vt, idx_ld(kvd), 0, F32(W.o32),
+                                qrow, LG, hd, L), 2);
+    og.a_bs = (long)LG * L; og.b_bs = hd; og.c_bs = (long)G * hd;
     BW_DO(gemm(og));
+    UNO_HIP(c, launch_bw_own_pv(Po, BF(W.Vs) + (size_t)s * L * kvd, F32(W.o32), L, Hq, Hkv, hd, B,
+                                BF(W.o) + (size_t)s * L * qd, st));
   }
   UNO_HIP(c, hipMemcpyAsync(F32(W.x2), xin, sizeof(float) * N * d, hipMemcpyDeviceToDevice, st));
   BW_DO(proj_fwd(3, BF(W.o), nullptr, F32(W.x2), true));
@@ -1096,27 +1112,27 @@ uno_status layer_backward(uno_ctx* c, int l, int S, int L, int B, const float* x
                                      F32(W.dx2), N, d, st));
   BW_DO(proj_back(3, F32(W.dx2), BF(W.o), nullptr, F32(W.dh), false, 0));   // dh = dO
   for (int s = 0; s < S; ++s) {
-    const float* P = F32(W.P) + s * p_seq;
-    float* dP = F32(W.dP);
+    const bf16* Qs = BF(W.Q) + (size_t)s * L * qd;
+    const bf16* Kt = kc + s * kv_seq_stride;
+    const bf16* Vt = vc + s * kv_seq_stride;
+    const float* Pt = F32(W.Pt) + s * pt_seq;
+    const float* Po = F32(W.Po) + s * po_seq;
+    float* dPt = F32(W.dPt);
+    float* dPo = F32(W.dPo);
     const float* dO = F32(W.dh) + (size_t)s * L * qd;
-    BwGemm pg = bw_mk(BW_A_K32, BW_B_K16, dO, qrow, BF(W.Va) + s * kv_seq, idx_ld(hd), 0, dP,
-                      idx_ld(2 * L), LG, 2 * L, hd);
-    pg.batch = Hkv; pg.a_bs = (long)G * hd; pg.b_bs = 2L * L * hd; pg.c_bs = (long)LG * 2 * L;
+    BwGemm pg = attn_gemm(bw_mk(BW_A_K32, BW_B_K16, dO, qrow, Vt, idx_ld(kvd), 0, dPt, idx_ld(L),
+                                LG, L, hd), 1);
+    pg.a_bs = (long)G * hd; pg.b_bs = hd; pg.c_bs = (long)LG * L;
     BW_DO(gemm(pg));
-    UNO_HIP(c, launch_bw_softmax_back(P, dP, L, G, Hkv, ascale, st));
-    BwGemm qg = bw_mk(BW_A_K32, BW_B_N16, dP, idx_ld(2 * L), BF(W.Ka) + s * kv_seq, idx_ld(hd), 0,
-                      F32(W.dq) + (size_t)s * L * qd, qrow, LG, hd, 2 * L);
-    qg.batch = Hkv; qg.a_bs = (long)LG * 2 * L; qg.b_bs = 2L * L * hd; qg.c_bs = (long)G * hd;
+    UNO_HIP(c, launch_bw_own_dp(dO, BF(W.Vs) + (size_t)s * L * kvd, L, Hq, Hkv, hd, B, dPo, st));
+    UNO_HIP(c, launch_bw_softmax_back(Pt, Po, dPt, dPo, L, G, Hkv, B, ascale, st));
+    BwGemm qg = attn_gemm(bw_mk(BW_A_K32, BW_B_N16, dPt, idx_ld(L), Kt, idx_ld(kvd), 0,
+                                F32(W.dq) + (size_t)s * L * qd, qrow, LG, hd, L), 2);
+    qg.a_bs = (long)LG * L; qg.b_bs = hd; qg.c_bs = (long)G * hd;
     BW_DO(gemm(qg));
-    // the z1 keys (columns L..2L-1): dk = dS^T q, dv = P^T dO
-    BwGemm kg = bw_mk(BW_A_M32, BW_B_N16, dP + L, idx_ld(2 * L), BF(W.Q) + (size_t)s * L * qd, qrow,
-                      0, F32(W.dk) + (size_t)s * L * kvd, idx_ld(kvd), L, hd, LG);
-    kg.batch = Hkv; kg.a_bs = (long)LG * 2 * L; kg.b_bs = (long)G * hd; kg.c_bs = hd;
-    BW_DO(gemm(kg));
-    BwGemm vg = bw_mk(BW_A_M32, BW_B_N32, P + L, idx_ld(2 * L), dO, qrow, 0,
-                      F32(W.dv) + (size_t)s * L * kvd, idx_ld(kvd), L, hd, LG);
-    vg.batch = Hkv; vg.a_bs = (long)LG * 2 * L; vg.b_bs = (long)G * hd; vg.c_bs = hd;
-    BW_DO(gemm(vg));
+    UNO_HIP(c, launch_bw_own_back(dPo, Po, Qs, BF(W.Ks) + (size_t)s * L * kvd, dO, L, Hq, Hkv, hd, B,
+                                  F32(W.dq) + (size_t)s * L * qd, F32(W.dk) + (size_t)s * L * kvd,
+                                  F32(W.dv) + (size_t)s * L * kvd, st));
   }
   UNO_HIP(c, launch_bw_qkv_back(F32(W.dq), F32(W.dk), F32(W.dv), rcos, rsin, N, L, Hq, Hkv, hd,
                                 F32(W.Yq), F32(W.Yk), F32(W.Yv), st));
