@@ -968,7 +968,7 @@ int bw_splits(int M, int N, int K, size_t part_floats) {
   return s;
 }
 
-uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes) {
+uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes, bool rope = true) {
   const uno_config& g = c->cfg;
   if (!c->bf16) return fail(c, UNO_ERR_UNSUPPORTED, "the backward runs in bf16 contexts");
   if (!c->has_lora) return fail(c, UNO_ERR_INVALID_ARG, "the context has no LoRA");
@@ -976,7 +976,8 @@ uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes
   if (G & (G - 1)) return fail(c, UNO_ERR_UNSUPPORTED, "backward: query group must be a power of 2");
   if (S < 1 || L < 16 || L % 16 || B < 1 || B > kBwMaxB || L % B)
     return fail(c, UNO_ERR_INVALID_ARG, "backward: batch >= 1, L a multiple of 16 and of B");
-  if (L > c->maxpp * g.page_size) return fail(c, UNO_ERR_INVALID_ARG, "backward: L beyond the RoPE table");
+  if (rope && L > c->maxpp * g.page_size)
+    return fail(c, UNO_ERR_INVALID_ARG, "backward: L beyond the RoPE table");
   if (!scratch || bytes < bw_layout(g, S, L).total)
     return fail(c, UNO_ERR_INVALID_ARG, "backward: scratch smaller than uno_query_backward_bytes");
   return UNO_OK;
@@ -1779,7 +1780,7 @@ uno_status uno_lm_head_backward(uno_ctx* c, int32_t rows, const float* d_x_final
   if (!d_x_final || !d_dlogits || !d_dx) return fail(c, UNO_ERR_INVALID_ARG, "lm_head_backward: null buffer");
   if (!c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no LM head");
   if (rows < 16 || rows % 16) return fail(c, UNO_ERR_INVALID_ARG, "lm_head_backward: rows a multiple of 16");
-  if (uno_status s = bw_check(c, 1, rows, 1, d_scratch, scratch_bytes)) return s;
+  if (uno_status s = bw_check(c, 1, rows, 1, d_scratch, scratch_bytes, false)) return s;
   return lm_backward(c, rows, d_x_final, d_dlogits, nullptr, nullptr, rows, nullptr, d_dx,
                      static_cast<char*>(d_scratch), bw_layout(c->cfg, 1, rows));
 }

@@ -193,6 +193,12 @@ def test_distill_backward_two_layers():
     T, S, _, _ = eng.distill_forward(dev(x), B)
     loss, tv, ga, gb = eng.distill_backward(B, T, S)
     eng.sync()
+    # deterministic: a second backward gives the same bits (fixed-order reductions only)
+    loss2, tv2, ga2, gb2 = eng.distill_backward(B, T, S)
+    eng.sync()
+    assert np.array_equal(host(loss), host(loss2)) and np.array_equal(host(tv), host(tv2))
+    for p in PROJ:
+        assert np.array_equal(host(ga[p]), host(ga2[p])) and np.array_equal(host(gb[p]), host(gb2[p]))
     eng.set_distill_checkpoint(None, L)
     # checkpoint against the oracle's forward (bf16 storage): within forward noise
     ock = dg.distill_checkpoint(cfg, w, x, B)
