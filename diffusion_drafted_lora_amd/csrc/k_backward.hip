@@ -11,8 +11,10 @@
 // hi = bf16(v) and lo = bf16(v - hi), so that its 16 leading bits take part; the
 // other operand is a stored bf16 value (weight, activation) and exact, and the
 // products accumulate in float32.  Attention is formed explicitly per sequence
-// and KV head: scores and their gradients as GEMMs, the block-causal softmax and
-// its backward as row kernels.
+// and KV head: the scores against the x rows' keys, P V, dP and dq are GEMMs that
+// skip the tiles and k steps past a tile's block-causal limit; each z1 block's own
+// B keys (scores, P V, dP, and the dq, dk, dv of the block) run in small kernels;
+// the softmax and its backward over both parts are row kernels.
 #include "uno_internal.h"
 
 namespace {
