@@ -35,6 +35,7 @@ class UnoConfig:
     rope_theta: float = 1.0e6
     rms_eps: float = 1.0e-6
     page_size: int = 16
+    qk_norm: bool = False        # Qwen3-style RMSNorm of each q / k head before RoPE
     # workload
     batch: int = 1
     prompt_len: int = 16

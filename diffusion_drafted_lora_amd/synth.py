@@ -51,6 +51,9 @@ def weights_numpy(cfg, seed, std=0.02, lm_head_std=None, lora_b_std=None,
         lw = {"attn_norm": np.ones(cfg.d_model, dtype=np.float32),
               "mlp_norm": np.ones(cfg.d_model, dtype=np.float32),
               "w": {}, "la": {}, "lb": {}}
+        if cfg.qk_norm:
+            lw["q_norm"] = np.ones(cfg.head_dim, dtype=np.float32)
+            lw["k_norm"] = np.ones(cfg.head_dim, dtype=np.float32)
         for p, (o, i) in proj_shapes(cfg).items():
             lw["w"][p] = draw((o, i), std)
             if with_lora:
@@ -89,6 +92,9 @@ def weights_torch(cfg, seed, device, std=0.02, with_embed=True, with_lora=True):
         lw = {"attn_norm": torch.ones(cfg.d_model, dtype=dt, device=device),
               "mlp_norm": torch.ones(cfg.d_model, dtype=dt, device=device),
               "w": {}, "la": {}, "lb": {}}
+        if cfg.qk_norm:
+            lw["q_norm"] = torch.ones(cfg.head_dim, dtype=dt, device=device)
+            lw["k_norm"] = torch.ones(cfg.head_dim, dtype=dt, device=device)
         for p, (o, i) in proj_shapes(cfg).items():
             lw["w"][p] = draw((o, i), std)
             if with_lora:

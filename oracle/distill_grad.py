@@ -270,7 +270,10 @@ def distill_checkpoint(cfg, weights, x, B):
 
 def distill_grad(cfg, weights, x, B):
     """L_TV of the [x, z1] forward and its gradient with respect to every LoRA
-    matrix.  Returns (loss, [per layer {proj: (dA [r, in], dB [out, r])}])."""
+    matrix.  Returns (loss, [per layer {proj: (dA [r, in], dB [out, r])}]).
+    The per-head QK-norm option is not part of this gradient."""
+    if getattr(cfg, "qk_norm", False):
+        raise NotImplementedError("distill_grad: QK-norm configurations are not covered")
     ck = distill_checkpoint(cfg, weights, x, B)
     loss = tv_loss(ck["teacher"], ck["student"])
     dz = tv_logit_grad(ck["teacher"], ck["student"])

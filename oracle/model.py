@@ -16,7 +16,10 @@ What the pages leave open and this oracle reads plainly (listed in the design
 notes): a Qwen3-8B-shaped pre-norm decoder with RMSNorm, rotate-half RoPE, grouped
 query attention, SwiGLU MLP, no biases, untied embedding / LM head; the LoRA term
 on every one of the seven projections is gate * (alpha/r) * (h A^T) B^T; the MASK
-id is vocab-1 and its logit is -inf.
+id is vocab-1 and its logit is -inf.  Optionally (``cfg.qk_norm``) each query and
+key head is RMS-normalised over its head_dim with a learned gain before RoPE, as in
+the Qwen3 attention of the base model the pages augment (Uno_Qwen: Qwen3-8B plus a
+LoRA, [summary] method key points); off by default.
 
 Numerics: float64 throughout.  When ``cfg.dtype == "bf16"`` values are rounded to
 bfloat16 (round-to-nearest-even) at the points where the library stores bf16:
@@ -147,13 +150,17 @@ def _proj(cfg, lw, name, h, gate):
 def qkv_stage(cfg, lw, x, pos, gate):
     """Attention inputs of rows x [S, R, d]: q [S, R, Hq, hd] and k [S, R, Hkv, hd]
     after RoPE at positions ``pos``, and v, from the pre-attention RMSNorm and the
-    gated q / k / v projections."""
+    gated q / k / v projections (with ``cfg.qk_norm``, q and k are RMS-normalised
+    per head with the gains ``q_norm`` / ``k_norm`` before RoPE)."""
     S, R, _ = x.shape
     Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     h = norm_input(cfg, x, lw["attn_norm"], cfg.rms_eps)
     q = _proj(cfg, lw, "q", h, gate).reshape(S, R, Hq, hd)
     k = _proj(cfg, lw, "k", h, gate).reshape(S, R, Hkv, hd)
     v = _proj(cfg, lw, "v", h, gate).reshape(S, R, Hkv, hd)
+    if getattr(cfg, "qk_norm", False):
+        q = rms_norm(q, lw["q_norm"], cfg.rms_eps)
+        k = rms_norm(k, lw["k_norm"], cfg.rms_eps)
     return rope(q, pos, cfg.rope_theta), rope(k, pos, cfg.rope_theta), v
 
 

@@ -151,8 +151,12 @@ def _torch_forward(cfg, w, tokens, gate, store=()):
             u = st["lora"](s * F.linear(hh, T(lw["la"][p])))
             return F.linear(hh, T(lw["w"][p])) + g * F.linear(u, T(lw["lb"][p]))
         h = norm(x, lw["attn_norm"])
-        q = st["q"](rot(lin("q", h).view(R, Hq, hd))).transpose(0, 1)
-        k = st["k"](rot(lin("k", h).view(R, Hkv, hd))).transpose(0, 1)
+        qr, kr = lin("q", h).view(R, Hq, hd), lin("k", h).view(R, Hkv, hd)
+        if cfg.qk_norm:
+            qr = F.rms_norm(qr, (hd,), T(lw["q_norm"]), cfg.rms_eps)
+            kr = F.rms_norm(kr, (hd,), T(lw["k_norm"]), cfg.rms_eps)
+        q = st["q"](rot(qr)).transpose(0, 1)
+        k = st["k"](rot(kr)).transpose(0, 1)
         v = st["v"](lin("v", h).view(R, Hkv, hd)).transpose(0, 1)
         k = k.repeat_interleave(Hq // Hkv, 0)
         v = v.repeat_interleave(Hq // Hkv, 0)
@@ -283,3 +287,52 @@ def test_bf16_storage_pin_has_power(skip):
     ref = _torch_forward(cfg, w, toks, gate, store=tuple(p for p in STORE_POINTS if p != skip))
     fin = np.isfinite(ref)
     assert np.abs(got[fin] - ref[fin]).max() > 1e-5
+
+
+def _qk_norm_weights(cfg, seed):
+    w = synth.weights_numpy(cfg, seed)
+    r = np.random.default_rng(seed)
+    for lw in w["layers"]:
+        lw["q_norm"] = 1.0 + 0.3 * r.standard_normal(cfg.head_dim)
+        lw["k_norm"] = 1.0 + 0.3 * r.standard_normal(cfg.head_dim)
+    return w
+
+
+def test_qk_norm_forward_matches_torch():
+    """The Qwen3-style option: q and k RMS-normalised per head before RoPE, against
+    the independent torch forward using torch's rms_norm over the head dimension."""
+    cfg = TINY.with_(qk_norm=True)
+    w = _qk_norm_weights(cfg, 77)
+    r = np.random.default_rng(78)
+    R = 10
+    toks = r.integers(0, cfg.vocab, size=R)
+    gate = (r.random(R) < 0.5).astype(np.float64)
+    ref = _torch_forward(cfg, w, toks, gate)
+    cache = model.new_cache(cfg, 1, R)
+    logits, _ = model.forward(cfg, w, toks[None], np.arange(R)[None], gate[None], cache)
+    fin = np.isfinite(ref)
+    assert np.allclose(logits[0][fin], ref[fin], rtol=1e-9, atol=1e-12)
+
+
+def test_qk_norm_is_scale_invariant_and_not_a_no_op():
+    """With QK-norm (and eps 0), scaling the q / k projections (and their LoRA up
+    rows) by any positive factor leaves the logits unchanged; without it, it changes
+    them."""
+    for qk in (True, False):
+        cfg = TINY.with_(qk_norm=qk, rms_eps=0.0)     # eps would break exact scale invariance
+        w = _qk_norm_weights(cfg, 79) if qk else synth.weights_numpy(cfg, 79)
+        toks = np.random.default_rng(80).integers(0, cfg.vocab - 1, size=8)
+        base, _ = model.forward(cfg, w, toks[None], np.arange(8)[None], np.ones((1, 8)),
+                                model.new_cache(cfg, 1, 8))
+        w2 = {**w, "layers": []}
+        for lw in w["layers"]:
+            lw2 = {**lw, "w": dict(lw["w"]), "lb": dict(lw["lb"])}
+            for p in ("q", "k"):
+                lw2["w"][p] = lw["w"][p] * 3.0
+                lw2["lb"][p] = lw["lb"][p] * 3.0
+            w2["layers"].append(lw2)
+        scaled, _ = model.forward(cfg, w2, toks[None], np.arange(8)[None], np.ones((1, 8)),
+                                  model.new_cache(cfg, 1, 8))
+        fin = np.isfinite(base)
+        same = np.allclose(scaled[fin], base[fin], rtol=1e-6, atol=1e-6)
+        assert same == qk, qk
