@@ -18,6 +18,7 @@
 
 #include "../../include/uno.h"
 #include "uno_internal.h"
+#include "uno_qknorm.h"
 
 template <typename T> size_t attn_smem_bytes(int G, int hd);
 
@@ -44,6 +45,7 @@ struct Layout {
   size_t call_seq, call_n, call_it, row_tok, row_pos, row_gate, row_slot, row_vis, row_nc;
   size_t x, xn, qbuf, obuf, hbuf, ubuf, tfx, ss;
   size_t part_o, part_ml;
+  size_t qkv32;                      // float32 q|k|v rows before the QK RMSNorm (qk_norm only)
   size_t part_o_floats, part_rows;   // capacities: float words, (row, head, chunk) triples / Hq
   size_t logits, tile_stats, row_ml, probs_d, probs_v;
   size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32, tv;
@@ -107,6 +109,7 @@ Layout make_layout(const uno_config& c) {
   L.part_o_floats = std::max(L.part_rows * c.n_q_heads * c.head_dim, (size_t)4 * R * d);
   L.part_o = take(L.part_o_floats * 4);
   L.part_ml = take(L.part_rows * c.n_q_heads * 2 * 4);
+  L.qkv32 = take(c.qk_norm ? R * (q + 2 * kv) * 4 : 0);
   L.logits = take(R * V * 4);
   L.tile_stats = take(R * (V / 16) * 2 * 4);
   L.row_ml = take(R * 2 * 4);
@@ -138,6 +141,7 @@ struct uno_ctx {
   const void* lm_head = nullptr;
   const void* final_norm = nullptr;
   std::vector<const void*> attn_norm, mlp_norm, w[7], la[7], lb[7];
+  std::vector<const void*> q_norm, k_norm;   // QK RMSNorm gains (qk_norm contexts)
   bool has_lora = false;
   // host page bookkeeping
   std::vector<int> free_pages;
@@ -292,6 +296,7 @@ uno_status check_config(const uno_config* c) {
   if (c->max_rows < c->max_seqs * c->block_size)
     return fail(nullptr, UNO_ERR_INVALID_ARG, "max_rows < max_seqs * block_size");
   if (!(c->top_p >= 0.0f)) return fail(nullptr, UNO_ERR_INVALID_ARG, "top_p < 0 or NaN");
+  if (c->qk_norm != 0 && c->qk_norm != 1) return fail(nullptr, UNO_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
   return UNO_OK;
 }
 
@@ -725,13 +730,32 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       }
       clear(a, 3, r);
       norm_in(a, 2 * l);
-      a.epi = EPI_QKV;
-      a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
-      a.seq_fixed = seq_fixed;
-      if (f.mode == 4) a.row_slot = rs.row_slot;
-      a.n_q_heads = Hq; a.rcos = c->at<float>(c->L.rope_cos); a.rsin = c->at<float>(c->L.rope_sin);
-      a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
-      if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
+      const int32_t* slot = f.mode == 4 ? rs.row_slot : nullptr;
+      if (!c->cfg.qk_norm) {
+        a.epi = EPI_QKV;
+        a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
+        a.seq_fixed = seq_fixed;
+        a.row_slot = slot;
+        a.n_q_heads = Hq; a.rcos = c->at<float>(c->L.rope_cos); a.rsin = c->at<float>(c->L.rope_sin);
+        a.qbuf = qbuf; a.kv = kv; a.layer = l; a.err = err;
+        if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
+      } else {
+        // QK RMSNorm: the head's norm spans tiles of several workgroups, so the
+        // projection is stored as float32 and a row kernel normalises, rotates and
+        // writes q and the pages
+        float* y = c->at<float>(c->L.qkv32);
+        a.epi = EPI_STORE_F32; a.ldo = qd + 2 * kvd; a.out = y;
+        if (uno_status st = run_gemm(a, qd + 2 * kvd, UNO_KC_LINEAR)) return st;
+        QkNormArgs qa{};
+        qa.in = y; qa.ldi = qd + 2 * kvd; qa.M = R; qa.n_q_heads = Hq; qa.perm = c->bf16 ? 1 : 0;
+        qa.q_gain = c->q_norm[l]; qa.k_gain = c->k_norm[l]; qa.eps = g.rms_eps;
+        qa.row_pos = rs.row_pos; qa.row_slot = slot; qa.call_seq = rs.call_seq;
+        qa.seq_fixed = seq_fixed; qa.rows_per_seq = f.rows_per_seq;
+        qa.rcos = c->at<float>(c->L.rope_cos); qa.rsin = c->at<float>(c->L.rope_sin);
+        qa.qbuf = qbuf; qa.kv = kv; qa.layer = l; qa.err = err;
+        Timed t(c, UNO_KC_MISC, (double)R * (qd + 2 * kvd) * (4 + sizeof(T)), 0);
+        UNO_HIP(c, launch_qk_norm_rope<T>(qa, s));
+      }
     }
     if (tr && tr->q)
       UNO_HIP(c, hipMemcpyAsync(tr->q, qbuf, sizeof(T) * R * qd, hipMemcpyDeviceToDevice, s));
@@ -976,6 +1000,8 @@ uno_status bw_check(uno_ctx* c, int S, int L, int B, void* scratch, size_t bytes
   if (G & (G - 1)) return fail(c, UNO_ERR_UNSUPPORTED, "backward: query group must be a power of 2");
   if (S < 1 || L < 16 || L % 16 || B < 1 || B > kBwMaxB || L % B)
     return fail(c, UNO_ERR_INVALID_ARG, "backward: batch >= 1, L a multiple of 16 and of B");
+  if (rope && g.qk_norm)
+    return fail(c, UNO_ERR_UNSUPPORTED, "backward: the QK RMSNorm is not part of the layer backward");
   if (rope && L > c->maxpp * g.page_size)
     return fail(c, UNO_ERR_INVALID_ARG, "backward: L beyond the RoPE table");
   if (!scratch || bytes < bw_layout(g, S, L).total)
@@ -1243,6 +1269,11 @@ uno_status uno_init(const uno_config* cfg, const uno_weights* wts, void* d_kv_po
   if (any_lora && cfg->lora_rank <= 0) return fail(nullptr, UNO_ERR_INVALID_ARG, "LoRA without rank");
   for (int l = 0; l < nl; ++l)
     if (!wts->attn_norm[l] || !wts->mlp_norm[l]) return fail(nullptr, UNO_ERR_INVALID_ARG, "null norm");
+  if (cfg->qk_norm) {
+    if (!wts->q_norm || !wts->k_norm) return fail(nullptr, UNO_ERR_INVALID_ARG, "qk_norm: null q_norm / k_norm array");
+    for (int l = 0; l < nl; ++l)
+      if (!wts->q_norm[l] || !wts->k_norm[l]) return fail(nullptr, UNO_ERR_INVALID_ARG, "qk_norm: null q / k norm");
+  }
 
   uno_ctx* c = new (std::nothrow) uno_ctx();
   if (!c) return fail(nullptr, UNO_ERR_DEVICE, "host allocation failed");
@@ -1258,6 +1289,10 @@ uno_status uno_init(const uno_config* cfg, const uno_weights* wts, void* d_kv_po
   c->final_norm = wts->final_norm;
   c->attn_norm.assign(wts->attn_norm, wts->attn_norm + nl);
   c->mlp_norm.assign(wts->mlp_norm, wts->mlp_norm + nl);
+  if (cfg->qk_norm) {
+    c->q_norm.assign(wts->q_norm, wts->q_norm + nl);
+    c->k_norm.assign(wts->k_norm, wts->k_norm + nl);
+  }
   for (int p = 0; p < 7; ++p) {
     c->w[p].assign(wts->w[p], wts->w[p] + nl);
     if (any_lora) {

@@ -29,14 +29,17 @@ def _to_storage(cfg, a):
 
 
 def weights_numpy(cfg, seed, std=0.02, lm_head_std=None, lora_b_std=None,
-                  with_embed=True, with_lora=True):
+                  with_embed=True, with_lora=True, qk_gain_std=0.0):
     """All weights as float32 numpy arrays (bf16-representable for bf16 configs).
 
     Draw order is fixed: embed, lm_head, then per layer and per projection W, A, B.
     ``lm_head_std`` / ``lora_b_std`` override std for those matrices (used for a
-    stress variant whose draft and AR distributions differ a lot).
+    stress variant whose draft and AR distributions differ a lot).  With
+    ``cfg.qk_norm`` the per-head q / k gains are 1, or 1 + N(0, qk_gain_std^2) from
+    a generator of their own (the other draws do not move).
     """
     g = np.random.Generator(np.random.Philox(seed))
+    gq = np.random.Generator(np.random.Philox(seed + 7919))
 
     def draw(shape, s):
         return _to_storage(cfg, g.standard_normal(shape, dtype=np.float32) * np.float32(s))
@@ -52,8 +55,9 @@ def weights_numpy(cfg, seed, std=0.02, lm_head_std=None, lora_b_std=None,
               "mlp_norm": np.ones(cfg.d_model, dtype=np.float32),
               "w": {}, "la": {}, "lb": {}}
         if cfg.qk_norm:
-            lw["q_norm"] = np.ones(cfg.head_dim, dtype=np.float32)
-            lw["k_norm"] = np.ones(cfg.head_dim, dtype=np.float32)
+            for k in ("q_norm", "k_norm"):
+                lw[k] = _to_storage(cfg, 1.0 + gq.standard_normal(cfg.head_dim, dtype=np.float32)
+                                    * np.float32(qk_gain_std))
         for p, (o, i) in proj_shapes(cfg).items():
             lw["w"][p] = draw((o, i), std)
             if with_lora:

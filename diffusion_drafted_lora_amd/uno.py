@@ -46,7 +46,7 @@ class UnoConfigC(C.Structure):
                [("lora_alpha", C.c_float), ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + \
                [(n, C.c_int32) for n in ("block_size", "page_size", "max_seqs", "max_seq_len",
                                          "n_pages", "max_rows", "dtype")] + \
-               [("seed", C.c_uint64), ("top_p", C.c_float)]
+               [("seed", C.c_uint64), ("top_p", C.c_float), ("qk_norm", C.c_int32)]
 
 
 PP = C.POINTER(C.c_void_p)
@@ -67,7 +67,8 @@ TRACE_FIELDS = ("x_in", "q", "attn", "x_mid", "act", "x_out")
 class UnoWeightsC(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("lm_head", C.c_void_p), ("final_norm", C.c_void_p),
                 ("attn_norm", PP), ("mlp_norm", PP),
-                ("w", PP * 7), ("lora_a", PP * 7), ("lora_b", PP * 7)]
+                ("w", PP * 7), ("lora_a", PP * 7), ("lora_b", PP * 7),
+                ("q_norm", PP), ("k_norm", PP)]
 
 
 _lib = None
@@ -144,6 +145,7 @@ def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, 
     c.dtype = 1 if cfg.dtype == "bf16" else 0
     c.seed = seed
     c.top_p = top_p
+    c.qk_norm = 1 if getattr(cfg, "qk_norm", False) else 0
     return c
 
 
@@ -201,6 +203,9 @@ class Engine:
         L = weights["layers"]
         wc.attn_norm = arr([l["attn_norm"] for l in L])
         wc.mlp_norm = arr([l["mlp_norm"] for l in L])
+        if self.ccfg.qk_norm:
+            wc.q_norm = arr([l["q_norm"] for l in L])
+            wc.k_norm = arr([l["k_norm"] for l in L])
         has_lora = "la" in L[0] and len(L[0]["la"]) == 7
         for i, p in enumerate(PROJ):
             wc.w[i] = arr([l["w"][p] for l in L])
@@ -224,6 +229,9 @@ class Engine:
         for l in w["layers"]:
             yield l["attn_norm"]
             yield l["mlp_norm"]
+            for k in ("q_norm", "k_norm"):
+                if k in l:
+                    yield l[k]
             for d in ("w", "la", "lb"):
                 for t in l.get(d, {}).values():
                     yield t
@@ -565,6 +573,7 @@ def pack_weights(cfg, w):
     out["layers"] = []
     for lw in w["layers"]:
         d = {"attn_norm": lw["attn_norm"], "mlp_norm": lw["mlp_norm"], "w": {}}
+        d.update({k: lw[k] for k in ("q_norm", "k_norm") if k in lw})
         for p, t in lw["w"].items():
             d["w"][p] = pk(t, cfg.head_dim if p in ("q", "k", "v") else 0)
         if "la" in lw:
@@ -589,6 +598,7 @@ def to_device(weights_np, cfg, device="cuda"):
     for lw in weights_np["layers"]:
         d = {"attn_norm": t(lw["attn_norm"]), "mlp_norm": t(lw["mlp_norm"]),
              "w": {p: t(a) for p, a in lw["w"].items()}}
+        d.update({k: t(lw[k]) for k in ("q_norm", "k_norm") if k in lw})
         if "la" in lw:
             d["la"] = {p: t(a) for p, a in lw["la"].items()}
             d["lb"] = {p: t(a) for p, a in lw["lb"].items()}

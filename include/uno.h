@@ -91,6 +91,14 @@ typedef struct {
                                uno_top_p rule, applied right after each softmax):
                                0 (the zero-initialised default) or >= 1 turns it off;
                                negative or NaN is UNO_ERR_INVALID_ARG              */
+  int32_t qk_norm;          /* 1: RMS-normalise every query and key head over its
+                               head_dim (gain uno_weights.q_norm / k_norm, eps
+                               rms_eps) after the projection and before RoPE, as in
+                               the Qwen3 attention of the base model the pages
+                               augment (Qwen3-8B plus a LoRA [summary]); 0 (default):
+                               off; other values are UNO_ERR_INVALID_ARG.  The
+                               distillation backward calls return
+                               UNO_ERR_UNSUPPORTED on such a context              */
 } uno_config;
 
 /* Weights: host arrays of device pointers, copied at uno_init (the device memory
@@ -101,7 +109,8 @@ typedef struct {
  * float32 contexts take every matrix row-major.  bf16 contexts take lm_head, w,
  * lora_a and lora_b in the fragment-tiled layout that uno_pack_weight produces
  * from the row-major matrix (q, k, v and their lora_b packed with pair_hd =
- * head_dim, all others with pair_hd = 0); embed and the norms stay row-major. */
+ * head_dim, all others with pair_hd = 0); embed and the norm gains (final, attn,
+ * mlp, q and k) stay row-major. */
 typedef struct {
   const void* embed;                 /* [vocab, d]                 */
   const void* lm_head;               /* [vocab, d]                 */
@@ -111,6 +120,9 @@ typedef struct {
   const void* const* w[7];           /* [n_layers] -> [out, in]    */
   const void* const* lora_a[7];      /* [n_layers] -> [r, in]      */
   const void* const* lora_b[7];      /* [n_layers] -> [out, r]     */
+  const void* const* q_norm;         /* [n_layers] -> [head_dim]; read only when
+                                        uno_config.qk_norm is 1 (then required) */
+  const void* const* k_norm;         /* [n_layers] -> [head_dim]   */
 } uno_weights;
 
 /* Repack a row-major bf16 matrix [rows, cols] (device) into the fragment-tiled

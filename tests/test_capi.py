@@ -65,6 +65,18 @@ def test_invalid_configs_rejected():
         assert e.value.status == 1
     for tp in (0.0, 0.95, 1.0, 2.0):              # off, on, off, off
         uno.query_sizes(uno.make_config(configs.TINY, top_p=tp))
+    bad = uno.make_config(configs.TINY)
+    bad.qk_norm = 2
+    with pytest.raises(uno.UnoError) as e:
+        uno.query_sizes(bad)
+    assert e.value.status == 1
+    # QK-norm adds one float32 q|k|v staging buffer of max_rows rows to the workspace
+    c0, c1 = uno.make_config(configs.TINY), uno.make_config(configs.TINY.with_(qk_norm=True))
+    assert c1.qk_norm == 1
+    T = configs.TINY
+    grow = uno.query_sizes(c1)[1] - uno.query_sizes(c0)[1]
+    need = c0.max_rows * (T.n_q_heads + 2 * T.n_kv_heads) * T.head_dim * 4
+    assert need <= grow <= need + 256
 
 
 def test_init_rejects_null_buffers_before_touching_the_device():
