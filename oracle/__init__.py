@@ -31,4 +31,6 @@ Modules:
   nucleus  the top-p truncation of a probability row (exact fixed-point reading).
   distill_grad  the block-wise TV loss and its gradient with respect to the LoRA
            (base frozen), layer by layer over the z1 rows.
+  tree     the tree sampler: K drafted chains, one verify per chain, recursive
+           rejection along the tree of common prefixes.
 """

@@ -150,8 +150,8 @@ class Decoder:
             self.t[s] = pr[-1]
             self.it[s] = 0
 
-    def draft(self):
-        """Draft forward and draft sampling.  Returns (y [S, B], P_d float32 [S, B, V])."""
+    def draft_laws(self):
+        """The draft forward: P_d float32 [S, B, V] (row j is the law of position n+j+1)."""
         cfg, B, S = self.cfg, self.cfg.block_size, self.S
         toks = np.full((S, B), cfg.mask_id, dtype=np.int64)
         toks[:, 0] = self.t
@@ -159,7 +159,12 @@ class Decoder:
         gate = np.ones((S, B))
         gate[:, 0] = 0.0
         logits, _ = model.forward(cfg, self.w, toks, pos, gate, self.cache)
-        P_d = self._law(logits)
+        return self._law(logits)
+
+    def draft(self):
+        """Draft forward and draft sampling.  Returns (y [S, B], P_d float32 [S, B, V])."""
+        B, S = self.cfg.block_size, self.S
+        P_d = self.draft_laws()
         y = np.empty((S, B), dtype=np.int64)
         for j in range(1, B + 1):
             word = rng.draw_word(self.seed, self.seq_ids, self.n + j, rng.STREAM_DRAFT, self.it)

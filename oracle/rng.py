@@ -77,16 +77,17 @@ def philox4x64(ctr, key, rounds=10):
     return np.stack(c, axis=-1)
 
 
-def draw_word(seed, seq_id, pos, stream, it):
-    """Word 0 of Philox(key=(seed, seq_id), counter=(pos, stream, it, 0)).
+def draw_word(seed, seq_id, pos, stream, it, ctr3=0):
+    """Word 0 of Philox(key=(seed, seq_id), counter=(pos, stream, it, ctr3)).
 
-    All arguments broadcast; returns uint64.
+    All arguments broadcast; returns uint64.  ``ctr3`` is 0 for the linear
+    sampler; the tree sampler puts the chain (draft) or trial (accept) index there.
     """
-    seed, seq_id, pos, stream, it = np.broadcast_arrays(
+    seed, seq_id, pos, stream, it, ctr3 = np.broadcast_arrays(
         np.asarray(seed, dtype=U64), np.asarray(seq_id, dtype=U64),
         np.asarray(pos, dtype=U64), np.asarray(stream, dtype=U64),
-        np.asarray(it, dtype=U64))
-    ctr = np.stack([pos, stream, it, np.zeros_like(pos)], axis=-1)
+        np.asarray(it, dtype=U64), np.asarray(ctr3, dtype=U64))
+    ctr = np.stack([pos, stream, it, ctr3], axis=-1)
     key = np.stack([seed, seq_id], axis=-1)
     return philox4x64(ctr, key)[..., 0]
 
@@ -114,6 +115,19 @@ def threshold(word, total):
     """tau = floor(word * total / 2^64), i.e. the high word of the 128-bit product."""
     hi, _ = mulhilo64(word, total)
     return hi
+
+
+def sample_int(W, word):
+    """Categorical draw over the last axis of integer weights ``W`` (uint64) using
+    ``word``: the smallest j whose inclusive prefix sum exceeds floor(word * T /
+    2^64).  Returns (index, total); index is -1 where T == 0."""
+    W = np.asarray(W, dtype=U64)
+    cum = np.cumsum(W, axis=-1, dtype=U64)
+    total = cum[..., -1]
+    tau = threshold(word, total)
+    idx = np.sum(cum <= tau[..., None], axis=-1).astype(np.int64)
+    idx = np.where(total == 0, -1, idx)
+    return idx, total
 
 
 def sample_icdf(w, word):
