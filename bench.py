@@ -183,6 +183,46 @@ def run_batch(cfg, w, dev, batch, ctx, steps, warmup, prompt_len, log_prefix="bs
     }
 
 
+def run_tree(cfg, w, dev, chains, steps, warmup, prompt_len):
+    """Batch-1 tree sampler (uno_tree_step) on the headline's prompt and seed, for
+    each chain count K: accepted tokens/s, tokens per forward and the step time
+    (its verify forward carries 1 + K (B - 1) rows)."""
+    import torch
+    from diffusion_drafted_lora_amd import synth, uno
+
+    B = cfg.block_size
+    res = []
+    for K in chains:
+        Rv = 1 + K * (B - 1)
+        max_len = prompt_len + (warmup + steps + 2) * (B + 1) + 2 + K * (B - 1) + B
+        eng = uno.Engine(cfg, w, max_seqs=1, max_seq_len=max_len, max_rows=max(256, Rv),
+                         seed=3002, device=dev, tree_chains=K)
+        prompt = synth.prompts(cfg, 2002, 1, prompt_len)[0]
+        log(f"tree K={K}: prefill {prompt_len} tokens")
+        eng.prefill([0], [prompt])
+        outs = torch.empty((1, B + 1), dtype=torch.int32, device=dev)
+        nouts = torch.empty((warmup + steps,), dtype=torch.int32, device=dev)
+        for i in range(warmup):
+            eng.tree_step([0], K, out=outs, n_out=nouts[i:i + 1])
+        eng.sync()
+        ctx0 = eng.seq_state(0)[0]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            eng.tree_step([0], K, out=outs, n_out=nouts[i:i + 1])
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        eng.sync()
+        tok = int(nouts[warmup:].sum().item())
+        res.append({"chains": K, "verify_rows": Rv, "steps": steps, "warmup": warmup,
+                    "context_start": int(ctx0), "accepted_tokens_per_s": tok / sec,
+                    "tokens_per_forward": tok / (2.0 * steps), "ms_per_step": 1e3 * sec / steps})
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_bytes_per_iteration(cfg, contexts):
     """Mean algorithmic bytes of a batch-1 iteration over contexts [c0, c_last]: both
     forwards' weights, the draft's LoRA and the K/V of the context read twice (the
@@ -474,6 +514,10 @@ def main():
     ap.add_argument("--distill-b-sweep", type=str, default="4,8,32",
                     help="further block sizes of the distillation leg, one timed forward "
                          "each ('none' skips them)")
+    ap.add_argument("--tree-steps", type=int, default=40,
+                    help="timed steps of the batch-1 tree-sampler leg (0: skip)")
+    ap.add_argument("--tree-chains", type=str, default="2,4",
+                    help="chain counts of the tree-sampler leg")
     ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
                     help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -619,6 +663,9 @@ def main():
             run["hbm_gbs_algorithmic"] = run_bytes_per_iteration(cfg, run["contexts"]) / 1e9 / \
                 (run["mean_ms_per_step"] / 1e3)
             run["hbm_frac"] = run["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
+    if args.tree_steps > 0:
+        result["tree"] = run_tree(cfg, w, dev, [int(k) for k in args.tree_chains.split(",")],
+                                  args.tree_steps, 4, args.prompt)
     if args.bs128_steps > 0:
         result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
                            for c in args.bs128_ctx.split(",")]

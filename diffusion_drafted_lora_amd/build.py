@@ -15,6 +15,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libuno.so")
 
 SOURCES = ["uno_runtime.hip", "k_linear.hip", "k_attn.hip", "k_misc.hip", "k_sample.hip", "k_qknorm.hip",
+           "k_tree.hip",
            "uno_noalloc.hip", "k_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -64,6 +64,34 @@ __global__ void k_rows_setup(RowsSetup a) {
       a.row_vis[3 * r + 2] = noisy ? Lx + jj : -1;
       break;
     }
+    case 5: {  // tree verify: y_1 at n+1 (slot n+1), then chain k's depths 2..B
+      // at positions n+2.. in slots base_k.. (base_k = n + 2 + k (B - 1), so chain
+      // 0 sits at its own positions); every row sees the context through y_1 and
+      // its own chain up to itself, gate 0
+      const int Bm = a.B - 1;
+      const int32_t* ch = a.draft_tok + (size_t)i * a.K * a.B;
+      int slot, c0, d0;
+      if (j == 0) {
+        tok = ch[0];
+        pos = n + 1;
+        slot = n + 1;
+        c0 = INT_MAX;
+        d0 = -1;
+      } else {
+        const int k = (j - 1) / Bm, dd = (j - 1) % Bm + 2;
+        tok = ch[k * a.B + dd - 1];
+        pos = n + dd;
+        c0 = n + 2 + k * Bm;
+        slot = c0 + dd - 2;
+        d0 = slot;
+      }
+      g = 0;
+      a.row_slot[r] = slot;
+      a.row_vis[3 * r] = n + 2;
+      a.row_vis[3 * r + 1] = c0;
+      a.row_vis[3 * r + 2] = d0;
+      break;
+    }
     default:  // prefill rows of one sequence
       tok = a.in_tok[r];
       pos = a.pos0 + r;

@@ -15,6 +15,13 @@
 
 namespace {
 
+// Integer weight of entry j: modes 0 / 1 take trunc(w * 2^40) of the float row;
+// mode 2 reads the integer masses of a uint64 row (the tree sampler's residual).
+__device__ uint64_t row_iweight(const RowDesc& d, int mode, int j, int32_t* err) {
+  if (mode == 2) return reinterpret_cast<const uint64_t*>(d.a)[j];
+  return int_weight(row_weight(d, mode, j), err);
+}
+
 // Inclusive Hillis-Steele scan of one uint64 per thread in LDS; returns the
 // exclusive prefix of this thread and writes the block total to *total.
 __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* sh, uint64_t* total) {
@@ -41,7 +48,7 @@ __device__ uint64_t chunk_sum(const RowDesc& d, int mode, int c, int V, int32_t*
   uint64_t s = 0;
   for (int e = 0; e < per; ++e) {
     const int j = j0 + e;
-    if (j < V) s += int_weight(row_weight(d, mode, j), err);
+    if (j < V) s += row_iweight(d, mode, j, err);
   }
   uint64_t tot;
   block_excl_scan(s, sh, &tot);
@@ -85,7 +92,7 @@ k_cdf_select(const RowDesc* __restrict__ desc, int V, int n_chunks,
     __syncthreads();
     T = sh[0];
     __syncthreads();
-    if (T != 0 || mode == 0) break;
+    if (T != 0 || mode != 1) break;
     // residual without integer mass: fall back to the plain row a[]
     mode = 0;
     for (int c = 0; c < n_chunks; ++c) {
@@ -117,7 +124,7 @@ k_cdf_select(const RowDesc* __restrict__ desc, int V, int n_chunks,
   uint64_t s = 0;
   for (int e = 0; e < per; ++e) {
     const int j = j0 + e;
-    w[e] = (j < V) ? int_weight(row_weight(d, mode, j), nullptr) : 0;
+    w[e] = (j < V) ? row_iweight(d, mode, j, nullptr) : 0;
     s += w[e];
   }
   uint64_t tot;

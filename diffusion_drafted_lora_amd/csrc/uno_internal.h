@@ -78,10 +78,10 @@ enum : int32_t {
 
 enum : int32_t { STREAM_DRAFT = 0, STREAM_ACCEPT = 1, STREAM_RESAMPLE = 2 };
 
-// Word 0 of Philox4x64-10(key = (k0, k1), counter = (c0, c1, c2, 0)).
+// Word 0 of Philox4x64-10(key = (k0, k1), counter = (c0, c1, c2, c3)).
 UNO_DEV uint64_t philox_word0(uint64_t k0, uint64_t k1, uint64_t c0, uint64_t c1,
-                              uint64_t c2) {
-  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = 0;
+                              uint64_t c2, uint64_t c3 = 0) {
+  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = c3;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += PHILOX_W0; k1 += PHILOX_W1; }
@@ -93,11 +93,13 @@ UNO_DEV uint64_t philox_word0(uint64_t k0, uint64_t k1, uint64_t c0, uint64_t c1
   return x0;
 }
 
-// The draw deciding absolute position `pos` in `stream` at iteration `it`.
+// The draw deciding absolute position `pos` in `stream` at iteration `it`; `c3`
+// is 0 in the linear sampler and the chain / trial index in the tree sampler.
 UNO_DEV uint64_t draw_word(uint64_t seed, int32_t seq_id, int32_t pos, int32_t stream,
-                           int32_t it) {
+                           int32_t it, int32_t c3 = 0) {
   return philox_word0(seed, (uint64_t)(uint32_t)seq_id, (uint64_t)(uint32_t)pos,
-                      (uint64_t)(uint32_t)stream, (uint64_t)(uint32_t)it);
+                      (uint64_t)(uint32_t)stream, (uint64_t)(uint32_t)it,
+                      (uint64_t)(uint32_t)c3);
 }
 
 // Uniform in [0, 1 - 2^-24]: the top 24 bits of the word, exact in float32.
@@ -331,8 +333,10 @@ template <typename T> hipError_t launch_gemm(const GemmArgs& a, int n_cols_total
 
 struct RowsSetup {
   int32_t mode;          // 0 draft, 1 verify, 2 forward (caller rows), 3 prefill,
-                         // 4 distillation rows [x | MASK^L] (B = its block size)
+                         // 4 distillation rows [x | MASK^L] (B = its block size),
+                         // 5 tree verify (y_1, then K chains of depths 2..B)
   int32_t n, rows_per_seq, B, mask_id;
+  int32_t K;                 // mode 5: chains per sequence (draft_tok is [n, K, B])
   const int32_t* call_seq;   // [n] sequence ids
   const int32_t* len;        // [max_seqs]
   const int32_t* pending;    // [max_seqs]
@@ -345,8 +349,8 @@ struct RowsSetup {
   int32_t* row_tok;
   int32_t* row_pos;
   uint8_t* row_gate;
-  int32_t* row_slot;         // mode 4: KV slot of each row
-  int32_t* row_vis;          // mode 4: [R][3] visible slots [0, a) and [c, d]
+  int32_t* row_slot;         // modes 4, 5: KV slot of each row
+  int32_t* row_vis;          // modes 4, 5: [R][3] visible slots [0, a) and [c, d]
   int32_t* call_n;           // [n] pending position n of each call sequence
   int32_t* call_it;          // [n] iteration
 };

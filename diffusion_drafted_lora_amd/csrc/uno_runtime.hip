@@ -19,6 +19,7 @@
 #include "../../include/uno.h"
 #include "uno_internal.h"
 #include "uno_qknorm.h"
+#include "uno_tree.h"
 
 template <typename T> size_t attn_smem_bytes(int G, int hd);
 
@@ -49,6 +50,7 @@ struct Layout {
   size_t part_o_floats, part_rows;   // capacities: float words, (row, head, chunk) triples / Hq
   size_t logits, tile_stats, row_ml, probs_d, probs_v;
   size_t desc, chunk_tot, draft_tok, acc_k, acc_z, aux_i32, tv;
+  size_t tree_res, tree_path, tree_kstar;   // tree sampler (tree_chains > 0)
   size_t total;
 };
 
@@ -66,7 +68,10 @@ Layout make_layout(const uno_config& c) {
                kv = (size_t)c.n_kv_heads * c.head_dim, F = c.ffn_dim, V = c.vocab,
                r = c.lora_rank > 0 ? c.lora_rank : 0, B = c.block_size;
   const size_t n_chunks_cdf = (V + CDF_CHUNK - 1) / CDF_CHUNK;
-  const size_t rows_any = std::max(R, S * B);
+  const size_t Kt = c.tree_chains > 0 ? (size_t)c.tree_chains : 0;
+  // draws of one draft (K chains of B), rows of one verify (1 + K (B - 1))
+  const size_t rows_any = std::max(std::max(R, S * B), S * Kt * B);
+  const size_t v_rows = std::max(B, 1 + Kt * (B - 1));
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.len = take(S * 4);
@@ -114,14 +119,17 @@ Layout make_layout(const uno_config& c) {
   L.tile_stats = take(R * (V / 16) * 2 * 4);
   L.row_ml = take(R * 2 * 4);
   L.probs_d = take(S * B * V * 4);
-  L.probs_v = take(S * B * V * 4);
+  L.probs_v = take(S * v_rows * V * 4);
   L.desc = take(rows_any * sizeof(RowDesc));
   L.chunk_tot = take(rows_any * n_chunks_cdf * 8);
-  L.draft_tok = take(S * B * 4);
+  L.draft_tok = take(S * B * std::max<size_t>(1, Kt) * 4);
   L.acc_k = take(S * 4);
   L.acc_z = take(S * 4);
   L.aux_i32 = take(rows_any * 4);
   L.tv = take(R * 4);
+  L.tree_res = take(Kt ? S * V * 8 : 0);
+  L.tree_path = take(S * B * 4);
+  L.tree_kstar = take(S * 4);
   L.total = o;
   return L;
 }
@@ -153,6 +161,7 @@ struct uno_ctx {
   std::vector<int> uploaded_call;   // call_seq contents on the device
   // draft bookkeeping
   std::vector<int> drafted_ids;
+  int drafted_tree = 0;             // chains of the pending draft (0: a linear draft)
   // asynchronous length snapshot
   int32_t* snap_host = nullptr;
   hipEvent_t snap_event = nullptr;
@@ -297,6 +306,8 @@ uno_status check_config(const uno_config* c) {
     return fail(nullptr, UNO_ERR_INVALID_ARG, "max_rows < max_seqs * block_size");
   if (!(c->top_p >= 0.0f)) return fail(nullptr, UNO_ERR_INVALID_ARG, "top_p < 0 or NaN");
   if (c->qk_norm != 0 && c->qk_norm != 1) return fail(nullptr, UNO_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
+  if (c->tree_chains < 0 || c->tree_chains > TREE_KMAX)
+    return fail(nullptr, UNO_ERR_INVALID_ARG, "tree_chains must be 0..16");
   return UNO_OK;
 }
 
@@ -453,6 +464,7 @@ struct FwdIn {
   // teacher / student logits [n, L, V] (nullptr: workspace), per-row TV [n, L]
   // (nullptr: workspace) and per-block TV [n, L / dB] (nullptr: not formed)
   int dB;
+  int tree_K;               // mode 5: chains per sequence
   float* teacher;
   float* student;
   float* tv_row;
@@ -497,6 +509,9 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   rs.row_slot = c->at<int32_t>(c->L.row_slot);
   rs.row_vis = c->at<int32_t>(c->L.row_vis);
   if (f.mode == 4) rs.B = f.dB;
+  rs.K = f.tree_K;
+  // rows whose K/V slot and visible window are given per row (not by position)
+  const bool windowed = f.mode == 4 || f.mode == 5;
   rs.call_n = c->at<int32_t>(c->L.call_n);
   rs.call_it = c->at<int32_t>(c->L.call_it);
   {
@@ -730,7 +745,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       }
       clear(a, 3, r);
       norm_in(a, 2 * l);
-      const int32_t* slot = f.mode == 4 ? rs.row_slot : nullptr;
+      const int32_t* slot = windowed ? rs.row_slot : nullptr;
       if (!c->cfg.qk_norm) {
         a.epi = EPI_QKV;
         a.row_pos = rs.row_pos; a.call_seq = rs.call_seq; a.rows_per_seq = f.rows_per_seq;
@@ -763,7 +778,7 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
       AttnArgs a{};
       a.q = qbuf; a.out = obuf; a.row_pos = rs.row_pos; a.call_seq = rs.call_seq;
       a.seq_fixed = seq_fixed;
-      a.row_vis = f.mode == 4 ? rs.row_vis : nullptr;
+      a.row_vis = windowed ? rs.row_vis : nullptr;
       a.row_nc = c->at<int32_t>(c->L.row_nc);
       a.err = err;
       a.n = f.n; a.rows_per_seq = f.rows_per_seq; a.n_q_heads = Hq;
@@ -1392,51 +1407,75 @@ uno_status uno_prefill(uno_ctx* c, int32_t n, const int32_t* seq_ids, const int3
   return UNO_OK;
 }
 
-uno_status uno_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_draft, float* d_probs) {
+namespace {
+
+// The draft forward and its draws: K == 0 the linear block (B tokens), K >= 1 the
+// tree's K chains of B tokens ([n, K, B], y_1 shared).
+uno_status draft_impl(uno_ctx* c, int32_t n, const int32_t* seq_ids, int K, int32_t* d_tok,
+                      float* d_probs) {
   if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
   std::vector<int> seqs;
   uno_status st = check_seqs(c, n, seq_ids, seqs, true);
   if (st) return st;
   if (!c->embed || !c->lm_head) return fail(c, UNO_ERR_INVALID_ARG, "no embedding / LM head");
   const int B = c->cfg.block_size, V = c->cfg.vocab;
+  // positions a step may write: the draft's n..n+B-1, the verify's n+1..n+B, and
+  // for a tree the side chains' slots up to n + 1 + K (B - 1)
+  const int span = std::max(B + 1, K > 0 ? 2 + K * (B - 1) : 0);
+  if (K > 0 && n * (1 + K * (B - 1)) > c->cfg.max_rows)
+    return fail(c, UNO_ERR_INVALID_ARG, "tree verify rows n * (1 + K (B - 1)) exceed max_rows");
   poll_snapshot(c);
   std::vector<int> upto(n);
-  int bound = 0;
   for (int i = 0; i < n; ++i) {
-    upto[i] = c->len_hi[seqs[i]] + B + 1;
+    upto[i] = c->len_hi[seqs[i]] + span;
     if (upto[i] > c->cfg.max_seq_len) {   // the bound may be loose: get exact lengths
       if ((st = exact_lengths(c))) return st;
-      for (int j = 0; j < n; ++j) upto[j] = c->len_hi[seqs[j]] + B + 1;
+      for (int j = 0; j < n; ++j) upto[j] = c->len_hi[seqs[j]] + span;
       break;
     }
   }
-  for (int i = 0; i < n; ++i) bound = std::max(bound, upto[i]);
+  int bound = 0;
+  for (int i = 0; i < n; ++i) bound = std::max(bound, c->len_hi[seqs[i]] + B);
   if ((st = reserve(c, seqs, upto))) return st;
   if ((st = flush_pages(c))) return st;
   if ((st = upload_call(c, seqs))) return st;
   FwdIn f{};
   f.mode = 0; f.n = n; f.rows_per_seq = B;
-  f.ctx_bound = bound - 1;
+  f.ctx_bound = bound;
   f.lora = true;
   f.probs_out = c->at<float>(c->L.probs_d);
   if ((st = forward(c, f))) return st;
   hipStream_t s = c->stream;
   RowDesc* desc = c->at<RowDesc>(c->L.desc);
-  Timed tsm(c, UNO_KC_SAMPLING, (double)n * B * V * 8, 0);
+  const int draws = n * B * std::max(1, K);
+  Timed tsm(c, UNO_KC_SAMPLING, (double)draws * V * 8, 0);
   if (top_p_on(c->cfg))
     UNO_HIP(c, launch_top_p(f.probs_out, f.probs_out, n * B, V, c->cfg.top_p, s));
-  UNO_HIP(c, launch_draft_desc(f.probs_out, n, B, V, c->cfg.seed, c->at<int32_t>(c->L.call_seq),
-                               c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
-                               c->at<int32_t>(c->L.draft_tok), desc, s));
-  UNO_HIP(c, launch_cdf(desc, n * B, V, c->at<uint64_t>(c->L.chunk_tot), c->at<int32_t>(c->L.err), s));
-  if (d_draft)
-    UNO_HIP(c, hipMemcpyAsync(d_draft, c->at<int32_t>(c->L.draft_tok), sizeof(int32_t) * n * B,
+  if (K == 0)
+    UNO_HIP(c, launch_draft_desc(f.probs_out, n, B, V, c->cfg.seed, c->at<int32_t>(c->L.call_seq),
+                                 c->at<int32_t>(c->L.call_n), c->at<int32_t>(c->L.call_it),
+                                 c->at<int32_t>(c->L.draft_tok), desc, s));
+  else
+    UNO_HIP(c, launch_tree_draft_desc(f.probs_out, n, K, B, V, c->cfg.seed,
+                                      c->at<int32_t>(c->L.call_seq), c->at<int32_t>(c->L.call_n),
+                                      c->at<int32_t>(c->L.call_it), c->at<int32_t>(c->L.draft_tok),
+                                      desc, s));
+  UNO_HIP(c, launch_cdf(desc, draws, V, c->at<uint64_t>(c->L.chunk_tot), c->at<int32_t>(c->L.err), s));
+  if (d_tok)
+    UNO_HIP(c, hipMemcpyAsync(d_tok, c->at<int32_t>(c->L.draft_tok), sizeof(int32_t) * draws,
                               hipMemcpyDeviceToDevice, s));
   if (d_probs)
     UNO_HIP(c, hipMemcpyAsync(d_probs, f.probs_out, sizeof(float) * (size_t)n * B * V,
                               hipMemcpyDeviceToDevice, s));
   c->drafted_ids = seqs;
+  c->drafted_tree = K;
   return UNO_OK;
+}
+
+}  // namespace
+
+uno_status uno_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_draft, float* d_probs) {
+  return draft_impl(c, n, seq_ids, 0, d_draft, d_probs);
 }
 
 uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_out,
@@ -1445,7 +1484,8 @@ uno_status uno_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_
   std::vector<int> seqs;
   uno_status st = check_seqs(c, n, seq_ids, seqs, true);
   if (st) return st;
-  if (seqs != c->drafted_ids) return fail(c, UNO_ERR_STATE, "verify without a matching draft");
+  if (seqs != c->drafted_ids || c->drafted_tree != 0)
+    return fail(c, UNO_ERR_STATE, "verify without a matching linear draft");
   if ((st = upload_call(c, seqs))) return st;     // another call may have changed the list
   const int B = c->cfg.block_size, V = c->cfg.vocab;
   int bound = 0;
@@ -1484,6 +1524,117 @@ uno_status uno_step(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_ou
   uno_status st = uno_draft(c, n, seq_ids, nullptr, nullptr);
   if (st) return st;
   return uno_verify(c, n, seq_ids, d_out, d_n_out, nullptr);
+}
+
+uno_status uno_tree_draft(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t n_chains,
+                          int32_t* d_chains, float* d_probs) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (n_chains < 1 || n_chains > c->cfg.tree_chains)
+    return fail(c, UNO_ERR_INVALID_ARG, "n_chains must be 1..tree_chains");
+  return draft_impl(c, n, seq_ids, n_chains, d_chains, d_probs);
+}
+
+uno_status uno_tree_verify(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t* d_out,
+                           int32_t* d_n_out, int32_t* d_kstar, float* d_probs) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  std::vector<int> seqs;
+  uno_status st = check_seqs(c, n, seq_ids, seqs, true);
+  if (st) return st;
+  if (seqs != c->drafted_ids || c->drafted_tree < 1)
+    return fail(c, UNO_ERR_STATE, "tree verify without a matching tree draft");
+  if ((st = upload_call(c, seqs))) return st;
+  const int B = c->cfg.block_size, V = c->cfg.vocab, K = c->drafted_tree;
+  const int Rv = 1 + K * (B - 1);
+  int bound = 0;
+  for (int sq : seqs) bound = std::max(bound, c->len_hi[sq] + std::max(B + 1, 2 + K * (B - 1)));
+  FwdIn f{};
+  f.mode = 5; f.n = n; f.rows_per_seq = Rv; f.tree_K = K;
+  f.ctx_bound = bound;
+  f.lora = false;
+  f.probs_out = c->at<float>(c->L.probs_v);
+  if ((st = forward(c, f))) return st;
+  hipStream_t s = c->stream;
+  int32_t* err = c->at<int32_t>(c->L.err);
+  Timed tsm(c, UNO_KC_SAMPLING, (double)n * V * 8 * 2, 0);
+  if (top_p_on(c->cfg))
+    UNO_HIP(c, launch_top_p(f.probs_out, f.probs_out, n * Rv, V, c->cfg.top_p, s));
+  TreeAcceptArgs ta{};
+  ta.p = f.probs_out; ta.p_rows = Rv;
+  ta.q = c->at<float>(c->L.probs_d); ta.q_rows = B;
+  ta.chains = c->at<int32_t>(c->L.draft_tok);
+  ta.seq_ids = c->at<int32_t>(c->L.call_seq);
+  ta.pos = c->at<int32_t>(c->L.call_n);
+  ta.iter = c->at<int32_t>(c->L.call_it);
+  ta.K = K; ta.B = B; ta.V = V; ta.seed = c->cfg.seed;
+  ta.resid = c->at<uint64_t>(c->L.tree_res);
+  ta.path = c->at<int32_t>(c->L.tree_path);
+  ta.k_out = c->at<int32_t>(c->L.acc_k);
+  ta.kstar = c->at<int32_t>(c->L.tree_kstar);
+  ta.z = c->at<int32_t>(c->L.acc_z);
+  ta.desc = c->at<RowDesc>(c->L.desc);
+  ta.err = err;
+  UNO_HIP(c, launch_tree_accept(ta, n, s));
+  UNO_HIP(c, launch_cdf(ta.desc, n, V, c->at<uint64_t>(c->L.chunk_tot), err, s));
+  const KvLayout kv = kv_layout(c);
+  if (c->bf16)
+    UNO_HIP(c, launch_tree_kv_move<bf16>(kv, n, B, c->cfg.n_layers, ta.seq_ids, ta.pos, ta.k_out,
+                                         ta.kstar, err, s));
+  else
+    UNO_HIP(c, launch_tree_kv_move<float>(kv, n, B, c->cfg.n_layers, ta.seq_ids, ta.pos, ta.k_out,
+                                          ta.kstar, err, s));
+  UNO_HIP(c, launch_accept_commit(n, B, ta.path, ta.k_out, ta.z, ta.seq_ids, d_out, d_n_out,
+                                  c->at<int32_t>(c->L.len), c->at<int32_t>(c->L.pending),
+                                  c->at<int32_t>(c->L.iter), s));
+  if (d_kstar)
+    UNO_HIP(c, hipMemcpyAsync(d_kstar, ta.kstar, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, s));
+  if (d_probs)
+    UNO_HIP(c, hipMemcpyAsync(d_probs, f.probs_out, sizeof(float) * (size_t)n * Rv * V,
+                              hipMemcpyDeviceToDevice, s));
+  for (int sq : seqs) c->len_hi[sq] += B + 1;
+  c->drafted_ids.clear();
+  c->drafted_tree = 0;
+  return start_snapshot(c);
+}
+
+uno_status uno_tree_step(uno_ctx* c, int32_t n, const int32_t* seq_ids, int32_t n_chains,
+                         int32_t* d_out, int32_t* d_n_out) {
+  uno_status st = uno_tree_draft(c, n, seq_ids, n_chains, nullptr, nullptr);
+  if (st) return st;
+  return uno_tree_verify(c, n, seq_ids, d_out, d_n_out, nullptr, nullptr);
+}
+
+uno_status uno_tree_accept(uno_ctx* c, int32_t n, int32_t n_chains, const float* d_p,
+                           const float* d_q, const int32_t* d_chains, const int32_t* d_seq_ids,
+                           const int32_t* d_pos, const int32_t* d_iter, int32_t* d_out,
+                           int32_t* d_n_out, int32_t* d_kstar) {
+  if (!c) return fail(nullptr, UNO_ERR_INVALID_ARG, "null ctx");
+  if (c->cfg.tree_chains < 1) return fail(c, UNO_ERR_UNSUPPORTED, "context without tree_chains");
+  if (n < 1 || n > c->cfg.max_seqs) return fail(c, UNO_ERR_INVALID_ARG, "bad count");
+  if (n_chains < 1 || n_chains > TREE_KMAX) return fail(c, UNO_ERR_INVALID_ARG, "n_chains must be 1..16");
+  if (!d_p || !d_q || !d_chains || !d_seq_ids || !d_pos || !d_iter)
+    return fail(c, UNO_ERR_INVALID_ARG, "null input");
+  const int B = c->cfg.block_size, V = c->cfg.vocab;
+  hipStream_t s = c->stream;
+  int32_t* err = c->at<int32_t>(c->L.err);
+  TreeAcceptArgs ta{};
+  ta.p = d_p; ta.p_rows = 1 + n_chains * (B - 1);
+  ta.q = d_q; ta.q_rows = B;
+  ta.chains = d_chains; ta.seq_ids = d_seq_ids; ta.pos = d_pos; ta.iter = d_iter;
+  ta.K = n_chains; ta.B = B; ta.V = V; ta.seed = c->cfg.seed;
+  ta.resid = c->at<uint64_t>(c->L.tree_res);
+  ta.path = c->at<int32_t>(c->L.tree_path);
+  ta.k_out = c->at<int32_t>(c->L.acc_k);
+  ta.kstar = c->at<int32_t>(c->L.tree_kstar);
+  ta.z = c->at<int32_t>(c->L.acc_z);
+  ta.desc = c->at<RowDesc>(c->L.desc);
+  ta.err = err;
+  UNO_HIP(c, launch_tree_accept(ta, n, s));
+  UNO_HIP(c, launch_cdf(ta.desc, n, V, c->at<uint64_t>(c->L.chunk_tot), err, s));
+  UNO_HIP(c, launch_accept_commit(n, B, ta.path, ta.k_out, ta.z, d_seq_ids, d_out, d_n_out, nullptr,
+                                  nullptr, nullptr, s));
+  if (d_kstar)
+    UNO_HIP(c, hipMemcpyAsync(d_kstar, ta.kstar, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, s));
+  return UNO_OK;
 }
 
 uno_status uno_accept(uno_ctx* c, int32_t n, const float* d_p, const float* d_q, const int32_t* d_draft,

@@ -26,7 +26,8 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_distill_forward", "uno_pack_weight", "uno_top_p", "uno_accept_noalloc",
             "uno_set_trace", "uno_query_backward_bytes", "uno_set_distill_checkpoint",
             "uno_tv_backward", "uno_lm_head_backward", "uno_lora_layer_backward",
-            "uno_distill_backward")
+            "uno_distill_backward", "uno_tree_draft", "uno_tree_verify", "uno_tree_step",
+            "uno_tree_accept")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -46,7 +47,8 @@ class UnoConfigC(C.Structure):
                [("lora_alpha", C.c_float), ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + \
                [(n, C.c_int32) for n in ("block_size", "page_size", "max_seqs", "max_seq_len",
                                          "n_pages", "max_rows", "dtype")] + \
-               [("seed", C.c_uint64), ("top_p", C.c_float), ("qk_norm", C.c_int32)]
+               [("seed", C.c_uint64), ("top_p", C.c_float), ("qk_norm", C.c_int32),
+                ("tree_chains", C.c_int32)]
 
 
 PP = C.POINTER(C.c_void_p)
@@ -91,6 +93,10 @@ def lib():
         L.uno_draft.argtypes = [vp, i32, P(i32), vp, vp]
         L.uno_verify.argtypes = [vp, i32, P(i32), vp, vp, vp]
         L.uno_step.argtypes = [vp, i32, P(i32), vp, vp]
+        L.uno_tree_draft.argtypes = [vp, i32, P(i32), i32, vp, vp]
+        L.uno_tree_verify.argtypes = [vp, i32, P(i32), vp, vp, vp, vp]
+        L.uno_tree_step.argtypes = [vp, i32, P(i32), i32, vp, vp]
+        L.uno_tree_accept.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.uno_accept.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.uno_sample.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
         L.uno_accept_noalloc.argtypes = [u64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -128,7 +134,7 @@ def lib():
 
 
 def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, seed=0,
-                top_p=0.0):
+                top_p=0.0, tree_chains=0):
     """uno_config for a configs.UnoConfig plus decoding limits."""
     max_seq_len = max_seq_len or cfg.max_len
     pages_per_seq = -(-max_seq_len // cfg.page_size)
@@ -146,6 +152,7 @@ def make_config(cfg, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None, 
     c.seed = seed
     c.top_p = top_p
     c.qk_norm = 1 if getattr(cfg, "qk_norm", False) else 0
+    c.tree_chains = tree_chains
     return c
 
 
@@ -170,14 +177,15 @@ class Engine:
     """A libuno context over torch-allocated device memory."""
 
     def __init__(self, cfg, weights, max_seqs=1, max_seq_len=None, n_pages=None, max_rows=None,
-                 seed=0, device="cuda", stream=None, top_p=0.0):
+                 seed=0, device="cuda", stream=None, top_p=0.0, tree_chains=0):
         import torch
         self.torch = torch
         self.cfg = cfg
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed, top_p)
+        self.ccfg = make_config(cfg, max_seqs, max_seq_len, n_pages, max_rows, seed, top_p,
+                                tree_chains)
         self.n_pages = self.ccfg.n_pages
         kv_bytes, ws_bytes = query_sizes(self.ccfg)
         self.kv = torch.empty(max(kv_bytes, 1), dtype=torch.uint8, device=self.device)
@@ -291,6 +299,52 @@ class Engine:
         self._check(lib().uno_accept(self.h, n, _ptr(p), _ptr(q), _ptr(draft), _ptr(seq_ids),
                                      _ptr(pos), _ptr(iters), _ptr(out), _ptr(n_out)))
         return out, n_out
+
+    def tree_draft(self, seq_ids, n_chains, want_probs=False):
+        """uno_tree_draft: (chains [n, K, B], draft laws [n, B, V] or None)."""
+        ids, pids = _i32(seq_ids)
+        B, V = self.cfg.block_size, self.cfg.vocab
+        ch = self._empty((len(ids), n_chains, B), self.torch.int32)
+        pr = self._empty((len(ids), B, V), self.torch.float32) if want_probs else None
+        self._check(lib().uno_tree_draft(self.h, len(ids), pids, n_chains, _ptr(ch), _ptr(pr)))
+        return ch, pr
+
+    def tree_verify(self, seq_ids, n_chains, want_probs=False):
+        """uno_tree_verify: (out [n, B+1], n_out [n], kstar [n], verify laws
+        [n, 1 + K (B-1), V] or None); n_chains is the pending draft's K."""
+        ids, pids = _i32(seq_ids)
+        B, V = self.cfg.block_size, self.cfg.vocab
+        n = len(ids)
+        out = self._empty((n, B + 1), self.torch.int32)
+        n_out = self._empty((n,), self.torch.int32)
+        kstar = self._empty((n,), self.torch.int32)
+        pr = self._empty((n, 1 + n_chains * (B - 1), V), self.torch.float32) if want_probs else None
+        self._check(lib().uno_tree_verify(self.h, n, pids, _ptr(out), _ptr(n_out), _ptr(kstar),
+                                          _ptr(pr)))
+        return out, n_out, kstar, pr
+
+    def tree_step(self, seq_ids, n_chains, out=None, n_out=None):
+        ids, pids = _i32(seq_ids)
+        B = self.cfg.block_size
+        if out is None:
+            out = self._empty((len(ids), B + 1), self.torch.int32)
+        if n_out is None:
+            n_out = self._empty((len(ids),), self.torch.int32)
+        self._check(lib().uno_tree_step(self.h, len(ids), pids, n_chains, _ptr(out), _ptr(n_out)))
+        return out, n_out
+
+    def tree_accept(self, p, q, chains, seq_ids, pos, iters):
+        """Tree acceptance on given tensors: p [n, 1 + K (B-1), V], q [n, B, V],
+        chains [n, K, B]; seq_ids, pos, iters device int32 [n].  Returns (out, n_out,
+        kstar)."""
+        n, K, B = chains.shape
+        out = self._empty((n, B + 1), self.torch.int32)
+        n_out = self._empty((n,), self.torch.int32)
+        kstar = self._empty((n,), self.torch.int32)
+        self._check(lib().uno_tree_accept(self.h, n, K, _ptr(p), _ptr(q), _ptr(chains), _ptr(seq_ids),
+                                          _ptr(pos), _ptr(iters), _ptr(out), _ptr(n_out),
+                                          _ptr(kstar)))
+        return out, n_out, kstar
 
     def sample(self, w, seq_ids, pos, iters, stream_id):
         rows = w.shape[0]

@@ -99,6 +99,11 @@ typedef struct {
                                off; other values are UNO_ERR_INVALID_ARG.  The
                                distillation backward calls return
                                UNO_ERR_UNSUPPORTED on such a context              */
+  int32_t tree_chains;      /* most chains a tree call may use (0..16; 0, the
+                               default: no tree calls).  The workspace grows by
+                               max_seqs * (vocab * 8 + (1 + tree_chains (B - 1))
+                               * vocab * 4) bytes or so; a tree call on n sequences
+                               also needs max_rows >= n * (1 + K (B - 1))          */
 } uno_config;
 
 /* Weights: host arrays of device pointers, copied at uno_init (the device memory
@@ -215,6 +220,59 @@ uno_status uno_step(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_
 uno_status uno_accept(uno_ctx* ctx, int32_t n, const float* d_p, const float* d_q,
                       const int32_t* d_draft, const int32_t* d_seq_ids, const int32_t* d_pos,
                       const int32_t* d_iter, int32_t* d_out, int32_t* d_n_out);
+
+/* Tree sampler (the batch-1 mode of the Psi-Spec sampler) [summary: a linear
+ * sampler for system throughput and a tree sampler for single-request throughput;
+ * blog Psi-Spec sampler: one-step draft from the noise block, AR rejection keeps
+ * the output law].  The pages lost how the tree's candidates are chosen; the
+ * library reads it as follows.  The draft forward is uno_draft's; K chains share
+ * y_1 and draw depths d = 2..B independently from the draft laws (chain k's draw
+ * uses Philox counter (n + d, stream 0, iteration, k); chain 0 is uno_draft's
+ * block).  The verify forward scores row y_1 at position n+1 and, for each chain,
+ * its depths 2..B at positions n+2..n+B, every row seeing the context through y_1
+ * and its own chain (the chains' K/V go to slots n + 2 + k (B - 1) + d - 2, so
+ * chain 0 sits at its positions): 1 + K (B - 1) rows per sequence, gate 0.
+ * Acceptance walks the depths: the live chains (those matching the accepted path)
+ * are tried in chain order; trial j uses u_j = Philox counter (n + d, stream 1,
+ * iteration, j); trial 0 is uno_verify's float32 test against p_d (the law of the
+ * lowest live chain's previous row), a rejection replaces the target by the
+ * integer residual R_1 = trunc(max(0, p_d - q_d) 2^40) (p_d when empty), later
+ * ones by R_{j+1} = R_j - min(R_j, floor(T_j trunc(q_d 2^40) / 2^40)) (T_j = sum
+ * R_j; kept when empty), and trial j >= 1 accepts c iff (u_j q_d(c)) T_j < R_j(c)
+ * in float64.  When every live chain fails at depth d the step emits d tokens, the
+ * last drawn from the last residual (counter (n + d, stream 2, iteration, 0));
+ * when every depth passes it emits B + 1, the last from the lowest live chain's
+ * bonus law.  The accepted path's K/V end at their positions.  With K = 1 this is
+ * uno_draft + uno_verify draw for draw.  Requires uno_config.tree_chains >= K. */
+
+/* Draft forward plus K chains: d_chains (device int32 [n, K, B], or NULL; entry 0
+ * of every chain is y_1), d_probs as uno_draft.  UNO_ERR_INVALID_ARG for K outside
+ * 1..tree_chains or n (1 + K (B - 1)) > max_rows. */
+uno_status uno_tree_draft(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t n_chains,
+                          int32_t* d_chains, float* d_probs);
+
+/* Verify forward of the pending tree draft, acceptance, K/V of the accepted path,
+ * commit.  d_out [n, B+1], d_n_out [n] as uno_verify; d_kstar (device int32 [n],
+ * or NULL): the lowest chain on the accepted path; d_probs (or NULL): the verify
+ * laws [n, 1 + K (B - 1), V] in row order (y_1, then chain k's depths 2..B).
+ * UNO_ERR_STATE without a matching uno_tree_draft. */
+uno_status uno_tree_verify(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t* d_out,
+                           int32_t* d_n_out, int32_t* d_kstar, float* d_probs);
+
+/* uno_tree_draft followed by uno_tree_verify. */
+uno_status uno_tree_step(uno_ctx* ctx, int32_t n, const int32_t* seq_ids, int32_t n_chains,
+                         int32_t* d_out, int32_t* d_n_out);
+
+/* The tree acceptance on caller-given laws (its parity entry): d_p [n, 1 + K (B-1),
+ * V] verify laws in uno_tree_verify's row order, d_q [n, B, V] the draft laws
+ * (depth d uses row d - 1), d_chains [n, K, B]; d_seq_ids, d_pos, d_iter as
+ * uno_accept.  Outputs d_out [n, B+1], d_n_out [n], d_kstar [n] (or NULL); the
+ * sequence state is not touched.  Needs a context with tree_chains >= 1
+ * (UNO_ERR_UNSUPPORTED otherwise); K <= 16, n <= max_seqs. */
+uno_status uno_tree_accept(uno_ctx* ctx, int32_t n, int32_t n_chains, const float* d_p,
+                           const float* d_q, const int32_t* d_chains, const int32_t* d_seq_ids,
+                           const int32_t* d_pos, const int32_t* d_iter, int32_t* d_out,
+                           int32_t* d_n_out, int32_t* d_kstar);
 
 /* Accept/resample without a context and without allocating anything, for callers
  * that cannot allocate device memory: code under HIP graph capture, tight serving

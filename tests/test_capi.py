@@ -70,6 +70,17 @@ def test_invalid_configs_rejected():
     with pytest.raises(uno.UnoError) as e:
         uno.query_sizes(bad)
     assert e.value.status == 1
+    for bad_k in (-1, 17):
+        bad = uno.make_config(configs.TINY, tree_chains=bad_k)
+        with pytest.raises(uno.UnoError) as e:
+            uno.query_sizes(bad)
+        assert e.value.status == 1
+    # tree chains size the verify laws, the chain table and one residual row per sequence
+    T = configs.TINY
+    t0 = uno.query_sizes(uno.make_config(T, max_seqs=2))[1]
+    t4 = uno.query_sizes(uno.make_config(T, max_seqs=2, tree_chains=4))[1]
+    extra = 2 * (1 + 4 * (T.block_size - 1) - T.block_size) * T.vocab * 4 + 2 * T.vocab * 8
+    assert extra <= t4 - t0 <= extra + 8192
     # QK-norm adds one float32 q|k|v staging buffer of max_rows rows to the workspace
     c0, c1 = uno.make_config(configs.TINY), uno.make_config(configs.TINY.with_(qk_norm=True))
     assert c1.qk_norm == 1
