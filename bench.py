@@ -516,7 +516,7 @@ def main():
                          "each ('none' skips them)")
     ap.add_argument("--tree-steps", type=int, default=40,
                     help="timed steps of the batch-1 tree-sampler leg (0: skip)")
-    ap.add_argument("--tree-chains", type=str, default="2,4",
+    ap.add_argument("--tree-chains", type=str, default="2,3,4",
                     help="chain counts of the tree-sampler leg")
     ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
                     help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")

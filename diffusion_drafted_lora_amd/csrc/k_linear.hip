@@ -551,6 +551,162 @@ k_gemm_bf16(GemmArgs a) {
 }
 
 
+// Few-row product without a LoRA phase over 17..64 rows (the tree sampler's
+// verify, verifies of two to four sequences): every weight block a wave streams
+// is multiplied against the activations of all MT row tiles, so the weights are
+// read from memory once per launch instead of once per 16-row tile.  Otherwise
+// as k_gemm_bf16 (WAVES waves split K, KU blocks in flight per wave, fixed-order
+// wave reduction in LDS, the same epilogues); row tiles past the rows are skipped.
+template <int NT, int WAVES, int KU, int MT>
+__global__ void __launch_bounds__(WAVES * 64)
+k_gemm_bf16_rows(GemmArgs a) {
+  static_assert(WAVES >= 4, "threads 0..255 own the 256 outputs of a tile");
+  __shared__ float red[WAVES][MT][NT][256];
+  __shared__ float fin[MT][256];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = blockIdx.x, mt0 = blockIdx.y * MT;
+  const int mtiles = (a.M + 15) / 16;
+  const int r16 = lane & 15;
+  const int nkb = a.K / 32;
+  const bf16* Wp[NT];
+  int tile0, col_paired = 0;
+  if (a.paired) {
+    col_paired = grp * 16;
+    tile0 = grp;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      Wp[t] = reinterpret_cast<const bf16*>(a.seg[t].W) + (size_t)grp * nkb * 512 + lane * 8;
+  } else {
+    tile0 = grp * NT;
+    const GemmSeg& sg = a.seg[find_seg(a, tile0 * 16)];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      Wp[t] = reinterpret_cast<const bf16*>(sg.W) + (size_t)(tile0 + t - sg.n0 / 16) * nkb * 512 +
+              lane * 8;
+  }
+  if (a.zero_ptr) {
+    const long nwg = (long)gridDim.x * gridDim.y, wg = (long)blockIdx.y * gridDim.x + grp;
+    const long share = ((long)a.zero_n + nwg - 1) / nwg;
+    const long z0 = wg * share, z1 = min((long)a.zero_n, z0 + share);
+    for (long i = z0 + threadIdx.x; i < z1; i += WAVES * 64) a.zero_ptr[i] = 0;
+  }
+  const bf16* Xp[MT];
+  bool tile_ok[MT];
+  i64x2 ssq0[MT], ssq1[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+    const int mt = mt0 + mi;
+    tile_ok[mi] = mt < mtiles;
+    Xp[mi] = reinterpret_cast<const bf16*>(a.X) + (size_t)(tile_ok[mi] ? mt : 0) * nkb * 512 + lane * 8;
+    ssq0[mi] = i64x2{0, 0};
+    ssq1[mi] = i64x2{0, 0};
+    if (a.ss_in && mt * 16 + (lane >> 2) < a.M) {
+      const i64x2* sp = reinterpret_cast<const i64x2*>(
+          a.ss_in + (size_t)(mt * 16 + (lane >> 2)) * SS_BANKS + (lane & 3) * 4);
+      ssq0[mi] = sp[0];
+      ssq1[mi] = sp[1];
+    }
+  }
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int jb = w * nkb / WAVES, je = (w + 1) * nkb / WAVES;
+  const int nfull = (je - jb) / KU, rem = (je - jb) % KU;
+  const bf16x8 zero8 = {};
+  bf16x8 ax[MT][KU], bw[NT][KU];
+  auto fill = [&](int u, int j) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) ax[mi][u] = tile_ok[mi] ? load8(Xp[mi] + (size_t)j * 512) : zero8;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bw[t][u] = load8_stream(Wp[t] + (size_t)j * 512);
+  };
+  auto consume = [&](int u) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[mi][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[mi][u], bw[t][u], acc[mi][t], 0, 0, 0);
+  };
+  int j = jb;
+  if (nfull > 0) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) fill(u, j + u);
+    for (int i = 1; i < nfull; ++i) {
+      j += KU;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        consume(u);
+        fill(u, j + u);
+      }
+    }
+    j += KU;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      consume(u);
+      if (u < rem) fill(u, j + u);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+      if (u < rem) fill(u, j + u);
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u)
+    if (u < rem) consume(u);
+  if (a.ss_in) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      long long sq = ssq0[mi].x + ssq0[mi].y + ssq1[mi].x + ssq1[mi].y;
+      if (w == 0) ss_check(ssq0[mi].x | ssq0[mi].y | ssq1[mi].x | ssq1[mi].y, a.err);
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long tot = __shfl(sq, ((lane >> 4) * 4 + i) * 4);
+        const float rs = 1.0f / sqrtf(fx_to_float(tot) * a.inv_d + a.eps);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[mi][t][i] *= rs;
+      }
+    }
+  }
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w][mi][t][((lane >> 4) * 4 + i) * 16 + r16] = acc[mi][t][i];
+  __syncthreads();
+  const int e = threadIdx.x & 255;
+  float v[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float sum = 0.0f;
+      for (int ww = 0; ww < WAVES; ++ww) sum += red[ww][mi][t][e];
+      v[mi][t] = sum;
+    }
+  if (threadIdx.x < 256)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) fin[mi][e] = v[mi][0];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int row = e >> 4, c = e & 15;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      if (!tile_ok[mi]) continue;
+      const int m = (mt0 + mi) * 16 + row;
+      if (a.epi == EPI_LOGITS) logits_epilogue<NT>(a, m, c, tile0, v[mi], m < a.M);
+      else epilogue<bf16, NT>(a, m, c, tile0, col_paired, v[mi], fin[mi][row * 16 + (c ^ 8)], m < a.M);
+    }
+  }
+}
+
+
 // Eight consecutive finished columns col .. col+7 (col % 8 == 0) of row m of the
 // large-M kernel: v holds them, vp the eight of columns col ^ 8 (the RoPE
 // partners inside the 16-column tile).  Stores are 16 / 32 bytes wide.  EPI_RESID
@@ -1374,6 +1530,16 @@ hipError_t launch_skinny(const GemmArgs& a, int n_cols_total, int mtiles, hipStr
   return hipGetLastError();
 }
 
+// Few-row launch without a LoRA phase over MT = 4 row tiles per workgroup.
+template <int NT, int WAVES, int KU>
+hipError_t launch_skinny_rows(const GemmArgs& a, int n_cols_total, int mtiles, hipStream_t s) {
+  const int per_wg = a.paired ? 16 : 16 * NT;
+  if (n_cols_total % per_wg) return hipErrorInvalidValue;
+  uno_launch(k_gemm_bf16_rows<NT, WAVES, KU, 4>, dim3(n_cols_total / per_wg, (mtiles + 3) / 4),
+             WAVES * 64, 0, s, a);
+  return hipGetLastError();
+}
+
 template <>
 hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
@@ -1387,6 +1553,17 @@ hipError_t launch_gemm<bf16>(const GemmArgs& a, int n_cols_total, hipStream_t s)
   }
   const int mtiles = (a.M + 15) / 16;
   const int nkb = a.K / 32;
+  // 17..64 rows without a LoRA phase: the weights are streamed once for all row
+  // tiles (shapes as the single-tile launches below, but two-tile workgroups keep
+  // 2 blocks in flight per wave so that their registers allow every gate/up
+  // workgroup to be resident at once)
+  if (mtiles > 1 && a.r == 0 && a.n_prod == 0 && nkb >= 64) {
+    if (a.paired) return launch_skinny_rows<2, 4, 2>(a, n_cols_total, mtiles, s);
+    if (a.epi == EPI_LOGITS && n_cols_total % 32 == 0 && a.nseg == 1)
+      return launch_skinny_rows<2, 4, 2>(a, n_cols_total, mtiles, s);
+    if (a.epi == EPI_QKV) return launch_skinny_rows<UNO_SK_QKV>(a, n_cols_total, mtiles, s);
+    return launch_skinny_rows<UNO_SK_O>(a, n_cols_total, mtiles, s);
+  }
   // Launch shapes measured at the 8B decode shapes (one MI355X): many small
   // workgroups beat few large ones -- the paired gate/up tiles at 4 waves of 4
   // blocks in flight, q|k|v at 8 waves of 2, o at 12 of 2, down at 12 of 2, the LM

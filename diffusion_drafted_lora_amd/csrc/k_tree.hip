@@ -49,23 +49,46 @@ __device__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
   return t;
 }
 
+// The passes over the vocabulary take four entries per thread and step (16-byte
+// loads of p and q, two 16-byte stores of R; the vocabulary is a multiple of 16)
+// and keep several steps' loads in flight: one workgroup streams the rows.
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+
 // R_1 = trunc(max(0, p - q) * 2^40), or trunc(p * 2^40) when that has no mass;
 // returns its sum.
 __device__ uint64_t resid_first(const float* p, const float* q, uint64_t* R, int V,
                                 uint64_t* red, int32_t* err) {
+  const f4_t* p4 = reinterpret_cast<const f4_t*>(p);
+  const f4_t* q4 = reinterpret_cast<const f4_t*>(q);
+  u64x2_t* R2 = reinterpret_cast<u64x2_t*>(R);
   uint64_t sum = 0;
-  for (int x = threadIdx.x; x < V; x += TREE_THREADS) {
-    const uint64_t w = int_weight(fmaxf(p[x] - q[x], 0.0f), err);
-    R[x] = w;
-    sum += w;
+#pragma unroll 4
+  for (int x = threadIdx.x; x < V / 4; x += TREE_THREADS) {
+    const f4_t pv = p4[x], qv = q4[x];
+    uint64_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[e] = int_weight(fmaxf(pv[e] - qv[e], 0.0f), err);
+      sum += w[e];
+    }
+    R2[2 * x] = u64x2_t{w[0], w[1]};
+    R2[2 * x + 1] = u64x2_t{w[2], w[3]};
   }
   uint64_t T = block_sum_u64(sum, red);
   if (T == 0) {
     sum = 0;
-    for (int x = threadIdx.x; x < V; x += TREE_THREADS) {
-      const uint64_t w = int_weight(p[x], err);
-      R[x] = w;
-      sum += w;
+#pragma unroll 4
+    for (int x = threadIdx.x; x < V / 4; x += TREE_THREADS) {
+      const f4_t pv = p4[x];
+      uint64_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[e] = int_weight(pv[e], err);
+        sum += w[e];
+      }
+      R2[2 * x] = u64x2_t{w[0], w[1]};
+      R2[2 * x + 1] = u64x2_t{w[2], w[3]};
     }
     T = block_sum_u64(sum, red);
   }
@@ -83,11 +106,25 @@ __device__ uint64_t resid_entry(uint64_t r, float qv, uint64_t T) {
 
 // R_{j+1} in place (R_j kept when the update leaves no mass); returns its sum.
 __device__ uint64_t resid_next(const float* q, uint64_t* R, int V, uint64_t T, uint64_t* red) {
+  const f4_t* q4 = reinterpret_cast<const f4_t*>(q);
+  u64x2_t* R2 = reinterpret_cast<u64x2_t*>(R);
   uint64_t sum = 0;
-  for (int x = threadIdx.x; x < V; x += TREE_THREADS) sum += resid_entry(R[x], q[x], T);
+#pragma unroll 4
+  for (int x = threadIdx.x; x < V / 4; x += TREE_THREADS) {
+    const f4_t qv = q4[x];
+    const u64x2_t r0 = R2[2 * x], r1 = R2[2 * x + 1];
+    sum += resid_entry(r0.x, qv[0], T) + resid_entry(r0.y, qv[1], T) +
+           resid_entry(r1.x, qv[2], T) + resid_entry(r1.y, qv[3], T);
+  }
   const uint64_t T2 = block_sum_u64(sum, red);
   if (T2 == 0) return T;
-  for (int x = threadIdx.x; x < V; x += TREE_THREADS) R[x] = resid_entry(R[x], q[x], T);
+#pragma unroll 4
+  for (int x = threadIdx.x; x < V / 4; x += TREE_THREADS) {
+    const f4_t qv = q4[x];
+    const u64x2_t r0 = R2[2 * x], r1 = R2[2 * x + 1];
+    R2[2 * x] = u64x2_t{resid_entry(r0.x, qv[0], T), resid_entry(r0.y, qv[1], T)};
+    R2[2 * x + 1] = u64x2_t{resid_entry(r1.x, qv[2], T), resid_entry(r1.y, qv[3], T)};
+  }
   __syncthreads();
   return T2;
 }
@@ -228,7 +265,8 @@ hipError_t launch_tree_draft_desc(const float* probs, int n, int K, int B, int V
 
 hipError_t launch_tree_accept(const TreeAcceptArgs& a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (a.K < 1 || a.K > TREE_KMAX || a.B < 1 || a.p_rows < 1 + a.K * (a.B - 1) || a.q_rows < a.B)
+  if (a.K < 1 || a.K > TREE_KMAX || a.B < 1 || a.p_rows < 1 + a.K * (a.B - 1) || a.q_rows < a.B ||
+      a.V % 4 != 0)
     return hipErrorInvalidValue;
   uno_launch(k_tree_accept, n, TREE_THREADS, 0, s, a);
   return hipGetLastError();

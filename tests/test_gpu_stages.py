@@ -69,15 +69,17 @@ def test_layer_stages_batch1(ctx):
     eng.sync()
 
 
-def test_layer_stages_three_sequences():
-    """48 rows (three row tiles of the few-row kernels, each with its own LoRA
-    down-projection producers): three sequences of 16 draft rows at contexts 1024,
-    700 and 3000."""
+@pytest.mark.parametrize("lora", [True, False])
+def test_layer_stages_three_sequences(lora):
+    """48 rows: three sequences of 16 draft rows at contexts 1024, 700 and 3000.
+    With the adapter, three row tiles of the few-row kernels, each with its own
+    LoRA down-projection producers; without it, the kernel that multiplies each
+    weight block against all three row tiles."""
     import torch
     ctxs, rows = [1024, 700, 3000], 16
     n = len(ctxs)
-    log("stages 3 sequences x 16 rows")
-    w = synth.weights_numpy(CFG, 1001, with_embed=False)
+    log(f"stages 3 sequences x 16 rows, lora={lora}")
+    w = synth.weights_numpy(CFG, 1001, with_embed=False, with_lora=lora)
     lw = w["layers"][0]
     eng = engine(CFG, w, max_seqs=n, max_seq_len=3000 + 64, max_rows=n * rows)
     gen = torch.Generator(device="cuda").manual_seed(7321)
