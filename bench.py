@@ -223,6 +223,63 @@ def run_tree(cfg, w, dev, chains, steps, warmup, prompt_len):
     return res
 
 
+def run_qk_norm(cfg, w, dev, steps, warmup, prompt_len):
+    """Batch-1 decode of the same model with the per-head QK RMSNorm off and on
+    (unit gains added to the same weights), on the headline's prompt and seed: step
+    time, accepted tokens/s, and the time of the norm kernels (the difference of
+    the misc class, where they are timed, between the two runs)."""
+    import torch
+    from diffusion_drafted_lora_amd import synth, uno
+
+    B = cfg.block_size
+    res = {}
+    for on in (False, True):
+        c = cfg.with_(qk_norm=on)
+        wq = w
+        if on:
+            ones = torch.ones(cfg.head_dim, dtype=torch.bfloat16, device=dev)
+            wq = dict(w)
+            wq["layers"] = [dict(lw, q_norm=ones, k_norm=ones) for lw in w["layers"]]
+        max_len = prompt_len + (warmup + steps + 8) * (B + 1) + B + 2
+        eng = uno.Engine(c, wq, max_seqs=1, max_seq_len=max_len, max_rows=256, seed=3002,
+                         device=dev)
+        prompt = synth.prompts(cfg, 2002, 1, prompt_len)[0]
+        log(f"qk-norm {'on' if on else 'off'}: prefill {prompt_len} tokens")
+        eng.prefill([0], [prompt])
+        outs = torch.empty((1, B + 1), dtype=torch.int32, device=dev)
+        nouts = torch.empty((warmup + steps,), dtype=torch.int32, device=dev)
+        for i in range(warmup):
+            eng.step([0], out=outs, n_out=nouts[i:i + 1])
+        eng.sync()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            eng.step([0], out=outs, n_out=nouts[i:i + 1])
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        eng.sync()
+        tok = int(nouts[warmup:].sum().item())
+        eng.timing(["misc"])
+        for i in range(4):
+            eng.step([0])
+        eng.sync()
+        n_m, ms_m, _, _ = eng.timing_read("misc")
+        eng.timing([])
+        res["on" if on else "off"] = {"ms_per_step": 1e3 * sec / steps,
+                                      "accepted_tokens_per_s": tok / sec,
+                                      "tokens_per_forward": tok / (2.0 * steps),
+                                      "misc_ms_per_step": ms_m / 4, "misc_launches_per_step": n_m / 4}
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+    extra = res["on"]["misc_launches_per_step"] - res["off"]["misc_launches_per_step"]
+    res["norm_kernel_us_per_launch"] = (
+        1e3 * (res["on"]["misc_ms_per_step"] - res["off"]["misc_ms_per_step"]) / extra if extra else None)
+    res["norm_launches_per_step"] = extra
+    res["steps"] = steps
+    return res
+
+
 def run_bytes_per_iteration(cfg, contexts):
     """Mean algorithmic bytes of a batch-1 iteration over contexts [c0, c_last]: both
     forwards' weights, the draft's LoRA and the K/V of the context read twice (the
@@ -518,6 +575,8 @@ def main():
                     help="timed steps of the batch-1 tree-sampler leg (0: skip)")
     ap.add_argument("--tree-chains", type=str, default="2,3,4",
                     help="chain counts of the tree-sampler leg")
+    ap.add_argument("--qk-norm-steps", type=int, default=40,
+                    help="timed steps of the batch-1 QK-norm leg (0: skip)")
     ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
                     help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -663,6 +722,8 @@ def main():
             run["hbm_gbs_algorithmic"] = run_bytes_per_iteration(cfg, run["contexts"]) / 1e9 / \
                 (run["mean_ms_per_step"] / 1e3)
             run["hbm_frac"] = run["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
+    if args.qk_norm_steps > 0:
+        result["qk_norm"] = run_qk_norm(cfg, w, dev, args.qk_norm_steps, 4, args.prompt)
     if args.tree_steps > 0:
         result["tree"] = run_tree(cfg, w, dev, [int(k) for k in args.tree_chains.split(",")],
                                   args.tree_steps, 4, args.prompt)
