@@ -38,18 +38,21 @@ def _i32(a):
     return dev(np.asarray(a, dtype=np.int32))
 
 
-def test_tree_decode_matches_oracle(stress_w):
+@pytest.mark.parametrize("top_p", [0.0, 0.9])
+def test_tree_decode_matches_oracle(stress_w, top_p):
+    """With top-p 0.9 both sides truncate every draft and verify row to its nucleus
+    before drawing and accepting."""
     K, S, seed = 3, 5, 3300
     lens = [16, 9, 1, 16, 4]
     prompts = [synth.prompts(TINY, 2300 + i, 1, L)[0] for i, L in enumerate(lens)]
     ids = [4, 0, 2, 1, 3]
     B = TINY.block_size
     cap = TINY.max_len + 60
-    log(f"tiny tree decode K={K}")
+    log(f"tiny tree decode K={K} top_p={top_p}")
     eng = engine(TINY, stress_w, max_seqs=S, max_seq_len=cap, seed=seed,
-                 max_rows=S * (1 + K * (B - 1)), tree_chains=K)
+                 max_rows=S * (1 + K * (B - 1)), tree_chains=K, top_p=top_p)
     eng.prefill(ids, prompts)
-    dec = tree.TreeDecoder(TINY, stress_w, ids, seed, cap)
+    dec = tree.TreeDecoder(TINY, stress_w, ids, seed, cap, top_p=top_p if top_p > 0 else 1.0)
     dec.prefill(prompts)
     seen_side = False
     for step in range(8):
