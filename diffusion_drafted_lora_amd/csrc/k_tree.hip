@@ -277,7 +277,7 @@ hipError_t launch_tree_kv_move(const KvLayout& kv, int n, int B, int n_layers,
                                const int32_t* call_seq, const int32_t* call_n,
                                const int32_t* k_out, const int32_t* kstar, int32_t* err,
                                hipStream_t s) {
-  if (n <= 0 || B < 3) return hipSuccess;
+  if (n <= 0 || B < 2) return hipSuccess;       // B = 1: no drafted depth to move
   uno_launch(k_tree_kv_move<T>, dim3(n, n_layers * 2 * kv.n_kv_heads), 256, 0, s, kv, B, call_seq,
              call_n, k_out, kstar, err);
   return hipGetLastError();

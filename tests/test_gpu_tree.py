@@ -38,21 +38,21 @@ def _i32(a):
     return dev(np.asarray(a, dtype=np.int32))
 
 
-@pytest.mark.parametrize("top_p", [0.0, 0.9])
-def test_tree_decode_matches_oracle(stress_w, top_p):
-    """With top-p 0.9 both sides truncate every draft and verify row to its nucleus
-    before drawing and accepting."""
-    K, S, seed = 3, 5, 3300
+@pytest.mark.parametrize("B,K,top_p", [(4, 3, 0.0), (4, 3, 0.9), (2, 2, 0.0), (1, 2, 0.0)])
+def test_tree_decode_matches_oracle(stress_w, B, K, top_p):
+    """Blocks of 4 (with and without top-p 0.9: both sides truncate every draft
+    and verify row to its nucleus), 2 and 1 (no drafted depth: y_1 and the bonus)."""
+    S, seed = 5, 3300
     lens = [16, 9, 1, 16, 4]
-    prompts = [synth.prompts(TINY, 2300 + i, 1, L)[0] for i, L in enumerate(lens)]
+    cfg = TINY.with_(block_size=B)
+    prompts = [synth.prompts(cfg, 2300 + i, 1, L)[0] for i, L in enumerate(lens)]
     ids = [4, 0, 2, 1, 3]
-    B = TINY.block_size
-    cap = TINY.max_len + 60
-    log(f"tiny tree decode K={K} top_p={top_p}")
-    eng = engine(TINY, stress_w, max_seqs=S, max_seq_len=cap, seed=seed,
-                 max_rows=S * (1 + K * (B - 1)), tree_chains=K, top_p=top_p)
+    cap = cfg.max_len + 60
+    log(f"tiny tree decode B={B} K={K} top_p={top_p}")
+    eng = engine(cfg, stress_w, max_seqs=S, max_seq_len=cap, seed=seed,
+                 max_rows=S * max(B, 1 + K * (B - 1)), tree_chains=K, top_p=top_p)
     eng.prefill(ids, prompts)
-    dec = tree.TreeDecoder(TINY, stress_w, ids, seed, cap, top_p=top_p if top_p > 0 else 1.0)
+    dec = tree.TreeDecoder(cfg, stress_w, ids, seed, cap, top_p=top_p if top_p > 0 else 1.0)
     dec.prefill(prompts)
     seen_side = False
     for step in range(8):
@@ -63,7 +63,7 @@ def test_tree_decode_matches_oracle(stress_w, top_p):
         assert np.array_equal(host(ch_g), own.astype(np.int32)), step
         out_g, n_g, ks_g, pv_g = eng.tree_verify(ids, K, want_probs=True)
         r = dec.step_tree(K)
-        assert _tv(host(pd_g), r["P_d"]).max() <= TV_TOL
+        assert _tv(host(pd_g), r["P_d"]).max() <= TV_TOL, step
         assert np.array_equal(host(ch_g), r["chains"].astype(np.int32)), step
         assert _tv(host(pv_g), r["P_v"]).max() <= TV_TOL, step
         assert np.array_equal(host(out_g), r["out"]), step
@@ -168,12 +168,14 @@ def _accept_engine(B, V, S, seed):
     return engine(cfg, w, max_seqs=S, seed=seed, max_seq_len=64, tree_chains=4)
 
 
-def test_one_chain_equals_the_linear_step(stress_w):
-    S, seed, B = 3, 3600, TINY.block_size
-    prompts = list(synth.prompts(TINY, 2600, S))
+@pytest.mark.parametrize("B", [4, 2, 1])
+def test_one_chain_equals_the_linear_step(stress_w, B):
+    S, seed = 3, 3600
+    cfg = TINY.with_(block_size=B)
+    prompts = list(synth.prompts(cfg, 2600, S))
     ids = [0, 1, 2]
-    lin = engine(TINY, stress_w, max_seqs=S, seed=seed)
-    tr = engine(TINY, stress_w, max_seqs=S, seed=seed, max_rows=S * B, tree_chains=1)
+    lin = engine(cfg, stress_w, max_seqs=S, seed=seed)
+    tr = engine(cfg, stress_w, max_seqs=S, seed=seed, max_rows=S * B, tree_chains=1)
     lin.prefill(ids, prompts)
     tr.prefill(ids, prompts)
     for step in range(6):
