@@ -604,6 +604,13 @@ constexpr int RSTAGE = RMK * HD * 2 * 2;        // one stage: K and V of RMK key
 constexpr int RVOFF = RMK * HD * 2;             // V part of a stage
 constexpr int RLOADS = RSTAGE / 1024 / 4;       // 1 KB load instructions per wave and stage
 
+// Windowed rows (WIN: the distillation forward's [x, z1] rows, the tree verify's
+// chains) number their keys in whole pages: virtual pages below A16 = A rounded up
+// to a page are the slots' own pages, the rest continue at the page of C rounded
+// down (A = max a, C = min c, over the tile's rows).  The two ranges may share a
+// page; each occurrence of a slot is masked by its own range -- slot < a in the
+// first, c <= slot <= d in the second -- so no row sees a slot twice.
+template <bool WIN>
 __global__ void __launch_bounds__(256, 1)
 k_attn_ring(AttnArgs a, KvLayout kv) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -636,8 +643,21 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   }
   const float sc = a.scale * 1.4426950408889634f;    // scores in the exp2 domain
   __syncthreads();
-  int At, Ct, nv;
-  tile_window(sW, &At, &Ct, &nv);
+  int A16 = 0, C16 = 0, Am = 0, nv;
+  if (WIN) {
+    int am = 0, cm = INT_MAX, dm = -1;
+    for (int i = 0; i < 16; ++i) {
+      am = max(am, sW[i]);
+      if (sW[16 + i] <= sW[32 + i]) { cm = min(cm, sW[16 + i]); dm = max(dm, sW[32 + i]); }
+    }
+    Am = am;
+    A16 = (am + 15) & ~15;
+    C16 = dm >= cm ? (cm & ~15) : A16;
+    nv = A16 + (dm >= cm ? dm - C16 + 1 : 0);
+  } else {
+    int At, Ct;
+    tile_window(sW, &At, &Ct, &nv);
+  }
   publish_nc(a, c, kvh, tid, r0, nrows, nv);
   const int kbeg = c * a.chunk;
   if (kbeg >= nv) return;
@@ -649,8 +669,9 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   const int p0 = kbeg >> 4, npg = nsub * RPG;
   const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
   for (int i = tid; i < npg; i += 256) {
-    const int pi = p0 + i;
-    int page = (pi < kv.max_pages_per_seq && (pi << 4) < kend) ? bt[pi] : 0;
+    const int vp = p0 + i;
+    const int pi = (WIN && vp >= (A16 >> 4)) ? (C16 >> 4) + vp - (A16 >> 4) : vp;
+    int page = (pi < kv.max_pages_per_seq && (vp << 4) < kend) ? bt[pi] : 0;
     sPg[i] = (page >= 0 && page < kv.n_pages) ? page : 0;
   }
   const size_t pstride = (size_t)kv.n_kv_heads * 16 * HD;
@@ -688,9 +709,13 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
 #pragma unroll
   for (int d = 0; d < HD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int lim[4];
+  int lim[4], wc[4], wd[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lim[i] = min(kend, sW[grp * 4 + i]);
+  for (int i = 0; i < 4; ++i) {
+    lim[i] = WIN ? sW[grp * 4 + i] : min(kend, sW[grp * 4 + i]);
+    wc[i] = WIN ? sW[16 + grp * 4 + i] : 0;
+    wd[i] = WIN ? sW[32 + grp * 4 + i] : 0;
+  }
   bf16* myP = sP + w * 16 * RPPAD;
 
 #pragma unroll
@@ -707,11 +732,17 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
     const int k0 = kbeg + it * RMK;
     const char* stK = smem_raw + (size_t)(it % RNS) * RSTAGE;
     const char* stV = stK + RVOFF;
-    if (k0 + RMK > kend) {
-      // zero the V entries of keys at or past the chunk end (tokens of this stage)
+    // zero the V entries of keys no row may see whose slots need not hold data:
+    // keys at or past the chunk end and, windowed, the first range's slots
+    // [A, A16) up to its page end (tokens of this stage, relative indices)
+    const int z0 = min(RMK, max(kend, k0) - k0);
+    const int g0 = WIN ? max(Am, k0) - k0 : RMK, g1 = WIN ? min(A16, k0 + RMK) - k0 : 0;
+    if (z0 < RMK || g0 < g1) {
       bf16* zV = reinterpret_cast<bf16*>(const_cast<char*>(stV));
-      for (int e = tid; e < (k0 + RMK - kend) * HD; e += 256) {
-        const int kk = kend - k0 + e / HD, d = e % HD;
+      const int nz = RMK - z0, ng = g0 < g1 ? g1 - g0 : 0;
+      for (int e = tid; e < (nz + ng) * HD; e += 256) {
+        const int t = e / HD, d = e % HD;
+        const int kk = t < nz ? z0 + t : g0 + (t - nz);
         const int pg = kk >> 4, tk = kk & 15, h = (tk >> 3) ^ ((d >> 3) & 1);
         zV[(pg * 4096 + d * 32 + h * 16) / 2 + (tk & 7)] = (bf16)0.0f;
       }
@@ -731,7 +762,8 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
         s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[j], 0, 0, 0);
       }
     }
-    // mask (row grp*4+i sees keys below lim[i]) and the online softmax
+    // mask (row grp*4+i sees keys below lim[i]; windowed rows: their slot ranges)
+    // and the online softmax
     float mt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -739,7 +771,15 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         float v = s[j][i] * sc;
-        if (k0 + j * 16 + r16 >= lim[i]) v = -INFINITY;
+        const int kk = k0 + j * 16 + r16;
+        bool hide;
+        if (WIN) {
+          const int sl = kk < A16 ? kk : C16 + (kk - A16);
+          hide = kk >= kend || (kk < A16 ? sl >= lim[i] : (sl < wc[i] || sl > wd[i]));
+        } else {
+          hide = kk >= lim[i];
+        }
+        if (hide) v = -INFINITY;
         s[j][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -834,14 +874,16 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
         if (ea != hipSuccess) return ea;
       }
     }
-    const bool ring = !a.row_vis && kv.page_size == 16 && a.chunk % 64 == 0 &&
-                      a.chunk >= kAttnRingMinChunk && a.chunk <= PGC * 16;
+    const bool ring = kv.page_size == 16 && a.chunk % 64 == 0 && a.chunk >= kAttnRingMinChunk &&
+                      a.chunk <= PGC * 16;
     if (ring) {
       const size_t rsmem = (size_t)RNS * RSTAGE + (size_t)G * 16 * RPPAD * 2;
-      hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_ring),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)rsmem);
+      const void* f = a.row_vis ? reinterpret_cast<const void*>(&k_attn_ring<true>)
+                                : reinterpret_cast<const void*>(&k_attn_ring<false>);
+      hipError_t ea = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rsmem);
       if (ea != hipSuccess) return ea;
-      uno_launch(k_attn_ring, grid, 256, (uint32_t)rsmem, s, a, kv);
+      if (a.row_vis) uno_launch(k_attn_ring<true>, grid, 256, (uint32_t)rsmem, s, a, kv);
+      else uno_launch(k_attn_ring<false>, grid, 256, (uint32_t)rsmem, s, a, kv);
     } else if (a.row_vis) {
       uno_launch(k_attn_mfma<true>, grid, 64 * G, smem, s, a, kv);
     } else {

@@ -584,9 +584,12 @@ uno_status forward_t(uno_ctx* c, const FwdIn& f) {
   const int row_tiles = (f.rows_per_seq + 15) / 16;
   const int groups = f.n * Hkv * row_tiles;
   int target = std::max(1, std::min(kMaxChunks, (kAttnTargetWG + groups - 1) / groups));
-  int chunk = (f.ctx_bound + target - 1) / target;
+  // windowed rows number a tile's keys in whole pages of both ranges: up to 48
+  // more than its rows' slots span
+  const int ctxb = f.ctx_bound + (windowed ? 48 : 0);
+  int chunk = (ctxb + target - 1) / target;
   chunk = std::max(kAttnMinChunk, (chunk + kAttnMinChunk - 1) / kAttnMinChunk * kAttnMinChunk);
-  const int n_chunks = (f.ctx_bound + chunk - 1) / chunk;
+  const int n_chunks = (ctxb + chunk - 1) / chunk;
   if (n_chunks > kMaxChunks || (size_t)R * n_chunks > c->L.part_rows)
     return fail(c, UNO_ERR_INVALID_ARG, "attention chunking exceeds the partial buffers");
 

@@ -215,17 +215,49 @@ def test_tree_call_order_errors(stress_w):
     assert e.value.status == 1
 
 
+def _exact_chain_laws(cfg, wt, prompt, chains, pos):
+    """float64 oracle laws of each chain's block after the prompt, on the same
+    (bf16-valued) weights."""
+    from oracle import model
+
+    def h(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    wn = {"embed": h(wt["embed"]), "lm_head": h(wt["lm_head"]), "final_norm": h(wt["final_norm"]),
+          "layers": [{"attn_norm": h(lw["attn_norm"]), "mlp_norm": h(lw["mlp_norm"]),
+                      "w": {p: h(t) for p, t in lw["w"].items()},
+                      "la": {p: h(t) for p, t in lw["la"].items()},
+                      "lb": {p: h(t) for p, t in lw["lb"].items()}} for lw in wt["layers"]]}
+    cf = cfg.with_(dtype="f32")
+    cache = model.new_cache(cf, 1, int(pos.max()) + 2)
+    toks = np.asarray(prompt, np.int64)
+    model.forward(cf, wn, toks[None], np.arange(len(toks))[None], np.zeros((1, len(toks))), cache,
+                  want_logits=False)
+    out = []
+    for k in range(chains.shape[0]):
+        ck = {"k": cache["k"].copy(), "v": cache["v"].copy()}
+        lg, _ = model.forward(cf, wn, chains[k][None], pos[k][None], np.zeros((1, len(pos[k]))), ck)
+        out.append(model.probs(lg)[0].astype(np.float64))
+    return out
+
+
 def test_tree_verify_bf16_8b_layers_match_plain_forwards():
     """The bf16 kernels at the 8B layer shape (two layers, vocabulary 2048): every
-    row of a K = 3 tree verify (46 rows: the few-row GEMMs, windowed attention,
-    side-chain KV slots) has the law of a plain causal forward of that chain's
-    tokens on a second context (TV <= 1e-3), and after acceptance the accepted
-    path's K/V sit at their positions (within bf16 rounding of the plain forward's)."""
+    row of a K = 3 tree verify (46 rows: the few-row GEMMs over three row tiles,
+    the windowed ring attention, side-chain KV slots) against the float64 oracle
+    of its chain, beside plain causal forwards of the same chains on a second
+    context (16-row GEMM tiles, the plain ring).  Both store the same bf16 values;
+    their attention rounds P to bf16 against running maxima of different key
+    groupings, so they differ from each other by bf16 noise.  The bar: the tree
+    rows are no farther from the exact laws than the plain forwards (x 1.25 +
+    1e-4), and within 1e-2 of them.  After acceptance the accepted path's K/V sit
+    at their positions (within bf16 rounding of the plain forward's)."""
     import torch
     cfg = configs.LAYER8B.with_(n_layers=2, vocab=2048)
     K, B = 3, cfg.block_size
-    log("8B-shape bf16 tree verify vs plain forwards")
-    w = uno.pack_weights(cfg, synth.weights_torch(cfg, 7100, "cuda"))
+    log("8B-shape bf16 tree verify vs plain forwards and the float64 oracle")
+    wt = synth.weights_torch(cfg, 7100, "cuda")
+    w = uno.pack_weights(cfg, wt)
     prompt = synth.prompts(cfg, 7101, 1, 300)[0]
     eng = uno.Engine(cfg, w, max_seqs=1, max_seq_len=600, max_rows=64, seed=7102, tree_chains=K)
     ref = uno.Engine(cfg, w, max_seqs=K, max_seq_len=600, max_rows=64, seed=7102)
@@ -234,7 +266,7 @@ def test_tree_verify_bf16_8b_layers_match_plain_forwards():
     n = len(prompt) - 1
     ch, _ = eng.tree_draft([0], K)
     out, n_out, ks, pv = eng.tree_verify([0], K, want_probs=True)
-    ch, pv = host(ch)[0], host(pv)[0]
+    ch, pv = host(ch)[0], host(pv)[0].astype(np.float64)
     # reference: the pending token at n, then each chain's block at n+1..n+B
     ids = list(range(K))
     ref.forward(ids, 1, _i32(np.full(K, n)), dev(np.zeros(K, np.uint8)),
@@ -246,12 +278,18 @@ def test_tree_verify_bf16_8b_layers_match_plain_forwards():
     lg -= lg.max(-1, keepdims=True)
     P = np.exp(lg)
     P /= P.sum(-1, keepdims=True)
-    worst = 0.0
+    ex = _exact_chain_laws(cfg, wt, prompt, ch.astype(np.int64), pos)
+    t_tree = t_plain = t_pair = 0.0
     for k in range(K):
         for dt in range(1, B + 1):
-            worst = max(worst, float(_tv(pv[tree.verify_row(k, dt, B)], P[k, dt - 1])))
-    log(f"  max TV tree row vs plain forward {worst:.2e}")
-    assert worst <= TV_TOL
+            row = pv[tree.verify_row(k, dt, B)]
+            t_tree = max(t_tree, float(_tv(row, ex[k][dt - 1])))
+            t_plain = max(t_plain, float(_tv(P[k, dt - 1], ex[k][dt - 1])))
+            t_pair = max(t_pair, float(_tv(row, P[k, dt - 1])))
+    log(f"  max TV to the exact laws: tree rows {t_tree:.2e}, plain forwards {t_plain:.2e}; "
+        f"between them {t_pair:.2e}")
+    assert t_tree <= 1.25 * t_plain + 1e-4
+    assert t_pair <= 1e-2
     k_out, kstar = int(host(n_out)[0]), int(host(ks)[0])
     L = n + k_out
     assert eng.seq_state(0)[0] == L
