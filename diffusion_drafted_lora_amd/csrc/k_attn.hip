@@ -602,7 +602,6 @@ constexpr int kAttnRingMinChunk = UNO_ATTN_RING_MIN_CHUNK;   // shorter chunks: 
 static_assert(RNS >= 2 && RNS <= 4, "ring depth");
 constexpr int RSTAGE = RMK * HD * 2 * 2;        // one stage: K and V of RMK keys
 constexpr int RVOFF = RMK * HD * 2;             // V part of a stage
-constexpr int RLOADS = RSTAGE / 1024 / 4;       // 1 KB load instructions per wave and stage
 
 // Windowed rows (WIN: the distillation forward's [x, z1] rows, the tree verify's
 // chains) number their keys in whole pages: virtual pages below A16 = A rounded up
@@ -610,26 +609,38 @@ constexpr int RLOADS = RSTAGE / 1024 / 4;       // 1 KB load instructions per wa
 // down (A = max a, C = min c, over the tile's rows).  The two ranges may share a
 // page; each occurrence of a slot is masked by its own range -- slot < a in the
 // first, c <= slot <= d in the second -- so no row sees a slot twice.
-template <bool WIN>
-__global__ void __launch_bounds__(256, 1)
+//
+// RT row tiles per workgroup (RT x 4 waves; wave w takes query head w % 4 of its
+// KV head and row tile w / 4 of the group): the tiles share every K/V stage, so
+// long row sets (prefill, the distillation forward) stream their keys once per
+// RT * 16 rows.  The keys walked are the union of the group's rows' windows.
+template <bool WIN, int RT>
+__global__ void __launch_bounds__(256 * RT, 1)
 k_attn_ring(AttnArgs a, KvLayout kv) {
+  constexpr int NWV = 4 * RT, NTH = 256 * RT, NR = 16 * RT;
+  constexpr int RL = RSTAGE / 1024 / NWV;       // 1 KB load instructions per wave and stage
+  static_assert(RL >= 1 && RL * NWV * 1024 == RSTAGE, "stage loads split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16* sP = reinterpret_cast<bf16*>(smem_raw + (size_t)RNS * RSTAGE);   // [4][16][RPPAD]
-  __shared__ int sW[48];
+  bf16* sP = reinterpret_cast<bf16*>(smem_raw + (size_t)RNS * RSTAGE);   // [NWV][16][RPPAD]
+  __shared__ int sW[3 * NR];
   __shared__ int sPg[PGC];
 
   const int c = blockIdx.x, kvh = blockIdx.y;
-  const int row_tiles = (a.rows_per_seq + 15) / 16;
-  const int si = blockIdx.z / row_tiles, rt = blockIdx.z % row_tiles;
+  const int row_tiles = (a.rows_per_seq + 15) / 16, groups = (row_tiles + RT - 1) / RT;
+  const int si = blockIdx.z / groups, tg = blockIdx.z % groups;
   const int G = 4;
   const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[si];
-  const int r0 = si * a.rows_per_seq + rt * 16;
-  const int nrows = min(16, a.rows_per_seq - rt * 16);
+  const int rg0 = tg * NR;                                   // first row of the group
+  const int r0g = si * a.rows_per_seq + rg0;
+  const int nrows_g = min(NR, a.rows_per_seq - rg0);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, grp = lane >> 4;
+  const int wt = w >> 2;                                     // this wave's row tile
+  const int r0 = r0g + wt * 16;
+  const int nrows = max(0, min(16, nrows_g - wt * 16));
 
-  if (tid < 16) row_window(a, r0 + tid, tid < nrows, sW + tid, sW + 16 + tid, sW + 32 + tid);
-  const int head = kvh * G + w;
+  if (tid < NR) row_window(a, r0g + tid, tid < nrows_g, sW + tid, sW + NR + tid, sW + 2 * NR + tid);
+  const int head = kvh * G + (w & 3);
   const bf16* Q = reinterpret_cast<const bf16*>(a.q);
   bf16x8 qf[HD / 32];
   {
@@ -646,19 +657,21 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   int A16 = 0, C16 = 0, Am = 0, nv;
   if (WIN) {
     int am = 0, cm = INT_MAX, dm = -1;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NR; ++i) {
       am = max(am, sW[i]);
-      if (sW[16 + i] <= sW[32 + i]) { cm = min(cm, sW[16 + i]); dm = max(dm, sW[32 + i]); }
+      if (sW[NR + i] <= sW[2 * NR + i]) { cm = min(cm, sW[NR + i]); dm = max(dm, sW[2 * NR + i]); }
     }
-    Am = am;
-    A16 = (am + 15) & ~15;
-    C16 = dm >= cm ? (cm & ~15) : A16;
-    nv = A16 + (dm >= cm ? dm - C16 + 1 : 0);
+    // tile-wide values: scalars (every lane computed the same)
+    Am = __builtin_amdgcn_readfirstlane(am);
+    A16 = (Am + 15) & ~15;
+    C16 = __builtin_amdgcn_readfirstlane(dm >= cm ? (cm & ~15) : A16);
+    nv = __builtin_amdgcn_readfirstlane(A16 + (dm >= cm ? dm - C16 + 1 : 0));
   } else {
-    int At, Ct;
-    tile_window(sW, &At, &Ct, &nv);
+    int am = 0;
+    for (int i = 0; i < NR; ++i) am = max(am, sW[i]);
+    nv = __builtin_amdgcn_readfirstlane(am);
   }
-  publish_nc(a, c, kvh, tid, r0, nrows, nv);
+  publish_nc(a, c, kvh, tid, r0g, nrows_g, nv);
   const int kbeg = c * a.chunk;
   if (kbeg >= nv) return;
   const int kend = min(kbeg + a.chunk, nv);
@@ -668,7 +681,7 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   // entries outside the sequence's pages read page 0 (masked / zeroed below)
   const int p0 = kbeg >> 4, npg = nsub * RPG;
   const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
-  for (int i = tid; i < npg; i += 256) {
+  for (int i = tid; i < npg; i += NTH) {
     const int vp = p0 + i;
     const int pi = (WIN && vp >= (A16 >> 4)) ? (C16 >> 4) + vp - (A16 >> 4) : vp;
     int page = (pi < kv.max_pages_per_seq && (vp << 4) < kend) ? bt[pi] : 0;
@@ -679,13 +692,13 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   const bf16* vb0 = kv_block<const bf16>(kv, a.layer, 1, 0, kvh);
   __syncthreads();
 
-  // wave w issues the stage's load instructions w * RLOADS .. + RLOADS - 1: first
-  // the K pages (four instructions of four tokens each), then the V pages (four
+  // wave w issues the stage's load instructions w * RL .. + RL - 1: first the K
+  // pages (four instructions of four tokens each), then the V pages (four
   // instructions of 32 dims each)
   auto issue = [&](int sub, int slot) {
 #pragma unroll
-    for (int q = 0; q < RLOADS; ++q) {
-      const int ins = w * RLOADS + q, kind = ins / (4 * RPG), pg = (ins % (4 * RPG)) >> 2,
+    for (int q = 0; q < RL; ++q) {
+      const int ins = w * RL + q, kind = ins / (4 * RPG), pg = (ins % (4 * RPG)) >> 2,
                 part = ins & 3;
       const int page = sPg[sub * RPG + pg];
       const bf16* src;
@@ -712,9 +725,10 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   int lim[4], wc[4], wd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lim[i] = WIN ? sW[grp * 4 + i] : min(kend, sW[grp * 4 + i]);
-    wc[i] = WIN ? sW[16 + grp * 4 + i] : 0;
-    wd[i] = WIN ? sW[32 + grp * 4 + i] : 0;
+    const int ri = wt * 16 + grp * 4 + i;                  // row of the group
+    lim[i] = WIN ? sW[ri] : min(kend, sW[ri]);
+    wc[i] = WIN ? sW[NR + ri] : 0;
+    wd[i] = WIN ? sW[2 * NR + ri] : 0;
   }
   bf16* myP = sP + w * 16 * RPPAD;
 
@@ -724,8 +738,8 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
   for (int it = 0; it < nsub; ++it) {
     // this wave's loads of sub-chunk it are done once at most the later ones remain
     const int newer = min(RNS - 2, nsub - 1 - it);
-    if (newer >= 2) wait_vmcnt<2 * RLOADS>();
-    else if (newer == 1) wait_vmcnt<RLOADS>();
+    if (newer >= 2) wait_vmcnt<2 * RL>();
+    else if (newer == 1) wait_vmcnt<RL>();
     else wait_vmcnt<0>();
     __syncthreads();                 // every wave's loads landed; sub-chunk it - 1 consumed
     if (it + RNS - 1 < nsub) issue(it + RNS - 1, (it + RNS - 1) % RNS);
@@ -740,7 +754,7 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
     if (z0 < RMK || g0 < g1) {
       bf16* zV = reinterpret_cast<bf16*>(const_cast<char*>(stV));
       const int nz = RMK - z0, ng = g0 < g1 ? g1 - g0 : 0;
-      for (int e = tid; e < (nz + ng) * HD; e += 256) {
+      for (int e = tid; e < (nz + ng) * HD; e += NTH) {
         const int t = e / HD, d = e % HD;
         const int kk = t < nz ? z0 + t : g0 + (t - nz);
         const int pg = kk >> 4, tk = kk & 15, h = (tk >> 3) ^ ((d >> 3) & 1);
@@ -877,13 +891,25 @@ hipError_t launch_attention(const AttnArgs& a, const KvLayout& kv, hipStream_t s
     const bool ring = kv.page_size == 16 && a.chunk % 64 == 0 && a.chunk >= kAttnRingMinChunk &&
                       a.chunk <= PGC * 16;
     if (ring) {
-      const size_t rsmem = (size_t)RNS * RSTAGE + (size_t)G * 16 * RPPAD * 2;
-      const void* f = a.row_vis ? reinterpret_cast<const void*>(&k_attn_ring<true>)
-                                : reinterpret_cast<const void*>(&k_attn_ring<false>);
+      // 128 rows per sequence or more (prefill, the distillation forward): four row
+      // tiles per workgroup share each K/V stage; decode blocks keep one
+      const bool multi = a.rows_per_seq >= 128;
+      const int RTn = multi ? 4 : 1;
+      const size_t rsmem = (size_t)RNS * RSTAGE + (size_t)G * RTn * 16 * RPPAD * 2;
+      const void* f = multi ? (a.row_vis ? reinterpret_cast<const void*>(&k_attn_ring<true, 4>)
+                                         : reinterpret_cast<const void*>(&k_attn_ring<false, 4>))
+                            : (a.row_vis ? reinterpret_cast<const void*>(&k_attn_ring<true, 1>)
+                                         : reinterpret_cast<const void*>(&k_attn_ring<false, 1>));
       hipError_t ea = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rsmem);
       if (ea != hipSuccess) return ea;
-      if (a.row_vis) uno_launch(k_attn_ring<true>, grid, 256, (uint32_t)rsmem, s, a, kv);
-      else uno_launch(k_attn_ring<false>, grid, 256, (uint32_t)rsmem, s, a, kv);
+      if (multi) {
+        dim3 g4(a.n_chunks, kv.n_kv_heads, a.n * ((row_tiles + 3) / 4));
+        if (a.row_vis) uno_launch(k_attn_ring<true, 4>, g4, 1024, (uint32_t)rsmem, s, a, kv);
+        else uno_launch(k_attn_ring<false, 4>, g4, 1024, (uint32_t)rsmem, s, a, kv);
+      } else {
+        if (a.row_vis) uno_launch(k_attn_ring<true, 1>, grid, 256, (uint32_t)rsmem, s, a, kv);
+        else uno_launch(k_attn_ring<false, 1>, grid, 256, (uint32_t)rsmem, s, a, kv);
+      }
     } else if (a.row_vis) {
       uno_launch(k_attn_mfma<true>, grid, 64 * G, smem, s, a, kv);
     } else {
