@@ -653,6 +653,21 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
     }
   }
   const float sc = a.scale * 1.4426950408889634f;    // scores in the exp2 domain
+  // plain rows: the pages of the chunk's whole key range go out with the row and
+  // query loads (virtual page p is the sequence's page p); which of them the rows
+  // see is settled below.  Entries past the sequence's table read as -1.
+  const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
+  const int p0 = (c * a.chunk) >> 4;
+  constexpr int PPT = (PGC + NTH - 1) / NTH;
+  int praw[PPT];
+  if (!WIN) {
+    const int npg_max = a.chunk >> 4;          // the launcher keeps a.chunk <= PGC * 16
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int i = tid + k * NTH;
+      praw[k] = (i < npg_max && p0 + i < kv.max_pages_per_seq) ? bt[p0 + i] : -1;
+    }
+  }
   __syncthreads();
   int A16 = 0, C16 = 0, Am = 0, nv;
   if (WIN) {
@@ -679,13 +694,23 @@ k_attn_ring(AttnArgs a, KvLayout kv) {
 
   // pages of the chunk's keys (kbeg is a multiple of 64, so of the page size);
   // entries outside the sequence's pages read page 0 (masked / zeroed below)
-  const int p0 = kbeg >> 4, npg = nsub * RPG;
-  const int32_t* bt = kv.block_table + (size_t)seq * kv.max_pages_per_seq;
-  for (int i = tid; i < npg; i += NTH) {
-    const int vp = p0 + i;
-    const int pi = (WIN && vp >= (A16 >> 4)) ? (C16 >> 4) + vp - (A16 >> 4) : vp;
-    int page = (pi < kv.max_pages_per_seq && (vp << 4) < kend) ? bt[pi] : 0;
-    sPg[i] = (page >= 0 && page < kv.n_pages) ? page : 0;
+  const int npg = nsub * RPG;
+  if (WIN) {
+    for (int i = tid; i < npg; i += NTH) {
+      const int vp = p0 + i;
+      const int pi = vp >= (A16 >> 4) ? (C16 >> 4) + vp - (A16 >> 4) : vp;
+      int page = (pi < kv.max_pages_per_seq && (vp << 4) < kend) ? bt[pi] : 0;
+      sPg[i] = (page >= 0 && page < kv.n_pages) ? page : 0;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int i = tid + k * NTH;
+      if (i < npg) {
+        const int page = ((p0 + i) << 4) < kend ? praw[k] : 0;
+        sPg[i] = (page >= 0 && page < kv.n_pages) ? page : 0;
+      }
+    }
   }
   const size_t pstride = (size_t)kv.n_kv_heads * 16 * HD;
   const bf16* kb0 = kv_block<const bf16>(kv, a.layer, 0, 0, kvh);
