@@ -13,7 +13,8 @@ Reported: accepted tokens/s (value), positions/s, tokens per forward, whole-step
 algorithmic HBM GB/s, the roofline of the dominant kernel (the gate/up
 gated-LoRA linear, timed with HIP events on the library's stream), a per-class
 kernel time breakdown, batch-1 and batch-128 windows at contexts 1024, 5120 and 9216
-with their integrals over the 1K-in / 8K-out run, the nucleus (top-p) truncation
+with their integrals over the 1K-in / 8K-out run, the HBM floor of each batch-1
+linear launch shape (a read-only stream of its weight bytes), the nucleus (top-p) truncation
 kernel at the batch-1 and batch-128 row counts, and the CPU oracle timed on a
 bounded sample on the host (with its thread counts and a one-thread figure).
 """
@@ -426,6 +427,41 @@ def run_distill_backward(cfg, w, dev, batch, L, B, reps):
             "mfma_frac": fl / 1e9 / ms / BF16_PEAK_TFLOPS, "loss": lval, "grad_norm": gnorm}
 
 
+def run_stream_floor(cfg, reps):
+    """HBM floor of each batch-1 linear launch shape: uno_stream_read over the launch's
+    weight bytes with its grid (workgroups x threads, weight loads in flight per
+    thread), windows rotating over 2 GiB so that no launch is served from a cache;
+    `reps` back-to-back launches per shape timed with events on the current stream."""
+    import torch
+    from diffusion_drafted_lora_amd import uno
+    d, F, V = cfg.d_model, cfg.ffn_dim, cfg.vocab
+    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    # (name, weight bytes, workgroups, threads, loads in flight) of the verify launches
+    shapes = [("q|k|v", qkv * d * 2, qkv // 16, 8 * 64, 2),
+              ("o", d * cfg.n_q_heads * cfg.head_dim * 2, d // 16, 12 * 64, 2),
+              ("gate/up", 2 * F * d * 2, F // 16, 4 * 64, 8),
+              ("down", d * F * 2, d // 16, 12 * 64, 2),
+              ("lm_head", V * d * 2, V // 32, 4 * 64, 8)]
+    total = 2 << 30
+    buf = torch.zeros(total, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(max(s[2] for s in shapes), dtype=torch.int32, device="cuda:0")
+    out = {}
+    for name, nb, wg, th, ld in shapes:
+        nb = nb // 16 * 16
+        uno.stream_read(buf, nb, wg, th, ld, sink, reps=2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        uno.stream_read(buf, nb, wg, th, ld, sink, reps=reps)     # one call: no host gaps
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        out[name] = {"MB": nb / 1e6, "workgroups": wg, "threads": th, "loads_in_flight": ld,
+                     "us_per_launch": us, "GB/s": nb / 1e3 / us}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_top_p(V, rows_list, top_p=0.95, reps=20):
     """Nucleus truncation (uno_top_p) on float32 probability rows of the model's
     vocabulary: softmax rows of N(0, 3^2) logits, out of place.  Timed with HIP
@@ -577,6 +613,8 @@ def main():
                     help="chain counts of the tree-sampler leg")
     ap.add_argument("--qk-norm-steps", type=int, default=40,
                     help="timed steps of the batch-1 QK-norm leg (0: skip)")
+    ap.add_argument("--stream-floor-reps", type=int, default=20,
+                    help="launches per shape of the read-only stream floor leg (0: skip)")
     ap.add_argument("--no-top-p-leg", dest="top_p_leg", action="store_false",
                     help="skip timing the nucleus truncation at the batch-1 / batch-128 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -743,6 +781,9 @@ def main():
         if args.distill_backward_reps > 0:
             result["distill_backward"] = run_distill_backward(cfg, w, dev, db, dl, dbs,
                                                               args.distill_backward_reps)
+    if args.stream_floor_reps > 0:
+        log("stream floor of the batch-1 linear launch shapes")
+        result["stream_floor"] = run_stream_floor(cfg, args.stream_floor_reps)
     if args.top_p_leg:
         # one launch filters the B draft (or verify) rows of every sequence
         result["top_p"] = run_top_p(cfg.vocab, [B, 128 * B])

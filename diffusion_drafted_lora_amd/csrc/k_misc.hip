@@ -286,6 +286,40 @@ __global__ void k_kv_copy(KvLayout kv, int seq, int len, T* k, T* v, int to_page
   }
 }
 
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Read-only stream of n16 16-byte words: thread t reads words t, t + T, t + 2T, ...
+// (T threads in the grid; each wave's loads are 1 KB contiguous), U loads in flight
+// per thread, nontemporal like the linear kernels' weight stream; the xor of what a
+// workgroup read goes to sink[workgroup], so the loads cannot be dropped.
+template <int U>
+__global__ void __launch_bounds__(1024)
+k_stream_read(const i32x4_t* __restrict__ src, size_t n16, int32_t* sink) {
+  __shared__ int red[16];
+  const size_t T = (size_t)gridDim.x * blockDim.x;
+  i32x4_t acc = {0, 0, 0, 0};
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += U * T) {
+    i32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t j = i + (size_t)u * T;
+      v[u] = j < n16 ? __builtin_nontemporal_load(src + j) : i32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  int x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int r = 0;
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) r ^= red[w];
+    sink[blockIdx.x] = r;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rows_setup(const RowsSetup& a, hipStream_t s) {
@@ -374,3 +408,17 @@ hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int 
   template hipError_t launch_kv_copy<T>(const KvLayout&, int, int, T*, T*, int, hipStream_t);
 UNO_INST(float)
 UNO_INST(bf16)
+
+hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, int loads,
+                              int32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const i32x4_t* p = static_cast<const i32x4_t*>(src);
+  switch (loads) {
+    case 1: uno_launch(k_stream_read<1>, workgroups, threads, 0, s, p, n16, sink); break;
+    case 2: uno_launch(k_stream_read<2>, workgroups, threads, 0, s, p, n16, sink); break;
+    case 4: uno_launch(k_stream_read<4>, workgroups, threads, 0, s, p, n16, sink); break;
+    case 8: uno_launch(k_stream_read<8>, workgroups, threads, 0, s, p, n16, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

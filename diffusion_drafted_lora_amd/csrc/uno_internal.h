@@ -423,6 +423,11 @@ struct SetList {            // small device scatter passed by value: dst[idx[i]]
   int32_t val[240];
 };
 hipError_t launch_set_list(const SetList& l, hipStream_t s);
+// Read-only stream of `bytes` (a multiple of 16) by workgroups x threads threads,
+// `loads` (1, 2, 4 or 8) 16-byte loads in flight per thread; sink: one int32 per
+// workgroup.
+hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, int loads,
+                              int32_t* sink, hipStream_t s);
 
 template <typename T>
 hipError_t launch_kv_copy(const KvLayout& kv, int seq, int len, T* k, T* v, int to_pages,

@@ -1246,6 +1246,26 @@ uno_status uno_top_p(const float* d_in, float* d_out, int32_t rows, int32_t voca
   return UNO_OK;
 }
 
+uno_status uno_stream_read(const void* d_src, size_t region_bytes, size_t bytes, int32_t reps,
+                           int32_t workgroups, int32_t threads, int32_t loads, int32_t* d_sink,
+                           void* stream) {
+  if (!d_src || !d_sink || bytes == 0 || bytes % 16 || bytes > region_bytes || reps < 1 ||
+      workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 ||
+      (loads != 1 && loads != 2 && loads != 4 && loads != 8))
+    return fail(nullptr, UNO_ERR_INVALID_ARG,
+                "stream_read: buffers, bytes a multiple of 16 within the region, reps >= 1, "
+                "64..1024 threads (multiple of 64), loads 1, 2, 4 or 8 required");
+  const size_t nwin = region_bytes / bytes;
+  for (int32_t i = 0; i < reps; ++i) {
+    const char* p = static_cast<const char*>(d_src) + (size_t)(i % nwin) * bytes;
+    hipError_t e = launch_stream_read(p, bytes, workgroups, threads, loads, d_sink,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(nullptr, UNO_ERR_DEVICE, std::string("stream_read: ") + hipGetErrorString(e));
+  }
+  return UNO_OK;
+}
+
 uno_status uno_query_sizes(const uno_config* cfg, size_t* kv_pool_bytes, size_t* workspace_bytes) {
   uno_status s = check_config(cfg);
   if (s) return s;

@@ -27,7 +27,7 @@ EXPORTED = ("uno_query_sizes", "uno_init", "uno_prefill", "uno_draft", "uno_veri
             "uno_set_trace", "uno_query_backward_bytes", "uno_set_distill_checkpoint",
             "uno_tv_backward", "uno_lm_head_backward", "uno_lora_layer_backward",
             "uno_distill_backward", "uno_tree_draft", "uno_tree_verify", "uno_tree_step",
-            "uno_tree_accept")
+            "uno_tree_accept", "uno_stream_read")
 
 # kernel classes of uno_timing (uno_kernel_class)
 KC = {"linear": 0, "linear_swiglu": 1, "lora_down": 2, "attention": 3, "lm_head": 4,
@@ -123,6 +123,7 @@ def lib():
         L.uno_distill_backward.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                            P(vp), P(vp), vp, C.c_size_t]
         L.uno_timing.argtypes = [vp, C.c_uint32]
+        L.uno_stream_read.argtypes = [vp, C.c_size_t, C.c_size_t, i32, i32, i32, i32, vp, vp]
         L.uno_timing_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double), P(C.c_double),
                                       P(C.c_double)]
         for name in EXPORTED:
@@ -565,6 +566,22 @@ def top_p(probs, p, out=None):
     if st != UNO_OK:
         raise UnoError(st, lib().uno_last_error(None).decode())
     return out
+
+
+def stream_read(src, nbytes, workgroups, threads, loads, sink, reps=1):
+    """uno_stream_read: `reps` read-only launches of nbytes each, over windows
+    rotating through the device tensor src (sink: int32 device tensor of at least
+    `workgroups` entries), on the current stream."""
+    import torch
+    region = src.numel() * src.element_size()
+    if not (src.is_cuda and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= workgroups
+            and nbytes <= region):
+        raise ValueError("stream_read: device buffers of the right sizes required")
+    st = lib().uno_stream_read(_ptr(src), int(region), int(nbytes), int(reps), int(workgroups),
+                               int(threads), int(loads), _ptr(sink),
+                               C.c_void_p(torch.cuda.current_stream(src.device).cuda_stream))
+    if st != UNO_OK:
+        raise UnoError(st, lib().uno_last_error(None).decode())
 
 
 def tv_backward(teacher, student, n_rows_total=None, dlogits=None, tv_row=None):

@@ -158,6 +158,20 @@ uno_status uno_pack_weight(const void* d_src, void* d_dst, int32_t rows, int32_t
 uno_status uno_top_p(const float* d_in, float* d_out, int32_t rows, int32_t vocab, float top_p,
                      void* stream);
 
+/* Measurement helper, not a step of the method: `reps` back-to-back launches, launch
+ * i reading `bytes` (a multiple of 16) of device memory at d_src + (i mod w) * bytes,
+ * w = region_bytes / bytes, with `workgroups` workgroups of `threads` threads
+ * (64..1024, a multiple of 64), each thread keeping `loads` (1, 2, 4 or 8)
+ * nontemporal 16-byte loads in flight -- the weight stream of a linear launch
+ * without its products, so the time per launch is the HBM floor of that launch
+ * shape (a region well above the memory-side cache keeps every window in HBM).
+ * d_sink: device int32 [workgroups], receives the xor of what each workgroup of the
+ * last launch read.  Enqueued on `stream` (a hipStream_t; NULL: the null stream).
+ * UNO_ERR_INVALID_ARG on a null buffer or a size outside these ranges. */
+uno_status uno_stream_read(const void* d_src, size_t region_bytes, size_t bytes, int32_t reps,
+                           int32_t workgroups, int32_t threads, int32_t loads, int32_t* d_sink,
+                           void* stream);
+
 /* Sizes of the caller-allocated KV pool and workspace for a config.
  * KV pool layout (exposed for inspection only; use uno_kv_import/export):
  * [layer][K|V][page][kv_head] blocks of page_size x head_dim of the storage type,
