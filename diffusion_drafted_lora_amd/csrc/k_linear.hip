@@ -76,12 +76,17 @@ UNO_DEV T* kv_dst(const KvLayout& kv, int layer, int which, int seq, int slot, i
 // partner).  Every thread of a 16-lane row group calls this (row sums use
 // shuffles); `ok` says whether row m exists.
 // Epilogue operands that do not depend on the product, which the skinny kernel
-// loads before its K loop: the residual values and next-norm gains of the
-// thread's columns (EPI_RESID) and the row's position (EPI_QKV).
+// loads before or during its K loop: the residual values and next-norm gains of
+// the thread's columns (EPI_RESID); the row's position and, once it has landed,
+// the rotation of the thread's pair and the K/V page of the row's slot (EPI_QKV).
 template <int NT> struct EpiPre {
   float res[NT];
   float g[NT];
   int pos;
+  float cs, sn;   // EPI_QKV, q and k tiles: cos / sin of the thread's pair at pos
+  int page;       // EPI_QKV, k and v tiles: page of the row's slot (-1: outside)
+  int seq;        // EPI_QKV, k and v tiles: the row's sequence
+  bool rot;       // cs, sn, page and seq are loaded
 };
 
 template <typename T, int NT, int EPI = -1>
@@ -136,6 +141,7 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       const int i = 8 * j + (c & 7);                 // pair index within the head
       const int dim = (c < 8) ? i : half + i;
       const int pos = pre ? pre->pos : a.row_pos[m];
+      const bool rot = pre && pre->rot;
       const int Hq = a.n_q_heads, Hkv = a.kv.n_kv_heads;
       float val = v[0];
       if (head < Hq + Hkv) {                         // q or k: rotate the pair
@@ -144,7 +150,8 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
           break;
         }
         const float x1 = c < 8 ? v[0] : vp, x2 = c < 8 ? vp : v[0];
-        const float cs = a.rcos[(size_t)pos * half + i], sn = a.rsin[(size_t)pos * half + i];
+        const float cs = rot ? pre->cs : a.rcos[(size_t)pos * half + i];
+        const float sn = rot ? pre->sn : a.rsin[(size_t)pos * half + i];
         val = (c < 8) ? x1 * cs - x2 * sn : x2 * cs + x1 * sn;
       }
       if (head < Hq) {
@@ -152,9 +159,15 @@ UNO_DEV void epilogue(const GemmArgs& a, int m, int c, int tile0, int col_paired
       } else {
         const int which = head < Hq + Hkv ? 0 : 1;
         const int h = head - Hq - which * Hkv;
-        const int seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[m / a.rows_per_seq];
+        const int seq = rot ? pre->seq : a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[m / a.rows_per_seq];
         const int slot = a.row_slot ? a.row_slot[m] : pos;
-        T* dst = kv_dst<T>(a.kv, a.layer, which, seq, slot, h, a.err);
+        T* dst;
+        if (rot) {
+          if (pre->page < 0 && a.err) atomicOr(a.err, UNO_DEVERR_BOUNDS);
+          dst = pre->page < 0 ? nullptr : kv_block<T>(a.kv, a.layer, which, pre->page, h);
+        } else {
+          dst = kv_dst<T>(a.kv, a.layer, which, seq, slot, h, a.err);
+        }
         if (dst) dst[kv_elem(a.kv, which, slot % a.kv.page_size, dim)] = from_f<T>(val);
       }
       break;
@@ -412,10 +425,33 @@ k_gemm_bf16(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u], bw[t][u], acc[t], 0, 0, 0);
   };
+  // q|k|v: the rotation and page loads depend on the row's position, so they go out
+  // once the first ring round is in flight and land during the weight stream
+  auto late_pre = [&]() {
+    if (a.epi != EPI_QKV || threadIdx.x >= 256) return;
+    const int e = threadIdx.x & 255, m = mt * 16 + (e >> 4), c = e & 15;
+    if (m >= a.M) return;
+    const int hd = a.kv.head_dim, half = hd / 2, tph = hd / 16;
+    const int head = tile0 / tph, i = 8 * (tile0 % tph) + (c & 7);
+    const int Hq = a.n_q_heads, Hkv = a.kv.n_kv_heads, pos = pre.pos;
+    pre.cs = pre.sn = 0.0f;
+    pre.page = -1;
+    pre.seq = 0;
+    if (head < Hq + Hkv && pos >= 0 && pos < a.kv.max_pages_per_seq * a.kv.page_size) {
+      pre.cs = a.rcos[(size_t)pos * half + i];
+      pre.sn = a.rsin[(size_t)pos * half + i];
+    }
+    if (head >= Hq) {
+      pre.seq = a.seq_fixed > 0 ? a.seq_fixed - 1 : a.call_seq[m / a.rows_per_seq];
+      pre.page = kv_page(a.kv, pre.seq, a.row_slot ? a.row_slot[m] : pos);
+    }
+    pre.rot = true;
+  };
   int j = jb;
   if (nfull > 0) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) fill(u, j + u);
+    late_pre();
     for (int i = 1; i < nfull; ++i) {
       j += KU;
 #pragma unroll
@@ -434,6 +470,7 @@ k_gemm_bf16(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       if (u < rem) fill(u, j + u);
+    late_pre();
   }
 #pragma unroll
   for (int u = 0; u < KU; ++u)
