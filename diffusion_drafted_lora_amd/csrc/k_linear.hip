@@ -357,33 +357,16 @@ k_gemm_bf16(GemmArgs a) {
     ssq0 = sp[0];
     ssq1 = sp[1];
   }
-  // (b) LoRA: wave w's first rank block -- the raw fixed-point t of its row and
-  // the up-projection fragment
-  // (four-tile LM-head instances have no adapter and keep their registers)
+  // (b) LoRA: wave w takes rank block w.  Its row's gate is read here; the raw
+  // fixed-point t and the up-projection fragment are read after the weight stream
+  // (a fused launch's intermediate is only ready then), which keeps their
+  // registers free during the ring, so more workgroups fit a CU.
+  // (four-tile LM-head instances have no adapter)
   constexpr bool kPreLora = NT <= 2;
-  // (a fused launch's intermediate is only ready after the wait below: then just the
-  // up-projection fragment is loaded here)
   const bool fused = a.sync != nullptr;
   const bool lora_pre = kPreLora && a.r > 0 && w < nrb && Uu[0] == nullptr;
-  i64x2 tq[NT][4];
-  bf16x8 bq[NT];
   bool gate_on = false;
-  if (lora_pre) {
-    gate_on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      bq[t] = bf16x8{};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) tq[t][q] = i64x2{0, 0};
-      if (Up[t] == nullptr || Bp[t] == nullptr) continue;
-      if (row_ok && !fused) {
-        const i64x2* tp = reinterpret_cast<const i64x2*>(Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tq[t][q] = tp[q];
-      }
-      bq[t] = load8(Bp[t] + (size_t)w * 512);
-    }
-  }
+  if (lora_pre) gate_on = row_ok && (a.gate == nullptr || a.gate[m_lane] != 0);
   // (c) epilogue operands of this thread's output element (threads 0..255)
   EpiPre<NT> pre{};
   {
@@ -507,16 +490,29 @@ k_gemm_bf16(GemmArgs a) {
       }
     }
     __syncthreads();
-    if (lora_pre && gate_on) {
+  }
+  // the wave's first rank block: fixed-point t of its row and the LoRA-up fragment
+  i64x2 tq[NT][4];
+  bf16x8 bq[NT];
+  if (lora_pre) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (Up[t] == nullptr || Bp[t] == nullptr) continue;
-        const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq;
+    for (int t = 0; t < NT; ++t) {
+      bq[t] = bf16x8{};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tq[t][q] = i64x2{0, 0};
+      if (Up[t] == nullptr || Bp[t] == nullptr) continue;
+      bq[t] = load8(Bp[t] + (size_t)w * 512);
+      if (!gate_on) continue;
+      const long long* tp = Up[t] + (size_t)m_lane * ldu[t] + w * 32 + kq;
+      if (fused) {          // published by this launch's producers
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           tq[t][q].x = __hip_atomic_load(tp + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           tq[t][q].y = __hip_atomic_load(tp + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tq[t][q] = reinterpret_cast<const i64x2*>(tp)[q];
       }
     }
   }
