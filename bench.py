@@ -427,6 +427,20 @@ def run_distill_backward(cfg, w, dev, batch, L, B, reps):
             "mfma_frac": fl / 1e9 / ms / BF16_PEAK_TFLOPS, "loss": lval, "grad_norm": gnorm}
 
 
+def stream_floor_shapes(cfg):
+    """(name, bf16 weight bytes, workgroups, threads, weight loads in flight per thread)
+    of the batch-1 verify launches of the few-row linear kernel: one workgroup per 16
+    output columns (q|k|v, o, down: one 16-column tile; gate/up: a 16-column gate and
+    up pair; LM head: two tiles), waves x 64 threads, tiles x blocks in flight."""
+    d, F, V = cfg.d_model, cfg.ffn_dim, cfg.vocab
+    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    return [("q|k|v", qkv * d * 2, qkv // 16, 8 * 64, 1 * 2),
+            ("o", d * cfg.n_q_heads * cfg.head_dim * 2, d // 16, 12 * 64, 1 * 2),
+            ("gate/up", 2 * F * d * 2, F // 16, 4 * 64, 2 * 4),
+            ("down", d * F * 2, d // 16, 12 * 64, 1 * 2),
+            ("lm_head", V * d * 2, V // 32, 4 * 64, 2 * 4)]
+
+
 def run_stream_floor(cfg, reps):
     """HBM floor of each batch-1 linear launch shape: uno_stream_read over the launch's
     weight bytes with its grid (workgroups x threads, weight loads in flight per
@@ -434,14 +448,7 @@ def run_stream_floor(cfg, reps):
     `reps` back-to-back launches per shape timed with events on the current stream."""
     import torch
     from diffusion_drafted_lora_amd import uno
-    d, F, V = cfg.d_model, cfg.ffn_dim, cfg.vocab
-    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
-    # (name, weight bytes, workgroups, threads, loads in flight) of the verify launches
-    shapes = [("q|k|v", qkv * d * 2, qkv // 16, 8 * 64, 2),
-              ("o", d * cfg.n_q_heads * cfg.head_dim * 2, d // 16, 12 * 64, 2),
-              ("gate/up", 2 * F * d * 2, F // 16, 4 * 64, 8),
-              ("down", d * F * 2, d // 16, 12 * 64, 2),
-              ("lm_head", V * d * 2, V // 32, 4 * 64, 8)]
+    shapes = stream_floor_shapes(cfg)
     total = 2 << 30
     buf = torch.zeros(total, dtype=torch.uint8, device="cuda:0")
     sink = torch.zeros(max(s[2] for s in shapes), dtype=torch.int32, device="cuda:0")

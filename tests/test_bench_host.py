@@ -47,3 +47,20 @@ def test_run_bytes_per_iteration_counts_weights_lora_and_mean_context():
     assert bench.kv_bytes_per_pos(cfg) == 147456
     b = bench.run_bytes_per_iteration(cfg, [1024, 5120, 9216])
     assert abs(b - (2 * fixed + lora + 147456 * (2 * 5120 + 32))) < 1
+
+
+def test_stream_floor_shapes_match_the_batch1_launches():
+    """The read-only streams mirror the few-row launches of the 8B shape: the grids the
+    kernel trace shows (q|k|v 384 x 512 threads, o and down 256 x 768, gate/up 768 x 256,
+    LM head 4748 x 256) and each launch's weight bytes."""
+    from diffusion_drafted_lora_amd import configs
+    cfg = configs.MODEL8B
+    sh = {n: (b, wg, th, ld) for n, b, wg, th, ld in bench.stream_floor_shapes(cfg)}
+    assert sh["q|k|v"] == (6144 * 4096 * 2, 384, 512, 2)
+    assert sh["o"] == (4096 * 4096 * 2, 256, 768, 2)
+    assert sh["gate/up"] == (2 * 12288 * 4096 * 2, 768, 256, 8)
+    assert sh["down"] == (12288 * 4096 * 2, 256, 768, 2)
+    assert sh["lm_head"] == (151936 * 4096 * 2, 4748, 256, 8)
+    # every shape's bytes split into whole 16-byte words over whole waves
+    for b, wg, th, ld in sh.values():
+        assert b % 16 == 0 and th % 64 == 0 and ld in (1, 2, 4, 8)
