@@ -99,6 +99,56 @@ def test_decode_iterations_match_oracle(stress, top_p):
     eng.sync()
 
 
+@pytest.mark.parametrize("B,laws", [(1, "stress"), (2, "stress"), (7, "stress"), (16, "stress"),
+                                     (2, "flat"), (7, "flat"), (16, "flat")])
+def test_decode_block_sizes_match_oracle(B, laws):
+    """The linear sampler at block sizes other than the tiny model's 4: B = 1 (the
+    draft holds only the AR slot, so every iteration emits exactly 2 tokens), B = 2,
+    a ragged B = 7 and the 8B workload's B = 16; 6 iterations of 3 ragged sequences,
+    tokens, accept lengths, laws and cache against the oracle.  "stress" weights
+    give draft laws far from the AR laws (short accepted prefixes); "flat" weights
+    (LM head N(0, 1e-3)) make every law nearly uniform, so whole blocks are accepted
+    and the bonus token past the block is drawn from the verify law."""
+    log(f"tiny decode block size {B}, {laws} laws")
+    cfg = TINY.with_(block_size=B)
+    w = synth.weights_numpy(cfg, 1001, lm_head_std=0.35, lora_b_std=0.6) if laws == "stress" \
+        else synth.weights_numpy(cfg, 1002, lm_head_std=1e-3)
+    S, seed, iters = 3, 3100 + B, 6
+    lens = [16, 5, 1]
+    prompts = [synth.prompts(cfg, 2100 + i, 1, L)[0] for i, L in enumerate(lens)]
+    seq_ids = [2, 0, 1]
+    max_len = cfg.prompt_len + iters * (B + 1) + B + 2
+    eng = engine(cfg, w, max_seqs=S, max_seq_len=max_len, seed=seed)
+    eng.prefill(seq_ids, prompts)
+    dec = psispec.Decoder(cfg, w, seq_ids, seed, max_len)
+    dec.prefill(prompts)
+    hist = []
+    for step in range(iters):
+        y_g, pd_g = eng.draft(seq_ids, want_probs=True)
+        out_g, n_g, pv_g = eng.verify(seq_ids, want_probs=True)
+        r = dec.step()
+        pd, pv = host(pd_g), host(pv_g)
+        assert _tv(pd, r["P_d"]).max() <= TV_TOL
+        assert _tv(pv, r["P_v"]).max() <= TV_TOL
+        assert np.array_equal(host(y_g), r["y"].astype(np.int32)), step
+        assert np.array_equal(host(n_g), r["n_out"]), step
+        assert np.array_equal(host(out_g), r["out"]), step
+        hist += r["n_out"].tolist()
+    for i, s in enumerate(seq_ids):
+        L, t, it = eng.seq_state(s)
+        assert (L, t, it) == (int(dec.n[i]), int(dec.t[i]), int(dec.it[i]))
+        k, v = eng.kv_export(s, L)
+        assert np.abs(host(k) - dec.cache["k"][:, i, :L]).max() <= 1e-5
+        assert np.abs(host(v) - dec.cache["v"][:, i, :L]).max() <= 1e-5
+    assert min(hist) >= 2 and max(hist) <= B + 1
+    if B == 1:
+        assert set(hist) == {2}
+    if laws == "flat":
+        assert max(hist) == B + 1
+    log(f"  accept lengths {sorted(set(hist))}")
+    eng.sync()
+
+
 def test_top_p_config_filters_draft_bit_exact():
     """The top_p config field applies exactly the nucleus rule to the softmax rows:
     two contexts on the same weights and seed, one with top_p 0.9, give draft laws
