@@ -310,6 +310,26 @@ def integrate_windows(windows, batch, B):
             "positions_per_s": batch * 2 * B / (mean_ms / 1e3)}
 
 
+# Tokens per forward of trained Uno models (shibing624 reading notes of the Uno paper,
+# "实验" section: 2.25 before and 2.10 after RL with the adapter frozen, part "RL 加速与
+# 漂移问题"; 4.21 for Uno_Qwen on MBPP in the comparison with lossy methods, part
+# "战线二").  Random-init weights accept far less, so the measured TPF is much lower.
+PAGES_TPF = (2.10, 2.25, 4.21)
+
+
+def tpf_projection(ms_per_step, batch, tpfs=PAGES_TPF):
+    """Accepted tokens/s of a leg at the trained models' tokens per forward, holding its
+    measured iteration time: an iteration runs the same two forwards of B rows whatever
+    is accepted (acceptance only sets how many positions are committed), so the rate
+    scales with TPF.  A projection, not a measurement; over a whole 1K-in / 8K-out run a
+    higher TPF also means fewer iterations at the same mean context."""
+    if not ms_per_step or ms_per_step <= 0:
+        return None
+    return {"kind": "projection", "basis": "measured ms per iteration x tokens per forward",
+            "ms_per_step": ms_per_step,
+            "accepted_tokens_per_s": {f"{t:.2f}": batch * 2 * t / (ms_per_step / 1e3) for t in tpfs}}
+
+
 def run_distill(cfg, w, dev, batch, L, B, reps):
     """The [x, z1] distillation forward: `batch` sequences of L uniform clean tokens
     with L MASK tokens, block size B; teacher and student logits written to
@@ -753,6 +773,7 @@ def main():
             "launches": n_sw, "sampled_every": ROOFLINE_EVERY,
         },
         "breakdown": breakdown,
+        "tpf_projection": tpf_projection(1e3 * sec / K, 1),
     }
     eng.close()
     del eng
@@ -767,6 +788,7 @@ def main():
             run["hbm_gbs_algorithmic"] = run_bytes_per_iteration(cfg, run["contexts"]) / 1e9 / \
                 (run["mean_ms_per_step"] / 1e3)
             run["hbm_frac"] = run["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
+            run["tpf_projection"] = tpf_projection(run["mean_ms_per_step"], 1)
     if args.qk_norm_steps > 0:
         result["qk_norm"] = run_qk_norm(cfg, w, dev, args.qk_norm_steps, 4, args.prompt)
     if args.tree_steps > 0:
@@ -776,6 +798,9 @@ def main():
         result["bs128"] = [run_batch(cfg, w, dev, 128, int(c), args.bs128_steps, 2, args.prompt)
                            for c in args.bs128_ctx.split(",")]
         result["bs128_run"] = integrate_windows(result["bs128"], 128, B)
+        if result["bs128_run"]:
+            result["bs128_run"]["tpf_projection"] = tpf_projection(
+                result["bs128_run"]["mean_ms_per_step"], 128)
     if args.distill != "none":
         db, dl, dbs = (int(v) for v in args.distill.split(","))
         result["distill"] = run_distill(cfg, w, dev, db, dl, dbs, args.distill_reps)

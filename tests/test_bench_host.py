@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (no GPU): integrating the batch windows over a run,
-and reporting counter traffic only for the kernel sources it was measured on."""
+reporting counter traffic only for the kernel sources it was measured on, and the
+projection of a leg to the trained models' tokens per forward."""
 import bench
 
 
@@ -64,3 +65,17 @@ def test_stream_floor_shapes_match_the_batch1_launches():
     # every shape's bytes split into whole 16-byte words over whole waves
     for b, wg, th, ld in sh.values():
         assert b % 16 == 0 and th % 64 == 0 and ld in (1, 2, 4, 8)
+
+
+def test_tpf_projection_scales_the_measured_iteration():
+    # 8 ms per iteration at batch 1: TPF 2.10 -> 2 * 2.10 tokens per 8 ms = 525 tokens/s
+    p = bench.tpf_projection(8.0, 1)
+    assert p["kind"] == "projection"
+    assert set(p["accepted_tokens_per_s"]) == {"2.10", "2.25", "4.21"}
+    assert abs(p["accepted_tokens_per_s"]["2.10"] - 525.0) < 1e-9
+    # batch 128 at 100 ms: 128 * 2 * 4.21 / 0.1 s
+    q = bench.tpf_projection(100.0, 128)
+    assert abs(q["accepted_tokens_per_s"]["4.21"] - 128 * 2 * 4.21 / 0.1) < 1e-6
+    # every projection stays within the method's bound TPF <= (B + 1) / 2 at B = 16
+    assert max(bench.PAGES_TPF) <= (16 + 1) / 2
+    assert bench.tpf_projection(0.0, 1) is None
