@@ -218,6 +218,69 @@ def test_state_errors(w_np):
     eng.sync()
 
 
+def test_page_pool_and_length_limits_leave_state_intact():
+    """Capacity limits during decode: a step that needs more KV pages than the pool has
+    left fails with OUT_OF_PAGES and changes nothing (lengths, pending tokens, cache);
+    after the other sequence is released the same sequence steps on and matches an
+    oracle decoder of that sequence alone; a step that could write past max_seq_len
+    fails with INVALID_ARG, again leaving the state and cache as they were, and no
+    device flag is raised.  The pool holds 5 pages of 16 positions for two sequences
+    of up to 64 (4 pages each)."""
+    from diffusion_drafted_lora_amd import uno
+    log("tiny decode at the page-pool and length limits")
+    w = synth.weights_numpy(TINY, 1001, lm_head_std=0.35, lora_b_std=0.6)
+    seed, max_len = 3300, 64
+    prompts = [synth.prompts(TINY, 2300 + i, 1, 16)[0] for i in range(2)]
+    eng = engine(TINY, w, max_seqs=2, max_seq_len=max_len, n_pages=5, seed=seed)
+    eng.prefill([0, 1], prompts)
+    decs = []
+    for s in (0, 1):
+        d = psispec.Decoder(TINY, w, [s], seed, max_len)
+        d.prefill([prompts[s]])
+        decs.append(d)
+
+    def states(ids):
+        return [eng.seq_state(s) for s in ids]
+
+    def check_step(ids):
+        out, n_out = eng.step(ids)
+        for j, s in enumerate(ids):
+            r = decs[s].step()
+            assert int(host(n_out)[j]) == int(r["n_out"][0])
+            assert np.array_equal(host(out)[j], r["out"][0])
+
+    for _ in range(60):
+        before = states([0, 1])
+        try:
+            check_step([0, 1])
+        except uno.UnoError as e:
+            assert e.status == 2, e
+            assert states([0, 1]) == before
+            break
+    else:
+        pytest.fail("the 5-page pool never ran out")
+    log(f"  pool exhausted at lengths {[b[0] for b in before]}")
+    eng.release(1)
+    for _ in range(60):
+        before = states([0])
+        try:
+            check_step([0])
+        except uno.UnoError as e:
+            assert e.status == 1, e
+            assert states([0]) == before
+            break
+    else:
+        pytest.fail("max_seq_len was never reached")
+    L, t, it = before[0]
+    log(f"  length limit at length {L}")
+    assert L + TINY.block_size + 1 > max_len
+    assert (L, t, it) == (int(decs[0].n[0]), int(decs[0].t[0]), int(decs[0].it[0]))
+    k, v = eng.kv_export(0, L)
+    assert np.abs(host(k) - decs[0].cache["k"][:, 0, :L]).max() <= 1e-5
+    assert np.abs(host(v) - decs[0].cache["v"][:, 0, :L]).max() <= 1e-5
+    eng.sync()
+
+
 def test_timing_records_every_nth_call(w_np):
     """Kernel timing: every call of an enabled class is recorded by default; with
     a period n only the first of every n calls is, and the untimed calls still
